@@ -1,0 +1,30 @@
+"""DSpark draft -> schedule -> verify hot path on MI355X (gfx950).
+
+The compute lives in libdspark.so (hand-written HIP kernels behind the C ABI
+declared in include/dspark.h).  This package is a thin ctypes binding with the
+same names as the C entry points; PyTorch only provides device memory and the
+stream.  ``workloads`` holds the seeded synthetic input generators.
+
+The binding is loaded on first use and raises if the library is not built:
+there is no fallback path.
+"""
+
+_BINDING_NAMES = {
+    "dspark_markov_draft", "dspark_schedule", "dspark_verify",
+    "dspark_markov_draft_workspace_bytes", "dspark_verify_workspace_bytes",
+    "dspark_status_string", "dspark_version", "dspark_uniforms",
+    "dspark_profiler_enable", "dspark_profiler_reset", "dspark_profiler_read",
+    "DSparkError", "load_library", "library_path",
+    "DSPARK_F32", "DSPARK_BF16",
+    "DSPARK_SCHED_EARLY_STOP", "DSPARK_SCHED_GLOBAL", "DSPARK_SCHED_TOPK",
+}
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
+
+
+__all__ = sorted(_BINDING_NAMES)

@@ -1,0 +1,252 @@
+"""ctypes binding of libdspark (argument marshalling only).
+
+Each function takes torch tensors on the GPU, checks dtype / shape /
+contiguity, allocates the outputs and the workspace if the caller passes
+none, and calls the C entry point of the same name on the current torch
+stream.  Every step of the method runs in the library's HIP kernels.
+"""
+import ctypes
+import os
+
+import torch
+
+from ._build import lib_path as _lib_path
+
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+DSPARK_SCHED_EARLY_STOP = 0
+DSPARK_SCHED_GLOBAL = 1
+DSPARK_SCHED_TOPK = 2
+
+_lib = None
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.dspark_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+def library_path():
+    return _lib_path()
+
+
+def load_library():
+    """Load libdspark.so from the package's lib/ folder (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError("libdspark.so is not built (%s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    c_int, c_size, c_u64, vp, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_float
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_status_string.argtypes = [c_int]
+    lib.dspark_version.restype = c_int
+    lib.dspark_markov_draft_workspace_bytes.restype = c_size
+    lib.dspark_markov_draft_workspace_bytes.argtypes = [c_int] * 4
+    lib.dspark_markov_draft.restype = c_int
+    lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp,
+                                        c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_schedule.restype = c_int
+    lib.dspark_schedule.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp]
+    lib.dspark_verify_workspace_bytes.restype = c_size
+    lib.dspark_verify_workspace_bytes.argtypes = [c_int] * 5
+    lib.dspark_verify.restype = c_int
+    lib.dspark_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp,
+                                  c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, c_size, vp]
+    lib.dspark_uniforms.restype = c_int
+    lib.dspark_uniforms.argtypes = [c_u64, c_u64, c_int, c_int, c_int, vp, vp]
+    lib.dspark_profiler_enable.restype = c_int
+    lib.dspark_profiler_enable.argtypes = [c_int]
+    lib.dspark_profiler_reset.restype = c_int
+    lib.dspark_profiler_read.restype = c_int
+    lib.dspark_profiler_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    raise TypeError("logits must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _check(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _workspace(nbytes, device):
+    # torch's caching allocator returns 256-byte aligned blocks on ROCm
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def dspark_status_string(status):
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+def dspark_version():
+    return load_library().dspark_version()
+
+
+def dspark_markov_draft_workspace_bytes(B, K, V, r):
+    return load_library().dspark_markov_draft_workspace_bytes(B, K, V, r)
+
+
+def dspark_verify_workspace_bytes(R, K, V, r, N):
+    return load_library().dspark_verify_workspace_bytes(R, K, V, r, N)
+
+
+def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, workspace=None):
+    """Sequential Markov-head draft.
+
+    U [B, K, V] f32/bf16; W1 [V, r] bf16; W2 the r x V factor in column-major
+    storage, i.e. a [V, r] bf16 tensor whose row v produces logit v; x0 [B]
+    int32.  W1 = W2 = None means no Markov head (r = 0).
+    Returns (x [B, K] int32, q_tok [B, K] f32, lse [B, K] f32).
+    """
+    lib = load_library()
+    B, K, V = U.shape
+    _check(U, "U")
+    r = 0
+    if W1 is not None or W2 is not None:
+        r = W1.shape[1]
+        _check(W1, "W1", torch.bfloat16, (V, r))
+        _check(W2, "W2", torch.bfloat16, (V, r))
+    _check(x0, "x0", torch.int32, (B,))
+    dev = U.device
+    if out is None:
+        out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev))
+    x, q, lse = out
+    need = lib.dspark_markov_draft_workspace_bytes(B, K, V, r)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_markov_draft(B, K, V, r, float(temperature), _ptr(U), _dtype_code(U), _ptr(W1), _ptr(W2),
+                                 _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_markov_draft", st)
+    return x, q, lse
+
+
+def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None):
+    """Algorithm 1 on confidences c [R, K] f32 and the SPS table sps [L] f64.
+
+    Returns dict with a [R, K] f32, ell [R] int32, cu_seqlens [R+1] int32,
+    n_admitted [1] int32 and theta [1] f64 (all on the GPU).
+    """
+    lib = load_library()
+    R, K = c.shape
+    _check(c, "c", torch.float32)
+    _check(sps, "sps", torch.float64)
+    dev = c.device
+    if out is None:
+        out = {"a": torch.empty((R, K), dtype=torch.float32, device=dev),
+               "ell": torch.empty(R, dtype=torch.int32, device=dev),
+               "cu_seqlens": torch.empty(R + 1, dtype=torch.int32, device=dev),
+               "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
+               "theta": torch.empty(1, dtype=torch.float64, device=dev)}
+    st = lib.dspark_schedule(R, K, _ptr(c), _ptr(sps), sps.numel(), int(mode), int(capacity), _ptr(out["a"]),
+                             _ptr(out["ell"]), _ptr(out["cu_seqlens"]), _ptr(out["n_admitted"]),
+                             _ptr(out["theta"]), _stream())
+    if st != 0:
+        raise DSparkError("dspark_schedule", st)
+    return out
+
+
+def dspark_verify(P, cu_seqlens, D, W1, W2, x0, x, q_tok, lse_d, temperature, seed, step, out=None,
+                  workspace=None):
+    """Rejection-sampling verification over the flat batch.
+
+    P [N, V] target logits; cu_seqlens [R+1] int32; D [R, K, V] draft base
+    logits; W1 / W2 as for dspark_markov_draft (or None); x0 [R]; x, q_tok,
+    lse_d [R, K] from the draft.  Returns (n_acc [R] int32, tok [R] int32).
+    """
+    lib = load_library()
+    N, V = P.shape
+    R, K, V2 = D.shape
+    if V2 != V:
+        raise ValueError("P and D disagree on V")
+    _check(P, "P")
+    _check(D, "D")
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,))
+    _check(x0, "x0", torch.int32, (R,))
+    _check(x, "x", torch.int32, (R, K))
+    r = 0
+    if W1 is not None or W2 is not None:
+        r = W1.shape[1]
+        _check(W1, "W1", torch.bfloat16, (V, r))
+        _check(W2, "W2", torch.bfloat16, (V, r))
+    if q_tok is not None:
+        _check(q_tok, "q_tok", torch.float32, (R, K))
+    if lse_d is not None:
+        _check(lse_d, "lse_d", torch.float32, (R, K))
+    dev = P.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev))
+    n_acc, tok = out
+    need = lib.dspark_verify_workspace_bytes(R, K, V, r, N)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_verify(R, K, V, float(temperature), _ptr(P), _dtype_code(P), N, _ptr(cu_seqlens), _ptr(D),
+                           _dtype_code(D), _ptr(W1), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(q_tok), _ptr(lse_d),
+                           int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_verify", st)
+    return n_acc, tok
+
+
+def dspark_uniforms(seed, step, n, position, purpose, out=None):
+    """u(seed, step, request i, position, purpose) for i in [0, n), float32 on the GPU."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    st = lib.dspark_uniforms(int(seed), int(step), int(n), int(position), int(purpose), _ptr(out), _stream())
+    if st != 0:
+        raise DSparkError("dspark_uniforms", st)
+    return out
+
+
+def dspark_profiler_enable(on=True):
+    return load_library().dspark_profiler_enable(1 if on else 0)
+
+
+def dspark_profiler_reset():
+    return load_library().dspark_profiler_reset()
+
+
+def dspark_profiler_read():
+    """{kernel name: (launches, total ms)} for the events recorded so far."""
+    lib = load_library()
+    n = lib.dspark_profiler_read(0, None, None, None)
+    res = {}
+    for i in range(n):
+        name = ctypes.c_char_p()
+        launches = ctypes.c_int64()
+        ms = ctypes.c_double()
+        if lib.dspark_profiler_read(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms)) == 0:
+            res[name.value.decode()] = (launches.value, ms.value)
+    return res

@@ -1,0 +1,200 @@
+// C ABI of libdspark: argument validation, workspace sizing, dispatch to the
+// kernel launchers, and the event-based kernel timer.  Declarations and the
+// documented contract live in include/dspark.h.
+#include "../../include/dspark.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+#include <vector>
+
+namespace dspark {
+size_t draft_workspace_bytes(int B, int V);
+int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
+              const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
+              float* lse_out, void* workspace, hipStream_t stream);
+int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
+                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, hipStream_t stream);
+size_t verify_workspace_bytes(int R, int V, int N);
+int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N, const int32_t* cu,
+               const void* D, bool d_bf16, const void* W1, const void* W2, int r, const int32_t* x0,
+               const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed, uint64_t step,
+               int32_t* n_acc_out, int32_t* tok_out, void* workspace, hipStream_t stream);
+int run_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, hipStream_t stream);
+
+// ---- kernel timer --------------------------------------------------------
+namespace {
+struct Pending {
+  int kernel;
+  hipEvent_t start, stop;
+};
+struct KernelTotal {
+  std::string name;
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+bool g_prof = false;
+std::vector<KernelTotal> g_totals;
+std::vector<Pending> g_pending;
+Pending g_open{-1, nullptr, nullptr};
+
+int kernel_index(const char* name) {
+  for (size_t i = 0; i < g_totals.size(); ++i)
+    if (g_totals[i].name == name) return (int)i;
+  g_totals.push_back(KernelTotal{name, 0, 0.0});
+  return (int)g_totals.size() - 1;
+}
+
+void drain_pending() {
+  for (Pending& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) == hipSuccess && hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+      g_totals[p.kernel].ms += ms;
+      g_totals[p.kernel].launches += 1;
+    }
+    (void)hipEventDestroy(p.start);
+    (void)hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+}
+}  // namespace
+
+bool profiler_on() { return g_prof; }
+
+void profiler_begin(const char* name, hipStream_t stream) {
+  g_open.kernel = kernel_index(name);
+  if (hipEventCreate(&g_open.start) != hipSuccess || hipEventCreate(&g_open.stop) != hipSuccess) {
+    g_open.kernel = -1;
+    return;
+  }
+  (void)hipEventRecord(g_open.start, stream);
+}
+
+void profiler_end(hipStream_t stream) {
+  if (g_open.kernel < 0) return;
+  (void)hipEventRecord(g_open.stop, stream);
+  g_pending.push_back(g_open);
+  g_open.kernel = -1;
+}
+}  // namespace dspark
+
+namespace {
+bool is_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+bool rank_ok(int r) { return r >= 0 && r <= DSPARK_MAX_RANK && r % 8 == 0; }
+int hip_status(int rc) { return rc == 0 ? DSPARK_OK : DSPARK_E_HIP; }
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_E_NULL: return "a required pointer is NULL";
+    case DSPARK_E_SHAPE: return "a dimension is out of its documented range";
+    case DSPARK_E_DTYPE: return "unsupported dtype";
+    case DSPARK_E_RANGE: return "a scalar argument is out of range";
+    case DSPARK_E_WORKSPACE: return "workspace missing or too small";
+    case DSPARK_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int dspark_version(void) { return 100; }
+
+size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
+  (void)K;
+  (void)r;
+  if (B <= 0 || V <= 0) return 0;
+  return dspark::draft_workspace_bytes(B, V);
+}
+
+int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
+                        const void* W1, const void* W2, const int32_t* x0, uint64_t seed, uint64_t step,
+                        int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if ((int64_t)B * V >= (int64_t)1 << 31 || (int64_t)B * K * V >= (int64_t)1 << 40) return DSPARK_E_SHAPE;
+  if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
+  if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
+  if (!workspace || workspace_bytes < dspark::draft_workspace_bytes(B, V)) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
+    return DSPARK_E_RANGE;
+  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, x0, seed,
+                                      step, x_out, q_tok_out, lse_out, workspace,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len, int mode, int capacity,
+                    float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out, int32_t* n_admitted_out,
+                    double* theta_out, void* stream) {
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
+  if (mode < DSPARK_SCHED_EARLY_STOP || mode > DSPARK_SCHED_TOPK) return DSPARK_E_RANGE;
+  if (capacity < 0) return DSPARK_E_RANGE;
+  if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
+  if (!c || !sps || !a_out || !ell_out || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
+  return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, a_out, ell_out, cu_seqlens_out,
+                                         n_admitted_out, theta_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_verify_workspace_bytes(int R, int K, int V, int r, int N) {
+  (void)K;
+  (void)r;
+  if (R <= 0 || V <= 0 || N <= 0) return 0;
+  return dspark::verify_workspace_bytes(R, V, N);
+}
+
+int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_dtype, int N,
+                  const int32_t* cu_seqlens, const void* D, int d_dtype, const void* W1, const void* W2, int r,
+                  const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
+                  uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
+  if ((int64_t)N * V >= (int64_t)1 << 31 || (int64_t)R * K * V >= (int64_t)1 << 40) return DSPARK_E_SHAPE;
+  if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!P || !cu_seqlens || !D || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
+  if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
+  if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
+  if (!workspace || workspace_bytes < dspark::verify_workspace_bytes(R, V, N)) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
+    return DSPARK_E_RANGE;
+  return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
+                                       d_dtype == DSPARK_BF16, W1, W2, r, x0, x, q_tok, lse_d, seed, step,
+                                       n_acc_out, tok_out, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, void* stream) {
+  if (n <= 0) return DSPARK_E_SHAPE;
+  if (position < 0 || position >= (1 << 30) || purpose < 0 || purpose > 2) return DSPARK_E_RANGE;
+  if (!out) return DSPARK_E_NULL;
+  return hip_status(dspark::run_uniforms(seed, step, n, position, purpose, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_profiler_enable(int on) {
+  dspark::g_prof = on != 0;
+  return DSPARK_OK;
+}
+
+int dspark_profiler_reset(void) {
+  dspark::drain_pending();
+  dspark::g_totals.clear();
+  return DSPARK_OK;
+}
+
+int dspark_profiler_read(int index, const char** name, int64_t* launches, double* total_ms) {
+  dspark::drain_pending();
+  if (!name) return (int)dspark::g_totals.size();
+  if (index < 0 || index >= (int)dspark::g_totals.size()) return DSPARK_E_RANGE;
+  *name = dspark::g_totals[index].name.c_str();
+  if (launches) *launches = dspark::g_totals[index].launches;
+  if (total_ms) *total_ms = dspark::g_totals[index].ms;
+  return DSPARK_OK;
+}
+
+}  // extern "C"

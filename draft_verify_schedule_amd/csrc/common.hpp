@@ -1,0 +1,180 @@
+// Device-side building blocks shared by the draft, schedule and verify
+// kernels: bf16 loads, Philox4x32-10 uniforms, wave64 reductions and scans,
+// softmax partial merging, and the MFMA fragment types of gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Purposes of the per-decision uniforms.
+constexpr uint32_t kPurposeDraft = 0;
+constexpr uint32_t kPurposeAccept = 1;
+constexpr uint32_t kPurposeResample = 2;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplications mixed with the other counter words and the round
+// key; the key advances by the two Weyl constants between rounds.  Only the
+// first output word is needed per decision.
+__device__ __forceinline__ uint32_t philox_first_word(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                      uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * c0;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Uniform in [0, 1) for decision (request, position, purpose) of `step`:
+// the top 24 bits of the first Philox word, an exact float.
+__device__ __forceinline__ float decision_uniform(uint64_t seed, uint64_t step, uint32_t request,
+                                                  uint32_t position, uint32_t purpose) {
+  const uint32_t w = philox_first_word((uint32_t)step, (uint32_t)(step >> 32), request,
+                                       (position << 2) | purpose, (uint32_t)seed,
+                                       (uint32_t)(seed >> 32));
+  return (float)(w >> 8) * (1.0f / 16777216.0f);
+}
+
+// ---- wave64 helpers ------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes in lane order.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Lowest lane whose predicate holds, or -1.
+__device__ __forceinline__ int wave_first_lane(bool pred) {
+  const unsigned long long m = __ballot(pred);
+  return m ? __ffsll((long long)m) - 1 : -1;
+}
+
+// (max, sum of exp2(x - max)) pairs: merge two partial softmax statistics.
+// A pair with max == -inf carries no mass.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  const float a = (m == -INFINITY) ? 0.0f : s * exp2f(m - M);
+  const float b = (m2 == -INFINITY) ? 0.0f : s2 * exp2f(m2 - M);
+  m = M;
+  s = a + b;
+}
+
+// (max, first index) pairs for greedy decoding: larger value wins, lowest index on ties.
+// An index of -1 marks an empty partial.
+__device__ __forceinline__ void merge_argmax(float& m, int& idx, float m2, int idx2) {
+  if (idx2 < 0) return;
+  if (idx < 0 || m2 > m || (m2 == m && idx2 < idx)) {
+    m = m2;
+    idx = idx2;
+  }
+}
+
+// Loads of 16 consecutive logits (bf16 or f32) starting at column n of a row,
+// masking columns >= V with -inf.  VEC: the row base is 16-byte aligned and V
+// is a multiple of the vector width, so each 16-byte vector is either entirely
+// inside the row or entirely past its end.
+template <typename T>
+struct Logits16;
+
+template <>
+struct Logits16<uint16_t> {  // bf16 stored as raw bits
+  template <bool VEC>
+  __device__ __forceinline__ static void load(const uint16_t* __restrict__ row, int n, int V,
+                                              float out[16]) {
+    if (VEC) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = n + 8 * h;
+        if (c < V) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(row + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            out[8 * h + 2 * e] = __uint_as_float(w[e] << 16);
+            out[8 * h + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[8 * h + e] = -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        out[e] = (n + e < V) ? bf16_bits_to_f32(row[n + e]) : -INFINITY;
+    }
+  }
+};
+
+template <>
+struct Logits16<float> {
+  template <bool VEC>
+  __device__ __forceinline__ static void load(const float* __restrict__ row, int n, int V,
+                                              float out[16]) {
+    if (VEC) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int c = n + 4 * h;
+        if (c < V) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(row + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[4 * h + e] = w[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[4 * h + e] = -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out[e] = (n + e < V) ? row[n + e] : -INFINITY;
+    }
+  }
+};
+
+__device__ __forceinline__ float load_logit(const uint16_t* row, int n) {
+  return bf16_bits_to_f32(row[n]);
+}
+__device__ __forceinline__ float load_logit(const float* row, int n) { return row[n]; }
+
+}  // namespace dspark

@@ -1,0 +1,263 @@
+// Hardware-aware prefix scheduler (DSpark paper, section 3.2.2, Algorithm 1;
+// modes of section 5.2; "Speculative decoding, from zero to DSpark", section 8).
+//
+// One workgroup of 1024 threads:
+//   1. survival a[r,j] = c[r,1]*...*c[r,j] (float32, left to right) and a 64-bit
+//      key per candidate with a > 0:
+//        key = ((0xFFFFFFFF - bits(a)) << 32) | ((j - 1) << 24) | r
+//      so ascending keys = a descending, then j ascending, then r ascending
+//      (a is positive, so its bit pattern orders like its value);
+//   2. bitonic sort of the keys in LDS (padded to a power of two with ~0);
+//   3. tau increments floor(a * 2^32) (exact int64 fixed point), block prefix
+//      scan, Theta_n = double(tau_n) * 2^-32 * SPS[R + n] for every admission
+//      count n; the cut n* is the first drop minus one (EARLY_STOP), the
+//      earliest maximum (GLOBAL) or min(capacity, |E|) (TOPK).  The fixed-point
+//      sum is exact, so this parallel evaluation equals the sequential walk
+//      bit for bit;
+//   4. l_r = number of r's candidates whose key lies below the n*-th sorted key
+//      (a prefix of positions by construction), and cu_seqlens by a block scan.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dspark {
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedMaxKeys = 16384;
+
+struct ScheduleArgs {
+  int R, K;
+  const float* c;
+  const double* sps;
+  int mode, capacity;
+  float* a_out;
+  int32_t* ell_out;
+  int32_t* cu_out;
+  int32_t* n_out;
+  double* theta_out;
+};
+
+__device__ __forceinline__ uint64_t make_key(float a, int j, int r) {
+  return ((uint64_t)(0xFFFFFFFFu - __float_as_uint(a)) << 32) | ((uint64_t)j << 24) | (uint64_t)r;
+}
+
+__device__ __forceinline__ uint64_t key_increment(uint64_t key) {
+  const float a = __uint_as_float(0xFFFFFFFFu - (uint32_t)(key >> 32));
+  return (uint64_t)((double)a * 4294967296.0);  // a in (0, 1]: exact, truncation = floor
+}
+
+// Block-wide exclusive scan of one uint64 per thread (1024 threads = 16 waves).
+__device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* wave_sums,
+                                                         uint64_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t w = lane < kSchedThreads / 64 ? wave_sums[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint64_t o = __shfl_up(w, off, 64);
+      if (lane >= off) w += o;
+    }
+    if (lane < kSchedThreads / 64) wave_sums[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const uint64_t before = wave ? wave_sums[wave - 1] : 0;
+  total = wave_sums[kSchedThreads / 64 - 1];
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
+  __shared__ uint64_t keys[kSchedMaxKeys];
+  __shared__ uint64_t wave_sums[kSchedThreads / 64];
+  __shared__ int bad;
+  __shared__ int red_i[kSchedThreads / 64];
+  __shared__ double red_d[kSchedThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int R = a.R, K = a.K;
+  const int n_cand = R * K;
+  int P2 = 2;
+  while (P2 < n_cand) P2 <<= 1;
+
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  // 1. survival products and keys
+  for (int r = tid; r < R; r += kSchedThreads) {
+    float acc = 1.0f;
+    for (int j = 0; j < K; ++j) {
+      const float cj = a.c[(size_t)r * K + j];
+      if (!(cj >= 0.0f && cj <= 1.0f)) bad = 1;  // NaN fails both tests
+      acc = __fmul_rn(acc, cj);
+      a.a_out[(size_t)r * K + j] = acc;
+      keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+    }
+  }
+  for (int i = n_cand + tid; i < P2; i += kSchedThreads) keys[i] = ~0ull;
+  __syncthreads();
+
+  if (bad) {  // documented data error: a valid layout with no drafts
+    for (int r = tid; r < R; r += kSchedThreads) {
+      a.ell_out[r] = 0;
+      a.cu_out[r + 1] = r + 1;
+    }
+    if (tid == 0) {
+      a.cu_out[0] = 0;
+      *a.n_out = -1;
+      *a.theta_out = __longlong_as_double(0x7FF8000000000000ll);
+    }
+    return;
+  }
+
+  // 2. bitonic sort, ascending
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < (P2 >> 1); i += kSchedThreads) {
+        const int pos = 2 * i - (i & (j - 1));
+        const int partner = pos + j;
+        const uint64_t x = keys[pos], y = keys[partner];
+        const bool up = (pos & k) == 0;
+        if ((x > y) == up) {
+          keys[pos] = y;
+          keys[partner] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // number of candidates = position of the first padding key
+  int cnt = 0;
+  for (int i = tid; i < P2; i += kSchedThreads) cnt += keys[i] != ~0ull;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  if (lane == 0) red_i[wave] = cnt;
+  __syncthreads();
+  int n_c = 0;
+  for (int w = 0; w < kSchedThreads / 64; ++w) n_c += red_i[w];
+  __syncthreads();
+
+  // 3. fixed-point tau over contiguous chunks, Theta per admission count
+  const int per = (P2 + kSchedThreads - 1) / kSchedThreads;
+  const int i0 = min(P2, tid * per);
+  const int i1 = min(P2, i0 + per);
+  uint64_t local = 0;
+  for (int i = i0; i < i1; ++i)
+    if (i < n_c) local += key_increment(keys[i]);
+  uint64_t total;
+  const uint64_t prefix = block_exclusive_scan(local, wave_sums, total);
+  const uint64_t tau0 = (uint64_t)R << 32;
+  const double theta0 = (double)tau0 * 0x1p-32 * a.sps[R];
+
+  // candidate answer of this thread: EARLY_STOP -> first n with a drop;
+  // GLOBAL -> best (Theta, smallest n)
+  int first_drop = 0x7FFFFFFF;
+  double best = (tid == 0) ? theta0 : -INFINITY;
+  int best_n = (tid == 0) ? 0 : 0x7FFFFFFF;
+  if (a.mode != 2) {
+    uint64_t tau = tau0 + prefix;
+    double prev_theta = 0.0;
+    if (i0 < n_c) {
+      prev_theta = (i0 == 0) ? theta0 : (double)tau * 0x1p-32 * a.sps[R + i0];
+    }
+    for (int i = i0; i < i1 && i < n_c; ++i) {
+      tau += key_increment(keys[i]);
+      const int n = i + 1;
+      const double theta = (double)tau * 0x1p-32 * a.sps[R + n];
+      if (theta <= prev_theta && n < first_drop) first_drop = n;
+      if (theta > best) {
+        best = theta;
+        best_n = n;
+      }
+      prev_theta = theta;
+    }
+  }
+  // block reductions: min first_drop; max (best, -best_n)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    first_drop = min(first_drop, __shfl_xor(first_drop, off, 64));
+    const double b2 = __shfl_xor(best, off, 64);
+    const int n2 = __shfl_xor(best_n, off, 64);
+    if (b2 > best || (b2 == best && n2 < best_n)) {
+      best = b2;
+      best_n = n2;
+    }
+  }
+  __shared__ int red_drop[kSchedThreads / 64];
+  if (lane == 0) {
+    red_drop[wave] = first_drop;
+    red_i[wave] = best_n;
+    red_d[wave] = best;
+  }
+  __syncthreads();
+  __shared__ int n_star_s;
+  if (tid == 0) {
+    int fd = 0x7FFFFFFF, bn = 0x7FFFFFFF;
+    double bv = -INFINITY;
+    for (int w = 0; w < kSchedThreads / 64; ++w) {
+      fd = min(fd, red_drop[w]);
+      if (red_d[w] > bv || (red_d[w] == bv && red_i[w] < bn)) {
+        bv = red_d[w];
+        bn = red_i[w];
+      }
+    }
+    int n_star;
+    if (a.mode == 0) n_star = (fd == 0x7FFFFFFF) ? n_c : fd - 1;
+    else if (a.mode == 1) n_star = bn;
+    else n_star = min(max(a.capacity, 0), n_c);
+    n_star_s = n_star;
+  }
+  __syncthreads();
+  const int n_star = n_star_s;
+  // Theta of the chosen admission count, from the thread owning sorted index n*-1
+  if (n_star == 0) {
+    if (tid == 0) *a.theta_out = theta0;
+  } else if (n_star - 1 >= i0 && n_star - 1 < i1) {
+    uint64_t tau = tau0 + prefix;
+    for (int i = i0; i < n_star; ++i) tau += key_increment(keys[i]);
+    *a.theta_out = (double)tau * 0x1p-32 * a.sps[R + n_star];
+  }
+  if (tid == 0) *a.n_out = n_star;
+  const uint64_t threshold = (n_star < P2) ? keys[n_star] : ~0ull;
+
+  // 4. lengths and the flattened layout
+  const int rper = (R + kSchedThreads - 1) / kSchedThreads;
+  const int r0 = min(R, tid * rper);
+  const int r1 = min(R, r0 + rper);
+  uint64_t mine = 0;
+  for (int r = r0; r < r1; ++r) {
+    int ell = 0;
+    float acc = 1.0f;
+    for (int j = 0; j < K; ++j) {
+      acc = __fmul_rn(acc, a.c[(size_t)r * K + j]);
+      if (acc > 0.0f && make_key(acc, j, r) < threshold) ++ell;
+    }
+    a.ell_out[r] = ell;
+    mine += 1 + ell;
+  }
+  uint64_t all;
+  uint64_t run = block_exclusive_scan(mine, wave_sums, all);
+  if (tid == 0) a.cu_out[0] = 0;
+  for (int r = r0; r < r1; ++r) {
+    run += 1 + a.ell_out[r];
+    a.cu_out[r + 1] = (int32_t)run;
+  }
+}
+
+int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
+                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out,
+                 hipStream_t stream) {
+  ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out};
+  return launch_kernel("schedule", schedule_kernel, dim3(1), dim3(kSchedThreads), stream, a);
+}
+
+}  // namespace dspark

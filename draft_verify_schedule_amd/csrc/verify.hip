@@ -1,0 +1,630 @@
+// Rejection-sampling verification over the flattened variable-length batch
+// (DSpark paper, section 2.1 and section 5.3; "Speculative decoding, from zero
+// to DSpark", section 2 and Appendix A1; the glean.smartcoder article's
+// five-step verification routine).
+//
+// Request r owns flat target rows cu[r] .. cu[r+1]-1 (its l_r drafts, then the
+// bonus row).  Launches:
+//   verify_rowstats   one HBM pass over every flat target row: per 256-column
+//                     slice the softmax partial (max, sum exp2) of t * log2(e)/T,
+//                     or (max, first argmax) when greedy;
+//   verify_accept     one wave per flat row: merges its partials into the
+//                     row normaliser and runs the min(1, p/q) test of the
+//                     draft token the row judges;
+//   verify_decide     one thread per request: first rejection -> n_acc and
+//                     which row needs a correction (residual) or bonus sample;
+//   verify_residual   (T > 0) for rejecting requests, one pass over the
+//                     rejected position's target and draft rows, the draft
+//                     row's Markov bias rebuilt on MFMA: per 64-column slice
+//                     the mass of max(0, p - q);
+//   verify_sample     (T > 0) one wave per request: inverse-CDF draw of the
+//                     correction (residual partials, 64-column re-scan) or the
+//                     bonus (target partials, 256-column re-scan).
+#include "bias_tile.hpp"
+#include "launch.hpp"
+
+namespace dspark {
+
+constexpr int kRowChunk = 8192;   // columns per rowstats workgroup (2048 per wave)
+constexpr int kRowSlice = 256;    // columns per target-row partial
+
+struct VerifyArgs {
+  int R, K, V, N, r;
+  float c2;                 // log2(e) / T, or 1 when greedy
+  const void* P;            // [N, V]
+  const int32_t* cu;        // [R + 1]
+  const void* D;            // [R, K, V]
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* x0;        // [R]
+  const int32_t* x;         // [R, K]
+  const float* q_tok;       // [R, K]
+  const float* lse_d;       // [R, K]
+  uint64_t seed, step;
+  int32_t* n_acc_out;
+  int32_t* tok_out;
+  // workspace
+  float2* ppart;            // [N, nsP]
+  float2* rowms;            // [N]  (max, sum) or (max, argmax bits)
+  int32_t* flag;            // [N]  1 accept, 0 reject, 2 bad row, 3 bonus row
+  int4* info;               // [R]  (mode, sample row, position, n_acc)
+  float* rpart;             // [R, ns64]
+  int nsP, ns64, nchunks;
+  int ncol_tiles, nstages;
+};
+
+// ---------------------------------------------------------------- rowstats --
+template <typename PT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
+  const int row = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x - row * a.nchunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
+  if (wbase >= a.V) return;
+  const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)row * a.V;
+  float2* out = a.ppart + (size_t)row * a.nsP;
+
+  if constexpr (VEC) {
+    constexpr int EPL = 16 / sizeof(PT);          // elements per 16-byte load
+    constexpr int COLS = 64 * EPL;                // columns per load instruction
+    constexpr int ITERS = (kRowChunk / 4) / COLS; // loads per wave
+    constexpr int LPS = kRowSlice / EPL;          // lanes per slice
+    float v[ITERS][EPL];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int c = wbase + it * COLS + lane * EPL;
+      if (c < a.V) {
+        if constexpr (sizeof(PT) == 2) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(prow + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[it][2 * e] = __uint_as_float(w[e] << 16);
+            v[it][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        } else {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(prow + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[it][e] = w[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[it][e] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int c = wbase + it * COLS + lane * EPL;
+      const int slice = (wbase + it * COLS) / kRowSlice + lane / LPS;
+      if constexpr (GREEDY) {
+        float m = -INFINITY;
+        int idx = -1;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          if (c + e < a.V && (idx < 0 || v[it][e] > m)) {
+            m = v[it][e];
+            idx = c + e;
+          }
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) {
+          const float m2 = __shfl_xor(m, off, 64);
+          const int i2 = __shfl_xor(idx, off, 64);
+          merge_argmax(m, idx, m2, i2);
+        }
+        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) out[slice] = make_float2(m, __int_as_float(idx));
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          v[it][e] *= a.c2;
+          m = fmaxf(m, v[it][e]);
+        }
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        float s = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s += exp2f(v[it][e] - m);
+        }
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
+        if ((lane % LPS) == 0 && slice < a.nsP && c < a.V) out[slice] = make_float2(m, s);
+      }
+    }
+  } else {
+    // any alignment: lane-strided scalar loads, one 256-column slice per 4 steps
+    for (int sl = 0; sl < (kRowChunk / 4) / kRowSlice; ++sl) {
+      const int sbase = wbase + sl * kRowSlice;
+      if (sbase >= a.V) break;
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = sbase + 64 * t + lane;
+        v[t] = (c < a.V) ? load_logit(prow, c) : -INFINITY;
+      }
+      const int slice = sbase / kRowSlice;
+      if constexpr (GREEDY) {
+        float m = -INFINITY;
+        int idx = -1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = sbase + 64 * t + lane;
+          if (c < a.V) merge_argmax(m, idx, v[t], c);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const float m2 = __shfl_xor(m, off, 64);
+          const int i2 = __shfl_xor(idx, off, 64);
+          merge_argmax(m, idx, m2, i2);
+        }
+        if (lane == 0) out[slice] = make_float2(m, __int_as_float(idx));
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] *= a.c2;
+          m = fmaxf(m, v[t]);
+        }
+        m = wave_max(m);
+        float s = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s += exp2f(v[t] - m);
+        }
+        s = wave_sum(s);
+        if (lane == 0) out[slice] = make_float2(m, s);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ accept --
+// Request owning flat row i: the largest r with cu[r] <= i (cu is validated by
+// the caller of the result, never trusted for indexing beyond [0, R]).
+__device__ __forceinline__ int owner_of(const int32_t* cu, int R, int i) {
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename PT, bool GREEDY>
+__global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= a.N) return;
+  const float2* part = a.ppart + (size_t)i * a.nsP;
+  float m = -INFINITY, s = 0.f;
+  int idx = -1;
+  for (int k = lane; k < a.nsP; k += 64) {
+    const float2 p = part[k];
+    if constexpr (GREEDY) merge_argmax(m, idx, p.x, __float_as_int(p.y));
+    else merge_ms(m, s, p.x, p.y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    if constexpr (GREEDY) {
+      const int i2 = __shfl_xor(idx, off, 64);
+      merge_argmax(m, idx, m2, i2);
+    } else {
+      const float s2 = __shfl_xor(s, off, 64);
+      merge_ms(m, s, m2, s2);
+    }
+  }
+  if (lane != 0) return;
+  a.rowms[i] = GREEDY ? make_float2(m, __int_as_float(idx)) : make_float2(m, s);
+
+  const int r = owner_of(a.cu, a.R, i);
+  const int c0 = a.cu[r], c1 = a.cu[r + 1];
+  if (!(c0 >= 0 && c0 <= i && i < c1 && c1 <= a.N && c1 - c0 <= a.K + 1)) {
+    a.flag[i] = 2;
+    return;
+  }
+  const int j = i - c0;             // this row judges draft position j + 1
+  if (j >= c1 - c0 - 1) {
+    a.flag[i] = 3;                  // bonus row
+    return;
+  }
+  const int xj = a.x[(size_t)r * a.K + j];
+  if (xj < 0 || xj >= a.V) {
+    a.flag[i] = 2;
+    return;
+  }
+  bool accept;
+  if constexpr (GREEDY) {
+    accept = (idx == xj);
+  } else {
+    const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)i * a.V;
+    const float t = load_logit(prow, xj) * a.c2;
+    const float p = exp2f(t - m) / s;
+    const float q = a.q_tok[(size_t)r * a.K + j];
+    const float ratio = (q > 0.f) ? p / q : INFINITY;
+    const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept);
+    accept = u < ratio;
+  }
+  a.flag[i] = accept ? 1 : 0;
+}
+
+// ------------------------------------------------------------------ decide --
+template <bool GREEDY>
+__global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.R) return;
+  const int c0 = a.cu[r], c1 = a.cu[r + 1];
+  bool ok = c0 >= 0 && c1 > c0 && c1 <= a.N && c1 - c0 <= a.K + 1;
+  int n = 0, L = 0;
+  if (ok) {
+    L = c1 - c0 - 1;
+    for (int j = 0; j <= L; ++j)
+      if (a.flag[c0 + j] == 2) ok = false;
+    if (!GREEDY && a.r > 0 && (a.x0[r] < 0 || a.x0[r] >= a.V)) ok = false;
+  }
+  if (!ok) {
+    a.info[r] = make_int4(-1, 0, 0, 0);
+    a.n_acc_out[r] = -1;
+    a.tok_out[r] = -1;
+    return;
+  }
+  while (n < L && a.flag[c0 + n] == 1) ++n;
+  const int mode = (n < L) ? 1 : 0;  // 1: correction from the residual, 0: bonus
+  a.info[r] = make_int4(mode, c0 + n, n + 1, n);
+  a.n_acc_out[r] = n;
+  if constexpr (GREEDY) a.tok_out[r] = __float_as_int(a.rowms[c0 + n].y);
+}
+
+// ---------------------------------------------------------------- residual --
+// max(0, p - q) over the rejected position, 64-column slice masses.
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC>
+__global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
+  int col_tile, stage;
+  if (!xcd_tile(blockIdx.x, a.ncol_tiles, a.nstages, col_tile, stage)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = col_tile * kTileCols + wave * kWaveCols;
+  const int row0 = stage * kStageRows;
+
+  __shared__ EStage<(KC > 0 ? KC : 1)> st;
+  bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  if constexpr (KC > 0) {
+    const int4* info = a.info;
+    const int32_t* x0 = a.x0;
+    const int32_t* x = a.x;
+    const int K = a.K;
+    stage_e<KC>(st, a.W1, a.r, a.V, row0, a.R, [&](int g) {
+      const int4 in = info[g];
+      if (in.x != 1) return -1;
+      return in.w == 0 ? x0[g] : x[(size_t)g * K + in.w - 1];
+    });
+    load_w2_frags<KC>(a.W2t, a.r, a.V, n0, lane, w2);
+    __syncthreads();
+  }
+  if (n0 >= a.V) return;
+  const int cbase = n0 + 16 * (lane >> 4);
+  const int slice = n0 / kWaveCols;
+  for (int g = 0; g < kStageRows / 16; ++g) {
+    if (row0 + 16 * g >= a.R) break;
+    const int rq = row0 + 16 * g + (lane & 15);
+    int4 in = make_int4(-1, 0, 0, 0);
+    if (rq < a.R) in = a.info[rq];
+    const bool live = in.x == 1;
+    float t[16], z[16];
+    float lp = 0.f, lq = 0.f;
+    if (live) {
+      const float2 ms = a.rowms[in.y];
+      lp = ms.x + log2f(ms.y);
+      lq = a.lse_d[(size_t)rq * a.K + in.w] * kLog2e;
+      const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)in.y * a.V;
+      const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)rq * a.K + in.w) * a.V;
+      Logits16<PT>::template load<VEC_P>(prow, cbase, a.V, t);
+      Logits16<DT>::template load<VEC_D>(drow, cbase, a.V, z);
+    }
+    if constexpr (KC > 0) {
+      f32x4 acc[4];
+      mfma_group<KC>(st, g, lane, w2, acc);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
+    }
+    float s = 0.f;
+    if (live) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (cbase + e < a.V) {
+          const float p = exp2f(t[e] * a.c2 - lp);
+          const float q = exp2f(z[e] * a.c2 - lq);
+          s += fmaxf(p - q, 0.f);
+        }
+      }
+    }
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (live && lane < 16) a.rpart[(size_t)rq * a.ns64 + slice] = s;
+  }
+}
+
+// ------------------------------------------------------------------ sample --
+// Inverse-CDF over slice masses w_s: the slice where the running sum first
+// exceeds target and the mass before it.  Lanes own contiguous slice chunks.
+struct SliceHit {
+  int slice;
+  float before;
+};
+
+template <typename WeightFn>
+__device__ __forceinline__ SliceHit find_slice(int ns, float target, float incl, float local, int s_begin,
+                                               int s_end, WeightFn weight) {
+  const int lane = threadIdx.x & 63;
+  int owner = wave_first_lane(incl > target);
+  if (owner < 0) {
+    const unsigned long long m = __ballot(local > 0.f);
+    owner = m ? 63 - __clzll((long long)m) : 0;
+  }
+  int s_star = -1;
+  float before = 0.f;
+  if (lane == owner) {
+    float acc = incl - local;
+    int last = -1;
+    float last_before = acc;
+    for (int s = s_begin; s < s_end; ++s) {
+      const float w = weight(s);
+      if (w > 0.f) {
+        last = s;
+        last_before = acc;
+        if (acc + w > target) {
+          s_star = s;
+          before = acc;
+          break;
+        }
+      }
+      acc += w;
+    }
+    if (s_star < 0) {
+      s_star = last;
+      before = last_before;
+    }
+  }
+  SliceHit h;
+  h.slice = __shfl(s_star, owner, 64);
+  h.before = __shfl(before, owner, 64);
+  if (h.slice < 0 || h.slice >= ns) h.slice = 0;
+  return h;
+}
+
+template <typename PT, typename DT>
+__global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= a.R) return;
+  const int4 in = a.info[r];
+  if (in.x < 0) return;  // decide already wrote -1
+  const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)in.z, kPurposeResample);
+  const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)in.y * a.V;
+  const float2 ms = a.rowms[in.y];
+  const float lp = ms.x + log2f(ms.y);
+  bool use_p = in.x == 0;
+
+  if (!use_p) {
+    // correction: residual mass per 64-column slice
+    const float* rp = a.rpart + (size_t)r * a.ns64;
+    const int ns = a.ns64;
+    const int per = (ns + 63) / 64;
+    const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
+    float local = 0.f;
+    for (int s = s_begin; s < s_end; ++s) local += rp[s];
+    const float incl = wave_inclusive_scan(local);
+    const float Z = __shfl(incl, 63, 64);
+    if (Z > 0.f && Z <= 2.f) {
+      const float target = u * Z;
+      const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return rp[s]; });
+      const int col = h.slice * kWaveCols + lane;
+      float rho = 0.f;
+      if (col < a.V) {
+        const int prev = in.w == 0 ? a.x0[r] : a.x[(size_t)r * a.K + in.w - 1];
+        const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)r * a.K + in.w) * a.V;
+        float zq = load_logit(drow, col);
+        if (a.r > 0) zq += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
+        const float lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
+        const float p = exp2f(load_logit(prow, col) * a.c2 - lp);
+        const float q = exp2f(zq * a.c2 - lq);
+        rho = fmaxf(p - q, 0.f);
+      }
+      const float cum = wave_inclusive_scan(rho);
+      int pick = wave_first_lane(cum > target - h.before && rho > 0.f);
+      if (pick < 0) {
+        const unsigned long long m = __ballot(rho > 0.f);
+        pick = m ? 63 - __clzll((long long)m) : 0;
+      }
+      if (lane == 0) a.tok_out[r] = h.slice * kWaveCols + pick;
+      return;
+    }
+    use_p = true;  // zero residual mass (rounding only): draw from p
+  }
+
+  // bonus (or fallback): target partials per 256-column slice
+  const float2* pp = a.ppart + (size_t)in.y * a.nsP;
+  const int ns = a.nsP;
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, pp[s].x);
+  M = wave_max(M);
+  auto weight = [&](int s) {
+    const float2 p = pp[s];
+    return (p.x == -INFINITY) ? 0.f : p.y * exp2f(p.x - M);
+  };
+  const int per = (ns + 63) / 64;
+  const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
+  float local = 0.f;
+  for (int s = s_begin; s < s_end; ++s) local += weight(s);
+  const float incl = wave_inclusive_scan(local);
+  const float S = __shfl(incl, 63, 64);
+  const float target = u * S;
+  const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, weight);
+  const float m_s = pp[h.slice].x;
+  const float t_in = (target - h.before) / exp2f(m_s - M);
+  // 256 columns, 4 consecutive per lane
+  float e[4];
+  float lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int col = h.slice * kRowSlice + 4 * lane + k;
+    e[k] = (col < a.V) ? exp2f(load_logit(prow, col) * a.c2 - m_s) : 0.f;
+    lsum += e[k];
+  }
+  const float incl2 = wave_inclusive_scan(lsum);
+  int owner = wave_first_lane(incl2 > t_in && lsum > 0.f);
+  if (owner < 0) {
+    const unsigned long long m = __ballot(lsum > 0.f);
+    owner = m ? 63 - __clzll((long long)m) : 0;
+  }
+  int pick = -1;
+  if (lane == owner) {
+    float acc = incl2 - lsum;
+    int last = 0;
+    for (int k = 0; k < 4; ++k) {
+      if (e[k] > 0.f) {
+        last = k;
+        if (acc + e[k] > t_in) {
+          pick = k;
+          break;
+        }
+      }
+      acc += e[k];
+    }
+    if (pick < 0) pick = last;
+    a.tok_out[r] = h.slice * kRowSlice + 4 * lane + pick;
+  }
+}
+
+// ------------------------------------------------------------------ host ---
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+struct VerifyLayout {
+  size_t ppart, rowms, flag, info, rpart, total;
+};
+
+static VerifyLayout verify_layout(int R, int V, int N) {
+  VerifyLayout l{};
+  const size_t nsP = (V + kRowSlice - 1) / kRowSlice;
+  const size_t ns64 = (V + kWaveCols - 1) / kWaveCols;
+  size_t off = 0;
+  l.ppart = off;
+  off += align256((size_t)N * nsP * sizeof(float2));
+  l.rowms = off;
+  off += align256((size_t)N * sizeof(float2));
+  l.flag = off;
+  off += align256((size_t)N * sizeof(int32_t));
+  l.info = off;
+  off += align256((size_t)R * sizeof(int4));
+  l.rpart = off;
+  off += align256((size_t)R * ns64 * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+size_t verify_workspace_bytes(int R, int V, int N) { return verify_layout(R, V, N).total; }
+
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC>
+static int launch_residual(const VerifyArgs& a, hipStream_t stream) {
+  return launch_kernel("verify_residual", verify_residual_kernel<PT, DT, VEC_P, VEC_D, KC>,
+                       dim3(xcd_grid(a.ncol_tiles, a.nstages)), dim3(256), stream, a);
+}
+
+template <typename PT, typename DT, bool VEC_P, bool VEC_D>
+static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
+  switch ((a.r + 31) / 32) {
+    case 0: return launch_residual<PT, DT, VEC_P, VEC_D, 0>(a, stream);
+    case 1: return launch_residual<PT, DT, VEC_P, VEC_D, 1>(a, stream);
+    case 2: return launch_residual<PT, DT, VEC_P, VEC_D, 2>(a, stream);
+    case 3: return launch_residual<PT, DT, VEC_P, VEC_D, 3>(a, stream);
+    case 4: return launch_residual<PT, DT, VEC_P, VEC_D, 4>(a, stream);
+    case 5: return launch_residual<PT, DT, VEC_P, VEC_D, 5>(a, stream);
+    case 6: return launch_residual<PT, DT, VEC_P, VEC_D, 6>(a, stream);
+    case 7: return launch_residual<PT, DT, VEC_P, VEC_D, 7>(a, stream);
+    case 8: return launch_residual<PT, DT, VEC_P, VEC_D, 8>(a, stream);
+    default: return -1;
+  }
+}
+
+template <typename PT, typename DT>
+static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, hipStream_t stream) {
+  int rc;
+  const dim3 b256(256);
+  if (greedy) {
+    rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, true, true>,
+                               dim3(a.N * a.nchunks), b256, stream, a)
+               : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, true>,
+                               dim3(a.N * a.nchunks), b256, stream, a);
+    if (rc) return rc;
+    rc = launch_kernel("verify_accept", verify_accept_kernel<PT, true>, dim3((a.N + 3) / 4), b256, stream, a);
+    if (rc) return rc;
+    return launch_kernel("verify_decide", verify_decide_kernel<true>, dim3((a.R + 255) / 256), b256, stream, a);
+  }
+  rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, true, false>,
+                             dim3(a.N * a.nchunks), b256, stream, a)
+             : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, false>,
+                             dim3(a.N * a.nchunks), b256, stream, a);
+  if (rc) return rc;
+  rc = launch_kernel("verify_accept", verify_accept_kernel<PT, false>, dim3((a.N + 3) / 4), b256, stream, a);
+  if (rc) return rc;
+  rc = launch_kernel("verify_decide", verify_decide_kernel<false>, dim3((a.R + 255) / 256), b256, stream, a);
+  if (rc) return rc;
+  if (vec_p && vec_d) rc = dispatch_residual<PT, DT, true, true>(a, stream);
+  else if (vec_p) rc = dispatch_residual<PT, DT, true, false>(a, stream);
+  else if (vec_d) rc = dispatch_residual<PT, DT, false, true>(a, stream);
+  else rc = dispatch_residual<PT, DT, false, false>(a, stream);
+  if (rc) return rc;
+  return launch_kernel("verify_sample", verify_sample_kernel<PT, DT>, dim3((a.R + 3) / 4), b256, stream, a);
+}
+
+int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N,
+               const int32_t* cu, const void* D, bool d_bf16, const void* W1, const void* W2, int r,
+               const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d,
+               uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
+               hipStream_t stream) {
+  const VerifyLayout l = verify_layout(R, V, N);
+  char* ws = reinterpret_cast<char*>(workspace);
+  VerifyArgs a{};
+  a.R = R;
+  a.K = K;
+  a.V = V;
+  a.N = N;
+  a.r = r;
+  const bool greedy = temperature == 0.f;
+  a.c2 = greedy ? 1.f : kLog2e / temperature;
+  a.P = P;
+  a.cu = cu;
+  a.D = D;
+  a.W1 = reinterpret_cast<const uint16_t*>(W1);
+  a.W2t = reinterpret_cast<const uint16_t*>(W2);
+  a.x0 = x0;
+  a.x = x;
+  a.q_tok = q_tok;
+  a.lse_d = lse_d;
+  a.seed = seed;
+  a.step = step;
+  a.n_acc_out = n_acc_out;
+  a.tok_out = tok_out;
+  a.ppart = reinterpret_cast<float2*>(ws + l.ppart);
+  a.rowms = reinterpret_cast<float2*>(ws + l.rowms);
+  a.flag = reinterpret_cast<int32_t*>(ws + l.flag);
+  a.info = reinterpret_cast<int4*>(ws + l.info);
+  a.rpart = reinterpret_cast<float*>(ws + l.rpart);
+  a.nsP = (V + kRowSlice - 1) / kRowSlice;
+  a.ns64 = (V + kWaveCols - 1) / kWaveCols;
+  a.nchunks = (V + kRowChunk - 1) / kRowChunk;
+  a.ncol_tiles = (V + kTileCols - 1) / kTileCols;
+  a.nstages = (R + kStageRows - 1) / kStageRows;
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
+  const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
+  const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
+  if (p_bf16 && d_bf16) return run_verify_typed<uint16_t, uint16_t>(a, greedy, vec_p, vec_d, stream);
+  if (p_bf16) return run_verify_typed<uint16_t, float>(a, greedy, vec_p, vec_d, stream);
+  if (d_bf16) return run_verify_typed<float, uint16_t>(a, greedy, vec_p, vec_d, stream);
+  return run_verify_typed<float, float>(a, greedy, vec_p, vec_d, stream);
+}
+
+}  // namespace dspark

@@ -1,0 +1,201 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft -> schedule -> verify hot path, gfx950.
+ *
+ * Three calls, following the problem statement on the pages that describe
+ * DSpark ("DSpark: Confidence-Scheduled Speculative Decoding with
+ * Semi-Autoregressive Generation", sections 2.1, 3.1, 3.2.2; restated in
+ * "Speculative decoding, from zero to DSpark", sections 2, 6, 8):
+ *
+ *   dspark_markov_draft  the sequential Markov head: adds W1[x_{k-1}] W2 to
+ *                        the backbone's base logits U_k, softmax, samples x_k
+ *                        left to right and keeps exact draft probabilities;
+ *   dspark_schedule      Algorithm 1: prefix-survival products, global sort,
+ *                        greedy admission against the SPS(B) cost table;
+ *   dspark_verify        rejection sampling over the flattened
+ *                        variable-length verify batch: accept with
+ *                        min(1, p/q), resample the first rejection from
+ *                        norm(max(0, p - q)), else draw a bonus token from p.
+ *
+ * Conventions (all calls):
+ *   - Array arguments are DEVICE pointers to caller-owned, contiguous,
+ *     row-major buffers.  The library never allocates, frees or retains them
+ *     and performs no host<->device synchronisation.  Scratch memory is the
+ *     caller-supplied `workspace` (size from the matching *_workspace_bytes
+ *     query, 256-byte aligned).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - The return value is a status.  Shape, pointer, dtype and workspace
+ *     errors are detected on the host before anything is enqueued (nothing is
+ *     written).  DSPARK_E_HIP means a launch failed.  Data-dependent errors
+ *     (token ids out of range, inconsistent cu_seqlens, confidences outside
+ *     [0, 1]) are reported through the outputs as documented per call; kernels
+ *     never read or write outside the buffers described here.
+ *   - Randomness: every random decision consumes one uniform
+ *     u = (w >> 8) * 2^-24 where w is the first word of Philox4x32-10
+ *     (Salmon et al., SC'11) with key (seed lo, seed hi) and counter
+ *     (step lo, step hi, request index, (position << 2) | purpose),
+ *     purpose 0 = draft sample, 1 = accept test, 2 = correction/bonus sample.
+ *     Every categorical draw is an inverse-CDF draw in ascending token id.
+ *   - Temperature T > 0 divides both draft and target logits; T == 0 selects
+ *     greedy decoding (first argmax; verify accepts iff argmax p == x).
+ *   - The Markov factors are bf16.  W1 is the V x r embedding table (row v at
+ *     W1 + v*r).  W2 (r x V in the pages' notation) is passed column-major:
+ *     column v, the r weights that produce logit v, is contiguous at W2 + v*r.
+ *     r must be a multiple of 8 and at most DSPARK_MAX_RANK; r == 0 means no
+ *     Markov head (W1 and W2 may then be NULL).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dspark_status {
+  DSPARK_OK = 0,
+  DSPARK_E_NULL = -1,      /* a required pointer is NULL */
+  DSPARK_E_SHAPE = -2,     /* a dimension is out of its documented range */
+  DSPARK_E_DTYPE = -3,     /* dtype code not supported for that argument */
+  DSPARK_E_RANGE = -4,     /* a scalar argument is out of range (temperature, mode, table length) */
+  DSPARK_E_WORKSPACE = -5, /* workspace NULL or smaller than the query */
+  DSPARK_E_HIP = -6        /* a HIP launch failed */
+};
+
+enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
+
+enum dspark_sched_mode {
+  DSPARK_SCHED_EARLY_STOP = 0, /* Algorithm 1: break at the first Theta <= Theta_best */
+  DSPARK_SCHED_GLOBAL = 1,     /* no break: best Theta on the sorted path (earliest on ties) */
+  DSPARK_SCHED_TOPK = 2        /* admit the first min(capacity, |E|) candidates */
+};
+
+#define DSPARK_MAX_K 16              /* draft positions per request */
+#define DSPARK_MAX_RANK 256          /* Markov rank r */
+#define DSPARK_MAX_CANDIDATES 16384  /* R * K for dspark_schedule */
+
+/* Human-readable text for a status code (static storage). */
+const char* dspark_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dspark_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Sequential Markov-head draft.  DSpark paper section 3.1 ("Sequential
+ * stage", "Markov head"); "Speculative decoding, from zero to DSpark",
+ * section 6 and Appendix A4.
+ *
+ * For k = 1..K in order and every request b:
+ *   z_k = (U[b,k-1,:] + W1[x_{k-1},:] W2) / T,  x_0 = x0[b]   (bias at every k)
+ *   x_k = inverse-CDF draw from softmax(z_k) with the uniform of (b, k, draft)
+ * Outputs (each [B, K]):
+ *   x_out      drafted token ids;
+ *   q_tok_out  q_k(x_k), the exact draft probability of the drawn token (1 when T == 0);
+ *   lse_out    log sum_v exp(z_k(v)) in natural-log units (when T == 0: the
+ *              largest biased logit).
+ * Inputs: U [B, K, V] (u_dtype f32 or bf16); W1 [V, r] and W2 (column-major
+ * r x V) bf16; x0 [B] int32.  Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
+ * r as in the header comment, B * V < 2^31.
+ * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
+ * that request's remaining positions x = -1, q_tok = lse = NaN.
+ * ------------------------------------------------------------------------ */
+size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r);
+int dspark_markov_draft(int B, int K, int V, int r, float temperature,
+                        const void* U, int u_dtype,
+                        const void* W1, const void* W2,
+                        const int32_t* x0,
+                        uint64_t seed, uint64_t step,
+                        int32_t* x_out, float* q_tok_out, float* lse_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Hardware-aware prefix scheduler.  DSpark paper section 3.2.2, Algorithm 1
+ * (modes GLOBAL and TOPK: section 5.2); "Speculative decoding, from zero to
+ * DSpark", section 8.
+ *
+ *   a[r,j] = c[r,1] * ... * c[r,j]   (float32, one rounding per factor)
+ *   candidates (r, j) with a > 0, sorted by a descending, then j ascending,
+ *   then r ascending; admitted greedily from B = R, tau = R, Theta = tau*SPS(B).
+ *   tau is accumulated in int64 fixed point (each a adds floor(a * 2^32));
+ *   Theta = double(tau) * 2^-32 * sps[B].
+ * Inputs: c [R, K] f32 in [0, 1]; sps [sps_len] f64, steps/s indexed by the
+ * verify batch size B (tokens), sps_len > R * (K + 1); capacity (TOPK only) >= 0.
+ * Outputs: a_out [R, K] f32; ell_out [R] int32 (verify lengths l*_r);
+ * cu_seqlens_out [R + 1] int32 (prefix sums of 1 + l*_r, the flattened verify
+ * layout); n_admitted_out [1] int32; theta_out [1] f64 (Theta of the choice).
+ * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R * K <= DSPARK_MAX_CANDIDATES.
+ * Data errors: any c outside [0, 1] or NaN gives ell = 0, cu_seqlens[r] = r,
+ * n_admitted = -1, theta = NaN (a valid no-draft layout).
+ * One workgroup; no workspace.
+ * ------------------------------------------------------------------------ */
+int dspark_schedule(int R, int K, const float* c,
+                    const double* sps, int sps_len,
+                    int mode, int capacity,
+                    float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out,
+                    int32_t* n_admitted_out, double* theta_out,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Rejection-sampling verification over the flattened variable-length batch.
+ * DSpark paper section 2.1 and section 5.3 (flattened variable-length
+ * batch); "Speculative decoding, from zero to DSpark", section 2 and
+ * Appendix A1; the five-step verification routine in the glean.smartcoder
+ * article on DSpark.
+ *
+ * Request r owns flat target rows cu_seqlens[r] .. cu_seqlens[r+1]-1 of P
+ * (l_r = cu_seqlens[r+1] - cu_seqlens[r] - 1 drafts, then the bonus row).
+ * For j = 1..l_r: p_j = softmax(P[cu[r]+j-1] / T); accept x_j iff
+ * u(r, j, accept) < p_j(x_j) / q_tok[r, j-1] (q_tok == 0 accepts).  At the first
+ * rejection the correction is drawn from norm(max(0, p_j - q_j)) with
+ * u(r, j, resample), q_j = softmax((D[r,j-1] + W1[x_{j-1}] W2) / T - lse_d),
+ * x_0 = x0[r]; if that mass is zero, from p_j.  If all l_r drafts survive the
+ * bonus is drawn from p_{l_r+1} with u(r, l_r + 1, resample).
+ * Inputs: P [N, V] (p_dtype), cu_seqlens [R+1] int32 with cu[0] = 0 and
+ * cu[R] = N; D [R, K, V] (d_dtype) draft base logits; W1/W2/r/x0 as for the
+ * draft (r == 0: no bias); x, q_tok, lse_d [R, K] as returned by
+ * dspark_markov_draft (q_tok, lse_d unused when T == 0).
+ * Outputs: n_acc_out [R] accepted drafts; tok_out [R] the correction or bonus
+ * token (emitted sequence: x_1..x_{n_acc}, tok).
+ * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), N * V < 2^31.
+ * Data errors: a request whose cu_seqlens slice is inconsistent (length < 1 or
+ * > K + 1, or outside [0, N]) or whose tokens are outside [0, V) gets
+ * n_acc = tok = -1.
+ * ------------------------------------------------------------------------ */
+size_t dspark_verify_workspace_bytes(int R, int K, int V, int r, int N);
+int dspark_verify(int R, int K, int V, float temperature,
+                  const void* P, int p_dtype, int N,
+                  const int32_t* cu_seqlens,
+                  const void* D, int d_dtype,
+                  const void* W1, const void* W2, int r,
+                  const int32_t* x0, const int32_t* x,
+                  const float* q_tok, const float* lse_d,
+                  uint64_t seed, uint64_t step,
+                  int32_t* n_acc_out, int32_t* tok_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * The per-decision uniforms themselves (the seeded counter-based stream the
+ * three calls consume): out[i] = u(seed, step, request i, position, purpose)
+ * for i in [0, n).  Limits: n >= 1, 0 <= position < 2^30, purpose in {0, 1, 2}.
+ * ------------------------------------------------------------------------ */
+int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Kernel timing (instrumentation, not part of the method).  While enabled,
+ * every kernel the calls above launch is bracketed by a pair of HIP events
+ * recorded on the caller's stream.  dspark_profiler_read waits for the
+ * recorded events and reports, per kernel name, the number of launches and the
+ * summed event time.  Host-side state, not thread-safe.
+ * ------------------------------------------------------------------------ */
+int dspark_profiler_enable(int on);
+int dspark_profiler_reset(void);
+/* index in [0, count); returns the number of distinct kernels when name == NULL. */
+int dspark_profiler_read(int index, const char** name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -60,11 +60,13 @@ def _first_argmax_and_gap(z):
     return idx, gap
 
 
-def draft_ref(U, W1, W2, x0, temperature, seed, step):
+def draft_ref(U, W1, W2, x0, temperature, seed, step, request_ids=None):
     """Draft K tokens per request with the Markov head.
 
     U: [B, K, V] base logits; W1: [V, r] or None; W2: [r, V] or None (r = 0,
-    no Markov head); x0: [B] anchors; temperature: float (0 = greedy).
+    no Markov head); x0: [B] anchors; temperature: float (0 = greedy);
+    request_ids: the requests' indices in their batch, which address their
+    uniforms (default 0..B-1; a subset of a batch passes its own indices).
     Returns dict with x [B, K] int64, q_tok [B, K] (q_k(x_k); 1 when greedy),
     lse [B, K] (log sum_v exp(z_k(v)); the max biased logit when greedy) and
     margin [B, K] (distance of the uniform from the chosen CDF bin's edges, or
@@ -81,7 +83,8 @@ def draft_ref(U, W1, W2, x0, temperature, seed, step):
     q_tok = np.zeros((B, K))
     lse = np.zeros((B, K))
     margin = np.zeros((B, K))
-    requests = np.arange(B)
+    rows = np.arange(B)
+    requests = rows if request_ids is None else np.asarray(request_ids, dtype=np.int64)
     for k in range(1, K + 1):                       # left to right over the block
         prev = x0 if k == 1 else x[:, k - 2]
         logits = U[:, k - 1, :].copy()
@@ -91,7 +94,7 @@ def draft_ref(U, W1, W2, x0, temperature, seed, step):
             tok, gap = _first_argmax_and_gap(logits)
             x[:, k - 1] = tok
             q_tok[:, k - 1] = 1.0
-            lse[:, k - 1] = logits[requests, tok]
+            lse[:, k - 1] = logits[rows, tok]
             margin[:, k - 1] = gap
             continue
         z = logits / temperature
@@ -102,7 +105,7 @@ def draft_ref(U, W1, W2, x0, temperature, seed, step):
         u = uniform(seed, step, requests, k, PURPOSE_DRAFT)
         tok, mg = _inverse_cdf(q, u)
         x[:, k - 1] = tok
-        q_tok[:, k - 1] = q[requests, tok]
+        q_tok[:, k - 1] = q[rows, tok]
         lse[:, k - 1] = m + np.log(s)
         margin[:, k - 1] = mg
     return {"x": x, "q_tok": q_tok, "lse": lse, "margin": margin}

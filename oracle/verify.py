@@ -69,12 +69,14 @@ def _top2_gap(z, idx):
     return z[rows, idx] - other.max(axis=1)
 
 
-def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step):
+def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step, request_ids=None):
     """Verify every request's scheduled prefix.
 
     P: [N, V] flat target logits (request r owns rows cu[r] .. cu[r+1]-1);
     cu_seqlens: [R+1]; D: [R, K, V] draft base logits; W1 [V, r] / W2 [r, V]
-    or None; x0: [R] anchors; x: [R, K] draft tokens; temperature (0 = greedy).
+    or None; x0: [R] anchors; x: [R, K] draft tokens; temperature (0 = greedy);
+    request_ids: the requests' indices in their batch, which address their
+    uniforms (default 0..R-1).
 
     Returns dict: n_acc [R], tok [R] (correction or bonus token), mode [R]
     (0 = bonus, 1 = correction), p_x / q_x / ratio [R, K] (NaN where a position
@@ -95,6 +97,7 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step):
     if np.any(ell < 0) or np.any(ell > K) or cu[0] != 0 or cu[-1] != P.shape[0]:
         raise ValueError("inconsistent cu_seqlens")
     greedy = temperature == 0
+    ids = np.arange(R) if request_ids is None else np.asarray(request_ids, dtype=np.int64)
 
     n_acc = np.full(R, -1, dtype=np.int64)
     tok = np.full(R, -1, dtype=np.int64)
@@ -134,7 +137,7 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step):
         pj, qj = p[rows, xj], q[rows, xj]
         with np.errstate(divide="ignore", invalid="ignore"):
             ratio = np.where(qj > 0, pj / qj, np.inf)
-        u = uniform(seed, step, rs, j, PURPOSE_ACCEPT)
+        u = uniform(seed, step, ids[rs], j, PURPOSE_ACCEPT)
         accepted = u < ratio
         p_x[rs, j - 1], q_x[rs, j - 1], ratio_out[rs, j - 1] = pj, qj, ratio
         accept_margin[rs, j - 1] = np.abs(u - ratio)
@@ -145,7 +148,7 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step):
         resid = _correction_distribution(p[sel], q[sel])
         zero = resid.sum(axis=1) <= 0
         resid[zero] = p[sel][zero]
-        u2 = uniform(seed, step, rej, j, PURPOSE_RESAMPLE)
+        u2 = uniform(seed, step, ids[rej], j, PURPOSE_RESAMPLE)
         y, mg = _inverse_cdf_unnormalised(resid, u2)
         n_acc[rej] = j - 1
         tok[rej] = y
@@ -164,7 +167,7 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step):
             sample_margin[rs] = _top2_gap(rows_bonus, top)
         else:
             p = _softmax(rows_bonus / temperature)
-            u2 = uniform(seed, step, rs, ell[rs] + 1, PURPOSE_RESAMPLE)
+            u2 = uniform(seed, step, ids[rs], ell[rs] + 1, PURPOSE_RESAMPLE)
             y, mg = _inverse_cdf_unnormalised(p, u2)
             tok[rs] = y
             sample_margin[rs] = mg

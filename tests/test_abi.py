@@ -1,0 +1,110 @@
+"""The C-ABI library: it loads, exports every entry point include/dspark.h
+declares, and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import __graft_entry__  # noqa: F401  (build helper)
+    from draft_verify_schedule_amd import binding
+    if not os.path.exists(binding.library_path()):
+        __graft_entry__.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("dspark_markov_draft", "dspark_schedule", "dspark_verify"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(-6, 1):
+        assert lib.dspark_status_string(st)
+    assert lib.dspark_version() >= 100
+
+
+def test_workspace_queries(lib):
+    assert lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 256) >= 512 * 2374 * 8
+    assert lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 256) % 256 == 0
+    assert lib.dspark_verify_workspace_bytes(512, 7, 151936, 256, 4096) > 0
+    assert lib.dspark_verify_workspace_bytes(0, 7, 10, 0, 1) == 0
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every case fails validation first
+
+
+def test_schedule_argument_errors(lib):
+    # R <= 0, K too large, too many candidates
+    assert lib.dspark_schedule(0, 7, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+    assert lib.dspark_schedule(4, 17, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+    assert lib.dspark_schedule(4096, 7, FAKE, FAKE, 10 ** 6, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+    # SPS table too short, bad mode, negative capacity
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 2, -1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
+    # NULL input
+    assert lib.dspark_schedule(4, 7, NULL, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -1
+
+
+def test_draft_argument_errors(lib):
+    f = ctypes.c_float
+    ws = ctypes.c_size_t(1 << 30)
+    base = dict(B=4, K=7, V=1024, r=16)
+
+    def call(B=4, K=7, V=1024, r=16, T=1.0, U=FAKE, dt=1, W1=FAKE, W2=FAKE, x0=FAKE, out=FAKE, wsp=FAKE, wsb=ws):
+        return lib.dspark_markov_draft(B, K, V, r, f(T), U, dt, W1, W2, x0, ctypes.c_uint64(1), ctypes.c_uint64(0),
+                                       out, out, out, wsp, wsb, NULL)
+    assert call(K=0) == -2
+    assert call(K=17) == -2
+    assert call(r=12) == -2          # not a multiple of 8
+    assert call(r=264) == -2         # above DSPARK_MAX_RANK
+    assert call(dt=5) == -3
+    assert call(T=-1.0) == -4
+    assert call(T=float("nan")) == -4
+    assert call(U=NULL) == -1
+    assert call(W1=NULL) == -1
+    assert call(wsb=ctypes.c_size_t(16)) == -5
+    assert call(wsp=NULL) == -5
+
+
+def test_verify_argument_errors(lib):
+    f = ctypes.c_float
+    ws = ctypes.c_size_t(1 << 30)
+
+    def call(R=4, K=7, V=1024, T=1.0, N=32, pdt=0, ddt=0, r=0, P=FAKE, q=FAKE, wsp=FAKE, wsb=ws):
+        return lib.dspark_verify(R, K, V, f(T), P, pdt, N, FAKE, FAKE, ddt, NULL, NULL, r, FAKE, FAKE, q, q,
+                                 ctypes.c_uint64(1), ctypes.c_uint64(0), FAKE, FAKE, wsp, wsb, NULL)
+    assert call(N=3) == -2           # fewer rows than requests
+    assert call(N=33) == -2          # more than R (K + 1)
+    assert call(pdt=7) == -3
+    assert call(T=-0.5) == -4
+    assert call(P=NULL) == -1
+    assert call(q=NULL) == -1        # T > 0 needs q_tok and lse_d
+    assert call(r=16) == -1          # Markov bias without factors
+    assert call(wsb=ctypes.c_size_t(0)) == -5
+
+
+def test_uniforms_argument_errors(lib):
+    assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 0, 1, 0, FAKE, NULL) == -2
+    assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 3, FAKE, NULL) == -4
+    assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 0, NULL, NULL) == -1

@@ -1,0 +1,353 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every test feeds both sides the same seeded inputs from
+draft_verify_schedule_amd.workloads (or an inline seeded generator for odd
+shapes); the oracle never sees an output of the HIP path.  Comparison rules
+are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+from tests.parity import Report, compare_draft, compare_verify
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import draft_verify_schedule_amd.binding as b
+    b.load_library()
+
+
+def ds():
+    import draft_verify_schedule_amd as m
+    return m
+
+
+def wl():
+    from draft_verify_schedule_amd import workloads
+    return workloads
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ uniforms
+@pytest.mark.parametrize("seed,step,position,purpose", [(0x5EED0001, 0, 1, 0), (7, 3, 5, 1),
+                                                        (2 ** 40 + 11, 2 ** 33 + 5, 8, 2)])
+def test_uniforms_bit_exact(seed, step, position, purpose):
+    n = 1 << 20
+    u = ds().dspark_uniforms(seed, step, n, position, purpose)
+    ref = oracle.uniform(seed, step, np.arange(n), position, purpose)
+    np.testing.assert_array_equal(u.cpu().numpy().astype(np.float64), ref)
+
+
+# --------------------------------------------------------------------- draft
+def _run_draft(U, W1, W2, x0, T, seed, step=0):
+    x, q, lse = ds().dspark_markov_draft(U.to(DEV), None if W1 is None else W1.to(DEV),
+                                         None if W2 is None else W2.to(DEV), x0.to(DEV), T, seed, step)
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), q.cpu().numpy(), lse.cpu().numpy()
+
+
+def _oracle_draft(U, W1, W2, x0, T, seed, step=0, request_ids=None):
+    return oracle.draft_ref(f64(U), None if W1 is None else f64(W1), None if W2 is None else f64(W2).T,
+                            x0.cpu().numpy(), T, seed, step, request_ids)
+
+
+def _random_draft_inputs(B, K, V, r, dtype, seed, scale=3.0, wscale=0.3):
+    g = torch.Generator().manual_seed(seed)
+    U = (torch.randn((B, K, V), generator=g) * scale).to(dtype)
+    W1 = W2 = None
+    if r:
+        W1 = (torch.randn((V, r), generator=g) * wscale).to(torch.bfloat16)
+        W2 = (torch.randn((V, r), generator=g) * wscale).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, dtype=torch.int32)
+    return U, W1, W2, x0
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_draft_tiny_workload(T):
+    w = wl().make("tiny")
+    _say("draft tiny T=%g" % T)
+    got = _run_draft(w.U, w.W1, w.W2, w.x0, T, w.rng_seed, 2)
+    ref = _oracle_draft(w.U, w.W1, w.W2, w.x0, T, w.rng_seed, 2)
+    rep = Report("draft tiny T=%g" % T)
+    same = compare_draft(rep, *got, ref, bf16_inputs=False, greedy=(T == 0))
+    rep.check_near_ties()
+    assert same.sum() >= 0.9 * same.size
+    _say(str(rep))
+
+
+@pytest.mark.parametrize("B,K,V,r,dtype,T", [
+    (37, 3, 1000, 24, torch.float32, 1.0),     # ragged rows and vocab tail, vector path
+    (5, 2, 1003, 8, torch.bfloat16, 1.0),      # V not a multiple of 8: scalar path
+    (70, 2, 4096, 256, torch.bfloat16, 1.0),   # full rank, two row stages
+    (3, 4, 64, 16, torch.float32, 0.9),        # a single slice
+    (1, 1, 7, 0, torch.float32, 1.0),          # V smaller than a wave, no Markov head
+    (17, 3, 2000, 64, torch.bfloat16, 0.0),    # greedy with bf16 ties
+    (9, 2, 520, 0, torch.bfloat16, 0.0),       # greedy, no bias, ragged tail
+])
+def test_draft_shapes(B, K, V, r, dtype, T):
+    _say("draft shape B=%d K=%d V=%d r=%d %s T=%g" % (B, K, V, r, dtype, T))
+    U, W1, W2, x0 = _random_draft_inputs(B, K, V, r, dtype, seed=B * 1000 + V)
+    got = _run_draft(U, W1, W2, x0, T, 99, 1)
+    ref = _oracle_draft(U, W1, W2, x0, T, 99, 1)
+    rep = Report("draft shape")
+    compare_draft(rep, *got, ref, bf16_inputs=(dtype == torch.bfloat16), greedy=(T == 0))
+    rep.check_near_ties()
+    _say(str(rep))
+
+
+def test_draft_invalid_anchor_flags_request():
+    U, W1, W2, x0 = _random_draft_inputs(4, 3, 256, 16, torch.float32, seed=5)
+    x0[1] = 256
+    x0[3] = -4
+    x, q, lse = _run_draft(U, W1, W2, x0, 1.0, 3)
+    assert np.all(x[[1, 3]] == -1) and np.all(np.isnan(q[[1, 3]]))
+    assert np.all((x[[0, 2]] >= 0) & (x[[0, 2]] < 256))
+
+
+# ------------------------------------------------------------------ schedule
+def _sched_gpu(c, sps, mode, cap=0):
+    out = ds().dspark_schedule(c.to(DEV), sps.to(DEV), mode, cap)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _sched_compare(c, sps, mode, cap=0):
+    got = _sched_gpu(c, sps, mode, cap)
+    ref = oracle.schedule_ref(c.numpy(), sps.numpy(), mode, cap)
+    np.testing.assert_array_equal(got["a"].view(np.uint32), ref["a"].view(np.uint32))
+    np.testing.assert_array_equal(got["ell"], ref["ell"])
+    np.testing.assert_array_equal(got["cu_seqlens"], ref["cu_seqlens"])
+    assert int(got["n_admitted"][0]) == ref["n_admitted"]
+    assert got["theta"].view(np.uint64)[0] == np.float64(ref["theta"]).view(np.uint64)
+    return got, ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds_stepped", "sched_stress", "full_step"])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_schedule_workloads_bit_exact(name, mode):
+    w = wl().make(name, device="cpu", V=64)      # V does not affect the schedule inputs
+    cap = (w.B * w.K) // 3
+    _say("schedule %s mode %d" % (name, mode))
+    got, ref = _sched_compare(w.c, w.sps, mode, cap)
+    _say("  n_admitted=%d theta=%.6f" % (ref["n_admitted"], ref["theta"]))
+
+
+def test_schedule_random_bit_exact():
+    rng = np.random.default_rng(77)
+    for i in range(60):
+        R = int(rng.integers(1, 600))
+        K = int(rng.integers(1, 17))
+        if R * K > 16384:
+            R = 16384 // K
+        c = rng.uniform(0, 1, size=(R, K)).astype(np.float32)
+        c[rng.uniform(size=(R, K)) < 0.1] = 1.0
+        c[rng.uniform(size=(R, K)) < 0.03] = 0.0
+        n = R * (K + 1) + 1 + int(rng.integers(0, 5))
+        kind = i % 3
+        if kind == 0:
+            sps = 1000.0 / (1.0 + np.arange(n) / rng.uniform(4, 400))
+        elif kind == 1:
+            sps = wl().sps_staircase(n, flat_until=max(64, int(R * rng.uniform(1, 5))))
+        else:
+            sps = rng.uniform(0.5, 2.0, size=n)
+        mode = int(rng.integers(0, 3))
+        _sched_compare(torch.from_numpy(c), torch.from_numpy(sps), mode, int(rng.integers(0, R * K + 2)))
+
+
+def test_schedule_maximum_candidates():
+    rng = np.random.default_rng(5)
+    c = torch.from_numpy(rng.uniform(0.3, 1, size=(1024, 16)).astype(np.float32))
+    sps = torch.from_numpy(wl().sps_staircase(1024 * 17 + 1, flat_until=4096))
+    for mode in (0, 1):
+        _sched_compare(c, sps, mode)
+
+
+def test_schedule_invalid_confidence():
+    c = torch.full((5, 3), 0.5)
+    c[2, 1] = float("nan")
+    got = _sched_gpu(c, torch.ones(64, dtype=torch.float64), 0)
+    assert got["n_admitted"][0] == -1 and np.isnan(got["theta"][0])
+    np.testing.assert_array_equal(got["cu_seqlens"], np.arange(6))
+
+
+# -------------------------------------------------------------------- verify
+def _verify_case(w, T, cu, x, q, lse, requests=None, step=0):
+    """GPU verify on (w, cu, x, q, lse) against the oracle's verify."""
+    P = wl().flat_target_rows(w.t, torch.as_tensor(cu, dtype=torch.int32))
+    n_acc, tok = ds().dspark_verify(P.to(DEV), torch.as_tensor(cu, dtype=torch.int32).to(DEV), w.U.to(DEV),
+                                    None if w.W1 is None else w.W1.to(DEV), None if w.W2 is None else w.W2.to(DEV),
+                                    w.x0.to(DEV), torch.as_tensor(x, dtype=torch.int32).to(DEV),
+                                    torch.as_tensor(q, dtype=torch.float32).to(DEV),
+                                    torch.as_tensor(lse, dtype=torch.float32).to(DEV), T, w.rng_seed, step)
+    torch.cuda.synchronize()
+    ref = oracle.verify_ref(f64(P), np.asarray(cu), f64(w.U), None if w.W1 is None else f64(w.W1),
+                            None if w.W2 is None else f64(w.W2).T, w.x0.numpy(), np.asarray(x), T, w.rng_seed, step)
+    return n_acc.cpu().numpy(), tok.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 1.0), ("tiny", 0.0), ("qwen_verify", 1.0), ("qwen_verify", 0.0)])
+def test_verify_all_positions(name, T):
+    w = wl().make(name)
+    _say("verify %s T=%g" % (name, T))
+    d = oracle.draft_ref(f64(w.U), None if w.W1 is None else f64(w.W1), None if w.W2 is None else f64(w.W2).T,
+                         w.x0.numpy(), T, w.rng_seed, 0)
+    cu = np.arange(0, w.B * (w.K + 1) + 1, w.K + 1)
+    n_acc, tok, ref = _verify_case(w, T, cu, d["x"], d["q_tok"], d["lse"])
+    rep = Report("verify %s T=%g" % (name, T))
+    compare_verify(rep, n_acc, tok, ref)
+    rep.check_near_ties()
+    _say(str(rep) + " mean n_acc %.3f" % n_acc.mean())
+
+
+@pytest.mark.parametrize("name", ["ds_stepped", "sched_stress"])
+def test_verify_scheduled_prefixes(name):
+    w = wl().make(name)
+    _say("verify scheduled %s" % name)
+    s = oracle.schedule_ref(w.c.numpy(), w.sps.numpy(), 0)
+    d = oracle.draft_ref(f64(w.U), None, None, w.x0.numpy(), 1.0, w.rng_seed, 0)
+    n_acc, tok, ref = _verify_case(w, 1.0, s["cu_seqlens"], d["x"], d["q_tok"], d["lse"])
+    rep = Report("verify %s" % name)
+    compare_verify(rep, n_acc, tok, ref)
+    rep.check_near_ties()
+    _say(str(rep) + " N=%d" % s["cu_seqlens"][-1])
+
+
+def test_verify_edge_layouts():
+    w = wl().make("tiny")
+    d = oracle.draft_ref(f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), 1.0, w.rng_seed, 0)
+    B, K = w.B, w.K
+    for ell in (np.zeros(B, dtype=np.int64), np.full(B, K), np.array([0, K, 1, 3])):
+        cu = np.concatenate([[0], np.cumsum(ell + 1)])
+        n_acc, tok, ref = _verify_case(w, 1.0, cu, d["x"], d["q_tok"], d["lse"], step=4)
+        rep = Report("edge")
+        compare_verify(rep, n_acc, tok, ref)
+        assert rep.near_ties == 0
+
+
+def test_verify_bad_tokens_flag_request():
+    w = wl().make("tiny")
+    d = oracle.draft_ref(f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), 1.0, w.rng_seed, 0)
+    x = d["x"].copy()
+    x[2, 0] = w.V + 5
+    cu = np.arange(0, w.B * (w.K + 1) + 1, w.K + 1)
+    P = wl().flat_target_rows(w.t, torch.as_tensor(cu, dtype=torch.int32))
+    n_acc, tok = ds().dspark_verify(P.to(DEV), torch.as_tensor(cu, dtype=torch.int32).to(DEV), w.U.to(DEV),
+                                    w.W1.to(DEV), w.W2.to(DEV), w.x0.to(DEV), torch.as_tensor(x, dtype=torch.int32).to(DEV),
+                                    torch.as_tensor(d["q_tok"], dtype=torch.float32).to(DEV),
+                                    torch.as_tensor(d["lse"], dtype=torch.float32).to(DEV), 1.0, w.rng_seed, 0)
+    torch.cuda.synchronize()
+    assert n_acc[2].item() == -1 and tok[2].item() == -1
+    assert all(n_acc[i].item() >= 0 for i in (0, 1, 3))
+
+
+def test_verify_p_equals_q_accepts_all():
+    """Target rows equal to the draft rows and no Markov head: every scheduled
+    draft is accepted (a counted near-tie aside) and the bonus is emitted."""
+    w = wl().make("qwen_verify", B=32)
+    t = torch.cat([w.U, w.t[:, w.K:]], dim=1).contiguous()
+    w.t = t
+    x, q, lse = ds().dspark_markov_draft(w.U.to(DEV), None, None, w.x0.to(DEV), 1.0, w.rng_seed, 0)
+    cu = np.arange(0, w.B * (w.K + 1) + 1, w.K + 1)
+    P = wl().flat_target_rows(t, torch.as_tensor(cu, dtype=torch.int32))
+    n_acc, tok = ds().dspark_verify(P.to(DEV), torch.as_tensor(cu, dtype=torch.int32).to(DEV), w.U.to(DEV), None,
+                                    None, w.x0.to(DEV), x, q, lse, 1.0, w.rng_seed, 0)
+    torch.cuda.synchronize()
+    assert (n_acc.cpu().numpy() == w.K).mean() >= 1 - 1e-3
+
+
+# ------------------------------------------------------------- whole step
+def _gpu_step(w, step=0, mode=0, dev_inputs=None):
+    U, W1, W2, x0, c, sps, t = dev_inputs or (w.U.to(DEV), w.W1.to(DEV), w.W2.to(DEV), w.x0.to(DEV), w.c.to(DEV),
+                                              w.sps.to(DEV), w.t.to(DEV))
+    x, q, lse = ds().dspark_markov_draft(U, W1, W2, x0, w.temperature, w.rng_seed, step)
+    s = ds().dspark_schedule(c, sps, mode)
+    cu = s["cu_seqlens"]
+    P = wl().flat_target_rows(t, cu)
+    n_acc, tok = ds().dspark_verify(P, cu, U, W1, W2, x0, x, q, lse, w.temperature, w.rng_seed, step)
+    torch.cuda.synchronize()
+    return {"x": x.cpu().numpy(), "q": q.cpu().numpy(), "lse": lse.cpu().numpy(),
+            "cu": cu.cpu().numpy(), "ell": s["ell"].cpu().numpy(), "n_acc": n_acc.cpu().numpy(),
+            "tok": tok.cpu().numpy()}
+
+
+def test_full_step_tiny():
+    w = wl().make("tiny")
+    for step in range(3):
+        g = _gpu_step(w, step)
+        tf = f64(w.t)
+        ref = oracle.run_step(f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), w.c.numpy(), w.sps.numpy(),
+                              lambda r, n: tf[r, :n], 1.0, w.rng_seed, step)
+        rep = Report("tiny step %d" % step)
+        same = compare_draft(rep, g["x"], g["q"], g["lse"], ref["draft"], bf16_inputs=False, greedy=False)
+        np.testing.assert_array_equal(g["cu"], ref["schedule"]["cu_seqlens"])
+        whole = [r for r in range(w.B) if same[r].all()]
+        compare_verify(rep, g["n_acc"], g["tok"], ref["verify"], whole)
+        rep.check_near_ties()
+
+
+def test_full_step_full_size_sampled():
+    """The full-step workload at its real shape (the benchmark's launch
+    configuration), GPU on all 512 requests; the oracle on a sample."""
+    w = wl().make("full_step", device=DEV)
+    _say("full step generated")
+    g = _gpu_step(w, step=0, dev_inputs=(w.U, w.W1, w.W2, w.x0, w.c, w.sps, w.t))
+    _say("full step gpu done: N=%d" % g["cu"][-1])
+    s = oracle.schedule_ref(w.c.cpu().numpy(), w.sps.cpu().numpy(), 0)
+    np.testing.assert_array_equal(g["cu"], s["cu_seqlens"])
+    sample = np.array([0, 1, 137, 256, 390, 511])
+    W1f, W2f = f64(w.W1), f64(w.W2).T
+    Us = f64(w.U[sample])
+    ref_d = oracle.draft_ref(Us, W1f, W2f, w.x0.cpu().numpy()[sample], 1.0, w.rng_seed, 0, request_ids=sample)
+    rep = Report("full step sampled")
+    same = compare_draft(rep, g["x"][sample], g["q"][sample], g["lse"][sample], ref_d, bf16_inputs=True,
+                         greedy=False)
+    ell = s["ell"][sample]
+    cu_s = np.concatenate([[0], np.cumsum(ell + 1)])
+    tf = w.t[sample].cpu()
+    P = torch.cat([tf[i, :ell[i] + 1] for i in range(len(sample))]).to(torch.float64).numpy()
+    ref_v = oracle.verify_ref(P, cu_s, Us, W1f, W2f, w.x0.cpu().numpy()[sample], ref_d["x"], 1.0, w.rng_seed, 0,
+                              request_ids=sample)
+    whole = [i for i in range(len(sample)) if same[i].all()]
+    compare_verify(rep, g["n_acc"][sample], g["tok"][sample], ref_v, whole)
+    rep.check_near_ties()
+    _say(str(rep) + " n_acc(sample)=%s" % g["n_acc"][sample].tolist())
+
+
+# ------------------------------------------------------- statistics on GPU
+def test_gpu_emitted_token_follows_target_and_acceptance_is_one_minus_tv():
+    n, V = 1_000_000, 8
+    lp = torch.tensor([1.5, -0.2, 0.3, 0.0, -1.1, 0.7, 0.2, -2.5])
+    lq = torch.tensor([-0.4, 0.4, 0.9, 0.8, -0.2, 0.3, 1.6, -1.0])
+    p = torch.softmax(lp.double(), 0).numpy()
+    q = torch.softmax(lq.double(), 0).numpy()
+    U = lq.expand(n, 1, V).contiguous().to(DEV)
+    x0 = torch.zeros(n, dtype=torch.int32, device=DEV)
+    x, qt, lse = ds().dspark_markov_draft(U, None, None, x0, 1.0, 4242, 0)
+    P = lp.expand(2 * n, V).contiguous().to(DEV)
+    cu = torch.arange(0, 2 * n + 1, 2, dtype=torch.int32, device=DEV)
+    n_acc, tok = ds().dspark_verify(P, cu, U, None, None, x0, x, qt, lse, 1.0, 4242, 0)
+    torch.cuda.synchronize()
+    n_acc, tok, x = n_acc.cpu().numpy(), tok.cpu().numpy(), x.cpu().numpy()[:, 0]
+    assert stats.chisquare(np.bincount(x, minlength=V), q * n).pvalue > 1e-6
+    alpha = np.minimum(p, q).sum()
+    assert abs((n_acc == 1).mean() - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / n)
+    first = np.where(n_acc >= 1, x, tok)
+    assert stats.chisquare(np.bincount(first, minlength=V), p * n).pvalue > 1e-6
