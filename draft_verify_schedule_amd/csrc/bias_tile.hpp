@@ -1,4 +1,4 @@
-// The rank-r Markov bias as an MFMA tile: for a stage of 64 rows (requests)
+// The rank-r Markov bias as an MFMA tile: for a stage of 128 rows (requests)
 // and one wave's 64 vocabulary columns, bias[m, n] = sum_i W1[prev_m, i] * W2[i, n]
 // on v_mfma_f32_16x16x32_bf16 (bf16 in, fp32 accumulate).  This is the one
 // dense contraction of the draft: B x r times r x V (DSpark paper, section
@@ -19,7 +19,8 @@
 
 namespace dspark {
 
-constexpr int kStageRows = 64;   // rows (requests) per LDS stage
+constexpr int kGroupsPerWG = 8;                  // 16-row MFMA groups per workgroup
+constexpr int kStageRows = 16 * kGroupsPerWG;     // rows (requests) per workgroup / LDS stage
 constexpr int kWaveCols = 64;    // vocabulary columns per wave (= one partial slice)
 constexpr int kTileCols = 256;   // columns per workgroup (4 waves)
 
@@ -47,59 +48,93 @@ __host__ __device__ inline int xcd_grid(int ncol_tiles, int nstages) {
   return 8 * nstages * ((ncol_tiles + 7) / 8);
 }
 
-// A-operand fragments of one wave's 64 columns (all r, in KC chunks of 32).
-template <int KC>
-__device__ __forceinline__ void load_w2_frags(const uint16_t* __restrict__ W2t, int r, int V,
-                                              int n0, int lane, bf16x8 (&fr)[4][KC]) {
-  const int a = lane & 15;
-  const int kq = (lane >> 4) * 8;
+// A-operand fragments of one wave's 64 columns (all r, in KC chunks of 32),
+// through a buffer resource over W2 (column-major, V * r bf16): the per-lane
+// part of the address is one VGPR, the block / chunk part is scalar.  Columns
+// past V read as zero.  For k >= r the fragment holds the next column's
+// weights; they meet zeros in E (staged as zero for k >= r) and add nothing.
+struct W2Frags {
+  rsrc_t rsrc;
+  uint32_t lane_off;   // bytes: lane's column within a block and its k group
+  uint32_t col_bytes;  // bytes per column (r * 2)
+  __device__ __forceinline__ void setup(const uint16_t* W2t, int r, int V, int lane) {
+    rsrc = make_rsrc(W2t, (uint32_t)V * (uint32_t)r * 2u);
+    const int a = lane & 15;
+    col_bytes = (uint32_t)r * 2u;
+    lane_off = (uint32_t)(16 * (a >> 2) + (a & 3)) * col_bytes + (uint32_t)((lane >> 4) * 8) * 2u;
+  }
+  template <int KC>
+  __device__ __forceinline__ void load(int n0, bf16x8 (&fr)[4][KC]) const {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int col = n0 + 16 * (a >> 2) + 4 * b + (a & 3);
+    for (int b = 0; b < 4; ++b) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int k = 32 * kc + kq;
-      if (col < V && k < r) {
-        fr[b][kc] = *reinterpret_cast<const bf16x8*>(W2t + (size_t)col * r + k);
-      } else {
-        fr[b][kc] = bf16x8{};
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint32_t soff = (uint32_t)(n0 + 4 * b) * col_bytes + (uint32_t)(64 * kc);
+        fr[b][kc] = __builtin_bit_cast(bf16x8, buffer_load16(rsrc, lane_off, soff));
       }
     }
   }
-}
+};
 
-// Stage E rows W1[prev(row)] of rows [row0, row0 + 64) into LDS (zeros for
-// rows past nrows, invalid previous tokens, or k >= r).  prev_of(row) returns
-// the previous token of that row or -1.  All 256 threads take part.
+// Stage E rows W1[prev(row)] of rows [row0, row0 + kStageRows) into LDS (zeros
+// for rows past nrows, invalid previous tokens, or k >= r).  prev_of(row)
+// returns the previous token of that row or -1.  All 256 threads take part:
+// two threads per row, each reading its row's token once and then issuing all
+// of its W1 loads back to back (unconditional loads from a valid address,
+// masked at the LDS store, so that nothing serialises them).
 template <int KC, typename PrevFn>
 __device__ __forceinline__ void stage_e(EStage<KC>& st, const uint16_t* __restrict__ W1, int r,
                                         int V, int row0, int nrows, PrevFn prev_of) {
   constexpr int kVecPerRow = 4 * KC;  // 16-byte vectors per padded row
-  for (int v = threadIdx.x; v < kStageRows * kVecPerRow; v += 256) {
-    const int row = v / kVecPerRow;
-    const int k = 8 * (v % kVecPerRow);
-    const int g = row0 + row;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (g < nrows && k < r) {
-      const int prev = prev_of(g);
-      if (prev >= 0 && prev < V)
-        val = *reinterpret_cast<const u32x4*>(W1 + (size_t)prev * r + k);
-    }
-    *reinterpret_cast<u32x4*>(&st.e[row][k]) = val;
+  constexpr int kThreadsPerRow = 256 / kStageRows;
+  constexpr int kVecPerThread = kVecPerRow / kThreadsPerRow;
+  static_assert(kVecPerRow % kThreadsPerRow == 0, "row split");
+  const int row = threadIdx.x / kThreadsPerRow;
+  const int part = threadIdx.x % kThreadsPerRow;
+  const int g = row0 + row;
+  const int prev = (g < nrows) ? prev_of(g) : -1;
+  const bool valid = prev >= 0 && prev < V;
+  const uint16_t* src = W1 + (size_t)(valid ? prev : 0) * r;
+  u32x4 vals[kVecPerThread];
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const int k = 8 * (part * kVecPerThread + i);
+    vals[i] = *reinterpret_cast<const u32x4*>(src + (k < r ? k : 0));
   }
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const int k = 8 * (part * kVecPerThread + i);
+    const bool keep = valid && k < r;
+    *reinterpret_cast<u32x4*>(&st.e[row][k]) = keep ? vals[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Byte offset of this lane's E fragment row within the stage (group 0,
+// chunk 0).  Callers that loop over column blocks pass it through
+// launder() once per block so that the compiler cannot hoist the (loop
+// invariant) LDS reads of all groups out of the loop and keep them live.
+template <int KC>
+__device__ __forceinline__ int e_lane_offset(int lane) {
+  return ((lane & 15) * EStage<KC>::kPitch + (lane >> 4) * 8) * 2;
+}
+
+__device__ __forceinline__ int launder(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // bias for 16 rows (group g of the stage) x the wave's 64 columns.
 // acc[b][i] = bias[row 16g + l%16, column n0 + 16*(l/16) + 4b + i].
 template <int KC>
 __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane,
-                                           const bf16x8 (&w2)[4][KC], f32x4 (&acc)[4]) {
+                                           const bf16x8 (&w2)[4][KC], f32x4 (&acc)[4],
+                                           int e_off = -1) {
   bf16x8 e[KC];
-  const int row = 16 * g + (lane & 15);
-  const int kq = (lane >> 4) * 8;
+  if (e_off < 0) e_off = e_lane_offset<KC>(lane);
+  const char* base = reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC>::kPitch * 2;
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
-    e[kc] = *reinterpret_cast<const bf16x8*>(&st.e[row][32 * kc + kq]);
+    e[kc] = *reinterpret_cast<const bf16x8*>(base + 64 * kc);
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -109,6 +144,104 @@ __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2[b][kc], e[kc], acc[b], 0, 0, 0);
   }
 }
+
+// The 16 logits a lane needs for one group (16 consecutive columns n.. of one
+// row), requested ahead of use.  Loads are unconditional (a masked vector is
+// read from column 0 of a valid row instead) so that no branch or register
+// copy sits between the request and its use; masking to -inf happens at
+// unpack time.  bf16 vectors stay packed (8 registers).
+template <typename T, bool VEC>
+struct GroupLogits {
+  float f[16];
+  __device__ __forceinline__ void load(const T* __restrict__ row, int n, int V) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = load_logit(row, (n + e < V) ? n + e : 0);
+  }
+  __device__ __forceinline__ void unpack(float out[16], int n, int V, bool live) const {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = (live && n + e < V) ? f[e] : -INFINITY;
+  }
+};
+
+template <>
+struct GroupLogits<float, true> {
+  f32x4 w[4];
+  __device__ __forceinline__ void load(const float* __restrict__ row, int n, int V) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[h] = *reinterpret_cast<const f32x4*>(row + ((n + 4 * h < V) ? n + 4 * h : 0));
+  }
+  __device__ __forceinline__ void unpack(float out[16], int n, int V, bool live) const {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const bool ok = live && n + 4 * h < V;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * h + e] = ok ? w[h][e] : -INFINITY;
+    }
+  }
+};
+
+template <>
+struct GroupLogits<uint16_t, true> {
+  u32x4 w[2];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int n, int V) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = *reinterpret_cast<const u32x4*>(row + ((n + 8 * h < V) ? n + 8 * h : 0));
+  }
+  __device__ __forceinline__ void unpack(float out[16], int n, int V, bool live) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = live && n + 8 * h < V;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[8 * h + 2 * e] = ok ? __uint_as_float(w[h][e] << 16) : -INFINITY;
+        out[8 * h + 2 * e + 1] = ok ? __uint_as_float(w[h][e] & 0xFFFF0000u) : -INFINITY;
+      }
+    }
+  }
+};
+
+// Group logits through a buffer resource (16-byte aligned rows): per-lane
+// offset in a VGPR, group / block offset scalar.
+template <typename T>
+struct GroupLogitsBuf;
+
+template <>
+struct GroupLogitsBuf<uint16_t> {
+  u32x4 w[2];
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    w[0] = buffer_load16(r, voff, soff);
+    w[1] = buffer_load16(r, voff, soff + 16u);
+  }
+  __device__ __forceinline__ void unpack(float out[16], int n, int V, bool live) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = live && n + 8 * h < V;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[8 * h + 2 * e] = ok ? __uint_as_float(w[h][e] << 16) : -INFINITY;
+        out[8 * h + 2 * e + 1] = ok ? __uint_as_float(w[h][e] & 0xFFFF0000u) : -INFINITY;
+      }
+    }
+  }
+};
+
+template <>
+struct GroupLogitsBuf<float> {
+  u32x4 w[4];
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t voff, uint32_t soff) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[h] = buffer_load16(r, voff, soff + 16u * h);
+  }
+  __device__ __forceinline__ void unpack(float out[16], int n, int V, bool live) const {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const bool ok = live && n + 4 * h < V;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * h + e] = ok ? __uint_as_float(w[h][e]) : -INFINITY;
+    }
+  }
+};
 
 // One bias value on the vector ALU (fp32 FMA in index order), used when a
 // single column of a single row is re-evaluated (the sampling re-scan).

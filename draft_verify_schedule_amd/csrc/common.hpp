@@ -59,6 +59,25 @@ __device__ __forceinline__ float decision_uniform(uint64_t seed, uint64_t step, 
   return (float)(w >> 8) * (1.0f / 16777216.0f);
 }
 
+// Raw buffer access: a buffer resource holds the base address and size; each
+// load takes a 32-bit per-lane byte offset (VGPR) plus a wave-uniform byte
+// offset (SGPR), so address arithmetic that is the same for the whole wave
+// stays in scalar registers.  Offsets at or past the size read as zero.
+// The fourth descriptor word is the gfx9-family data format (32-bit).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voffset, uint32_t soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, (int)soffset, 0));
+}
+
+// Hardware exp2 / log2 (v_exp_f32, v_log_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 // ---- wave64 helpers ------------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -95,8 +114,8 @@ __device__ __forceinline__ int wave_first_lane(bool pred) {
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;
-  const float a = (m == -INFINITY) ? 0.0f : s * exp2f(m - M);
-  const float b = (m2 == -INFINITY) ? 0.0f : s2 * exp2f(m2 - M);
+  const float a = (m == -INFINITY) ? 0.0f : s * fast_exp2(m - M);
+  const float b = (m2 == -INFINITY) ? 0.0f : s2 * fast_exp2(m2 - M);
   m = M;
   s = a + b;
 }

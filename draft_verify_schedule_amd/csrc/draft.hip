@@ -12,10 +12,14 @@
 //   draft_locate    one wave per request: merges the slice partials into the
 //                   normaliser, finds the slice where the CDF crosses u * S,
 //                   re-evaluates that slice's 64 logits and picks the token.
+#include <algorithm>
+
 #include "bias_tile.hpp"
 #include "launch.hpp"
 
 namespace dspark {
+
+constexpr int kPersistentWGs = 512;  // 2 per CU on 256 CUs
 
 struct DraftArgs {
   const void* U;           // [B, K, V]
@@ -34,98 +38,223 @@ struct DraftArgs {
   float* lse_out;
 };
 
-template <typename UT, bool VEC, int KC, bool GREEDY>
-__global__ __launch_bounds__(256) void draft_partials_kernel(DraftArgs a) {
-  int col_tile, stage;
-  if (!xcd_tile(blockIdx.x, a.ncol_tiles, a.nstages, col_tile, stage)) return;
+// Epilogue of one group: z = base logits + bias for 16 consecutive columns of
+// one row per lane; the four lanes sharing a row (l, l^16, l^32, l^48) cover the
+// wave's 64-column slice.  Writes the slice's (scaled max, sum exp2) or
+// (max, first argmax).
+template <bool GREEDY>
+__device__ __forceinline__ void slice_partial(const float (&z)[16], int cbase, int V, float c2, bool row_live,
+                                              float2* dst, int lane) {
+  if constexpr (GREEDY) {
+    float m = -INFINITY;
+    int idx = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (cbase + e < V && (idx < 0 || z[e] > m)) {
+        m = z[e];
+        idx = cbase + e;
+      }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(m, off, 64);
+      const int i2 = __shfl_xor(idx, off, 64);
+      merge_argmax(m, idx, m2, i2);
+    }
+    if (row_live && lane < 16) *dst = make_float2(m, __int_as_float(idx));
+  } else {
+    float m = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) m = fmaxf(m, z[e]);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float mc = m * c2;
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -mc));
+    }
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (row_live && lane < 16) *dst = make_float2(mc, s);
+  }
+}
+
+// Base-logit access of the fused pass.  Aligned rows (VEC) go through a
+// buffer resource: the lane's row-within-group and column offset is one VGPR,
+// the group and block offsets are scalar.  Rows past B read as zero (past the
+// resource) and are masked at unpack.  Unaligned rows use plain loads.
+template <typename UT, bool VEC>
+struct UAccess;
+
+template <typename UT>
+struct UAccess<UT, true> {
+  using Buf = GroupLogitsBuf<UT>;
+  rsrc_t rsrc;
+  uint32_t lane_off;
+  uint64_t row_bytes;  // K * V * sizeof(UT): request stride
+  __device__ __forceinline__ void setup(const DraftArgs& a, int lane) {
+    const UT* base = reinterpret_cast<const UT*>(a.U) + (size_t)(a.k - 1) * a.V;
+    const uint64_t total = ((uint64_t)a.B * a.K * a.V - (uint64_t)(a.k - 1) * a.V) * sizeof(UT);
+    rsrc = make_rsrc(base, (uint32_t)total);
+    row_bytes = (uint64_t)a.K * a.V * sizeof(UT);
+    lane_off = (uint32_t)((uint64_t)(lane & 15) * row_bytes + (uint64_t)(16 * (lane >> 4)) * sizeof(UT));
+  }
+  __device__ __forceinline__ void load(Buf& b, int row, int blk) const {
+    b.load(rsrc, lane_off, (uint32_t)((uint64_t)row * row_bytes + (uint64_t)blk * kWaveCols * sizeof(UT)));
+  }
+};
+
+template <typename UT>
+struct UAccess<UT, false> {
+  using Buf = GroupLogits<UT, false>;
+  const UT* U;
+  int B, K, V, k, lane;
+  __device__ __forceinline__ void setup(const DraftArgs& a, int lane_) {
+    U = reinterpret_cast<const UT*>(a.U);
+    B = a.B;
+    K = a.K;
+    V = a.V;
+    k = a.k;
+    lane = lane_;
+  }
+  __device__ __forceinline__ void load(Buf& b, int row, int blk) const {
+    const int rr = row + (lane & 15);
+    const UT* p = U + ((size_t)(rr < B ? rr : 0) * K + (k - 1)) * V;
+    b.load(p, blk * kWaveCols + 16 * (lane >> 4), V);
+  }
+};
+
+// Persistent workgroups: 4 waves, 128 rows (8 MFMA groups of 16), and a
+// contiguous range of 64-column blocks.  The W1 rows of the 128 requests are
+// staged in LDS once; each wave then sweeps the blocks w, w+4, ... of the
+// range, holding one block's W2 fragments in registers for all 8 groups.  The
+// (block, group) sequence is software-pipelined: several groups of base
+// logits are in flight (also across block boundaries), the MFMAs of group g+1
+// are issued before the epilogue of group g, and the next block's W2
+// fragments are requested as soon as the last MFMA of the current block has
+// issued.
+template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
+  int split, stage;
+  if (!xcd_tile(blockIdx.x, a.ncol_tiles, nstages, split, stage)) return;
+  stage += stage0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n0 = col_tile * kTileCols + wave * kWaveCols;
   const int row0 = stage * kStageRows;
+  const int ngroups = min(kGroupsPerWG, (a.B - row0 + 15) / 16);
+  const int nblocks = (a.V + kWaveCols - 1) / kWaveCols;
+  const int blk_begin = (int)((int64_t)split * nblocks / a.ncol_tiles);
+  const int blk_end = (int)((int64_t)(split + 1) * nblocks / a.ncol_tiles);
+  auto row_of = [&](int g) { return row0 + 16 * g + (lane & 15); };
+  auto row_live = [&](int g) { return row_of(g) < a.B; };
+  const int lane_col = 16 * (lane >> 4);
+
+  UAccess<UT, VEC> ua;
+  ua.setup(a, lane);
+  // groups of base logits in flight per wave: 8 registers per packed bf16 group, 16 per fp32
+  constexpr int kPrefetch = (VEC && sizeof(UT) == 2) ? 2 : 1;
+  typename UAccess<UT, VEC>::Buf buf[kPrefetch];
+  int blk = blk_begin + wave;
+  if (blk < blk_end) {
+#pragma unroll
+    for (int g = 0; g < kPrefetch; ++g)
+      if (g < ngroups) ua.load(buf[g], row0 + 16 * g, blk);
+  }
 
   __shared__ EStage<(KC > 0 ? KC : 1)> st;
   bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  W2Frags wf;
   if constexpr (KC > 0) {
     const int32_t* prev = a.prev;
     const int stride = a.prev_stride;
+    wf.setup(a.W2t, a.r, a.V, lane);
+    if (blk < blk_end) wf.load<KC>(blk * kWaveCols, w2);
     stage_e<KC>(st, a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
-    load_w2_frags<KC>(a.W2t, a.r, a.V, n0, lane, w2);
     __syncthreads();
   }
-  if (n0 >= a.V) return;
 
-  const UT* U = reinterpret_cast<const UT*>(a.U);
-  const int cbase = n0 + 16 * (lane >> 4);
-  const int slice = n0 / kWaveCols;
-  for (int g = 0; g < kStageRows / 16; ++g) {
-    const int row = row0 + 16 * g + (lane & 15);
-    if (row0 + 16 * g >= a.B) break;
-    float z[16];
-    const bool live = row < a.B;
-    if (live) {
-      const UT* urow = U + ((size_t)row * a.K + (a.k - 1)) * a.V;
-      Logits16<UT>::template load<VEC>(urow, cbase, a.V, z);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) z[e] = -INFINITY;
-    }
-    if constexpr (KC > 0) {
+  if constexpr (FULL) {
+    // full stage: static group count, the (block, group) sequence pipelined
+    // across block boundaries
+    for (; blk < blk_end; blk += 4) {
+      const int cbase = blk * kWaveCols + lane_col;
+      const int nxt_blk = blk + 4;
+      const bool has_next = nxt_blk < blk_end;
+      float2* part = a.part + blk;
+      const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1)>(lane));
       f32x4 acc[4];
-      mfma_group<KC>(st, g, lane, w2, acc);
+      if constexpr (KC > 0) mfma_group<KC>(st, 0, lane, w2, acc, e_off);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int g = 0; g < kGroupsPerWG; ++g) {
+        float z[16];
+        buf[g % kPrefetch].unpack(z, cbase, a.V, row_live(g));
+        if (g + kPrefetch < kGroupsPerWG) ua.load(buf[g % kPrefetch], row0 + 16 * (g + kPrefetch), blk);
+        else if (has_next) ua.load(buf[g % kPrefetch], row0 + 16 * (g + kPrefetch - kGroupsPerWG), nxt_blk);
+        if constexpr (KC > 0) {
+          // consume group g's bias, then reuse the accumulators for group g+1:
+          // its MFMAs run while the epilogue of group g executes
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
-    }
-    if constexpr (GREEDY) {
-      float m = -INFINITY;
-      int idx = -1;
+          for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (cbase + e < a.V && (z[e] > m || idx < 0)) {
-          m = z[e];
-          idx = cbase + e;
+            for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
+          if (g + 1 < kGroupsPerWG) mfma_group<KC>(st, g + 1, lane, w2, acc, e_off);
+          else if (has_next) wf.load<KC>(nxt_blk * kWaveCols, w2);
         }
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(m, off, 64);
-        const int i2 = __shfl_xor(idx, off, 64);
-        merge_argmax(m, idx, m2, i2);
+        slice_partial<GREEDY>(z, cbase, a.V, a.c2, row_live(g), part + (size_t)row_of(g) * a.nslices, lane);
       }
-      if (live && lane < 16) a.part[(size_t)row * a.nslices + slice] = make_float2(m, __int_as_float(idx));
-    } else {
-      float m = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        z[e] *= a.c2;
-        m = fmaxf(m, z[e]);
+    }
+  } else {
+    // partial stage (the last 128-row stage of a batch that is not a multiple
+    // of 128): plain per-group load, MFMA, epilogue
+    bool first = true;
+    for (; blk < blk_end; blk += 4) {
+      const int cbase = blk * kWaveCols + lane_col;
+      float2* part = a.part + blk;
+      if constexpr (KC > 0) {
+        if (!first) wf.load<KC>(blk * kWaveCols, w2);
       }
-      float s = 0.f;
-      if (m != -INFINITY) {
+      for (int g = 0; g < ngroups; ++g) {
+        typename UAccess<UT, VEC>::Buf one;
+        if (first && g < kPrefetch) one = buf[0];
+        ua.load(one, row0 + 16 * g, blk);
+        float z[16];
+        one.unpack(z, cbase, a.V, row_live(g));
+        if constexpr (KC > 0) {
+          f32x4 acc[4];
+          mfma_group<KC>(st, g, lane, w2, acc, launder(e_lane_offset<KC>(lane)));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s += exp2f(z[e] - m);
-      }
+          for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(m, off, 64);
-        const float s2 = __shfl_xor(s, off, 64);
-        merge_ms(m, s, m2, s2);
+            for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
+        }
+        slice_partial<GREEDY>(z, cbase, a.V, a.c2, row_live(g), part + (size_t)row_of(g) * a.nslices, lane);
       }
-      if (live && lane < 16) a.part[(size_t)row * a.nslices + slice] = make_float2(m, s);
+      first = false;
     }
   }
 }
 
-// One wave per request.
+// One workgroup (256 threads) per request.  Thread t owns a contiguous run
+// of slices; block reductions give the global max M and the normaliser
+// S = sum_s s_s 2^(m_s - M); a block scan of the per-thread sums finds the
+// thread whose run holds the crossing of u * S, that thread walks its run,
+// and wave 0 re-evaluates the chosen slice's 64 logits (one column per lane).
 template <typename UT, bool GREEDY>
 __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= a.B) return;
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  __shared__ float wave_tot[4];
+  __shared__ int sh_slice;
+  __shared__ float sh_before;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.x;
   const size_t out = (size_t)b * a.K + (a.k - 1);
   const int prev = a.prev[(size_t)b * a.prev_stride];
   if (prev < 0 || prev >= a.V) {
-    if (lane == 0) {
+    if (tid == 0) {
       a.x_out[out] = -1;
       a.q_out[out] = NAN;
       a.lse_out[out] = NAN;
@@ -134,11 +263,14 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   }
   const float2* part = a.part + (size_t)b * a.nslices;
   const int ns = a.nslices;
+  const int per = (ns + 255) / 256;
+  const int s0 = min(ns, tid * per);
+  const int s1 = min(ns, s0 + per);
 
   if constexpr (GREEDY) {
     float m = -INFINITY;
     int idx = -1;
-    for (int s = lane; s < ns; s += 64) {
+    for (int s = s0; s < s1; ++s) {
       const float2 p = part[s];
       merge_argmax(m, idx, p.x, __float_as_int(p.y));
     }
@@ -149,6 +281,12 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
       merge_argmax(m, idx, m2, i2);
     }
     if (lane == 0) {
+      red_f[wave] = m;
+      red_i[wave] = idx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < 4; ++w) merge_argmax(m, idx, red_f[w], red_i[w]);
       a.x_out[out] = idx;
       a.q_out[out] = 1.0f;
       a.lse_out[out] = m;
@@ -156,89 +294,112 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     return;
   }
 
-  // global max and normaliser S = sum_s s_s * 2^(m_s - M)
+  // global max
   float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part[s].x);
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, part[s].x);
   M = wave_max(M);
-  const int per = (ns + 63) / 64;
-  const int s_begin = min(ns, lane * per);
-  const int s_end = min(ns, s_begin + per);
-  float local = 0.f;
-  for (int s = s_begin; s < s_end; ++s) {
+  if (lane == 0) red_f[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  // per-thread mass and its block-wide inclusive scan (thread order = slice order)
+  auto weight = [&](int s) {
     const float2 p = part[s];
-    local += (p.x == -INFINITY) ? 0.f : p.y * exp2f(p.x - M);
-  }
-  const float incl = wave_inclusive_scan(local);
-  const float S = __shfl(incl, 63, 64);
+    return (p.x == -INFINITY) ? 0.f : p.y * fast_exp2(p.x - M);
+  };
+  float local = 0.f;
+  for (int s = s0; s < s1; ++s) local += weight(s);
+  float incl = wave_inclusive_scan(local);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  float before_wave = 0.f;
+  for (int w = 0; w < wave; ++w) before_wave += wave_tot[w];
+  incl += before_wave;
+  const float S = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
   const float u = decision_uniform(a.seed, a.step, (uint32_t)b, (uint32_t)a.k, kPurposeDraft);
   const float target = u * S;
-  int owner = wave_first_lane(incl > target);
-  if (owner < 0) {  // rounding put u*S at or past the total: last lane with mass
-    const unsigned long long m = __ballot(local > 0.f);
-    owner = m ? 63 - __clzll((long long)m) : 0;
+  // owner: first thread whose inclusive sum passes the target, else the last with mass
+  {
+    const int f = wave_first_lane(incl > target);
+    const unsigned long long mm = __ballot(local > 0.f);
+    if (lane == 0) {
+      red_i[wave] = f < 0 ? 0x7FFFFFFF : wave * 64 + f;
+      red_f[wave] = mm ? (float)(wave * 64 + 63 - __clzll((long long)mm)) : -1.f;
+    }
   }
-  // the owner walks its slices in order
-  int s_star = -1;
-  float before = 0.f;
-  if (lane == owner) {
+  __syncthreads();
+  int owner = min(min(red_i[0], red_i[1]), min(red_i[2], red_i[3]));
+  if (owner == 0x7FFFFFFF) {
+    const float last = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    owner = last < 0.f ? 0 : (int)last;
+  }
+  if (tid == owner) {
     float acc = incl - local;
-    int last = -1;
-    float last_before = acc;
-    for (int s = s_begin; s < s_end; ++s) {
-      const float2 p = part[s];
-      const float w = (p.x == -INFINITY) ? 0.f : p.y * exp2f(p.x - M);
+    int hit = -1, last = -1;
+    float hit_before = 0.f, last_before = acc;
+    for (int s = s0; s < s1; ++s) {
+      const float w = weight(s);
       if (w > 0.f) {
+        if (hit < 0 && acc + w > target) {
+          hit = s;
+          hit_before = acc;
+        }
         last = s;
         last_before = acc;
       }
-      if (acc + w > target && w > 0.f) {
-        s_star = s;
-        before = acc;
-        break;
-      }
       acc += w;
     }
-    if (s_star < 0) {
-      s_star = last;
-      before = last_before;
+    if (hit < 0) {
+      hit = last;
+      hit_before = last_before;
     }
+    sh_slice = hit < 0 ? 0 : hit;  // no mass at all (non-finite logits): stay in range
+    sh_before = hit_before;
   }
-  s_star = __shfl(s_star, owner, 64);
-  before = __shfl(before, owner, 64);
-  if (s_star < 0) s_star = 0;  // no mass at all (non-finite logits): keep indices in range
+  __syncthreads();
+  if (wave != 0) return;
+  const int s_star = sh_slice;
   const float m_s = part[s_star].x;
-  const float f_s = exp2f(m_s - M);
-  const float t_in = (target - before) / f_s;
+  const float t_in = (target - sh_before) / fast_exp2(m_s - M);
 
   // re-evaluate the 64 logits of slice s_star, one column per lane
   const int col = s_star * kWaveCols + lane;
-  float z2 = -INFINITY;
+  float z = -INFINITY;
   if (col < a.V) {
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((size_t)b * a.K + (a.k - 1)) * a.V;
-    float z = load_logit(urow, col);
+    z = load_logit(urow, col);
     if (a.r > 0) z += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
-    z2 = z * a.c2;
   }
-  const float e = (col < a.V) ? exp2f(z2 - m_s) : 0.f;
+  const float e = (col < a.V) ? fast_exp2(fmaf(z, a.c2, -m_s)) : 0.f;
   const float cum = wave_inclusive_scan(e);
   int pick = wave_first_lane(cum > t_in && e > 0.f);
   if (pick < 0) {
-    const unsigned long long m = __ballot(e > 0.f);
-    pick = m ? 63 - __clzll((long long)m) : 0;
+    const unsigned long long mm = __ballot(e > 0.f);
+    pick = mm ? 63 - __clzll((long long)mm) : 0;
   }
-  const float z2x = __shfl(z2, pick, 64);
+  const float zx = __shfl(z, pick, 64);
   if (lane == 0) {
     a.x_out[out] = s_star * kWaveCols + pick;
-    a.q_out[out] = exp2f(z2x - M) / S;
-    a.lse_out[out] = (M + log2f(S)) * kLn2;
+    a.q_out[out] = fast_exp2(fmaf(zx, a.c2, -M)) / S;
+    a.lse_out[out] = (M + fast_log2(S)) * kLn2;
   }
 }
 
+// Full 128-row stages and the trailing partial stage (B not a multiple of
+// 128) are separate launches of separately register-allocated variants.
 template <typename UT, bool VEC, int KC, bool GREEDY>
 static int launch_partials(const DraftArgs& a, hipStream_t stream) {
-  const int grid = xcd_grid(a.ncol_tiles, a.nstages);
-  return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY>, dim3(grid),
-                       dim3(256), stream, a);
+  const int full = VEC ? a.B / kStageRows : 0;  // unaligned rows: the plain variant throughout
+  const int partial = a.nstages - full;
+  if (full > 0) {
+    const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true>,
+                                 dim3(xcd_grid(a.ncol_tiles, full)), dim3(256), stream, a, 0, full);
+    if (rc) return rc;
+  }
+  if (partial > 0) {
+    return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, false>,
+                         dim3(xcd_grid(a.ncol_tiles, partial)), dim3(256), stream, a, full, partial);
+  }
+  return 0;
 }
 
 template <typename UT, bool VEC, bool GREEDY>
@@ -269,8 +430,7 @@ static int run_draft_typed(DraftArgs a, bool vec, hipStream_t stream) {
     }
     int rc = vec ? dispatch_kc<UT, true, GREEDY>(a, stream) : dispatch_kc<UT, false, GREEDY>(a, stream);
     if (rc) return rc;
-    rc = launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3((a.B + 3) / 4), dim3(256),
-                       stream, a);
+    rc = launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3(a.B), dim3(256), stream, a);
     if (rc) return rc;
   }
   return 0;
@@ -295,8 +455,10 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   a.V = V;
   a.r = r;
   a.nslices = (V + kWaveCols - 1) / kWaveCols;
-  a.ncol_tiles = (V + kTileCols - 1) / kTileCols;
+  // persistent grid: about two workgroups per CU; column ranges split the
+  // 64-column blocks evenly, row stages of 128 requests
   a.nstages = (B + kStageRows - 1) / kStageRows;
+  a.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / a.nstages));
   a.part = reinterpret_cast<float2*>(workspace);
   a.seed = seed;
   a.step = step;

@@ -277,7 +277,11 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------- residual --
-// max(0, p - q) over the rejected position, 64-column slice masses.
+// max(0, p - q) over the rejected position, 64-column slice masses.  Same
+// tiling and software pipeline as the draft's fused pass: 4 waves x 64
+// columns, 128 requests (8 MFMA groups) per workgroup, W2 fragments held in
+// registers, the target and draft rows of group g+2 requested before the
+// epilogue of group g.  Requests that are not correcting take no loads.
 template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC>
 __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   int col_tile, stage;
@@ -286,6 +290,30 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   const int wave = threadIdx.x >> 6;
   const int n0 = col_tile * kTileCols + wave * kWaveCols;
   const int row0 = stage * kStageRows;
+  const int ngroups = min(kGroupsPerWG, (a.R - row0 + 15) / 16);
+  const bool col_live = n0 < a.V;
+  const int cbase = n0 + 16 * (lane >> 4);
+  const int slice = n0 / kWaveCols;
+  auto req = [&](int g) { return row0 + 16 * g + (lane & 15); };
+  // requests that do not correct (or lie past R) read row 0 and are masked
+  auto info_of = [&](int g) { return req(g) < a.R ? a.info[req(g)] : make_int4(-1, 0, 0, 0); };
+  auto prow = [&](const int4& in) {
+    return reinterpret_cast<const PT*>(a.P) + (size_t)(in.x == 1 ? in.y : 0) * a.V;
+  };
+  auto drow = [&](int g, const int4& in) {
+    return reinterpret_cast<const DT*>(a.D) + (in.x == 1 ? ((size_t)req(g) * a.K + in.w) * a.V : 0);
+  };
+
+  GroupLogits<PT, VEC_P> pb0, pb1;
+  GroupLogits<DT, VEC_D> db0, db1;
+  int4 in0 = info_of(0), in1 = make_int4(-1, 0, 0, 0);
+  pb0.load(prow(in0), cbase, a.V);
+  db0.load(drow(0, in0), cbase, a.V);
+  if (ngroups > 1) {
+    in1 = info_of(1);
+    pb1.load(prow(in1), cbase, a.V);
+    db1.load(drow(1, in1), cbase, a.V);
+  }
 
   __shared__ EStage<(KC > 0 ? KC : 1)> st;
   bf16x8 w2[4][(KC > 0 ? KC : 1)];
@@ -299,51 +327,70 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
       if (in.x != 1) return -1;
       return in.w == 0 ? x0[g] : x[(size_t)g * K + in.w - 1];
     });
-    load_w2_frags<KC>(a.W2t, a.r, a.V, n0, lane, w2);
+    if (col_live) {
+      W2Frags wf;
+      wf.setup(a.W2t, a.r, a.V, lane);
+      wf.load<KC>(n0, w2);
+    }
     __syncthreads();
   }
-  if (n0 >= a.V) return;
-  const int cbase = n0 + 16 * (lane >> 4);
-  const int slice = n0 / kWaveCols;
-  for (int g = 0; g < kStageRows / 16; ++g) {
-    if (row0 + 16 * g >= a.R) break;
-    const int rq = row0 + 16 * g + (lane & 15);
-    int4 in = make_int4(-1, 0, 0, 0);
-    if (rq < a.R) in = a.info[rq];
-    const bool live = in.x == 1;
+  if (!col_live) return;
+
+  f32x4 acc[4], nxt[4];
+  if constexpr (KC > 0) mfma_group<KC>(st, 0, lane, w2, acc);
+#pragma unroll
+  for (int g = 0; g < kGroupsPerWG; ++g) {
+    if (g >= ngroups) break;
+    if constexpr (KC > 0) {
+      if (g + 1 < ngroups) mfma_group<KC>(st, g + 1, lane, w2, nxt);
+    }
     float t[16], z[16];
-    float lp = 0.f, lq = 0.f;
-    if (live) {
-      const float2 ms = a.rowms[in.y];
-      lp = ms.x + log2f(ms.y);
-      lq = a.lse_d[(size_t)rq * a.K + in.w] * kLog2e;
-      const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)in.y * a.V;
-      const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)rq * a.K + in.w) * a.V;
-      Logits16<PT>::template load<VEC_P>(prow, cbase, a.V, t);
-      Logits16<DT>::template load<VEC_D>(drow, cbase, a.V, z);
+    int4 in;
+    if (g & 1) {
+      in = in1;
+      pb1.unpack(t, cbase, a.V, in.x == 1);
+      db1.unpack(z, cbase, a.V, in.x == 1);
+      if (g + 2 < ngroups) {
+        in1 = info_of(g + 2);
+        pb1.load(prow(in1), cbase, a.V);
+        db1.load(drow(g + 2, in1), cbase, a.V);
+      }
+    } else {
+      in = in0;
+      pb0.unpack(t, cbase, a.V, in.x == 1);
+      db0.unpack(z, cbase, a.V, in.x == 1);
+      if (g + 2 < ngroups) {
+        in0 = info_of(g + 2);
+        pb0.load(prow(in0), cbase, a.V);
+        db0.load(drow(g + 2, in0), cbase, a.V);
+      }
     }
     if constexpr (KC > 0) {
-      f32x4 acc[4];
-      mfma_group<KC>(st, g, lane, w2, acc);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
+      if (g + 1 < ngroups) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b] = nxt[b];
+      }
     }
+    const bool live = in.x == 1;
     float s = 0.f;
     if (live) {
+      const float2 ms = a.rowms[in.y];
+      const float lp = ms.x + fast_log2(ms.y);
+      const float lq = a.lse_d[(size_t)req(g) * a.K + in.w] * kLog2e;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (cbase + e < a.V) {
-          const float p = exp2f(t[e] * a.c2 - lp);
-          const float q = exp2f(z[e] * a.c2 - lq);
-          s += fmaxf(p - q, 0.f);
-        }
+        const float p = fast_exp2(fmaf(t[e], a.c2, -lp));
+        const float q = fast_exp2(fmaf(z[e], a.c2, -lq));
+        s += fmaxf(p - q, 0.f);
       }
     }
     s += __shfl_xor(s, 16, 64);
     s += __shfl_xor(s, 32, 64);
-    if (live && lane < 16) a.rpart[(size_t)rq * a.ns64 + slice] = s;
+    if (live && lane < 16) a.rpart[(size_t)req(g) * a.ns64 + slice] = s;
   }
 }
 
@@ -405,7 +452,7 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)in.z, kPurposeResample);
   const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)in.y * a.V;
   const float2 ms = a.rowms[in.y];
-  const float lp = ms.x + log2f(ms.y);
+  const float lp = ms.x + fast_log2(ms.y);
   bool use_p = in.x == 0;
 
   if (!use_p) {
@@ -429,8 +476,8 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
         float zq = load_logit(drow, col);
         if (a.r > 0) zq += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
         const float lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
-        const float p = exp2f(load_logit(prow, col) * a.c2 - lp);
-        const float q = exp2f(zq * a.c2 - lq);
+        const float p = fast_exp2(fmaf(load_logit(prow, col), a.c2, -lp));
+        const float q = fast_exp2(fmaf(zq, a.c2, -lq));
         rho = fmaxf(p - q, 0.f);
       }
       const float cum = wave_inclusive_scan(rho);
