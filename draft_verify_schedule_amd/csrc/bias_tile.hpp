@@ -125,7 +125,9 @@ __device__ __forceinline__ int launder(int v) {
 
 // bias for 16 rows (group g of the stage) x the wave's 64 columns.
 // acc[b][i] = bias[row 16g + l%16, column n0 + 16*(l/16) + 4b + i].
-template <int KC>
+// With ZERO = false the accumulators arrive holding the base logits of the
+// same 16 x 64 tile, so the MFMAs leave base + bias in them directly.
+template <int KC, bool ZERO = true>
 __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane,
                                            const bf16x8 (&w2)[4][KC], f32x4 (&acc)[4],
                                            int e_off = -1) {
@@ -135,8 +137,10 @@ __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
     e[kc] = *reinterpret_cast<const bf16x8*>(base + 64 * kc);
+  if constexpr (ZERO) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll

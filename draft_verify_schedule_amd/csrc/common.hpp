@@ -92,6 +92,45 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Combine each lane's value with those of lanes l^16, l^32, l^48 (the same
+// position in the other three 16-lane rows) using the gfx950 row-swap
+// instructions, which run on the vector ALU instead of the LDS crossbar.
+// Each swap of a register with itself hands every lane its own row's value
+// and the partner row's value; the combine is symmetric, so which of the two
+// comes first does not matter.
+__device__ __forceinline__ void row_pair16(float v, float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void row_pair32(float v, float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void row_pair16(int v, int& a, int& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  a = (int)p[0];
+  b = (int)p[1];
+}
+__device__ __forceinline__ void row_pair32(int v, int& a, int& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  a = (int)p[0];
+  b = (int)p[1];
+}
+__device__ __forceinline__ float rows_max(float v) {
+  float a, b;
+  row_pair16(v, a, b);
+  row_pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  float a, b;
+  row_pair16(v, a, b);
+  row_pair32(a + b, a, b);
+  return a + b;
+}
+
 // Inclusive prefix sum across the 64 lanes in lane order.
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -54,28 +54,30 @@ __device__ __forceinline__ void slice_partial(const float (&z)[16], int cbase, i
         m = z[e];
         idx = cbase + e;
       }
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float m2 = __shfl_xor(m, off, 64);
-      const int i2 = __shfl_xor(idx, off, 64);
-      merge_argmax(m, idx, m2, i2);
+    {
+      float ma, mb;
+      int ia, ib;
+      row_pair16(m, ma, mb);
+      row_pair16(idx, ia, ib);
+      merge_argmax(ma, ia, mb, ib);
+      row_pair32(ma, m, mb);
+      row_pair32(ia, idx, ib);
+      merge_argmax(m, idx, mb, ib);
     }
     if (row_live && lane < 16) *dst = make_float2(m, __int_as_float(idx));
   } else {
     float m = z[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) m = fmaxf(m, z[e]);
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const float mc = m * c2;
+    m = rows_max(m);
+    // branch-free: a slice with no finite logit gets exp2(-inf) = 0 terms
+    const bool empty = m == -INFINITY;
+    const float mc = empty ? 0.f : m * c2;
     float s = 0.f;
-    if (m != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -mc));
-    }
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    if (row_live && lane < 16) *dst = make_float2(mc, s);
+    for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -mc));
+    s = rows_sum(s);
+    if (row_live && lane < 16) *dst = make_float2(empty ? -INFINITY : mc, s);
   }
 }
 
@@ -175,31 +177,48 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   }
 
   if constexpr (FULL) {
-    // full stage: static group count, the (block, group) sequence pipelined
-    // across block boundaries
+    // full stage: static group count; the (block, group) sequence is
+    // pipelined across block boundaries.  Group h's base logits sit in
+    // buf[h % kPrefetch] until they seed h's accumulators (one iteration
+    // before h's epilogue), and the freed slot is refilled kPrefetch groups
+    // ahead.
+    static_assert(kGroupsPerWG % kPrefetch == 0, "ring");
     for (; blk < blk_end; blk += 4) {
       const int cbase = blk * kWaveCols + lane_col;
       const int nxt_blk = blk + 4;
       const bool has_next = nxt_blk < blk_end;
       float2* part = a.part + blk;
       const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1)>(lane));
+      auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
+        if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
+        else if (has_next) ua.load(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt_blk);
+      };
       f32x4 acc[4];
-      if constexpr (KC > 0) mfma_group<KC>(st, 0, lane, w2, acc, e_off);
+      {
+        float u[16];
+        buf[0].unpack(u, cbase, a.V, row_live(0));
+        refill(kPrefetch);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
+        if constexpr (KC > 0) mfma_group<KC, false>(st, 0, lane, w2, acc, e_off);
+      }
 #pragma unroll
       for (int g = 0; g < kGroupsPerWG; ++g) {
         float z[16];
-        buf[g % kPrefetch].unpack(z, cbase, a.V, row_live(g));
-        if (g + kPrefetch < kGroupsPerWG) ua.load(buf[g % kPrefetch], row0 + 16 * (g + kPrefetch), blk);
-        else if (has_next) ua.load(buf[g % kPrefetch], row0 + 16 * (g + kPrefetch - kGroupsPerWG), nxt_blk);
-        if constexpr (KC > 0) {
-          // consume group g's bias, then reuse the accumulators for group g+1:
-          // its MFMAs run while the epilogue of group g executes
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
-          if (g + 1 < kGroupsPerWG) mfma_group<KC>(st, g + 1, lane, w2, acc, e_off);
-          else if (has_next) wf.load<KC>(nxt_blk * kWaveCols, w2);
+          for (int i = 0; i < 4; ++i) z[4 * b + i] = acc[b][i];
+        if (g + 1 < kGroupsPerWG) {
+          float u[16];
+          buf[(g + 1) % kPrefetch].unpack(u, cbase, a.V, row_live(g + 1));
+          refill(g + 1 + kPrefetch);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
+          // group g+1's MFMAs run while group g's epilogue executes
+          if constexpr (KC > 0) mfma_group<KC, false>(st, g + 1, lane, w2, acc, e_off);
+        } else if (KC > 0 && has_next) {
+          wf.load<(KC > 0 ? KC : 1)>(nxt_blk * kWaveCols, w2);
         }
         slice_partial<GREEDY>(z, cbase, a.V, a.c2, row_live(g), part + (size_t)row_of(g) * a.nslices, lane);
       }
@@ -236,10 +255,14 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
 }
 
 // One workgroup (256 threads) per request.  Thread t owns a contiguous run
-// of slices; block reductions give the global max M and the normaliser
-// S = sum_s s_s 2^(m_s - M); a block scan of the per-thread sums finds the
-// thread whose run holds the crossing of u * S, that thread walks its run,
-// and wave 0 re-evaluates the chosen slice's 64 logits (one column per lane).
+// of at most kLocPer slices, read once into registers; block reductions give
+// the global max M and the normaliser S = sum_s s_s 2^(m_s - M); a block scan
+// of the per-thread sums finds the thread whose run holds the crossing of
+// u * S, that thread walks its run (in registers), and wave 0 re-evaluates
+// the chosen slice's 64 logits (one column per lane).  Rows with more than
+// 256 * kLocPer slices take the same steps with reloads.
+constexpr int kLocPer = 16;
+
 template <typename UT, bool GREEDY>
 __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   __shared__ float red_f[4];
@@ -253,6 +276,17 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   const int b = blockIdx.x;
   const size_t out = (size_t)b * a.K + (a.k - 1);
   const int prev = a.prev[(size_t)b * a.prev_stride];
+  const float2* part = a.part + (size_t)b * a.nslices;
+  const int ns = a.nslices;
+  const int per = (ns + 255) / 256;
+  const int s0 = min(ns, tid * per);
+  const int s1 = min(ns, s0 + per);
+  const bool in_regs = per <= kLocPer;
+  float2 p[kLocPer];
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kLocPer; ++i) p[i] = (s0 + i < s1) ? part[s0 + i] : make_float2(-INFINITY, 0.f);
+  }
   if (prev < 0 || prev >= a.V) {
     if (tid == 0) {
       a.x_out[out] = -1;
@@ -261,18 +295,16 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     }
     return;
   }
-  const float2* part = a.part + (size_t)b * a.nslices;
-  const int ns = a.nslices;
-  const int per = (ns + 255) / 256;
-  const int s0 = min(ns, tid * per);
-  const int s1 = min(ns, s0 + per);
 
   if constexpr (GREEDY) {
     float m = -INFINITY;
     int idx = -1;
-    for (int s = s0; s < s1; ++s) {
-      const float2 p = part[s];
-      merge_argmax(m, idx, p.x, __float_as_int(p.y));
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kLocPer; ++i)
+        if (s0 + i < s1) merge_argmax(m, idx, p[i].x, __float_as_int(p[i].y));
+    } else {
+      for (int s = s0; s < s1; ++s) merge_argmax(m, idx, part[s].x, __float_as_int(part[s].y));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -296,25 +328,32 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
 
   // global max
   float M = -INFINITY;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, part[s].x);
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kLocPer; ++i) M = fmaxf(M, p[i].x);
+  } else {
+    for (int s = s0; s < s1; ++s) M = fmaxf(M, part[s].x);
+  }
   M = wave_max(M);
   if (lane == 0) red_f[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  auto weight = [&](float2 q) { return (q.x == -INFINITY) ? 0.f : q.y * fast_exp2(q.x - M); };
   // per-thread mass and its block-wide inclusive scan (thread order = slice order)
-  auto weight = [&](int s) {
-    const float2 p = part[s];
-    return (p.x == -INFINITY) ? 0.f : p.y * fast_exp2(p.x - M);
-  };
   float local = 0.f;
-  for (int s = s0; s < s1; ++s) local += weight(s);
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kLocPer; ++i) local += weight(p[i]);
+  } else {
+    for (int s = s0; s < s1; ++s) local += weight(part[s]);
+  }
   float incl = wave_inclusive_scan(local);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   float before_wave = 0.f;
   for (int w = 0; w < wave; ++w) before_wave += wave_tot[w];
   incl += before_wave;
-  const float S = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  const float S = ((wave_tot[0] + wave_tot[1]) + wave_tot[2]) + wave_tot[3];
   const float u = decision_uniform(a.seed, a.step, (uint32_t)b, (uint32_t)a.k, kPurposeDraft);
   const float target = u * S;
   // owner: first thread whose inclusive sum passes the target, else the last with mass
@@ -336,8 +375,7 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     float acc = incl - local;
     int hit = -1, last = -1;
     float hit_before = 0.f, last_before = acc;
-    for (int s = s0; s < s1; ++s) {
-      const float w = weight(s);
+    auto visit = [&](int s, float w) {
       if (w > 0.f) {
         if (hit < 0 && acc + w > target) {
           hit = s;
@@ -347,6 +385,13 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
         last_before = acc;
       }
       acc += w;
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kLocPer; ++i)
+        if (s0 + i < s1) visit(s0 + i, weight(p[i]));
+    } else {
+      for (int s = s0; s < s1; ++s) visit(s, weight(part[s]));
     }
     if (hit < 0) {
       hit = last;
