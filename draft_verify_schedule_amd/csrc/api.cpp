@@ -81,6 +81,9 @@ void profiler_end(hipStream_t stream) {
 
 namespace {
 bool is_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+uint64_t dtype_bytes(int d) { return d == DSPARK_BF16 ? 2 : 4; }
+// Kernels address each logit and factor buffer with 32-bit byte offsets.
+constexpr uint64_t kMaxBufferBytes = (uint64_t)1 << 32;
 bool rank_ok(int r) { return r >= 0 && r <= DSPARK_MAX_RANK && r % 8 == 0; }
 int hip_status(int rc) { return rc == 0 ? DSPARK_OK : DSPARK_E_HIP; }
 }  // namespace
@@ -114,8 +117,9 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
                         int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
-  if ((int64_t)B * V >= (int64_t)1 << 31 || (int64_t)B * K * V >= (int64_t)1 << 40) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
@@ -154,8 +158,10 @@ int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_d
                   void* stream) {
   if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
-  if ((int64_t)N * V >= (int64_t)1 << 31 || (int64_t)R * K * V >= (int64_t)1 << 40) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (!P || !cu_seqlens || !D || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
   if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;

@@ -20,6 +20,8 @@
 //   verify_sample     (T > 0) one wave per request: inverse-CDF draw of the
 //                     correction (residual partials, 64-column re-scan) or the
 //                     bonus (target partials, 256-column re-scan).
+#include <algorithm>
+
 #include "bias_tile.hpp"
 #include "launch.hpp"
 
@@ -49,6 +51,8 @@ struct VerifyArgs {
   int32_t* flag;            // [N]  1 accept, 0 reject, 2 bad row, 3 bonus row
   int4* info;               // [R]  (mode, sample row, position, n_acc)
   float* rpart;             // [R, ns64]
+  int32_t* rej_list;        // [R]  correcting requests, compacted (any order)
+  int32_t* rej_count;       // [1]
   int nsP, ns64, nchunks;
   int ncol_tiles, nstages;
 };
@@ -195,6 +199,7 @@ template <typename PT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.rej_count = 0;  // filled by the decide kernel
   if (i >= a.N) return;
   const float2* part = a.ppart + (size_t)i * a.nsP;
   float m = -INFINITY, s = 0.f;
@@ -272,6 +277,7 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
   while (n < L && a.flag[c0 + n] == 1) ++n;
   const int mode = (n < L) ? 1 : 0;  // 1: correction from the residual, 0: bonus
   a.info[r] = make_int4(mode, c0 + n, n + 1, n);
+  if (!GREEDY && mode == 1) a.rej_list[atomicAdd(a.rej_count, 1)] = r;
   a.n_acc_out[r] = n;
   if constexpr (GREEDY) a.tok_out[r] = __float_as_int(a.rowms[c0 + n].y);
 }
@@ -391,6 +397,119 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
     s += __shfl_xor(s, 16, 64);
     s += __shfl_xor(s, 32, 64);
     if (live && lane < 16) a.rpart[(size_t)req(g) * a.ns64 + slice] = s;
+  }
+}
+
+// Aligned-row variant: only the compacted correcting requests stream.
+// Persistent workgroups (about two per CU) pick a 128-request stage of the
+// list and a range of 64-column blocks at run time, from the list length the
+// decide kernel left on the device.  Per request, the row offsets and the
+// two log-normalisers sit in LDS; target and draft rows go through buffer
+// resources; each draft row seeds the MFMA accumulators, so the MFMAs leave
+// z = D + bias directly.
+struct ResidualRow {
+  uint32_t p_off, d_off;  // byte offsets of the target and draft rows
+  float lp, lq;           // log2-normalisers of p and q
+};
+
+template <typename PT, typename DT, int KC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void verify_residual_stream_kernel(VerifyArgs a) {
+  const int count = *a.rej_count;
+  if (count <= 0) return;
+  const int active = (count + kStageRows - 1) / kStageRows;
+  const int slots = gridDim.x / 8;
+  const int per_stage = slots / active;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int stage = slot % active, sp = slot / active;
+  if (sp >= per_stage) return;
+  const int nsplit = per_stage * 8, split = sp * 8 + xcd;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = stage * kStageRows;
+  const int nrows = min(kStageRows, count - row0);
+  const int ngroups = (nrows + 15) / 16;
+  const int nblocks = (a.V + kWaveCols - 1) / kWaveCols;
+  const int blk_begin = (int)((int64_t)split * nblocks / nsplit);
+  const int blk_end = (int)((int64_t)(split + 1) * nblocks / nsplit);
+
+  __shared__ ResidualRow rows[kStageRows];
+  __shared__ EStage<(KC > 0 ? KC : 1)> st;
+  if (threadIdx.x < kStageRows) {
+    ResidualRow rr{0u, 0u, 0.f, 0.f};
+    if ((int)threadIdx.x < nrows) {
+      const int r = a.rej_list[row0 + threadIdx.x];
+      const int4 in = a.info[r];
+      const float2 ms = a.rowms[in.y];
+      rr.p_off = (uint32_t)((uint64_t)in.y * a.V * sizeof(PT));
+      rr.d_off = (uint32_t)(((uint64_t)r * a.K + in.w) * a.V * sizeof(DT));
+      rr.lp = ms.x + fast_log2(ms.y);
+      rr.lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
+    }
+    rows[threadIdx.x] = rr;
+  }
+  bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  W2Frags wf;
+  if constexpr (KC > 0) {
+    const int32_t* list = a.rej_list;
+    const int4* info = a.info;
+    const int32_t* x0 = a.x0;
+    const int32_t* x = a.x;
+    const int K = a.K;
+    stage_e<KC>(st, a.W1, a.r, a.V, row0, count, [&](int g) {
+      const int r = list[g];
+      const int4 in = info[r];
+      return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
+    });
+    wf.setup(a.W2t, a.r, a.V, lane);
+  }
+  __syncthreads();
+
+  const rsrc_t prs = make_rsrc(a.P, (uint32_t)((uint64_t)a.N * a.V * sizeof(PT)));
+  const rsrc_t drs = make_rsrc(a.D, (uint32_t)((uint64_t)a.R * a.K * a.V * sizeof(DT)));
+  const uint32_t lane_col = (uint32_t)(16 * (lane >> 4));
+  auto row_info = [&](int g) { return rows[16 * g + (lane & 15)]; };
+  auto live = [&](int g) { return 16 * g + (lane & 15) < nrows; };
+
+  for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
+    const int cbase = blk * kWaveCols + (int)lane_col;
+    const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
+    if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
+    const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1)>(lane));
+    GroupLogitsBuf<PT> pb;
+    GroupLogitsBuf<DT> db;
+    ResidualRow ri = row_info(0);
+    pb.load(prs, ri.p_off + pcol, 0u);
+    db.load(drs, ri.d_off + dcol, 0u);
+    f32x4 acc[4];
+    for (int g = 0; g < ngroups; ++g) {
+      const ResidualRow cur = ri;
+      const bool lv = live(g);
+      float u[16];
+      db.unpack(u, cbase, a.V, lv);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
+      if constexpr (KC > 0) mfma_group<KC, false>(st, g, lane, w2, acc, e_off);
+      float t[16];
+      pb.unpack(t, cbase, a.V, lv);
+      if (g + 1 < ngroups) {  // next group's rows are requested before this epilogue
+        ri = row_info(g + 1);
+        pb.load(prs, ri.p_off + pcol, 0u);
+        db.load(drs, ri.d_off + dcol, 0u);
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * b + i;
+          const float p = fast_exp2(fmaf(t[e], a.c2, -cur.lp));
+          const float q = fast_exp2(fmaf(acc[b][i], a.c2, -cur.lq));
+          s += fmaxf(p - q, 0.f);
+        }
+      s = rows_sum(s);
+      if (lv && lane < 16) a.rpart[(size_t)a.rej_list[row0 + 16 * g + lane] * a.ns64 + blk] = s;
+    }
   }
 }
 
@@ -550,7 +669,7 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct VerifyLayout {
-  size_t ppart, rowms, flag, info, rpart, total;
+  size_t ppart, rowms, flag, info, rpart, rej, total;
 };
 
 static VerifyLayout verify_layout(int R, int V, int N) {
@@ -568,6 +687,8 @@ static VerifyLayout verify_layout(int R, int V, int N) {
   off += align256((size_t)R * sizeof(int4));
   l.rpart = off;
   off += align256((size_t)R * ns64 * sizeof(float));
+  l.rej = off;
+  off += align256((size_t)(R + 1) * sizeof(int32_t));
   l.total = off;
   return l;
 }
@@ -596,6 +717,30 @@ static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
   }
 }
 
+template <typename PT, typename DT, int KC>
+static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
+  // about two workgroups per CU, and enough 8-slot rows for every stage
+  const int slots = std::max(64, (a.R + kStageRows - 1) / kStageRows);
+  return launch_kernel("verify_residual", verify_residual_stream_kernel<PT, DT, KC>, dim3(8 * slots), dim3(256),
+                       stream, a);
+}
+
+template <typename PT, typename DT>
+static int dispatch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
+  switch ((a.r + 31) / 32) {
+    case 0: return launch_residual_stream<PT, DT, 0>(a, stream);
+    case 1: return launch_residual_stream<PT, DT, 1>(a, stream);
+    case 2: return launch_residual_stream<PT, DT, 2>(a, stream);
+    case 3: return launch_residual_stream<PT, DT, 3>(a, stream);
+    case 4: return launch_residual_stream<PT, DT, 4>(a, stream);
+    case 5: return launch_residual_stream<PT, DT, 5>(a, stream);
+    case 6: return launch_residual_stream<PT, DT, 6>(a, stream);
+    case 7: return launch_residual_stream<PT, DT, 7>(a, stream);
+    case 8: return launch_residual_stream<PT, DT, 8>(a, stream);
+    default: return -1;
+  }
+}
+
 template <typename PT, typename DT>
 static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, hipStream_t stream) {
   int rc;
@@ -619,7 +764,7 @@ static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, 
   if (rc) return rc;
   rc = launch_kernel("verify_decide", verify_decide_kernel<false>, dim3((a.R + 255) / 256), b256, stream, a);
   if (rc) return rc;
-  if (vec_p && vec_d) rc = dispatch_residual<PT, DT, true, true>(a, stream);
+  if (vec_p && vec_d) rc = dispatch_residual_stream<PT, DT>(a, stream);
   else if (vec_p) rc = dispatch_residual<PT, DT, true, false>(a, stream);
   else if (vec_d) rc = dispatch_residual<PT, DT, false, true>(a, stream);
   else rc = dispatch_residual<PT, DT, false, false>(a, stream);
@@ -660,6 +805,8 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   a.flag = reinterpret_cast<int32_t*>(ws + l.flag);
   a.info = reinterpret_cast<int4*>(ws + l.info);
   a.rpart = reinterpret_cast<float*>(ws + l.rpart);
+  a.rej_count = reinterpret_cast<int32_t*>(ws + l.rej);
+  a.rej_list = a.rej_count + 1;
   a.nsP = (V + kRowSlice - 1) / kRowSlice;
   a.ns64 = (V + kWaveCols - 1) / kWaveCols;
   a.nchunks = (V + kRowChunk - 1) / kRowChunk;

@@ -42,6 +42,9 @@
  *     column v, the r weights that produce logit v, is contiguous at W2 + v*r.
  *     r must be a multiple of 8 and at most DSPARK_MAX_RANK; r == 0 means no
  *     Markov head (W1 and W2 may then be NULL).
+ *   - Each logit buffer (U, P, D) and each Markov factor must be smaller than
+ *     4 GiB (kernels address them with 32-bit byte offsets); larger inputs
+ *     return DSPARK_E_SHAPE.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -96,7 +99,7 @@ int dspark_version(void);
  *              largest biased logit).
  * Inputs: U [B, K, V] (u_dtype f32 or bf16); W1 [V, r] and W2 (column-major
  * r x V) bf16; x0 [B] int32.  Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
- * r as in the header comment, B * V < 2^31.
+ * r as in the header comment, U smaller than 4 GiB.
  * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
  * that request's remaining positions x = -1, q_tok = lse = NaN.
  * ------------------------------------------------------------------------ */
@@ -157,7 +160,8 @@ int dspark_schedule(int R, int K, const float* c,
  * dspark_markov_draft (q_tok, lse_d unused when T == 0).
  * Outputs: n_acc_out [R] accepted drafts; tok_out [R] the correction or bonus
  * token (emitted sequence: x_1..x_{n_acc}, tok).
- * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), N * V < 2^31.
+ * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), P and D each
+ * smaller than 4 GiB.
  * Data errors: a request whose cu_seqlens slice is inconsistent (length < 1 or
  * > K + 1, or outside [0, N]) or whose tokens are outside [0, V) gets
  * n_acc = tok = -1.
