@@ -142,6 +142,18 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   return v;
 }
 
+// fp64 version, used for the slice-level CDF (thousands of slice masses per
+// row: an fp32 running sum would carry ~1e-6 relative error to the crossing).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
 // Lowest lane whose predicate holds, or -1.
 __device__ __forceinline__ int wave_first_lane(bool pred) {
   const unsigned long long m = __ballot(pred);

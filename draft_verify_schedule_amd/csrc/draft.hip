@@ -267,9 +267,9 @@ template <typename UT, bool GREEDY>
 __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   __shared__ float red_f[4];
   __shared__ int red_i[4];
-  __shared__ float wave_tot[4];
+  __shared__ double wave_tot[4];
   __shared__ int sh_slice;
-  __shared__ float sh_before;
+  __shared__ double sh_before;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -338,28 +338,29 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   if (lane == 0) red_f[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-  auto weight = [&](float2 q) { return (q.x == -INFINITY) ? 0.f : q.y * fast_exp2(q.x - M); };
+  // slice masses in fp32, their CDF in fp64
+  auto weight = [&](float2 q) { return (q.x == -INFINITY) ? 0.0 : (double)(q.y * fast_exp2(q.x - M)); };
   // per-thread mass and its block-wide inclusive scan (thread order = slice order)
-  float local = 0.f;
+  double local = 0.0;
   if (in_regs) {
 #pragma unroll
     for (int i = 0; i < kLocPer; ++i) local += weight(p[i]);
   } else {
     for (int s = s0; s < s1; ++s) local += weight(part[s]);
   }
-  float incl = wave_inclusive_scan(local);
+  double incl = wave_inclusive_scan(local);
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  float before_wave = 0.f;
+  double before_wave = 0.0;
   for (int w = 0; w < wave; ++w) before_wave += wave_tot[w];
   incl += before_wave;
-  const float S = ((wave_tot[0] + wave_tot[1]) + wave_tot[2]) + wave_tot[3];
+  const double S = ((wave_tot[0] + wave_tot[1]) + wave_tot[2]) + wave_tot[3];
   const float u = decision_uniform(a.seed, a.step, (uint32_t)b, (uint32_t)a.k, kPurposeDraft);
-  const float target = u * S;
+  const double target = (double)u * S;
   // owner: first thread whose inclusive sum passes the target, else the last with mass
   {
     const int f = wave_first_lane(incl > target);
-    const unsigned long long mm = __ballot(local > 0.f);
+    const unsigned long long mm = __ballot(local > 0.0);
     if (lane == 0) {
       red_i[wave] = f < 0 ? 0x7FFFFFFF : wave * 64 + f;
       red_f[wave] = mm ? (float)(wave * 64 + 63 - __clzll((long long)mm)) : -1.f;
@@ -372,11 +373,11 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     owner = last < 0.f ? 0 : (int)last;
   }
   if (tid == owner) {
-    float acc = incl - local;
+    double acc = incl - local;
     int hit = -1, last = -1;
-    float hit_before = 0.f, last_before = acc;
-    auto visit = [&](int s, float w) {
-      if (w > 0.f) {
+    double hit_before = 0.0, last_before = acc;
+    auto visit = [&](int s, double w) {
+      if (w > 0.0) {
         if (hit < 0 && acc + w > target) {
           hit = s;
           hit_before = acc;
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   if (wave != 0) return;
   const int s_star = sh_slice;
   const float m_s = part[s_star].x;
-  const float t_in = (target - sh_before) / fast_exp2(m_s - M);
+  const float t_in = (float)((target - sh_before) / (double)fast_exp2(m_s - M));
 
   // re-evaluate the 64 logits of slice s_star, one column per lane
   const int col = s_star * kWaveCols + lane;
@@ -424,8 +425,8 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   const float zx = __shfl(z, pick, 64);
   if (lane == 0) {
     a.x_out[out] = s_star * kWaveCols + pick;
-    a.q_out[out] = fast_exp2(fmaf(zx, a.c2, -M)) / S;
-    a.lse_out[out] = (M + fast_log2(S)) * kLn2;
+    a.q_out[out] = fast_exp2(fmaf(zx, a.c2, -M)) / (float)S;
+    a.lse_out[out] = (M + fast_log2((float)S)) * kLn2;
   }
 }
 

@@ -29,6 +29,7 @@ namespace dspark {
 
 constexpr int kRowChunk = 8192;   // columns per rowstats workgroup (2048 per wave)
 constexpr int kRowSlice = 256;    // columns per target-row partial
+constexpr int kRowstatsWGs = 2048;  // persistent rowstats grid: 8 workgroups per CU
 
 struct VerifyArgs {
   int R, K, V, N, r;
@@ -179,6 +180,97 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
         if (lane == 0) out[slice] = make_float2(m, s);
       }
     }
+  }
+}
+
+// Aligned-row variant: persistent grid-stride over (row, 8192-column chunk)
+// items with the next item's loads (buffer resource, per-lane VGPR offset,
+// scalar row offset) in flight while the current item is reduced.
+template <typename PT, bool GREEDY>
+__global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs a) {
+  constexpr int EPL = 16 / sizeof(PT);           // elements per 16-byte load
+  constexpr int COLS = 64 * EPL;                 // columns per load instruction
+  constexpr int ITERS = (kRowChunk / 4) / COLS;  // loads per wave per item
+  constexpr int LPS = kRowSlice / EPL;           // lanes per 256-column slice
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int items = a.N * a.nchunks;
+  const rsrc_t rs = make_rsrc(a.P, (uint32_t)((uint64_t)a.N * a.V * sizeof(PT)));
+  const uint32_t lane_off = (uint32_t)(lane * EPL * sizeof(PT));
+  auto issue = [&](int item, u32x4 (&w)[ITERS]) {
+    const int row = item / a.nchunks;
+    const int chunk = item - row * a.nchunks;
+    const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
+    const uint32_t soff = (uint32_t)(((uint64_t)row * a.V + wbase) * sizeof(PT));
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) w[it] = buffer_load16(rs, lane_off + (uint32_t)(it * COLS * sizeof(PT)), soff);
+  };
+  auto reduce = [&](int item, const u32x4 (&w)[ITERS]) {
+    const int row = item / a.nchunks;
+    const int chunk = item - row * a.nchunks;
+    const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
+    if (wbase >= a.V) return;
+    float2* out = a.ppart + (size_t)row * a.nsP;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int c = wbase + it * COLS + lane * EPL;
+      const int slice = (wbase + it * COLS) / kRowSlice + lane / LPS;
+      float v[EPL];
+      const bool ok = c < a.V;
+      if constexpr (sizeof(PT) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = ok ? __uint_as_float(w[it][e] << 16) : -INFINITY;
+          v[2 * e + 1] = ok ? __uint_as_float(w[it][e] & 0xFFFF0000u) : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ok ? __uint_as_float(w[it][e]) : -INFINITY;
+      }
+      if constexpr (GREEDY) {
+        float m = -INFINITY;
+        int idx = -1;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          if (ok && (idx < 0 || v[e] > m)) {
+            m = v[e];
+            idx = c + e;
+          }
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) {
+          const float m2 = __shfl_xor(m, off, 64);
+          const int i2 = __shfl_xor(idx, off, 64);
+          merge_argmax(m, idx, m2, i2);
+        }
+        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) out[slice] = make_float2(m, __int_as_float(idx));
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          v[e] *= a.c2;
+          m = fmaxf(m, v[e]);
+        }
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float mm = (m == -INFINITY) ? 0.f : m;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s += fast_exp2(v[e] - mm);
+#pragma unroll
+        for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
+        if ((lane % LPS) == 0 && slice < a.nsP && c < a.V) out[slice] = make_float2(m, s);
+      }
+    }
+  };
+  int item = blockIdx.x;
+  u32x4 cur[ITERS], nxt[ITERS];
+  if (item < items) issue(item, cur);
+  for (; item < items; item += gridDim.x) {
+    const int nitem = item + gridDim.x;
+    if (nitem < items) issue(nitem, nxt);
+    reduce(item, cur);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) cur[it] = nxt[it];
   }
 }
 
@@ -514,31 +606,32 @@ void verify_residual_stream_kernel(VerifyArgs a) {
 }
 
 // ------------------------------------------------------------------ sample --
-// Inverse-CDF over slice masses w_s: the slice where the running sum first
-// exceeds target and the mass before it.  Lanes own contiguous slice chunks.
+// Inverse-CDF over slice masses w_s (fp64 running sums: thousands of slices
+// per row): the slice where the running sum first exceeds target and the mass
+// before it.  Lanes own contiguous slice chunks.
 struct SliceHit {
   int slice;
-  float before;
+  double before;
 };
 
 template <typename WeightFn>
-__device__ __forceinline__ SliceHit find_slice(int ns, float target, float incl, float local, int s_begin,
+__device__ __forceinline__ SliceHit find_slice(int ns, double target, double incl, double local, int s_begin,
                                                int s_end, WeightFn weight) {
   const int lane = threadIdx.x & 63;
   int owner = wave_first_lane(incl > target);
   if (owner < 0) {
-    const unsigned long long m = __ballot(local > 0.f);
+    const unsigned long long m = __ballot(local > 0.0);
     owner = m ? 63 - __clzll((long long)m) : 0;
   }
   int s_star = -1;
-  float before = 0.f;
+  double before = 0.0;
   if (lane == owner) {
-    float acc = incl - local;
+    double acc = incl - local;
     int last = -1;
-    float last_before = acc;
+    double last_before = acc;
     for (int s = s_begin; s < s_end; ++s) {
-      const float w = weight(s);
-      if (w > 0.f) {
+      const double w = weight(s);
+      if (w > 0.0) {
         last = s;
         last_before = acc;
         if (acc + w > target) {
@@ -580,13 +673,13 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     const int ns = a.ns64;
     const int per = (ns + 63) / 64;
     const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
-    float local = 0.f;
-    for (int s = s_begin; s < s_end; ++s) local += rp[s];
-    const float incl = wave_inclusive_scan(local);
-    const float Z = __shfl(incl, 63, 64);
-    if (Z > 0.f && Z <= 2.f) {
-      const float target = u * Z;
-      const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return rp[s]; });
+    double local = 0.0;
+    for (int s = s_begin; s < s_end; ++s) local += (double)rp[s];
+    const double incl = wave_inclusive_scan(local);
+    const double Z = __shfl(incl, 63, 64);
+    if (Z > 0.0 && Z <= 2.0) {
+      const double target = (double)u * Z;
+      const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return (double)rp[s]; });
       const int col = h.slice * kWaveCols + lane;
       float rho = 0.f;
       if (col < a.V) {
@@ -599,8 +692,9 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
         const float q = fast_exp2(fmaf(zq, a.c2, -lq));
         rho = fmaxf(p - q, 0.f);
       }
+      const float t_in = (float)(target - h.before);
       const float cum = wave_inclusive_scan(rho);
-      int pick = wave_first_lane(cum > target - h.before && rho > 0.f);
+      int pick = wave_first_lane(cum > t_in && rho > 0.f);
       if (pick < 0) {
         const unsigned long long m = __ballot(rho > 0.f);
         pick = m ? 63 - __clzll((long long)m) : 0;
@@ -619,25 +713,25 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   M = wave_max(M);
   auto weight = [&](int s) {
     const float2 p = pp[s];
-    return (p.x == -INFINITY) ? 0.f : p.y * exp2f(p.x - M);
+    return (p.x == -INFINITY) ? 0.0 : (double)(p.y * fast_exp2(p.x - M));
   };
   const int per = (ns + 63) / 64;
   const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
-  float local = 0.f;
+  double local = 0.0;
   for (int s = s_begin; s < s_end; ++s) local += weight(s);
-  const float incl = wave_inclusive_scan(local);
-  const float S = __shfl(incl, 63, 64);
-  const float target = u * S;
+  const double incl = wave_inclusive_scan(local);
+  const double S = __shfl(incl, 63, 64);
+  const double target = (double)u * S;
   const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, weight);
   const float m_s = pp[h.slice].x;
-  const float t_in = (target - h.before) / exp2f(m_s - M);
+  const float t_in = (float)((target - h.before) / (double)fast_exp2(m_s - M));
   // 256 columns, 4 consecutive per lane
   float e[4];
   float lsum = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int col = h.slice * kRowSlice + 4 * lane + k;
-    e[k] = (col < a.V) ? exp2f(load_logit(prow, col) * a.c2 - m_s) : 0.f;
+    e[k] = (col < a.V) ? fast_exp2(load_logit(prow, col) * a.c2 - m_s) : 0.f;
     lsum += e[k];
   }
   const float incl2 = wave_inclusive_scan(lsum);
@@ -745,9 +839,10 @@ template <typename PT, typename DT>
 static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, hipStream_t stream) {
   int rc;
   const dim3 b256(256);
+  const dim3 stream_grid(std::min(a.N * a.nchunks, kRowstatsWGs));
   if (greedy) {
-    rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, true, true>,
-                               dim3(a.N * a.nchunks), b256, stream, a)
+    rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_stream_kernel<PT, true>, stream_grid, b256,
+                               stream, a)
                : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, true>,
                                dim3(a.N * a.nchunks), b256, stream, a);
     if (rc) return rc;
@@ -755,8 +850,8 @@ static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, 
     if (rc) return rc;
     return launch_kernel("verify_decide", verify_decide_kernel<true>, dim3((a.R + 255) / 256), b256, stream, a);
   }
-  rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, true, false>,
-                             dim3(a.N * a.nchunks), b256, stream, a)
+  rc = vec_p ? launch_kernel("verify_rowstats", verify_rowstats_stream_kernel<PT, false>, stream_grid, b256,
+                             stream, a)
              : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, false>,
                              dim3(a.N * a.nchunks), b256, stream, a);
   if (rc) return rc;
