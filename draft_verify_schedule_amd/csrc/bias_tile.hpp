@@ -57,19 +57,31 @@ struct W2Frags {
   rsrc_t rsrc;
   uint32_t lane_off;   // bytes: lane's column within a block and its k group
   uint32_t col_bytes;  // bytes per column (r * 2)
+  uint32_t bytes;      // resource size
   __device__ __forceinline__ void setup(const uint16_t* W2t, int r, int V, int lane) {
-    rsrc = make_rsrc(W2t, (uint32_t)V * (uint32_t)r * 2u);
+    bytes = (uint32_t)V * (uint32_t)r * 2u;
+    rsrc = make_rsrc(W2t, bytes);
     const int a = lane & 15;
     col_bytes = (uint32_t)r * 2u;
     lane_off = (uint32_t)(16 * (a >> 2) + (a & 3)) * col_bytes + (uint32_t)((lane >> 4) * 8) * 2u;
   }
   template <int KC>
   __device__ __forceinline__ void load(int n0, bf16x8 (&fr)[4][KC]) const {
+    load_from<KC>((uint32_t)n0 * col_bytes, fr);
+  }
+  // valid = false: every offset is past the resource, the registers read as
+  // zero and no memory is touched (wave-uniform select, no branch)
+  template <int KC>
+  __device__ __forceinline__ void load_if(int n0, bool valid, bf16x8 (&fr)[4][KC]) const {
+    load_from<KC>(valid ? (uint32_t)n0 * col_bytes : bytes, fr);
+  }
+  template <int KC>
+  __device__ __forceinline__ void load_from(uint32_t base, bf16x8 (&fr)[4][KC]) const {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const uint32_t soff = (uint32_t)(n0 + 4 * b) * col_bytes + (uint32_t)(64 * kc);
+        const uint32_t soff = base + (uint32_t)(4 * b) * col_bytes + (uint32_t)(64 * kc);
         fr[b][kc] = __builtin_bit_cast(bf16x8, buffer_load16(rsrc, lane_off, soff));
       }
     }
@@ -78,35 +90,62 @@ struct W2Frags {
 
 // Stage E rows W1[prev(row)] of rows [row0, row0 + kStageRows) into LDS (zeros
 // for rows past nrows, invalid previous tokens, or k >= r).  prev_of(row)
-// returns the previous token of that row or -1.  All 256 threads take part:
-// two threads per row, each reading its row's token once and then issuing all
-// of its W1 loads back to back (unconditional loads from a valid address,
-// masked at the LDS store, so that nothing serialises them).
+// returns the previous token of that row or -1.  The 256 threads (4 waves)
+// take 32 rows per wave; each load instruction covers two whole rows, 32
+// lanes x 16 contiguous bytes per row, so one instruction touches 8 cache
+// lines instead of 64.  Lane j reads the previous token of row j of its
+// wave's 32 once; the token of each loaded row comes by a lane shuffle.
+//
+// Split in two so that a kernel can request other data (its first base
+// logits and W2 fragments) between the W1 loads and the LDS stores: loads
+// complete in order, so the stores then wait for the W1 rows only.
+template <int KC>
+struct EStageLoad {
+  static_assert(kStageRows == 128, "4 waves x 32 rows");
+  static constexpr int kChunks = 4 * KC;  // 16-byte vectors per padded row, <= 32
+  static constexpr int kLoads = 16;       // two rows per load instruction
+  u32x4 vals[kLoads];
+  uint32_t valid;  // bit i: the row of load i has a valid token
+
+  template <typename PrevFn>
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ W1, int r, int V, int row0, int nrows,
+                                       PrevFn prev_of) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane & 31;
+    const int g = row0 + 32 * wave + c;
+    const int my_prev = (g < nrows) ? prev_of(g) : -1;
+    const int k = 8 * c;
+    const bool k_ok = c < kChunks && k < r;
+    valid = 0;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int prev = __shfl(my_prev, 2 * i + (lane >> 5), 64);
+      const bool ok = prev >= 0 && prev < V;
+      valid |= (ok && k_ok) ? (1u << i) : 0u;
+      vals[i] = *reinterpret_cast<const u32x4*>(W1 + (size_t)(ok ? prev : 0) * r + (k_ok ? k : 0));
+    }
+  }
+  __device__ __forceinline__ void store(EStage<KC>& st, int r) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane & 31;
+    if (c < kChunks) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int row = 32 * wave + 2 * i + (lane >> 5);
+        *reinterpret_cast<u32x4*>(&st.e[row][8 * c]) = ((valid >> i) & 1u) ? vals[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+};
+
 template <int KC, typename PrevFn>
 __device__ __forceinline__ void stage_e(EStage<KC>& st, const uint16_t* __restrict__ W1, int r,
                                         int V, int row0, int nrows, PrevFn prev_of) {
-  constexpr int kVecPerRow = 4 * KC;  // 16-byte vectors per padded row
-  constexpr int kThreadsPerRow = 256 / kStageRows;
-  constexpr int kVecPerThread = kVecPerRow / kThreadsPerRow;
-  static_assert(kVecPerRow % kThreadsPerRow == 0, "row split");
-  const int row = threadIdx.x / kThreadsPerRow;
-  const int part = threadIdx.x % kThreadsPerRow;
-  const int g = row0 + row;
-  const int prev = (g < nrows) ? prev_of(g) : -1;
-  const bool valid = prev >= 0 && prev < V;
-  const uint16_t* src = W1 + (size_t)(valid ? prev : 0) * r;
-  u32x4 vals[kVecPerThread];
-#pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
-    const int k = 8 * (part * kVecPerThread + i);
-    vals[i] = *reinterpret_cast<const u32x4*>(src + (k < r ? k : 0));
-  }
-#pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
-    const int k = 8 * (part * kVecPerThread + i);
-    const bool keep = valid && k < r;
-    *reinterpret_cast<u32x4*>(&st.e[row][k]) = keep ? vals[i] : u32x4{0u, 0u, 0u, 0u};
-  }
+  EStageLoad<KC> ld;
+  ld.load(W1, r, V, row0, nrows, prev_of);
+  ld.store(st, r);
 }
 
 // Byte offset of this lane's E fragment row within the stage (group 0,
@@ -228,6 +267,17 @@ struct GroupLogitsBuf<uint16_t> {
       }
     }
   }
+  // all 16 columns in range and the row live
+  __device__ __forceinline__ void unpack(float out[16]) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        out[8 * h + 2 * e] = __uint_as_float(w[h][e] << 16);
+        out[8 * h + 2 * e + 1] = __uint_as_float(w[h][e] & 0xFFFF0000u);
+      }
+    }
+  }
 };
 
 template <>
@@ -245,23 +295,59 @@ struct GroupLogitsBuf<float> {
       for (int e = 0; e < 4; ++e) out[4 * h + e] = ok ? __uint_as_float(w[h][e]) : -INFINITY;
     }
   }
+  __device__ __forceinline__ void unpack(float out[16]) const {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * h + e] = __uint_as_float(w[h][e]);
+  }
 };
 
-// One bias value on the vector ALU (fp32 FMA in index order), used when a
-// single column of a single row is re-evaluated (the sampling re-scan).
-__device__ __forceinline__ float valu_bias(const uint16_t* __restrict__ w1row,
-                                           const uint16_t* __restrict__ w2col, int r) {
+// Bias values on the vector ALU, used when the 64 columns of one slice of one
+// row are re-evaluated (the sampling re-scans): lane l owns column col and
+// accumulates sum_k W1[prev, k] * W2[k, col] over k in [k0, k0 + 64) in fp32
+// FMAs in index order.  All sixteen 16-byte loads of a chunk are requested
+// before the first FMA, so a chunk costs one memory round trip.  Requires
+// r % 8 == 0; k >= r contributes nothing.
+__device__ __forceinline__ float bias_chunk64(const uint16_t* __restrict__ w1row,
+                                             const uint16_t* __restrict__ w2col, int k0, int r) {
+  u32x4 av[8], bv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + 8 * i;
+    const bool ok = k < r;
+    av[i] = ok ? *reinterpret_cast<const u32x4*>(w1row + k) : u32x4{0u, 0u, 0u, 0u};
+    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2col + k) : u32x4{0u, 0u, 0u, 0u};
+  }
   float s = 0.f;
-  for (int k = 0; k < r; k += 8) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(w1row + k);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(w2col + k);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
-      s = fmaf(__uint_as_float(a[e] & 0xFFFF0000u), __uint_as_float(b[e] & 0xFFFF0000u), s);
+      s = fmaf(__uint_as_float(av[i][e] << 16), __uint_as_float(bv[i][e] << 16), s);
+      s = fmaf(__uint_as_float(av[i][e] & 0xFFFF0000u), __uint_as_float(bv[i][e] & 0xFFFF0000u), s);
     }
   }
   return s;
+}
+
+// One wave: the chunks of 64 in order, summed left to right.
+__device__ __forceinline__ float valu_bias(const uint16_t* __restrict__ w1row,
+                                           const uint16_t* __restrict__ w2col, int r) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < r; k0 += 64) s += bias_chunk64(w1row, w2col, k0, r);
+  return s;
+}
+
+// Four waves of a workgroup (r <= 256): wave w takes the chunk starting at
+// 64 w; the four chunk sums are combined in chunk order through LDS
+// (part[256], all waves must call it).  Returns the bias on every wave.
+__device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w1row,
+                                                  const uint16_t* __restrict__ w2col, int r, bool ok,
+                                                  int wave, int lane, float* part) {
+  part[wave * 64 + lane] = ok ? bias_chunk64(w1row, w2col, 64 * wave, r) : 0.f;
+  __syncthreads();
+  return ((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane];
 }
 
 }  // namespace dspark

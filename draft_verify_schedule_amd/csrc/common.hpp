@@ -21,6 +21,14 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar)
+// value: derived from threadIdx.x the compiler would otherwise treat it as
+// per-lane, and every buffer offset computed from it would need a
+// readfirstlane loop around the load.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -72,6 +80,34 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voffset, uint32_t soffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, (int)soffset, 0));
+}
+
+// Raw-buffer range checking covers voffset + soffset: a load whose offset is
+// at or past the resource size returns zeros without touching memory, and
+// such a store is dropped.  Kernels use this as a branch-free mask: an offset
+// of at least the resource size disables the access.
+__device__ __forceinline__ void buffer_store8(rsrc_t r, float2 v, uint32_t voffset, uint32_t soffset) {
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+  const u32x2 d = {__float_as_uint(v.x), __float_as_uint(v.y)};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voffset, (int)soffset, 0);
+}
+
+// The same 8-byte store issued as inline assembly, for loops that keep loads
+// in flight.  The compiler's wait-count tracking treats a store pending next
+// to loads as possibly completing out of order and then waits for all
+// outstanding memory operations (vmcnt(0)) before using any load.  A store it
+// does not see keeps its waits at "the loads issued after this one", which is
+// still exact: loads complete in order, so at most N operations outstanding
+// implies the load with N later loads has completed, whatever the stores do.
+// The resource words are the four dwords of a raw buffer descriptor.
+typedef int int4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4v raw_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return int4v{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ void buffer_store8_untracked(int4v r, float2 v, uint32_t voffset, uint32_t soffset) {
+  const double d = __hiloint2double((int)__float_as_uint(v.y), (int)__float_as_uint(v.x));
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, %3 offen" : : "v"(d), "v"(voffset), "s"(r), "s"(soffset));
 }
 
 // Hardware exp2 / log2 (v_exp_f32, v_log_f32).

@@ -40,17 +40,17 @@ struct DraftArgs {
 
 // Epilogue of one group: z = base logits + bias for 16 consecutive columns of
 // one row per lane; the four lanes sharing a row (l, l^16, l^32, l^48) cover the
-// wave's 64-column slice.  Writes the slice's (scaled max, sum exp2) or
-// (max, first argmax).
-template <bool GREEDY>
-__device__ __forceinline__ void slice_partial(const float (&z)[16], int cbase, int V, float c2, bool row_live,
-                                              float2* dst, int lane) {
+// wave's 64-column slice.  Returns, on all four lanes, the slice's (scaled
+// max, sum exp2) or (max, first argmax as int bits).  MASKED: columns >= V
+// are excluded; without it every column of the slice is in range.
+template <bool GREEDY, bool MASKED>
+__device__ __forceinline__ float2 slice_values(const float (&z)[16], int cbase, int V, float c2) {
   if constexpr (GREEDY) {
     float m = -INFINITY;
     int idx = -1;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      if (cbase + e < V && (idx < 0 || z[e] > m)) {
+      if ((!MASKED || cbase + e < V) && (idx < 0 || z[e] > m)) {
         m = z[e];
         idx = cbase + e;
       }
@@ -64,7 +64,7 @@ __device__ __forceinline__ void slice_partial(const float (&z)[16], int cbase, i
       row_pair32(ia, idx, ib);
       merge_argmax(m, idx, mb, ib);
     }
-    if (row_live && lane < 16) *dst = make_float2(m, __int_as_float(idx));
+    return make_float2(m, __int_as_float(idx));
   } else {
     float m = z[0];
 #pragma unroll
@@ -77,7 +77,7 @@ __device__ __forceinline__ void slice_partial(const float (&z)[16], int cbase, i
 #pragma unroll
     for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -mc));
     s = rows_sum(s);
-    if (row_live && lane < 16) *dst = make_float2(empty ? -INFINITY : mc, s);
+    return make_float2(empty ? -INFINITY : mc, s);
   }
 }
 
@@ -93,16 +93,23 @@ struct UAccess<UT, true> {
   using Buf = GroupLogitsBuf<UT>;
   rsrc_t rsrc;
   uint32_t lane_off;
+  uint32_t bytes;      // resource size
   uint64_t row_bytes;  // K * V * sizeof(UT): request stride
   __device__ __forceinline__ void setup(const DraftArgs& a, int lane) {
     const UT* base = reinterpret_cast<const UT*>(a.U) + (size_t)(a.k - 1) * a.V;
     const uint64_t total = ((uint64_t)a.B * a.K * a.V - (uint64_t)(a.k - 1) * a.V) * sizeof(UT);
-    rsrc = make_rsrc(base, (uint32_t)total);
+    bytes = (uint32_t)total;
+    rsrc = make_rsrc(base, bytes);
     row_bytes = (uint64_t)a.K * a.V * sizeof(UT);
     lane_off = (uint32_t)((uint64_t)(lane & 15) * row_bytes + (uint64_t)(16 * (lane >> 4)) * sizeof(UT));
   }
-  __device__ __forceinline__ void load(Buf& b, int row, int blk) const {
-    b.load(rsrc, lane_off, (uint32_t)((uint64_t)row * row_bytes + (uint64_t)blk * kWaveCols * sizeof(UT)));
+  __device__ __forceinline__ uint32_t offset(int row, int blk) const {
+    return (uint32_t)((uint64_t)row * row_bytes + (uint64_t)blk * kWaveCols * sizeof(UT));
+  }
+  __device__ __forceinline__ void load(Buf& b, int row, int blk) const { b.load(rsrc, lane_off, offset(row, blk)); }
+  // valid = false: offset past the resource, zeros, no memory access
+  __device__ __forceinline__ void load_if(Buf& b, int row, int blk, bool valid) const {
+    b.load(rsrc, lane_off, valid ? offset(row, blk) : bytes);
   }
 };
 
@@ -129,20 +136,26 @@ struct UAccess<UT, false> {
 // Persistent workgroups: 4 waves, 128 rows (8 MFMA groups of 16), and a
 // contiguous range of 64-column blocks.  The W1 rows of the 128 requests are
 // staged in LDS once; each wave then sweeps the blocks w, w+4, ... of the
-// range, holding one block's W2 fragments in registers for all 8 groups.  The
-// (block, group) sequence is software-pipelined: several groups of base
-// logits are in flight (also across block boundaries), the MFMAs of group g+1
-// are issued before the epilogue of group g, and the next block's W2
-// fragments are requested as soon as the last MFMA of the current block has
-// issued.
+// range, holding one block's W2 fragments in registers for all 8 groups.
+//
+// FULL (a stage of 128 live rows, 16-byte aligned rows): the complete blocks
+// are swept by a software pipeline with no branches: several groups of base
+// logits are in flight (also across block boundaries), group g+1's MFMAs are
+// issued before group g's epilogue, and the next block's W2 fragments are
+// requested as soon as the last MFMA of the current block has issued.  Loads
+// that have no block to read and the stores of lanes 16..63 get offsets past
+// their buffer resource (no memory access).  The block holding the column
+// tail (V not a multiple of 64) and partial stages take the plain path.
 template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
+  static_assert(!FULL || VEC, "the pipelined sweep reads through buffer resources");
+  constexpr int KCs = KC > 0 ? KC : 1;
   int split, stage;
   if (!xcd_tile(blockIdx.x, a.ncol_tiles, nstages, split, stage)) return;
   stage += stage0;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int row0 = stage * kStageRows;
   const int ngroups = min(kGroupsPerWG, (a.B - row0 + 15) / 16);
   const int nblocks = (a.V + kWaveCols - 1) / kWaveCols;
@@ -151,52 +164,63 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   auto row_of = [&](int g) { return row0 + 16 * g + (lane & 15); };
   auto row_live = [&](int g) { return row_of(g) < a.B; };
   const int lane_col = 16 * (lane >> 4);
+  // blocks [blk_begin, blk_stop) of a full stage are swept by the pipeline
+  const int blk_stop = FULL ? min(blk_end, a.V / kWaveCols) : blk_begin;
+  int blk = blk_begin + wave;
+
+  // Prologue, in request order: the previous tokens and their W1 rows (they
+  // gate the first MFMA through the LDS stage), then the first groups of
+  // base logits and the first block's W2 fragments; the LDS stores of the E
+  // stage wait for the W1 rows only.
+  __shared__ EStage<KCs> st;
+  EStageLoad<KCs> eld;
+  if constexpr (KC > 0) {
+    const int32_t* prev = a.prev;
+    const int stride = a.prev_stride;
+    eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
+  }
 
   UAccess<UT, VEC> ua;
   ua.setup(a, lane);
   // groups of base logits in flight per wave: 8 registers per packed bf16 group, 16 per fp32
-  constexpr int kPrefetch = (VEC && sizeof(UT) == 2) ? 2 : 1;
+  constexpr int kPrefetch = (FULL && sizeof(UT) == 2) ? 4 : 1;
   typename UAccess<UT, VEC>::Buf buf[kPrefetch];
-  int blk = blk_begin + wave;
-  if (blk < blk_end) {
+  if constexpr (FULL) {
 #pragma unroll
-    for (int g = 0; g < kPrefetch; ++g)
-      if (g < ngroups) ua.load(buf[g], row0 + 16 * g, blk);
+    for (int g = 0; g < kPrefetch; ++g) ua.load_if(buf[g], row0 + 16 * g, blk, blk < blk_stop);
   }
 
-  __shared__ EStage<(KC > 0 ? KC : 1)> st;
-  bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  bf16x8 w2[4][KCs];
   W2Frags wf;
   if constexpr (KC > 0) {
-    const int32_t* prev = a.prev;
-    const int stride = a.prev_stride;
     wf.setup(a.W2t, a.r, a.V, lane);
-    if (blk < blk_end) wf.load<KC>(blk * kWaveCols, w2);
-    stage_e<KC>(st, a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
+    if constexpr (FULL) wf.load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
+    eld.store(st, a.r);
     __syncthreads();
   }
 
   if constexpr (FULL) {
-    // full stage: static group count; the (block, group) sequence is
-    // pipelined across block boundaries.  Group h's base logits sit in
-    // buf[h % kPrefetch] until they seed h's accumulators (one iteration
-    // before h's epilogue), and the freed slot is refilled kPrefetch groups
-    // ahead.
+    const uint32_t part_bytes = (uint32_t)((uint64_t)a.B * a.nslices * sizeof(float2));
+    const int4v prs = raw_rsrc_words(a.part, part_bytes);
+    const uint32_t row_bytes = (uint32_t)a.nslices * (uint32_t)sizeof(float2);
+    const uint32_t st_voff = lane < 16 ? (uint32_t)lane * row_bytes : part_bytes;
+    // Group h's base logits sit in buf[h % kPrefetch] until they seed h's
+    // accumulators (one step before h's epilogue); the freed slot is refilled
+    // kPrefetch groups ahead.
     static_assert(kGroupsPerWG % kPrefetch == 0, "ring");
-    for (; blk < blk_end; blk += 4) {
+    for (; blk < blk_stop; blk += 4) {
       const int cbase = blk * kWaveCols + lane_col;
-      const int nxt_blk = blk + 4;
-      const bool has_next = nxt_blk < blk_end;
-      float2* part = a.part + blk;
-      const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1)>(lane));
+      const int nxt = blk + 4;
+      const bool has_next = nxt < blk_stop;
+      const int e_off = launder(e_lane_offset<KCs>(lane));
       auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
         if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
-        else if (has_next) ua.load(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt_blk);
+        else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
       };
       f32x4 acc[4];
       {
         float u[16];
-        buf[0].unpack(u, cbase, a.V, row_live(0));
+        buf[0].unpack(u);
         refill(kPrefetch);
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
@@ -211,45 +235,40 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
           for (int i = 0; i < 4; ++i) z[4 * b + i] = acc[b][i];
         if (g + 1 < kGroupsPerWG) {
           float u[16];
-          buf[(g + 1) % kPrefetch].unpack(u, cbase, a.V, row_live(g + 1));
+          buf[(g + 1) % kPrefetch].unpack(u);
           refill(g + 1 + kPrefetch);
 #pragma unroll
           for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
-          // group g+1's MFMAs run while group g's epilogue executes
           if constexpr (KC > 0) mfma_group<KC, false>(st, g + 1, lane, w2, acc, e_off);
-        } else if (KC > 0 && has_next) {
-          wf.load<(KC > 0 ? KC : 1)>(nxt_blk * kWaveCols, w2);
+        } else if constexpr (KC > 0) {
+          wf.load_if<KC>(nxt * kWaveCols, has_next, w2);
         }
-        slice_partial<GREEDY>(z, cbase, a.V, a.c2, row_live(g), part + (size_t)row_of(g) * a.nslices, lane);
+        const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
+        buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
       }
     }
-  } else {
-    // partial stage (the last 128-row stage of a batch that is not a multiple
-    // of 128): plain per-group load, MFMA, epilogue
-    bool first = true;
-    for (; blk < blk_end; blk += 4) {
-      const int cbase = blk * kWaveCols + lane_col;
-      float2* part = a.part + blk;
+  }
+
+  // plain path: partial stages, and the column-tail block of a full stage
+  for (; blk < blk_end; blk += 4) {
+    const int cbase = blk * kWaveCols + lane_col;
+    float2* part = a.part + blk;
+    if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
+    for (int g = 0; g < ngroups; ++g) {
+      typename UAccess<UT, VEC>::Buf one;
+      ua.load(one, row0 + 16 * g, blk);
+      float z[16];
+      one.unpack(z, cbase, a.V, row_live(g));
       if constexpr (KC > 0) {
-        if (!first) wf.load<KC>(blk * kWaveCols, w2);
-      }
-      for (int g = 0; g < ngroups; ++g) {
-        typename UAccess<UT, VEC>::Buf one;
-        if (first && g < kPrefetch) one = buf[0];
-        ua.load(one, row0 + 16 * g, blk);
-        float z[16];
-        one.unpack(z, cbase, a.V, row_live(g));
-        if constexpr (KC > 0) {
-          f32x4 acc[4];
-          mfma_group<KC>(st, g, lane, w2, acc, launder(e_lane_offset<KC>(lane)));
+        f32x4 acc[4];
+        mfma_group<KC>(st, g, lane, w2, acc, launder(e_lane_offset<KC>(lane)));
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
-        }
-        slice_partial<GREEDY>(z, cbase, a.V, a.c2, row_live(g), part + (size_t)row_of(g) * a.nslices, lane);
+          for (int i = 0; i < 4; ++i) z[4 * b + i] += acc[b][i];
       }
-      first = false;
+      const float2 v = slice_values<GREEDY, true>(z, cbase, a.V, a.c2);
+      if (row_live(g) && lane < 16) part[(size_t)row_of(g) * a.nslices] = v;
     }
   }
 }
@@ -270,9 +289,10 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   __shared__ double wave_tot[4];
   __shared__ int sh_slice;
   __shared__ double sh_before;
+  __shared__ float bias_part[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index();
   const int b = blockIdx.x;
   const size_t out = (size_t)b * a.K + (a.k - 1);
   const int prev = a.prev[(size_t)b * a.prev_stride];
@@ -402,18 +422,22 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     sh_before = hit_before;
   }
   __syncthreads();
-  if (wave != 0) return;
   const int s_star = sh_slice;
+  // re-evaluate the 64 logits of slice s_star, one column per lane; the four
+  // waves share the bias dot products (a quarter of r each)
+  const int col = s_star * kWaveCols + lane;
+  const bool col_ok = col < a.V;
+  float bias = 0.f;
+  if (a.r > 0)
+    bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok,
+                            wave, lane, bias_part);
+  if (wave != 0) return;
   const float m_s = part[s_star].x;
   const float t_in = (float)((target - sh_before) / (double)fast_exp2(m_s - M));
-
-  // re-evaluate the 64 logits of slice s_star, one column per lane
-  const int col = s_star * kWaveCols + lane;
   float z = -INFINITY;
-  if (col < a.V) {
+  if (col_ok) {
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((size_t)b * a.K + (a.k - 1)) * a.V;
-    z = load_logit(urow, col);
-    if (a.r > 0) z += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
+    z = load_logit(urow, col) + bias;
   }
   const float e = (col < a.V) ? fast_exp2(fmaf(z, a.c2, -m_s)) : 0.f;
   const float cum = wave_inclusive_scan(e);
@@ -436,10 +460,12 @@ template <typename UT, bool VEC, int KC, bool GREEDY>
 static int launch_partials(const DraftArgs& a, hipStream_t stream) {
   const int full = VEC ? a.B / kStageRows : 0;  // unaligned rows: the plain variant throughout
   const int partial = a.nstages - full;
-  if (full > 0) {
-    const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true>,
-                                 dim3(xcd_grid(a.ncol_tiles, full)), dim3(256), stream, a, 0, full);
-    if (rc) return rc;
+  if constexpr (VEC) {
+    if (full > 0) {
+      const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true>,
+                                   dim3(xcd_grid(a.ncol_tiles, full)), dim3(256), stream, a, 0, full);
+      if (rc) return rc;
+    }
   }
   if (partial > 0) {
     return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, false>,

@@ -7,7 +7,12 @@
 //        key = ((0xFFFFFFFF - bits(a)) << 32) | ((j - 1) << 24) | r
 //      so ascending keys = a descending, then j ascending, then r ascending
 //      (a is positive, so its bit pattern orders like its value);
-//   2. bitonic sort of the keys in LDS (padded to a power of two with ~0);
+//   2. bitonic sort of the keys (padded with ~0 to P = 1024 * E keys, E a
+//      power of two): thread t holds keys t*E .. t*E+E-1 in registers;
+//      compare-exchange stages whose partner distance is below E run in
+//      registers, below 64*E through wave shuffles, and only the longer ones
+//      through LDS (stored as key e of thread t at e*1024 + t, so that a
+//      wave's accesses are consecutive);
 //   3. tau increments floor(a * 2^32) (exact int64 fixed point), block prefix
 //      scan, Theta_n = double(tau_n) * 2^-32 * SPS[R + n] for every admission
 //      count n; the cut n* is the first drop minus one (EARLY_STOP), the
@@ -26,15 +31,24 @@ constexpr int kSchedMaxKeys = 16384;
 
 struct ScheduleArgs {
   int R, K;
-  const float* c;
-  const double* sps;
+  const float* __restrict__ c;
+  const double* __restrict__ sps;
   int mode, capacity;
-  float* a_out;
-  int32_t* ell_out;
-  int32_t* cu_out;
-  int32_t* n_out;
-  double* theta_out;
+  float* __restrict__ a_out;
+  int32_t* __restrict__ ell_out;
+  int32_t* __restrict__ cu_out;
+  int32_t* __restrict__ n_out;
+  double* __restrict__ theta_out;
 };
+
+constexpr int kSchedMaxK = 16;
+
+// The K confidences of request r, all requested before the first is used
+// (one memory round trip instead of K dependent ones).
+__device__ __forceinline__ void load_confidences(const ScheduleArgs& a, int r, float (&cv)[kSchedMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kSchedMaxK; ++j) cv[j] = (j < a.K) ? a.c[(size_t)r * a.K + j] : 1.0f;
+}
 
 __device__ __forceinline__ uint64_t make_key(float a, int j, int r) {
   return ((uint64_t)(0xFFFFFFFFu - __float_as_uint(a)) << 32) | ((uint64_t)j << 24) | (uint64_t)r;
@@ -49,7 +63,7 @@ __device__ __forceinline__ uint64_t key_increment(uint64_t key) {
 __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* wave_sums,
                                                          uint64_t& total) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   uint64_t incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -74,35 +88,114 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* w
   return before + incl - v;
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage of the bitonic network (block size k, partner
+// distance j) for the keys i = t*E + e of this thread, partner i ^ j: the
+// lower index of a pair keeps the smaller key in an ascending block
+// ((i & k) == 0) and the larger one in a descending block.
+template <int E, int J>
+__device__ __forceinline__ void stage_in_regs(uint64_t (&v)[E], int t, int k) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = e ^ J;
+    if (p > e) {
+      const int i = t * E + e;
+      const bool asc = (i & k) == 0;
+      const uint64_t x = v[e], y = v[p];
+      if ((x > y) == asc) {
+        v[e] = y;
+        v[p] = x;
+      }
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&v)[E], uint64_t* lds) {
+  constexpr int P = kSchedThreads * E;
+  const int t = threadIdx.x;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+        if constexpr (E > 1) {
+          switch (j) {
+            case 1: stage_in_regs<E, 1>(v, t, k); break;
+            case 2: stage_in_regs<E, (E > 2 ? 2 : 1)>(v, t, k); break;
+            case 4: stage_in_regs<E, (E > 4 ? 4 : 1)>(v, t, k); break;
+            default: stage_in_regs<E, (E > 8 ? 8 : 1)>(v, t, k); break;
+          }
+        }
+      } else if (j < 64 * E) {
+        const int tj = j / E;  // partner thread, same wave
+        const bool lower = (t & tj) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = t * E + e;
+          const bool asc = (i & k) == 0;
+          const uint64_t x = v[e];
+          const uint64_t y = shfl_xor_u64(x, tj);
+          v[e] = (asc == lower) ? (x < y ? x : y) : (x < y ? y : x);
+        }
+      } else {
+        const int tj = j / E;  // partner thread, another wave
+        const bool lower = (t & tj) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds[e * kSchedThreads + t] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = t * E + e;
+          const bool asc = (i & k) == 0;
+          const uint64_t x = v[e];
+          const uint64_t y = lds[e * kSchedThreads + (t ^ tj)];
+          v[e] = (asc == lower) ? (x < y ? x : y) : (x < y ? y : x);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+template <int E>
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
   __shared__ uint64_t keys[kSchedMaxKeys];
   __shared__ uint64_t wave_sums[kSchedThreads / 64];
   __shared__ int bad;
   __shared__ int red_i[kSchedThreads / 64];
   __shared__ double red_d[kSchedThreads / 64];
+  __shared__ uint64_t threshold_s;
+  constexpr int P = kSchedThreads * E;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index();
   const int R = a.R, K = a.K;
   const int n_cand = R * K;
-  int P2 = 2;
-  while (P2 < n_cand) P2 <<= 1;
 
   if (tid == 0) bad = 0;
   __syncthreads();
 
   // 1. survival products and keys
   for (int r = tid; r < R; r += kSchedThreads) {
+    float cv[kSchedMaxK];
+    load_confidences(a, r, cv);
     float acc = 1.0f;
-    for (int j = 0; j < K; ++j) {
-      const float cj = a.c[(size_t)r * K + j];
-      if (!(cj >= 0.0f && cj <= 1.0f)) bad = 1;  // NaN fails both tests
-      acc = __fmul_rn(acc, cj);
-      a.a_out[(size_t)r * K + j] = acc;
-      keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < kSchedMaxK; ++j) {
+      if (j < K) {
+        ok = ok && (cv[j] >= 0.0f && cv[j] <= 1.0f);  // NaN fails both tests
+        acc = __fmul_rn(acc, cv[j]);
+        a.a_out[(size_t)r * K + j] = acc;
+        keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+      }
     }
+    if (!ok) bad = 1;
   }
-  for (int i = n_cand + tid; i < P2; i += kSchedThreads) keys[i] = ~0ull;
   __syncthreads();
 
   if (bad) {  // documented data error: a valid layout with no drafts
@@ -118,26 +211,20 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     return;
   }
 
-  // 2. bitonic sort, ascending
-  for (int k = 2; k <= P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < (P2 >> 1); i += kSchedThreads) {
-        const int pos = 2 * i - (i & (j - 1));
-        const int partner = pos + j;
-        const uint64_t x = keys[pos], y = keys[partner];
-        const bool up = (pos & k) == 0;
-        if ((x > y) == up) {
-          keys[pos] = y;
-          keys[partner] = x;
-        }
-      }
-      __syncthreads();
-    }
+  // 2. sort; thread tid then holds sorted keys tid*E .. tid*E+E-1
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    v[e] = (i < n_cand) ? keys[i] : ~0ull;
   }
+  __syncthreads();
+  bitonic_sort<E>(v, keys);
 
   // number of candidates = position of the first padding key
   int cnt = 0;
-  for (int i = tid; i < P2; i += kSchedThreads) cnt += keys[i] != ~0ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt += v[e] != ~0ull;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
   if (lane == 0) red_i[wave] = cnt;
@@ -146,13 +233,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   for (int w = 0; w < kSchedThreads / 64; ++w) n_c += red_i[w];
   __syncthreads();
 
-  // 3. fixed-point tau over contiguous chunks, Theta per admission count
-  const int per = (P2 + kSchedThreads - 1) / kSchedThreads;
-  const int i0 = min(P2, tid * per);
-  const int i1 = min(P2, i0 + per);
+  // 3. fixed-point tau over this thread's chunk, Theta per admission count
+  const int i0 = tid * E;
+  const int i1 = i0 + E;
   uint64_t local = 0;
-  for (int i = i0; i < i1; ++i)
-    if (i < n_c) local += key_increment(keys[i]);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (i0 + e < n_c) local += key_increment(v[e]);
   uint64_t total;
   const uint64_t prefix = block_exclusive_scan(local, wave_sums, total);
   const uint64_t tau0 = (uint64_t)R << 32;
@@ -163,22 +250,26 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   int first_drop = 0x7FFFFFFF;
   double best = (tid == 0) ? theta0 : -INFINITY;
   int best_n = (tid == 0) ? 0 : 0x7FFFFFFF;
-  if (a.mode != 2) {
+  if (a.mode != 2 && i0 < n_c) {
+    // SPS[R + i0 .. R + i1] of this thread's admission counts, requested together
+    double spsv[E + 1];
+#pragma unroll
+    for (int e = 0; e <= E; ++e) spsv[e] = (i0 + e <= n_c) ? a.sps[R + i0 + e] : 0.0;
     uint64_t tau = tau0 + prefix;
-    double prev_theta = 0.0;
-    if (i0 < n_c) {
-      prev_theta = (i0 == 0) ? theta0 : (double)tau * 0x1p-32 * a.sps[R + i0];
-    }
-    for (int i = i0; i < i1 && i < n_c; ++i) {
-      tau += key_increment(keys[i]);
-      const int n = i + 1;
-      const double theta = (double)tau * 0x1p-32 * a.sps[R + n];
-      if (theta <= prev_theta && n < first_drop) first_drop = n;
-      if (theta > best) {
-        best = theta;
-        best_n = n;
+    double prev_theta = (i0 == 0) ? theta0 : (double)tau * 0x1p-32 * spsv[0];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (i0 + e < n_c) {
+        tau += key_increment(v[e]);
+        const int n = i0 + e + 1;
+        const double theta = (double)tau * 0x1p-32 * spsv[e + 1];
+        if (theta <= prev_theta && n < first_drop) first_drop = n;
+        if (theta > best) {
+          best = theta;
+          best_n = n;
+        }
+        prev_theta = theta;
       }
-      prev_theta = theta;
     }
   }
   // block reductions: min first_drop; max (best, -best_n)
@@ -215,19 +306,29 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     else if (a.mode == 1) n_star = bn;
     else n_star = min(max(a.capacity, 0), n_c);
     n_star_s = n_star;
+    if (n_star >= P) threshold_s = ~0ull;
   }
   __syncthreads();
   const int n_star = n_star_s;
-  // Theta of the chosen admission count, from the thread owning sorted index n*-1
+  // Theta of the chosen admission count and the threshold key (sorted index
+  // n*), from the threads owning those indices
   if (n_star == 0) {
     if (tid == 0) *a.theta_out = theta0;
   } else if (n_star - 1 >= i0 && n_star - 1 < i1) {
     uint64_t tau = tau0 + prefix;
-    for (int i = i0; i < n_star; ++i) tau += key_increment(keys[i]);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (i0 + e < n_star) tau += key_increment(v[e]);
     *a.theta_out = (double)tau * 0x1p-32 * a.sps[R + n_star];
   }
+  if (n_star >= i0 && n_star < i1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (i0 + e == n_star) threshold_s = v[e];
+  }
   if (tid == 0) *a.n_out = n_star;
-  const uint64_t threshold = (n_star < P2) ? keys[n_star] : ~0ull;
+  __syncthreads();
+  const uint64_t threshold = threshold_s;
 
   // 4. lengths and the flattened layout
   const int rper = (R + kSchedThreads - 1) / kSchedThreads;
@@ -235,11 +336,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   const int r1 = min(R, r0 + rper);
   uint64_t mine = 0;
   for (int r = r0; r < r1; ++r) {
+    float cv[kSchedMaxK];
+    load_confidences(a, r, cv);
     int ell = 0;
     float acc = 1.0f;
-    for (int j = 0; j < K; ++j) {
-      acc = __fmul_rn(acc, a.c[(size_t)r * K + j]);
-      if (acc > 0.0f && make_key(acc, j, r) < threshold) ++ell;
+#pragma unroll
+    for (int j = 0; j < kSchedMaxK; ++j) {
+      if (j < K) {
+        acc = __fmul_rn(acc, cv[j]);
+        if (acc > 0.0f && make_key(acc, j, r) < threshold) ++ell;
+      }
     }
     a.ell_out[r] = ell;
     mine += 1 + ell;
@@ -257,7 +363,12 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
                  int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out,
                  hipStream_t stream) {
   ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out};
-  return launch_kernel("schedule", schedule_kernel, dim3(1), dim3(kSchedThreads), stream, a);
+  const int n = R * K;
+  if (n <= kSchedThreads) return launch_kernel("schedule", schedule_kernel<1>, dim3(1), dim3(kSchedThreads), stream, a);
+  if (n <= 2 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<2>, dim3(1), dim3(kSchedThreads), stream, a);
+  if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a);
+  if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a);
+  return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a);
 }
 
 }  // namespace dspark

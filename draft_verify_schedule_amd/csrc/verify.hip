@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
   const int row = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x - row * a.nchunks;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
   if (wbase >= a.V) return;
   const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)row * a.V;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
   constexpr int ITERS = (kRowChunk / 4) / COLS;  // loads per wave per item
   constexpr int LPS = kRowSlice / EPL;           // lanes per 256-column slice
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int items = a.N * a.nchunks;
   const rsrc_t rs = make_rsrc(a.P, (uint32_t)((uint64_t)a.N * a.V * sizeof(PT)));
   const uint32_t lane_off = (uint32_t)(lane * EPL * sizeof(PT));
@@ -290,7 +290,7 @@ __device__ __forceinline__ int owner_of(const int32_t* cu, int R, int i) {
 template <typename PT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int i = blockIdx.x * 4 + wave_index();
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.rej_count = 0;  // filled by the decide kernel
   if (i >= a.N) return;
   const float2* part = a.ppart + (size_t)i * a.nsP;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   int col_tile, stage;
   if (!xcd_tile(blockIdx.x, a.ncol_tiles, a.nstages, col_tile, stage)) return;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int n0 = col_tile * kTileCols + wave * kWaveCols;
   const int row0 = stage * kStageRows;
   const int ngroups = min(kGroupsPerWG, (a.R - row0 + 15) / 16);
@@ -517,7 +517,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   if (sp >= per_stage) return;
   const int nsplit = per_stage * 8, split = sp * 8 + xcd;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
   const int row0 = stage * kStageRows;
   const int nrows = min(kStageRows, count - row0);
   const int ngroups = (nrows + 15) / 16;
@@ -657,7 +657,7 @@ __device__ __forceinline__ SliceHit find_slice(int ns, double target, double inc
 template <typename PT, typename DT>
 __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = blockIdx.x * 4 + wave_index();
   if (r >= a.R) return;
   const int4 in = a.info[r];
   if (in.x < 0) return;  // decide already wrote -1
