@@ -88,7 +88,8 @@ def main():
            "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
            "theta": torch.empty(1, dtype=torch.float64, device=dev)}
     ws_d = torch.empty(max(256, ds.dspark_markov_draft_workspace_bytes(B, K, V, r)), dtype=torch.uint8, device=dev)
-    ds.dspark_schedule(c, sps, args.mode, 0, out=sch)
+    ws_s = torch.empty(max(256, ds.dspark_schedule_workspace_bytes(B, K)), dtype=torch.uint8, device=dev)
+    ds.dspark_schedule(c, sps, args.mode, 0, out=sch, workspace=ws_s)
     cu0 = sch["cu_seqlens"].clone()
     N = int(cu0[-1].item())
     verified = int(sch["ell"].sum().item())
@@ -100,7 +101,7 @@ def main():
 
     def step(s):
         ds.dspark_markov_draft(U, W1, W2, x0, T, w.rng_seed, s, out=(x, q, lse), workspace=ws_d)
-        ds.dspark_schedule(c, sps, args.mode, 0, out=sch)
+        ds.dspark_schedule(c, sps, args.mode, 0, out=sch, workspace=ws_s)
         ds.dspark_verify(P, sch["cu_seqlens"], U, W1, W2, x0, x, q, lse, T, w.rng_seed, s, out=(n_acc, tok),
                          workspace=ws_v)
 

@@ -51,7 +51,9 @@ def load_library():
     lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp,
                                         c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
     lib.dspark_schedule.restype = c_int
-    lib.dspark_schedule.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp]
+    lib.dspark_schedule_workspace_bytes.restype = c_size
+    lib.dspark_schedule_workspace_bytes.argtypes = [c_int] * 2
+    lib.dspark_schedule.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_verify_workspace_bytes.restype = c_size
     lib.dspark_verify_workspace_bytes.argtypes = [c_int] * 5
     lib.dspark_verify.restype = c_int
@@ -151,7 +153,11 @@ def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, worksp
     return x, q, lse
 
 
-def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None):
+def dspark_schedule_workspace_bytes(R, K):
+    return load_library().dspark_schedule_workspace_bytes(R, K)
+
+
+def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None, workspace=None):
     """Algorithm 1 on confidences c [R, K] f32 and the SPS table sps [L] f64.
 
     Returns dict with a [R, K] f32, ell [R] int32, cu_seqlens [R+1] int32,
@@ -168,9 +174,13 @@ def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None):
                "cu_seqlens": torch.empty(R + 1, dtype=torch.int32, device=dev),
                "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
                "theta": torch.empty(1, dtype=torch.float64, device=dev)}
+    need = lib.dspark_schedule_workspace_bytes(R, K)
+    if workspace is None:
+        workspace = _workspace(need, dev)
     st = lib.dspark_schedule(R, K, _ptr(c), _ptr(sps), sps.numel(), int(mode), int(capacity), _ptr(out["a"]),
                              _ptr(out["ell"]), _ptr(out["cu_seqlens"]), _ptr(out["n_admitted"]),
-                             _ptr(out["theta"]), _stream())
+                             _ptr(out["theta"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream())
     if st != 0:
         raise DSparkError("dspark_schedule", st)
     return out

@@ -1,26 +1,29 @@
 // Hardware-aware prefix scheduler (DSpark paper, section 3.2.2, Algorithm 1;
 // modes of section 5.2; "Speculative decoding, from zero to DSpark", section 8).
 //
-// One workgroup of 1024 threads:
-//   1. survival a[r,j] = c[r,1]*...*c[r,j] (float32, left to right) and a 64-bit
-//      key per candidate with a > 0:
-//        key = ((0xFFFFFFFF - bits(a)) << 32) | ((j - 1) << 24) | r
-//      so ascending keys = a descending, then j ascending, then r ascending
-//      (a is positive, so its bit pattern orders like its value);
-//   2. bitonic sort of the keys (padded with ~0 to P = 1024 * E keys, E a
-//      power of two): thread t holds keys t*E .. t*E+E-1 in registers;
-//      compare-exchange stages whose partner distance is below E run in
-//      registers, below 64*E through wave shuffles, and only the longer ones
-//      through LDS (stored as key e of thread t at e*1024 + t, so that a
-//      wave's accesses are consecutive);
-//   3. tau increments floor(a * 2^32) (exact int64 fixed point), block prefix
-//      scan, Theta_n = double(tau_n) * 2^-32 * SPS[R + n] for every admission
-//      count n; the cut n* is the first drop minus one (EARLY_STOP), the
-//      earliest maximum (GLOBAL) or min(capacity, |E|) (TOPK).  The fixed-point
-//      sum is exact, so this parallel evaluation equals the sequential walk
-//      bit for bit;
-//   4. l_r = number of r's candidates whose key lies below the n*-th sorted key
-//      (a prefix of positions by construction), and cu_seqlens by a block scan.
+// Two launches:
+//   schedule_rank (one workgroup per 32 candidates): every workgroup builds
+//     all candidate keys in LDS,
+//       a[r,j] = c[r,1]*...*c[r,j] (float32, left to right), and for a > 0
+//       key = ((0xFFFFFFFF - bits(a)) << 32) | ((j - 1) << 24) | r
+//     so that ascending keys = a descending, then j ascending, then r
+//     ascending (a is positive, so its bit pattern orders like its value);
+//     keys are distinct, so the sorted position of a key is the number of
+//     keys below it: 32 partial counts per key (1024 threads), summed, and the
+//     key is written to that position of the workspace;
+//   schedule (one workgroup of 1024 threads):
+//     1. survival products again (a_out, the domain check, the candidate
+//        count n_c), then thread t loads sorted keys t*E .. t*E+E-1
+//        (E = candidates / 1024 rounded up to a power of two);
+//     2. tau increments floor(a * 2^32) (exact int64 fixed point), block
+//        prefix scan, Theta_n = double(tau_n) * 2^-32 * SPS[R + n] for every
+//        admission count n; the cut n* is the first drop minus one
+//        (EARLY_STOP), the earliest maximum (GLOBAL) or min(capacity, |E|)
+//        (TOPK).  The fixed-point sum is exact, so this parallel evaluation
+//        equals the sequential walk bit for bit;
+//     3. l_r = number of r's candidates whose key lies below the n*-th sorted
+//        key (a prefix of positions by construction), and cu_seqlens by a
+//        block scan.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -88,82 +91,50 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* w
   return before + incl - v;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
+constexpr int kRankKeysPerWG = 32;
+constexpr int kRankParts = kSchedThreads / kRankKeysPerWG;
 
-// One compare-exchange stage of the bitonic network (block size k, partner
-// distance j) for the keys i = t*E + e of this thread, partner i ^ j: the
-// lower index of a pair keeps the smaller key in an ascending block
-// ((i & k) == 0) and the larger one in a descending block.
-template <int E, int J>
-__device__ __forceinline__ void stage_in_regs(uint64_t (&v)[E], int t, int k) {
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int p = e ^ J;
-    if (p > e) {
-      const int i = t * E + e;
-      const bool asc = (i & k) == 0;
-      const uint64_t x = v[e], y = v[p];
-      if ((x > y) == asc) {
-        v[e] = y;
-        v[p] = x;
-      }
-    }
-  }
-}
-
-template <int E>
-__device__ __forceinline__ void bitonic_sort(uint64_t (&v)[E], uint64_t* lds) {
-  constexpr int P = kSchedThreads * E;
-  const int t = threadIdx.x;
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < E) {
-        if constexpr (E > 1) {
-          switch (j) {
-            case 1: stage_in_regs<E, 1>(v, t, k); break;
-            case 2: stage_in_regs<E, (E > 2 ? 2 : 1)>(v, t, k); break;
-            case 4: stage_in_regs<E, (E > 4 ? 4 : 1)>(v, t, k); break;
-            default: stage_in_regs<E, (E > 8 ? 8 : 1)>(v, t, k); break;
-          }
-        }
-      } else if (j < 64 * E) {
-        const int tj = j / E;  // partner thread, same wave
-        const bool lower = (t & tj) == 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = t * E + e;
-          const bool asc = (i & k) == 0;
-          const uint64_t x = v[e];
-          const uint64_t y = shfl_xor_u64(x, tj);
-          v[e] = (asc == lower) ? (x < y ? x : y) : (x < y ? y : x);
-        }
-      } else {
-        const int tj = j / E;  // partner thread, another wave
-        const bool lower = (t & tj) == 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) lds[e * kSchedThreads + t] = v[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = t * E + e;
-          const bool asc = (i & k) == 0;
-          const uint64_t x = v[e];
-          const uint64_t y = lds[e * kSchedThreads + (t ^ tj)];
-          v[e] = (asc == lower) ? (x < y ? x : y) : (x < y ? y : x);
-        }
-        __syncthreads();
-      }
-    }
-  }
-}
-
-template <int E>
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a) {
+__global__ __launch_bounds__(kSchedThreads) void schedule_rank_kernel(ScheduleArgs a, uint64_t* __restrict__ sorted) {
   __shared__ uint64_t keys[kSchedMaxKeys];
+  __shared__ uint32_t part_cnt[kRankParts][kRankKeysPerWG];
+  const int tid = threadIdx.x;
+  const int R = a.R, K = a.K;
+  const int n = R * K;
+  for (int r = tid; r < R; r += kSchedThreads) {
+    float cv[kSchedMaxK];
+    load_confidences(a, r, cv);
+    float acc = 1.0f;
+#pragma unroll
+    for (int j = 0; j < kSchedMaxK; ++j) {
+      if (j < K) {
+        acc = __fmul_rn(acc, cv[j]);
+        keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+      }
+    }
+  }
+  __syncthreads();
+  // thread (part p, key slot q): keys of part p below key kk
+  const int q = tid % kRankKeysPerWG;
+  const int p = tid / kRankKeysPerWG;
+  const int kk = blockIdx.x * kRankKeysPerWG + q;
+  const uint64_t x = kk < n ? keys[kk] : ~0ull;
+  const int y0 = (int)((int64_t)p * n / kRankParts);
+  const int y1 = (int)((int64_t)(p + 1) * n / kRankParts);
+  uint32_t cnt = 0;
+  for (int y = y0; y < y1; ++y) cnt += keys[y] < x ? 1u : 0u;
+  part_cnt[p][q] = cnt;
+  __syncthreads();
+  if (tid < kRankKeysPerWG && kk < n && x != ~0ull) {
+    uint32_t rank = 0;
+#pragma unroll
+    for (int i = 0; i < kRankParts; ++i) rank += part_cnt[i][tid];
+    sorted[rank] = x;  // rank < number of candidates with a > 0
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
+                                                                const uint64_t* __restrict__ sorted) {
   __shared__ uint64_t wave_sums[kSchedThreads / 64];
   __shared__ int bad;
   __shared__ int red_i[kSchedThreads / 64];
@@ -174,12 +145,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   const int lane = tid & 63;
   const int wave = wave_index();
   const int R = a.R, K = a.K;
-  const int n_cand = R * K;
 
   if (tid == 0) bad = 0;
   __syncthreads();
 
-  // 1. survival products and keys
+  // 1. survival products, the domain check and the number of candidates
+  int cnt = 0;
   for (int r = tid; r < R; r += kSchedThreads) {
     float cv[kSchedMaxK];
     load_confidences(a, r, cv);
@@ -191,11 +162,17 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
         ok = ok && (cv[j] >= 0.0f && cv[j] <= 1.0f);  // NaN fails both tests
         acc = __fmul_rn(acc, cv[j]);
         a.a_out[(size_t)r * K + j] = acc;
-        keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+        cnt += acc > 0.0f;
       }
     }
     if (!ok) bad = 1;
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  if (lane == 0) red_i[wave] = cnt;
+  __syncthreads();
+  int n_c = 0;
+  for (int w = 0; w < kSchedThreads / 64; ++w) n_c += red_i[w];
   __syncthreads();
 
   if (bad) {  // documented data error: a valid layout with no drafts
@@ -211,29 +188,15 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
     return;
   }
 
-  // 2. sort; thread tid then holds sorted keys tid*E .. tid*E+E-1
+  // thread tid holds sorted keys tid*E .. tid*E+E-1 (padding ~0)
   uint64_t v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid * E + e;
-    v[e] = (i < n_cand) ? keys[i] : ~0ull;
+    v[e] = (i < n_c) ? sorted[i] : ~0ull;
   }
-  __syncthreads();
-  bitonic_sort<E>(v, keys);
 
-  // number of candidates = position of the first padding key
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) cnt += v[e] != ~0ull;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-  if (lane == 0) red_i[wave] = cnt;
-  __syncthreads();
-  int n_c = 0;
-  for (int w = 0; w < kSchedThreads / 64; ++w) n_c += red_i[w];
-  __syncthreads();
-
-  // 3. fixed-point tau over this thread's chunk, Theta per admission count
+  // 2. fixed-point tau over this thread's chunk, Theta per admission count
   const int i0 = tid * E;
   const int i1 = i0 + E;
   uint64_t local = 0;
@@ -330,7 +293,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   __syncthreads();
   const uint64_t threshold = threshold_s;
 
-  // 4. lengths and the flattened layout
+  // 3. lengths and the flattened layout
   const int rper = (R + kSchedThreads - 1) / kSchedThreads;
   const int r0 = min(R, tid * rper);
   const int r1 = min(R, r0 + rper);
@@ -359,16 +322,25 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a)
   }
 }
 
+size_t schedule_workspace_bytes(int R, int K) {
+  return (((size_t)R * K * sizeof(uint64_t)) + 255) & ~(size_t)255;
+}
+
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
-                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out,
+                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, void* workspace,
                  hipStream_t stream) {
   ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out};
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(workspace);
   const int n = R * K;
-  if (n <= kSchedThreads) return launch_kernel("schedule", schedule_kernel<1>, dim3(1), dim3(kSchedThreads), stream, a);
-  if (n <= 2 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<2>, dim3(1), dim3(kSchedThreads), stream, a);
-  if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a);
-  if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a);
-  return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a);
+  int rc = launch_kernel("schedule_rank", schedule_rank_kernel, dim3((n + kRankKeysPerWG - 1) / kRankKeysPerWG),
+                         dim3(kSchedThreads), stream, a, sorted);
+  if (rc) return rc;
+  const uint64_t* cs = sorted;
+  if (n <= kSchedThreads) return launch_kernel("schedule", schedule_kernel<1>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+  if (n <= 2 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<2>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+  if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+  if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+  return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a, cs);
 }
 
 }  // namespace dspark

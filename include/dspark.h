@@ -130,13 +130,18 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature,
  * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R * K <= DSPARK_MAX_CANDIDATES.
  * Data errors: any c outside [0, 1] or NaN gives ell = 0, cu_seqlens[r] = r,
  * n_admitted = -1, theta = NaN (a valid no-draft layout).
- * One workgroup; no workspace.
+ * Workspace: dspark_schedule_workspace_bytes(R, K) bytes (the sorted
+ * candidate keys), caller-owned, contents need not be initialised.
+ * Two launches: candidate ranks across many workgroups, then one workgroup
+ * for the admission scan and the layout.
  * ------------------------------------------------------------------------ */
+size_t dspark_schedule_workspace_bytes(int R, int K);
 int dspark_schedule(int R, int K, const float* c,
                     const double* sps, int sps_len,
                     int mode, int capacity,
                     float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out,
                     int32_t* n_admitted_out, double* theta_out,
+                    void* workspace, size_t workspace_bytes,
                     void* stream);
 
 /* ------------------------------------------------------------------------ *

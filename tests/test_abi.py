@@ -47,23 +47,31 @@ def test_workspace_queries(lib):
     assert lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 256) % 256 == 0
     assert lib.dspark_verify_workspace_bytes(512, 7, 151936, 256, 4096) > 0
     assert lib.dspark_verify_workspace_bytes(0, 7, 10, 0, 1) == 0
+    assert lib.dspark_schedule_workspace_bytes(512, 7) >= 512 * 7 * 8
+    assert lib.dspark_schedule_workspace_bytes(512, 7) % 256 == 0
+    assert lib.dspark_schedule_workspace_bytes(4096, 7) == 0
 
 
 NULL = ctypes.c_void_p(0)
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every case fails validation first
+WS = ctypes.c_size_t(1 << 30)
 
 
 def test_schedule_argument_errors(lib):
     # R <= 0, K too large, too many candidates
-    assert lib.dspark_schedule(0, 7, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
-    assert lib.dspark_schedule(4, 17, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
-    assert lib.dspark_schedule(4096, 7, FAKE, FAKE, 10 ** 6, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+    assert lib.dspark_schedule(0, 7, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
+    assert lib.dspark_schedule(4, 17, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
+    assert lib.dspark_schedule(4096, 7, FAKE, FAKE, 10 ** 6, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
     # SPS table too short, bad mode, negative capacity
-    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
-    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
-    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 2, -1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -4
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -4
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -4
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 2, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -4
     # NULL input
-    assert lib.dspark_schedule(4, 7, NULL, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -1
+    assert lib.dspark_schedule(4, 7, NULL, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -1
+    # workspace missing or too small
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, WS, NULL) == -5
+    small = ctypes.c_size_t(lib.dspark_schedule_workspace_bytes(4, 7) - 1)
+    assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small, NULL) == -5
 
 
 def test_draft_argument_errors(lib):
