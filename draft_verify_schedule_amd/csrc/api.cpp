@@ -10,7 +10,7 @@
 #include <vector>
 
 namespace dspark {
-size_t draft_workspace_bytes(int B, int V);
+size_t draft_workspace_bytes(int B, int K, int V);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
               const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
               float* lse_out, void* workspace, hipStream_t stream);
@@ -110,7 +110,7 @@ size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
   (void)K;
   (void)r;
   if (B <= 0 || V <= 0) return 0;
-  return dspark::draft_workspace_bytes(B, V);
+  return dspark::draft_workspace_bytes(B, K, V);
 }
 
 int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
@@ -124,7 +124,7 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::draft_workspace_bytes(B, V)) return DSPARK_E_WORKSPACE;
+  if (!workspace || workspace_bytes < dspark::draft_workspace_bytes(B, K, V)) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
     return DSPARK_E_RANGE;

@@ -75,16 +75,21 @@ struct W2Frags {
   __device__ __forceinline__ void load_if(int n0, bool valid, bf16x8 (&fr)[4][KC]) const {
     load_from<KC>(valid ? (uint32_t)n0 * col_bytes : bytes, fr);
   }
-  template <int KC>
+  template <int KC, int K0 = 0, int K1 = KC>
   __device__ __forceinline__ void load_from(uint32_t base, bf16x8 (&fr)[4][KC]) const {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
+      for (int kc = K0; kc < K1; ++kc) {
         const uint32_t soff = base + (uint32_t)(4 * b) * col_bytes + (uint32_t)(64 * kc);
         fr[b][kc] = __builtin_bit_cast(bf16x8, buffer_load16(rsrc, lane_off, soff));
       }
     }
+  }
+  // k chunks [K0, K1) only (valid = false: zeros, no memory access)
+  template <int KC, int K0, int K1>
+  __device__ __forceinline__ void load_range_if(int n0, bool valid, bf16x8 (&fr)[4][KC]) const {
+    load_from<KC, K0, K1>(valid ? (uint32_t)n0 * col_bytes : bytes, fr);
   }
 };
 
@@ -166,7 +171,9 @@ __device__ __forceinline__ int launder(int v) {
 // acc[b][i] = bias[row 16g + l%16, column n0 + 16*(l/16) + 4b + i].
 // With ZERO = false the accumulators arrive holding the base logits of the
 // same 16 x 64 tile, so the MFMAs leave base + bias in them directly.
-template <int KC, bool ZERO = true>
+// Only the k chunks [K0, K1) (K0 = 0, K1 = KC: the whole contraction); ZERO
+// clears the accumulators first.
+template <int KC, bool ZERO = true, int K0 = 0, int K1 = KC>
 __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane,
                                            const bf16x8 (&w2)[4][KC], f32x4 (&acc)[4],
                                            int e_off = -1) {
@@ -174,14 +181,14 @@ __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane
   if (e_off < 0) e_off = e_lane_offset<KC>(lane);
   const char* base = reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC>::kPitch * 2;
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
+  for (int kc = K0; kc < K1; ++kc)
     e[kc] = *reinterpret_cast<const bf16x8*>(base + 64 * kc);
   if constexpr (ZERO) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
+  for (int kc = K0; kc < K1; ++kc) {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2[b][kc], e[kc], acc[b], 0, 0, 0);

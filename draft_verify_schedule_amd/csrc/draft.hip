@@ -239,9 +239,23 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
           refill(g + 1 + kPrefetch);
 #pragma unroll
           for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
-          if constexpr (KC > 0) mfma_group<KC, false>(st, g + 1, lane, w2, acc, e_off);
+          if constexpr (KC > 0) {
+            if (g + 2 < kGroupsPerWG) {
+              mfma_group<KC, false>(st, g + 1, lane, w2, acc, e_off);
+            } else {
+              // last group of the block: the first half of the next block's W2
+              // fragments is requested as soon as the MFMAs reading those
+              // registers have issued, the second half after the rest
+              constexpr int KH = KC / 2;
+              mfma_group<KC, false, 0, KH>(st, g + 1, lane, w2, acc, e_off);
+              __builtin_amdgcn_sched_barrier(0);
+              wf.load_range_if<KC, 0, KH>(nxt * kWaveCols, has_next, w2);
+              __builtin_amdgcn_sched_barrier(0);
+              mfma_group<KC, false, KH, KC>(st, g + 1, lane, w2, acc, e_off);
+            }
+          }
         } else if constexpr (KC > 0) {
-          wf.load_if<KC>(nxt * kWaveCols, has_next, w2);
+          wf.load_range_if<KC, KC / 2, KC>(nxt * kWaveCols, has_next, w2);
         }
         const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
         buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
@@ -289,6 +303,9 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   __shared__ double wave_tot[4];
   __shared__ int sh_slice;
   __shared__ double sh_before;
+  __shared__ double sh_w[kLocPer];
+  __shared__ double sh_acc0;
+  __shared__ int sh_s0;
   __shared__ float bias_part[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,53 +409,78 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     const float last = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
     owner = last < 0.f ? 0 : (int)last;
   }
+  // The owner's slices hold the crossing.  Registers path: the owner puts
+  // their masses in LDS and every wave finds the crossing with a wave scan.
+  // Otherwise the owner walks its run and shares the result.
   if (tid == owner) {
-    double acc = incl - local;
-    int hit = -1, last = -1;
-    double hit_before = 0.0, last_before = acc;
-    auto visit = [&](int s, double w) {
-      if (w > 0.0) {
-        if (hit < 0 && acc + w > target) {
-          hit = s;
-          hit_before = acc;
-        }
-        last = s;
-        last_before = acc;
-      }
-      acc += w;
-    };
+    const double acc0 = incl - local;
     if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < kLocPer; ++i)
-        if (s0 + i < s1) visit(s0 + i, weight(p[i]));
+      for (int i = 0; i < kLocPer; ++i) sh_w[i] = (s0 + i < s1) ? weight(p[i]) : 0.0;
+      sh_acc0 = acc0;
+      sh_s0 = s0;
     } else {
-      for (int s = s0; s < s1; ++s) visit(s, weight(part[s]));
+      double acc = acc0;
+      int hit = -1, last = -1;
+      double hit_before = 0.0, last_before = acc;
+      for (int s = s0; s < s1; ++s) {
+        const double w = weight(part[s]);
+        if (w > 0.0) {
+          if (hit < 0 && acc + w > target) {
+            hit = s;
+            hit_before = acc;
+          }
+          last = s;
+          last_before = acc;
+        }
+        acc += w;
+      }
+      if (hit < 0) {
+        hit = last;
+        hit_before = last_before;
+      }
+      sh_slice = hit < 0 ? 0 : hit;  // no mass at all (non-finite logits): stay in range
+      sh_before = hit_before;
     }
-    if (hit < 0) {
-      hit = last;
-      hit_before = last_before;
-    }
-    sh_slice = hit < 0 ? 0 : hit;  // no mass at all (non-finite logits): stay in range
-    sh_before = hit_before;
   }
   __syncthreads();
-  const int s_star = sh_slice;
+  int s_star;
+  double before;
+  if (in_regs) {
+    const double w = lane < kLocPer ? sh_w[lane] : 0.0;
+    const double acc0 = sh_acc0;
+    const double cum = acc0 + wave_inclusive_scan(w);
+    int pick = wave_first_lane(cum > target && w > 0.0);
+    if (pick < 0) {  // rounding: the last slice with mass
+      const unsigned long long mm = __ballot(w > 0.0);
+      pick = mm ? 63 - __clzll((long long)mm) : -1;
+    }
+    const double cb = __shfl(cum - w, pick < 0 ? 0 : pick, 64);
+    s_star = pick < 0 ? 0 : sh_s0 + pick;  // no mass at all (non-finite logits): stay in range
+    before = pick < 0 ? acc0 : cb;
+  } else {
+    s_star = sh_slice;
+    before = sh_before;
+  }
   // re-evaluate the 64 logits of slice s_star, one column per lane; the four
-  // waves share the bias dot products (a quarter of r each)
+  // waves share the bias dot products (a quarter of r each); wave 0's base
+  // logit and slice maximum are requested first
   const int col = s_star * kWaveCols + lane;
   const bool col_ok = col < a.V;
+  const UT* urow = reinterpret_cast<const UT*>(a.U) + ((size_t)b * a.K + (a.k - 1)) * a.V;
+  float base = 0.f;
+  float m_s = 0.f;
+  if (wave == 0) {
+    base = col_ok ? load_logit(urow, col) : 0.f;
+    m_s = part[s_star].x;
+  }
   float bias = 0.f;
   if (a.r > 0)
     bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok,
                             wave, lane, bias_part);
   if (wave != 0) return;
-  const float m_s = part[s_star].x;
-  const float t_in = (float)((target - sh_before) / (double)fast_exp2(m_s - M));
-  float z = -INFINITY;
-  if (col_ok) {
-    const UT* urow = reinterpret_cast<const UT*>(a.U) + ((size_t)b * a.K + (a.k - 1)) * a.V;
-    z = load_logit(urow, col) + bias;
-  }
+  const float t_in = (float)((target - before) / (double)fast_exp2(m_s - M));
+  const float z = col_ok ? base + bias : -INFINITY;
   const float e = (col < a.V) ? fast_exp2(fmaf(z, a.c2, -m_s)) : 0.f;
   const float cum = wave_inclusive_scan(e);
   int pick = wave_first_lane(cum > t_in && e > 0.f);
@@ -508,7 +550,8 @@ static int run_draft_typed(DraftArgs a, bool vec, hipStream_t stream) {
   return 0;
 }
 
-size_t draft_workspace_bytes(int B, int V) {
+size_t draft_workspace_bytes(int B, int K, int V) {
+  (void)K;
   const size_t ns = (size_t)(V + kWaveCols - 1) / kWaveCols;
   return ((size_t)B * ns * sizeof(float2) + 255) / 256 * 256;
 }

@@ -184,93 +184,107 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
 }
 
 // Aligned-row variant: persistent grid-stride over (row, 8192-column chunk)
-// items with the next item's loads (buffer resource, per-lane VGPR offset,
-// scalar row offset) in flight while the current item is reduced.
+// items.  Wave w covers columns [2048 w, 2048 w + 2048) of the chunk and lane
+// l the 32 contiguous columns from 32 l, so lanes 8s .. 8s+7 hold 256-column
+// slice s of the wave: each lane reduces its 32 values, then three lane swaps
+// finish the slice.  The next item's loads (buffer resource, per-lane VGPR
+// offset, scalar row offset) are issued before the current item is reduced;
+// the loop body has no branches: loads past the last item and stores of lanes
+// that do not lead a slice get offsets past their buffer resource.
 template <typename PT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs a) {
-  constexpr int EPL = 16 / sizeof(PT);           // elements per 16-byte load
-  constexpr int COLS = 64 * EPL;                 // columns per load instruction
-  constexpr int ITERS = (kRowChunk / 4) / COLS;  // loads per wave per item
-  constexpr int LPS = kRowSlice / EPL;           // lanes per 256-column slice
+  constexpr int kWaveColsR = kRowChunk / 4;     // 2048
+  constexpr int CPL = kWaveColsR / 64;          // columns per lane per item
+  constexpr int EPL = 16 / sizeof(PT);          // elements per 16-byte load
+  constexpr int LOADS = CPL / EPL;
+  constexpr int LPS = kRowSlice / CPL;          // lanes per slice
+  static_assert(LPS == 8, "three lane swaps per slice");
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const int items = a.N * a.nchunks;
-  const rsrc_t rs = make_rsrc(a.P, (uint32_t)((uint64_t)a.N * a.V * sizeof(PT)));
-  const uint32_t lane_off = (uint32_t)(lane * EPL * sizeof(PT));
-  auto issue = [&](int item, u32x4 (&w)[ITERS]) {
-    const int row = item / a.nchunks;
-    const int chunk = item - row * a.nchunks;
-    const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
-    const uint32_t soff = (uint32_t)(((uint64_t)row * a.V + wbase) * sizeof(PT));
+  const uint32_t pbytes = (uint32_t)((uint64_t)a.N * a.V * sizeof(PT));
+  const rsrc_t rs = make_rsrc(a.P, pbytes);
+  const uint32_t lane_off = (uint32_t)(lane * CPL * sizeof(PT));
+  const uint32_t obytes = (uint32_t)((uint64_t)a.N * a.nsP * sizeof(float2));
+  const int4v ors = raw_rsrc_words(a.ppart, obytes);
+  const bool leader = (lane % LPS) == 0;
+
+  auto issue = [&](int item, u32x4 (&w)[LOADS]) {
+    const bool live = item < items;
+    const int row = live ? item / a.nchunks : 0;
+    const int chunk = live ? item - row * a.nchunks : 0;
+    const int wbase = chunk * kRowChunk + wave * kWaveColsR;
+    const uint32_t soff = live ? (uint32_t)(((uint64_t)row * a.V + wbase) * sizeof(PT)) : pbytes;
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) w[it] = buffer_load16(rs, lane_off + (uint32_t)(it * COLS * sizeof(PT)), soff);
+    for (int l = 0; l < LOADS; ++l) w[l] = buffer_load16(rs, lane_off + (uint32_t)(16 * l), soff);
   };
-  auto reduce = [&](int item, const u32x4 (&w)[ITERS]) {
+  auto reduce = [&](int item, const u32x4 (&w)[LOADS]) {
     const int row = item / a.nchunks;
     const int chunk = item - row * a.nchunks;
-    const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
-    if (wbase >= a.V) return;
-    float2* out = a.ppart + (size_t)row * a.nsP;
+    const int wbase = chunk * kRowChunk + wave * kWaveColsR;
+    const int c0 = wbase + lane * CPL;
+    float v[CPL];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int c = wbase + it * COLS + lane * EPL;
-      const int slice = (wbase + it * COLS) / kRowSlice + lane / LPS;
-      float v[EPL];
-      const bool ok = c < a.V;
+    for (int l = 0; l < LOADS; ++l) {
+      const bool ok = c0 + l * EPL < a.V;  // V is a multiple of EPL: whole vectors are in or out
       if constexpr (sizeof(PT) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[2 * e] = ok ? __uint_as_float(w[it][e] << 16) : -INFINITY;
-          v[2 * e + 1] = ok ? __uint_as_float(w[it][e] & 0xFFFF0000u) : -INFINITY;
+          v[l * EPL + 2 * e] = ok ? __uint_as_float(w[l][e] << 16) : -INFINITY;
+          v[l * EPL + 2 * e + 1] = ok ? __uint_as_float(w[l][e] & 0xFFFF0000u) : -INFINITY;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = ok ? __uint_as_float(w[it][e]) : -INFINITY;
-      }
-      if constexpr (GREEDY) {
-        float m = -INFINITY;
-        int idx = -1;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          if (ok && (idx < 0 || v[e] > m)) {
-            m = v[e];
-            idx = c + e;
-          }
-#pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) {
-          const float m2 = __shfl_xor(m, off, 64);
-          const int i2 = __shfl_xor(idx, off, 64);
-          merge_argmax(m, idx, m2, i2);
-        }
-        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) out[slice] = make_float2(m, __int_as_float(idx));
-      } else {
-        float m = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          v[e] *= a.c2;
-          m = fmaxf(m, v[e]);
-        }
-#pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        const float mm = (m == -INFINITY) ? 0.f : m;
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s += fast_exp2(v[e] - mm);
-#pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
-        if ((lane % LPS) == 0 && slice < a.nsP && c < a.V) out[slice] = make_float2(m, s);
+        for (int e = 0; e < 4; ++e) v[l * EPL + e] = ok ? __uint_as_float(w[l][e]) : -INFINITY;
       }
     }
+    float2 res;
+    if constexpr (GREEDY) {
+      float m = -INFINITY;
+      int idx = -1;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+        if (c0 + e < a.V && (idx < 0 || v[e] > m)) {
+          m = v[e];
+          idx = c0 + e;
+        }
+#pragma unroll
+      for (int off = 1; off < LPS; off <<= 1) {
+        const float m2 = __shfl_xor(m, off, 64);
+        const int i2 = __shfl_xor(idx, off, 64);
+        merge_argmax(m, idx, m2, i2);
+      }
+      res = make_float2(m, __int_as_float(idx));
+    } else {
+      float m = v[0];
+#pragma unroll
+      for (int e = 1; e < CPL; ++e) m = fmaxf(m, v[e]);
+#pragma unroll
+      for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const bool empty = m == -INFINITY;
+      const float mc = empty ? 0.f : m * a.c2;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s += fast_exp2(fmaf(v[e], a.c2, -mc));
+#pragma unroll
+      for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
+      res = make_float2(empty ? -INFINITY : mc, s);
+    }
+    const int slice = wbase / kRowSlice + lane / LPS;
+    const uint32_t voff = (leader && slice < a.nsP) ? (uint32_t)(((uint64_t)row * a.nsP + slice) * sizeof(float2))
+                                                    : obytes;
+    buffer_store8_untracked(ors, res, voff, 0u);
   };
+
   int item = blockIdx.x;
-  u32x4 cur[ITERS], nxt[ITERS];
-  if (item < items) issue(item, cur);
+  u32x4 cur[LOADS], nxt[LOADS];
+  issue(item, cur);
   for (; item < items; item += gridDim.x) {
-    const int nitem = item + gridDim.x;
-    if (nitem < items) issue(nitem, nxt);
+    issue(item + gridDim.x, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next item's loads ahead of this item's waits
     reduce(item, cur);
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) cur[it] = nxt[it];
+    for (int l = 0; l < LOADS; ++l) cur[l] = nxt[l];
   }
 }
 
