@@ -54,6 +54,8 @@ def load_library():
     lib.dspark_schedule_workspace_bytes.restype = c_size
     lib.dspark_schedule_workspace_bytes.argtypes = [c_int] * 2
     lib.dspark_schedule.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_schedule_async.restype = c_int
+    lib.dspark_schedule_async.argtypes = [c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_verify_workspace_bytes.restype = c_size
     lib.dspark_verify_workspace_bytes.argtypes = [c_int] * 5
     lib.dspark_verify.restype = c_int
@@ -183,6 +185,36 @@ def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None, 
                              _stream())
     if st != 0:
         raise DSparkError("dspark_schedule", st)
+    return out
+
+
+def dspark_schedule_async(c, sps, capacity, out=None, workspace=None):
+    """Top-capacity admission of c [R, K] with the capacity read on the device
+    (capacity: int32 tensor of one element, e.g. the n_admitted of an earlier
+    GLOBAL schedule).  Returns the same dict as dspark_schedule."""
+    lib = load_library()
+    R, K = c.shape
+    _check(c, "c", torch.float32)
+    _check(sps, "sps", torch.float64)
+    _check(capacity, "capacity", torch.int32)
+    if capacity.numel() < 1:
+        raise ValueError("capacity: one int32 element expected")
+    dev = c.device
+    if out is None:
+        out = {"a": torch.empty((R, K), dtype=torch.float32, device=dev),
+               "ell": torch.empty(R, dtype=torch.int32, device=dev),
+               "cu_seqlens": torch.empty(R + 1, dtype=torch.int32, device=dev),
+               "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
+               "theta": torch.empty(1, dtype=torch.float64, device=dev)}
+    need = lib.dspark_schedule_workspace_bytes(R, K)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_schedule_async(R, K, _ptr(c), _ptr(sps), sps.numel(), _ptr(capacity), _ptr(out["a"]),
+                                   _ptr(out["ell"]), _ptr(out["cu_seqlens"]), _ptr(out["n_admitted"]),
+                                   _ptr(out["theta"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream())
+    if st != 0:
+        raise DSparkError("dspark_schedule_async", st)
     return out
 
 

@@ -15,8 +15,9 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
               const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
               float* lse_out, void* workspace, hipStream_t stream);
 size_t schedule_workspace_bytes(int R, int K);
-int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
-                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, void* workspace, hipStream_t stream);
+int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
+                 const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
+                 double* theta_out, void* workspace, hipStream_t stream);
 size_t verify_workspace_bytes(int R, int V, int N);
 int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N, const int32_t* cu,
                const void* D, bool d_bf16, const void* W1, const void* W2, int r, const int32_t* x0,
@@ -147,8 +148,21 @@ int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len
   if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
   if (!c || !sps || !a_out || !ell_out || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
   if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
-  return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, a_out, ell_out, cu_seqlens_out,
+  return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_seqlens_out,
                                          n_admitted_out, theta_out, workspace,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_schedule_async(int R, int K, const float* c, const double* sps, int sps_len, const int32_t* capacity,
+                          float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out, int32_t* n_admitted_out,
+                          double* theta_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
+  if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
+  if (!c || !sps || !capacity || !a_out || !ell_out || !cu_seqlens_out || !n_admitted_out || !theta_out)
+    return DSPARK_E_NULL;
+  if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
+  return hip_status(dspark::run_schedule(R, K, c, sps, DSPARK_SCHED_TOPK, 0, capacity, a_out, ell_out,
+                                         cu_seqlens_out, n_admitted_out, theta_out, workspace,
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 

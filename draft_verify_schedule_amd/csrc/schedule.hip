@@ -42,6 +42,7 @@ struct ScheduleArgs {
   int32_t* __restrict__ cu_out;
   int32_t* __restrict__ n_out;
   double* __restrict__ theta_out;
+  const int32_t* __restrict__ capacity_dev;  // TOPK capacity read on the device, or null
 };
 
 constexpr int kSchedMaxK = 16;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
     int n_star;
     if (a.mode == 0) n_star = (fd == 0x7FFFFFFF) ? n_c : fd - 1;
     else if (a.mode == 1) n_star = bn;
-    else n_star = min(max(a.capacity, 0), n_c);
+    else n_star = min(max(a.capacity_dev ? *a.capacity_dev : a.capacity, 0), n_c);
     n_star_s = n_star;
     if (n_star >= P) threshold_s = ~0ull;
   }
@@ -326,10 +327,10 @@ size_t schedule_workspace_bytes(int R, int K) {
   return (((size_t)R * K * sizeof(uint64_t)) + 255) & ~(size_t)255;
 }
 
-int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
-                 int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, void* workspace,
-                 hipStream_t stream) {
-  ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out};
+int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
+                 const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
+                 double* theta_out, void* workspace, hipStream_t stream) {
+  ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out, capacity_dev};
   uint64_t* sorted = reinterpret_cast<uint64_t*>(workspace);
   const int n = R * K;
   int rc = launch_kernel("schedule_rank", schedule_rank_kernel, dim3((n + kRankKeysPerWG - 1) / kRankKeysPerWG),

@@ -145,6 +145,29 @@ int dspark_schedule(int R, int K, const float* c,
                     void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Asynchronous capacity.  DSpark paper section 5.2 (the scheduler run
+ * asynchronously: capacity from the confidences of two steps earlier, fresh
+ * candidates ranked and cut to it); "Speculative decoding, from zero to
+ * DSpark", section 9.
+ *
+ * dspark_schedule in TOPK mode with the capacity read from device memory:
+ * `capacity` [1] int32 on the device, typically the n_admitted_out of a
+ * DSPARK_SCHED_GLOBAL call made two steps earlier, so that a serving loop
+ * fixes the next verify batch size without a host synchronisation.  The
+ * first min(max(capacity, 0), number of candidates) candidates of the
+ * current a are admitted; a negative capacity (e.g. -1 from a call that saw
+ * invalid confidences) admits nothing.  All other arguments, outputs, limits,
+ * data errors and the workspace are those of dspark_schedule.
+ * ------------------------------------------------------------------------ */
+int dspark_schedule_async(int R, int K, const float* c,
+                          const double* sps, int sps_len,
+                          const int32_t* capacity,
+                          float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out,
+                          int32_t* n_admitted_out, double* theta_out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Rejection-sampling verification over the flattened variable-length batch.
  * DSpark paper section 2.1 and section 5.3 (flattened variable-length
  * batch); "Speculative decoding, from zero to DSpark", section 2 and

@@ -40,13 +40,15 @@ Modules:
 
 from .philox import philox4x32_10, uniform, PURPOSE_DRAFT, PURPOSE_ACCEPT, PURPOSE_RESAMPLE
 from .draft import draft_ref, independent_draft_ref
-from .schedule import schedule_ref, schedule_bruteforce, SCHED_EARLY_STOP, SCHED_GLOBAL, SCHED_TOPK
+from .schedule import (schedule_ref, schedule_async_ref, schedule_bruteforce, SCHED_EARLY_STOP,
+                       SCHED_GLOBAL, SCHED_TOPK)
 from .verify import verify_ref
 from .step import run_step
 
 __all__ = [
     "philox4x32_10", "uniform", "PURPOSE_DRAFT", "PURPOSE_ACCEPT", "PURPOSE_RESAMPLE",
     "draft_ref", "independent_draft_ref",
-    "schedule_ref", "schedule_bruteforce", "SCHED_EARLY_STOP", "SCHED_GLOBAL", "SCHED_TOPK",
+    "schedule_ref", "schedule_async_ref", "schedule_bruteforce", "SCHED_EARLY_STOP", "SCHED_GLOBAL",
+    "SCHED_TOPK",
     "verify_ref", "run_step",
 ]

@@ -105,6 +105,20 @@ def schedule_ref(c, sps, mode=SCHED_EARLY_STOP, capacity=0):
             "thetas": np.asarray(thetas)}
 
 
+def schedule_async_ref(c_now, c_old, sps):
+    """Asynchronous capacity (DSpark paper, section 5.2; "Speculative decoding,
+    from zero to DSpark", section 9): the number of tokens the next pass can
+    verify is fixed beforehand by the no-break (GLOBAL) search over
+    confidences from two steps earlier; the current step then admits the
+    top-capacity candidates of its fresh survival values (TOPK).  The
+    capacity never depends on the current block's tokens, which is what makes
+    the no-break search lossless here."""
+    capacity = schedule_ref(c_old, sps, SCHED_GLOBAL)["n_admitted"]
+    out = schedule_ref(c_now, sps, SCHED_TOPK, capacity)
+    out["capacity"] = int(capacity)
+    return out
+
+
 def schedule_bruteforce(c, sps):
     """Exhaustive search over every (l_1..l_R) in {0..K}^R, exact rationals.
 

@@ -74,6 +74,18 @@ def test_schedule_argument_errors(lib):
     assert lib.dspark_schedule(4, 7, FAKE, FAKE, 33, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small, NULL) == -5
 
 
+def test_schedule_async_argument_errors(lib):
+    def call(R=4, K=7, c=FAKE, sps=FAKE, n=33, cap=FAKE, out=FAKE, ws=FAKE, wsb=WS):
+        return lib.dspark_schedule_async(R, K, c, sps, n, cap, out, out, out, out, out, ws, wsb, NULL)
+    assert call(R=0) == -2
+    assert call(K=17) == -2
+    assert call(n=32) == -4
+    assert call(cap=NULL) == -1
+    assert call(c=NULL) == -1
+    assert call(ws=NULL) == -5
+    assert call(wsb=ctypes.c_size_t(lib.dspark_schedule_workspace_bytes(4, 7) - 1)) == -5
+
+
 def test_draft_argument_errors(lib):
     f = ctypes.c_float
     ws = ctypes.c_size_t(1 << 30)

@@ -180,6 +180,40 @@ def test_schedule_maximum_candidates():
         _sched_compare(c, sps, mode)
 
 
+@pytest.mark.parametrize("name", ["ds_stepped", "sched_stress", "full_step"])
+def test_schedule_async_capacity_bit_exact(name):
+    """Asynchronous capacity: GLOBAL on the confidences of an earlier block
+    gives the capacity on the device; the async call admits the top-capacity
+    candidates of the current block without the capacity leaving the GPU."""
+    w = wl().make(name, device="cpu", V=64)
+    rng = np.random.default_rng(91)
+    c_old = w.c.numpy().copy()
+    c_old = np.clip(c_old * rng.uniform(0.8, 1.2, size=c_old.shape), 0, 1).astype(np.float32)   # an older block
+    sps = w.sps.to(DEV)
+    old = ds().dspark_schedule(torch.from_numpy(c_old).to(DEV), sps, 1, 0)
+    got = ds().dspark_schedule_async(w.c.to(DEV), sps, old["n_admitted"])
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in got.items()}
+    ref = oracle.schedule_async_ref(w.c.numpy(), c_old, w.sps.numpy())
+    _say("async %s capacity %d n_admitted %d" % (name, ref["capacity"], ref["n_admitted"]))
+    assert int(old["n_admitted"].cpu()[0]) == ref["capacity"]
+    np.testing.assert_array_equal(got["ell"], ref["ell"])
+    np.testing.assert_array_equal(got["cu_seqlens"], ref["cu_seqlens"])
+    assert int(got["n_admitted"][0]) == ref["n_admitted"]
+    assert got["theta"].view(np.uint64)[0] == np.float64(ref["theta"]).view(np.uint64)
+
+
+def test_schedule_async_capacity_edges():
+    c = torch.from_numpy(np.random.default_rng(3).uniform(0.2, 1, size=(40, 5)).astype(np.float32))
+    sps = torch.ones(40 * 6 + 1, dtype=torch.float64)
+    for cap in (-1, 0, 1, 17, 200, 10 ** 6):
+        got = ds().dspark_schedule_async(c.to(DEV), sps.to(DEV), torch.tensor([cap], dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        ref = oracle.schedule_ref(c.numpy(), sps.numpy(), 2, max(cap, 0))
+        assert int(got["n_admitted"].cpu()[0]) == ref["n_admitted"] == min(max(cap, 0), 200)
+        np.testing.assert_array_equal(got["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+
+
 def test_schedule_invalid_confidence():
     c = torch.full((5, 3), 0.5)
     c[2, 1] = float("nan")

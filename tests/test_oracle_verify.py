@@ -23,7 +23,7 @@ from scipy.special import logsumexp
 
 import oracle.verify as overify
 from oracle.draft import draft_ref
-from oracle.schedule import schedule_ref, SCHED_EARLY_STOP, SCHED_GLOBAL
+from oracle.schedule import schedule_async_ref, schedule_ref, SCHED_EARLY_STOP, SCHED_GLOBAL
 from oracle.step import run_step
 from oracle.verify import verify_ref
 
@@ -179,6 +179,41 @@ def test_appendix_a_composed_monte_carlo(mode, expect_key):
         outs[t] = d["x"][t, 0] if v["n_acc"][0] >= 1 else v["tok"][0]
     pa = np.mean(outs == 0)
     assert pa == pytest.approx(g[expect_key], abs=5 * np.sqrt(0.25 / trials))
+
+
+def test_appendix_a_async_capacity_monte_carlo():
+    """The same composed experiment with the asynchronous scheduler: the
+    capacity comes from the no-break search over the confidences of an
+    earlier, independent block (two steps back), the current block takes its
+    top-capacity candidates.  The capacity then cannot see x_1, so the first
+    emitted token is A with the target's probability 0.7, although the no-break
+    search itself is used (it gives 0.85 when run on the current block)."""
+    with open(os.path.join(GOLD, "appendix_a.json")) as f:
+        g = json.load(f)
+    sps = np.zeros(4)
+    for b, val in g["sps_by_batch"].items():
+        sps[int(b)] = val
+    p, q = np.array(g["target"]), np.array(g["draft"])
+    c2_of = lambda x1: g["case_high"]["c2"] if x1 == 0 else g["case_low"]["c2"]
+    trials = 20000
+    U = np.broadcast_to(np.log(q), (trials, 2, 2))
+    d = draft_ref(U, None, None, np.zeros(trials, dtype=np.int64), 1.0, 107, 0)
+    old = draft_ref(U, None, None, np.zeros(trials, dtype=np.int64), 1.0, 108, 0)   # the block two steps back
+    outs = np.empty(trials, dtype=np.int64)
+    caps = np.empty(trials, dtype=np.int64)
+    for t in range(trials):
+        c_now = np.array([[g["c1"], c2_of(d["x"][t, 0])]], dtype=np.float32)
+        c_old = np.array([[g["c1"], c2_of(old["x"][t, 0])]], dtype=np.float32)
+        s = schedule_async_ref(c_now, c_old, sps)
+        caps[t] = s["capacity"]
+        ell = int(s["ell"][0])
+        P = np.broadcast_to(np.log(p), (ell + 1, 2))
+        v = verify_ref(P, [0, ell + 1], U[t:t + 1], None, None, [0], d["x"][t:t + 1], 1.0, 107, t + 1)
+        outs[t] = d["x"][t, 0] if v["n_acc"][0] >= 1 else v["tok"][0]
+    # both capacities occur (2 after an old x_1 = A, 0 after B)
+    assert set(np.unique(caps)) == {0, 2}
+    pa = np.mean(outs == 0)
+    assert pa == pytest.approx(g["output_A_lossless"], abs=5 * np.sqrt(0.21 / trials))
 
 
 def test_end_to_end_zero_bias_equal_distributions_flat_sps():
