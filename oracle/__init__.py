@@ -43,6 +43,7 @@ from .draft import draft_ref, independent_draft_ref
 from .schedule import (schedule_ref, schedule_async_ref, schedule_bruteforce, SCHED_EARLY_STOP,
                        SCHED_GLOBAL, SCHED_TOPK)
 from .verify import verify_ref
+from .label import acceptance_label_ref
 from .step import run_step
 
 __all__ = [
@@ -50,5 +51,5 @@ __all__ = [
     "draft_ref", "independent_draft_ref",
     "schedule_ref", "schedule_async_ref", "schedule_bruteforce", "SCHED_EARLY_STOP", "SCHED_GLOBAL",
     "SCHED_TOPK",
-    "verify_ref", "run_step",
+    "verify_ref", "run_step", "acceptance_label_ref",
 ]
