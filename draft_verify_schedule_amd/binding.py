@@ -61,6 +61,11 @@ def load_library():
     lib.dspark_verify.restype = c_int
     lib.dspark_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp,
                                   c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, c_size, vp]
+    lib.dspark_acceptance_label_workspace_bytes.restype = c_size
+    lib.dspark_acceptance_label_workspace_bytes.argtypes = [c_int] * 4
+    lib.dspark_acceptance_label.restype = c_int
+    lib.dspark_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int, vp, vp,
+                                            vp, vp, vp, c_size, vp]
     lib.dspark_uniforms.restype = c_int
     lib.dspark_uniforms.argtypes = [c_u64, c_u64, c_int, c_int, c_int, vp, vp]
     lib.dspark_profiler_enable.restype = c_int
@@ -259,6 +264,43 @@ def dspark_verify(P, cu_seqlens, D, W1, W2, x0, x, q_tok, lse_d, temperature, se
     if st != 0:
         raise DSparkError("dspark_verify", st)
     return n_acc, tok
+
+
+def dspark_acceptance_label_workspace_bytes(B, K, V, r):
+    return load_library().dspark_acceptance_label_workspace_bytes(B, K, V, r)
+
+
+def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, workspace=None):
+    """Analytic acceptance probability c*[r, k] = 1 - TV(q_{r,k}, p_{r,k}).
+
+    P [B, K, V] target logits (row (r, k) judges draft position k+1); D
+    [B, K, V] draft base logits; W1 / W2 as for dspark_markov_draft (or None);
+    x0 [B]; x, lse_d [B, K] from dspark_markov_draft.  Returns c [B, K] f32.
+    """
+    lib = load_library()
+    B, K, V = D.shape
+    _check(P, "P", shape=(B, K, V))
+    _check(D, "D")
+    r = 0
+    if W1 is not None or W2 is not None:
+        r = W1.shape[1]
+        _check(W1, "W1", torch.bfloat16, (V, r))
+        _check(W2, "W2", torch.bfloat16, (V, r))
+    _check(x0, "x0", torch.int32, (B,))
+    _check(x, "x", torch.int32, (B, K))
+    _check(lse_d, "lse_d", torch.float32, (B, K))
+    dev = D.device
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.float32, device=dev)
+    need = lib.dspark_acceptance_label_workspace_bytes(B, K, V, r)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_acceptance_label(B, K, V, float(temperature), _ptr(P), _dtype_code(P), _ptr(D), _dtype_code(D),
+                                     _ptr(W1), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(lse_d), _ptr(out),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_acceptance_label", st)
+    return out
 
 
 def dspark_uniforms(seed, step, n, position, purpose, out=None):

@@ -19,6 +19,10 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
                  double* theta_out, void* workspace, hipStream_t stream);
 size_t verify_workspace_bytes(int R, int V, int N);
+size_t label_workspace_bytes(int B, int K, int V);
+int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
+              const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
+              float* c_out, void* workspace, hipStream_t stream);
 int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N, const int32_t* cu,
                const void* D, bool d_bf16, const void* W1, const void* W2, int r, const int32_t* x0,
                const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed, uint64_t step,
@@ -195,6 +199,34 @@ int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_d
   return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
                                        d_dtype == DSPARK_BF16, W1, W2, r, x0, x, q_tok, lse_d, seed, step,
                                        n_acc_out, tok_out, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
+  (void)r;
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0) return 0;
+  return dspark::label_workspace_bytes(B, K, V);
+}
+
+int dspark_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
+                            int d_dtype, const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x,
+                            const float* lse_d, float* c_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!P || !D || !x0 || !x || !c_out) return DSPARK_E_NULL;
+  if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
+  if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
+  if (!workspace || workspace_bytes < dspark::label_workspace_bytes(B, K, V)) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
+    return DSPARK_E_RANGE;
+  return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
+                                      W1, W2, r, x0, x, lse_d, c_out, workspace,
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, void* stream) {

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
 // columns, 128 requests (8 MFMA groups) per workgroup, W2 fragments held in
 // registers, the target and draft rows of group g+2 requested before the
 // epilogue of group g.  Requests that are not correcting take no loads.
-template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC>
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL = false>
 __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   int col_tile, stage;
   if (!xcd_tile(blockIdx.x, a.ncol_tiles, a.nstages, col_tile, stage)) return;
@@ -402,18 +402,25 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   const int wave = wave_index();
   const int n0 = col_tile * kTileCols + wave * kWaveCols;
   const int row0 = stage * kStageRows;
-  const int ngroups = min(kGroupsPerWG, (a.R - row0 + 15) / 16);
+  // LABEL: one item per (request, position) pair, item i = r * K + k; its
+  // target row is P row i, its draft row D row i
+  const int nrow = LABEL ? a.R * a.K : a.R;
+  const int ngroups = min(kGroupsPerWG, (nrow - row0 + 15) / 16);
   const bool col_live = n0 < a.V;
   const int cbase = n0 + 16 * (lane >> 4);
   const int slice = n0 / kWaveCols;
   auto req = [&](int g) { return row0 + 16 * g + (lane & 15); };
   // requests that do not correct (or lie past R) read row 0 and are masked
-  auto info_of = [&](int g) { return req(g) < a.R ? a.info[req(g)] : make_int4(-1, 0, 0, 0); };
+  auto info_of = [&](int g) {
+    if constexpr (LABEL) return req(g) < nrow ? make_int4(1, req(g), 0, 0) : make_int4(-1, 0, 0, 0);
+    else return req(g) < a.R ? a.info[req(g)] : make_int4(-1, 0, 0, 0);
+  };
   auto prow = [&](const int4& in) {
     return reinterpret_cast<const PT*>(a.P) + (size_t)(in.x == 1 ? in.y : 0) * a.V;
   };
   auto drow = [&](int g, const int4& in) {
-    return reinterpret_cast<const DT*>(a.D) + (in.x == 1 ? ((size_t)req(g) * a.K + in.w) * a.V : 0);
+    const size_t row = LABEL ? (size_t)req(g) : (size_t)req(g) * a.K + in.w;
+    return reinterpret_cast<const DT*>(a.D) + (in.x == 1 ? row * a.V : 0);
   };
 
   GroupLogits<PT, VEC_P> pb0, pb1;
@@ -434,7 +441,8 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
     const int32_t* x0 = a.x0;
     const int32_t* x = a.x;
     const int K = a.K;
-    stage_e<KC>(st, a.W1, a.r, a.V, row0, a.R, [&](int g) {
+    stage_e<KC>(st, a.W1, a.r, a.V, row0, nrow, [&](int g) {
+      if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
       const int4 in = info[g];
       if (in.x != 1) return -1;
       return in.w == 0 ? x0[g] : x[(size_t)g * K + in.w - 1];
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
     if (live) {
       const float2 ms = a.rowms[in.y];
       const float lp = ms.x + fast_log2(ms.y);
-      const float lq = a.lse_d[(size_t)req(g) * a.K + in.w] * kLog2e;
+      const float lq = a.lse_d[LABEL ? (size_t)req(g) : (size_t)req(g) * a.K + in.w] * kLog2e;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = fast_exp2(fmaf(t[e], a.c2, -lp));
@@ -518,10 +526,12 @@ struct ResidualRow {
   float lp, lq;           // log2-normalisers of p and q
 };
 
-template <typename PT, typename DT, int KC>
+template <typename PT, typename DT, int KC, bool LABEL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void verify_residual_stream_kernel(VerifyArgs a) {
-  const int count = *a.rej_count;
+  // LABEL: one item per (request, position) pair, item i = r * K + k, with
+  // target row i and draft row i; otherwise the compacted correcting requests
+  const int count = LABEL ? a.R * a.K : *a.rej_count;
   if (count <= 0) return;
   const int active = (count + kStageRows - 1) / kStageRows;
   const int slots = gridDim.x / 8;
@@ -544,13 +554,15 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   if (threadIdx.x < kStageRows) {
     ResidualRow rr{0u, 0u, 0.f, 0.f};
     if ((int)threadIdx.x < nrows) {
-      const int r = a.rej_list[row0 + threadIdx.x];
-      const int4 in = a.info[r];
+      const int item = row0 + threadIdx.x;
+      const int r = LABEL ? item : a.rej_list[item];
+      const int4 in = LABEL ? make_int4(1, item, 0, 0) : a.info[r];
+      const uint64_t drow = LABEL ? (uint64_t)item : (uint64_t)r * a.K + in.w;
       const float2 ms = a.rowms[in.y];
       rr.p_off = (uint32_t)((uint64_t)in.y * a.V * sizeof(PT));
-      rr.d_off = (uint32_t)(((uint64_t)r * a.K + in.w) * a.V * sizeof(DT));
+      rr.d_off = (uint32_t)(drow * a.V * sizeof(DT));
       rr.lp = ms.x + fast_log2(ms.y);
-      rr.lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
+      rr.lq = a.lse_d[drow] * kLog2e;
     }
     rows[threadIdx.x] = rr;
   }
@@ -563,6 +575,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     const int32_t* x = a.x;
     const int K = a.K;
     stage_e<KC>(st, a.W1, a.r, a.V, row0, count, [&](int g) {
+      if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
       const int r = list[g];
       const int4 in = info[r];
       return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
@@ -614,7 +627,10 @@ void verify_residual_stream_kernel(VerifyArgs a) {
           s += fmaxf(p - q, 0.f);
         }
       s = rows_sum(s);
-      if (lv && lane < 16) a.rpart[(size_t)a.rej_list[row0 + 16 * g + lane] * a.ns64 + blk] = s;
+      if (lv && lane < 16) {
+        const int item = row0 + 16 * g + lane;
+        a.rpart[(size_t)(LABEL ? item : a.rej_list[item]) * a.ns64 + blk] = s;
+      }
     }
   }
 }
@@ -803,48 +819,108 @@ static VerifyLayout verify_layout(int R, int V, int N) {
 
 size_t verify_workspace_bytes(int R, int V, int N) { return verify_layout(R, V, N).total; }
 
-template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC>
+// ------------------------------------------------------- acceptance label --
+// c*_i = 1 - 1/2 ||q_i - p_i||_1 for every (request, position) item
+// i = r * K + k (DSpark paper, section 3.2.1: the confidence head's label is
+// the per-step acceptance rate fixed by the total variation distance between
+// the draft and target distributions; "Speculative decoding, from zero to
+// DSpark", section 2).  The passes of verification are reused: row
+// statistics of the target rows, their merge into the normaliser below, the
+// residual mass sum_v max(0, p - q) per 64-column slice (the LABEL mapping of
+// the residual kernels), and 1 minus its fp64 total here.  Greedy: c* is 1
+// where the target row's first argmax is the drafted token.
+template <bool GREEDY>
+__global__ __launch_bounds__(256) void label_merge_kernel(VerifyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave_index();
+  if (i >= a.N) return;
+  const float2* part = a.ppart + (size_t)i * a.nsP;
+  float m = -INFINITY, s = 0.f;
+  int idx = -1;
+  for (int k = lane; k < a.nsP; k += 64) {
+    const float2 p = part[k];
+    if constexpr (GREEDY) merge_argmax(m, idx, p.x, __float_as_int(p.y));
+    else merge_ms(m, s, p.x, p.y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    if constexpr (GREEDY) {
+      const int i2 = __shfl_xor(idx, off, 64);
+      merge_argmax(m, idx, m2, i2);
+    } else {
+      const float s2 = __shfl_xor(s, off, 64);
+      merge_ms(m, s, m2, s2);
+    }
+  }
+  if (lane == 0) a.rowms[i] = GREEDY ? make_float2(m, __int_as_float(idx)) : make_float2(m, s);
+}
+
+template <bool GREEDY>
+__global__ __launch_bounds__(256) void label_reduce_kernel(VerifyArgs a, float* __restrict__ c_out) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave_index();
+  if (i >= a.N) return;
+  const int k = i % a.K;
+  const int prev = k == 0 ? a.x0[i / a.K] : a.x[i - 1];
+  const int xi = a.x[i];
+  const bool ok = prev >= 0 && prev < a.V && xi >= 0 && xi < a.V;
+  if constexpr (GREEDY) {
+    if (lane == 0) c_out[i] = ok ? ((__float_as_int(a.rowms[i].y) == xi) ? 1.f : 0.f) : NAN;
+    return;
+  }
+  const float* rp = a.rpart + (size_t)i * a.ns64;
+  double z = 0.0;
+  for (int s = lane; s < a.ns64; s += 64) z += (double)rp[s];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (lane == 0) c_out[i] = ok ? (float)fmin(1.0, fmax(0.0, 1.0 - z)) : NAN;
+}
+
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL>
 static int launch_residual(const VerifyArgs& a, hipStream_t stream) {
-  return launch_kernel("verify_residual", verify_residual_kernel<PT, DT, VEC_P, VEC_D, KC>,
+  return launch_kernel(LABEL ? "label_residual" : "verify_residual",
+                       verify_residual_kernel<PT, DT, VEC_P, VEC_D, KC, LABEL>,
                        dim3(xcd_grid(a.ncol_tiles, a.nstages)), dim3(256), stream, a);
 }
 
-template <typename PT, typename DT, bool VEC_P, bool VEC_D>
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, bool LABEL = false>
 static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
   switch ((a.r + 31) / 32) {
-    case 0: return launch_residual<PT, DT, VEC_P, VEC_D, 0>(a, stream);
-    case 1: return launch_residual<PT, DT, VEC_P, VEC_D, 1>(a, stream);
-    case 2: return launch_residual<PT, DT, VEC_P, VEC_D, 2>(a, stream);
-    case 3: return launch_residual<PT, DT, VEC_P, VEC_D, 3>(a, stream);
-    case 4: return launch_residual<PT, DT, VEC_P, VEC_D, 4>(a, stream);
-    case 5: return launch_residual<PT, DT, VEC_P, VEC_D, 5>(a, stream);
-    case 6: return launch_residual<PT, DT, VEC_P, VEC_D, 6>(a, stream);
-    case 7: return launch_residual<PT, DT, VEC_P, VEC_D, 7>(a, stream);
-    case 8: return launch_residual<PT, DT, VEC_P, VEC_D, 8>(a, stream);
+    case 0: return launch_residual<PT, DT, VEC_P, VEC_D, 0, LABEL>(a, stream);
+    case 1: return launch_residual<PT, DT, VEC_P, VEC_D, 1, LABEL>(a, stream);
+    case 2: return launch_residual<PT, DT, VEC_P, VEC_D, 2, LABEL>(a, stream);
+    case 3: return launch_residual<PT, DT, VEC_P, VEC_D, 3, LABEL>(a, stream);
+    case 4: return launch_residual<PT, DT, VEC_P, VEC_D, 4, LABEL>(a, stream);
+    case 5: return launch_residual<PT, DT, VEC_P, VEC_D, 5, LABEL>(a, stream);
+    case 6: return launch_residual<PT, DT, VEC_P, VEC_D, 6, LABEL>(a, stream);
+    case 7: return launch_residual<PT, DT, VEC_P, VEC_D, 7, LABEL>(a, stream);
+    case 8: return launch_residual<PT, DT, VEC_P, VEC_D, 8, LABEL>(a, stream);
     default: return -1;
   }
 }
 
-template <typename PT, typename DT, int KC>
+template <typename PT, typename DT, int KC, bool LABEL>
 static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   // about two workgroups per CU, and enough 8-slot rows for every stage
-  const int slots = std::max(64, (a.R + kStageRows - 1) / kStageRows);
-  return launch_kernel("verify_residual", verify_residual_stream_kernel<PT, DT, KC>, dim3(8 * slots), dim3(256),
-                       stream, a);
+  const int rows = LABEL ? a.R * a.K : a.R;
+  const int slots = std::max(64, (rows + kStageRows - 1) / kStageRows);
+  return launch_kernel(LABEL ? "label_residual" : "verify_residual", verify_residual_stream_kernel<PT, DT, KC, LABEL>,
+                       dim3(8 * slots), dim3(256), stream, a);
 }
 
-template <typename PT, typename DT>
+template <typename PT, typename DT, bool LABEL = false>
 static int dispatch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   switch ((a.r + 31) / 32) {
-    case 0: return launch_residual_stream<PT, DT, 0>(a, stream);
-    case 1: return launch_residual_stream<PT, DT, 1>(a, stream);
-    case 2: return launch_residual_stream<PT, DT, 2>(a, stream);
-    case 3: return launch_residual_stream<PT, DT, 3>(a, stream);
-    case 4: return launch_residual_stream<PT, DT, 4>(a, stream);
-    case 5: return launch_residual_stream<PT, DT, 5>(a, stream);
-    case 6: return launch_residual_stream<PT, DT, 6>(a, stream);
-    case 7: return launch_residual_stream<PT, DT, 7>(a, stream);
-    case 8: return launch_residual_stream<PT, DT, 8>(a, stream);
+    case 0: return launch_residual_stream<PT, DT, 0, LABEL>(a, stream);
+    case 1: return launch_residual_stream<PT, DT, 1, LABEL>(a, stream);
+    case 2: return launch_residual_stream<PT, DT, 2, LABEL>(a, stream);
+    case 3: return launch_residual_stream<PT, DT, 3, LABEL>(a, stream);
+    case 4: return launch_residual_stream<PT, DT, 4, LABEL>(a, stream);
+    case 5: return launch_residual_stream<PT, DT, 5, LABEL>(a, stream);
+    case 6: return launch_residual_stream<PT, DT, 6, LABEL>(a, stream);
+    case 7: return launch_residual_stream<PT, DT, 7, LABEL>(a, stream);
+    case 8: return launch_residual_stream<PT, DT, 8, LABEL>(a, stream);
     default: return -1;
   }
 }
@@ -928,6 +1004,81 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   if (p_bf16) return run_verify_typed<uint16_t, float>(a, greedy, vec_p, vec_d, stream);
   if (d_bf16) return run_verify_typed<float, uint16_t>(a, greedy, vec_p, vec_d, stream);
   return run_verify_typed<float, float>(a, greedy, vec_p, vec_d, stream);
+}
+
+size_t label_workspace_bytes(int B, int K, int V) {
+  const size_t N = (size_t)B * K;
+  const size_t nsP = (V + kRowSlice - 1) / kRowSlice, ns64 = (V + kWaveCols - 1) / kWaveCols;
+  return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(N * ns64 * sizeof(float));
+}
+
+template <typename PT, typename DT>
+static int run_label_typed(VerifyArgs& a, float* c_out, bool greedy, bool vec_p, bool vec_d, hipStream_t stream) {
+  int rc;
+  const dim3 b256(256);
+  const dim3 stream_grid(std::min(a.N * a.nchunks, kRowstatsWGs));
+  const dim3 per_row((a.N + 3) / 4);
+  if (greedy) {
+    rc = vec_p ? launch_kernel("label_rowstats", verify_rowstats_stream_kernel<PT, true>, stream_grid, b256, stream, a)
+               : launch_kernel("label_rowstats", verify_rowstats_kernel<PT, false, true>, dim3(a.N * a.nchunks), b256,
+                               stream, a);
+    if (rc) return rc;
+    rc = launch_kernel("label_merge", label_merge_kernel<true>, per_row, b256, stream, a);
+    if (rc) return rc;
+    return launch_kernel("label_reduce", label_reduce_kernel<true>, per_row, b256, stream, a, c_out);
+  }
+  rc = vec_p ? launch_kernel("label_rowstats", verify_rowstats_stream_kernel<PT, false>, stream_grid, b256, stream, a)
+             : launch_kernel("label_rowstats", verify_rowstats_kernel<PT, false, false>, dim3(a.N * a.nchunks), b256,
+                             stream, a);
+  if (rc) return rc;
+  rc = launch_kernel("label_merge", label_merge_kernel<false>, per_row, b256, stream, a);
+  if (rc) return rc;
+  if (vec_p && vec_d) rc = dispatch_residual_stream<PT, DT, true>(a, stream);
+  else if (vec_p) rc = dispatch_residual<PT, DT, true, false, true>(a, stream);
+  else if (vec_d) rc = dispatch_residual<PT, DT, false, true, true>(a, stream);
+  else rc = dispatch_residual<PT, DT, false, false, true>(a, stream);
+  if (rc) return rc;
+  return launch_kernel("label_reduce", label_reduce_kernel<false>, per_row, b256, stream, a, c_out);
+}
+
+int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
+              const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
+              float* c_out, void* workspace, hipStream_t stream) {
+  const int N = B * K;
+  char* ws = reinterpret_cast<char*>(workspace);
+  VerifyArgs a{};
+  a.R = B;
+  a.K = K;
+  a.V = V;
+  a.N = N;
+  a.r = r;
+  const bool greedy = temperature == 0.f;
+  a.c2 = greedy ? 1.f : kLog2e / temperature;
+  a.P = P;
+  a.D = D;
+  a.W1 = reinterpret_cast<const uint16_t*>(W1);
+  a.W2t = reinterpret_cast<const uint16_t*>(W2);
+  a.x0 = x0;
+  a.x = x;
+  a.lse_d = lse_d;
+  a.nsP = (V + kRowSlice - 1) / kRowSlice;
+  a.ns64 = (V + kWaveCols - 1) / kWaveCols;
+  a.nchunks = (V + kRowChunk - 1) / kRowChunk;
+  a.ncol_tiles = (V + kTileCols - 1) / kTileCols;
+  a.nstages = (N + kStageRows - 1) / kStageRows;
+  size_t off = 0;
+  a.ppart = reinterpret_cast<float2*>(ws + off);
+  off += align256((size_t)N * a.nsP * sizeof(float2));
+  a.rowms = reinterpret_cast<float2*>(ws + off);
+  off += align256((size_t)N * sizeof(float2));
+  a.rpart = reinterpret_cast<float*>(ws + off);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
+  const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
+  const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
+  if (p_bf16 && d_bf16) return run_label_typed<uint16_t, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);
+  if (p_bf16) return run_label_typed<uint16_t, float>(a, c_out, greedy, vec_p, vec_d, stream);
+  if (d_bf16) return run_label_typed<float, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);
+  return run_label_typed<float, float>(a, c_out, greedy, vec_p, vec_d, stream);
 }
 
 }  // namespace dspark

@@ -207,6 +207,38 @@ int dspark_verify(int R, int K, int V, float temperature,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Analytic acceptance probability per draft position, the confidence head's
+ * training label.  DSpark paper section 3.2.1 (Confidence Head: the label is
+ * the per-step acceptance rate set by the total variation distance between
+ * draft and target distributions); "Speculative decoding, from zero to
+ * DSpark", section 2 (the acceptance probability of one position) and
+ * Appendix A4.
+ *
+ *   c_out[r, k] = 1 - 1/2 || q_{r,k} - p_{r,k} ||_1 = sum_v min(q, p)
+ *   q_{r,k} = softmax((D[r, k] + W1[x_{r,k-1}] W2) / T),  x_{r,0} = x0[r]
+ *   p_{r,k} = softmax(P[r, k] / T)
+ * T == 0: c_out = 1 where the first argmax of P[r, k] is x[r, k], else 0.
+ *
+ * Inputs: P [B, K, V] (p_dtype) target logits, row (r, k) judging draft
+ * position k + 1; D [B, K, V] (d_dtype) draft base logits; W1/W2/r/x0 as for
+ * the draft; x [B, K] the drafted tokens and lse_d [B, K] their
+ * log-normalisers, as returned by dspark_markov_draft (lse_d unused when
+ * T == 0).  Output: c_out [B, K] f32.
+ * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, P and D each smaller than 4 GiB.
+ * Data errors: a position whose previous or own token is outside [0, V) gets
+ * NaN.  Workspace: dspark_acceptance_label_workspace_bytes(B, K, V, r) bytes,
+ * 256-byte aligned, contents need not be initialised.
+ * ------------------------------------------------------------------------ */
+size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r);
+int dspark_acceptance_label(int B, int K, int V, float temperature,
+                            const void* P, int p_dtype,
+                            const void* D, int d_dtype,
+                            const void* W1, const void* W2, int r,
+                            const int32_t* x0, const int32_t* x,
+                            const float* lse_d, float* c_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * The per-decision uniforms themselves (the seeded counter-based stream the
  * three calls consume): out[i] = u(seed, step, request i, position, purpose)
  * for i in [0, n).  Limits: n >= 1, 0 <= position < 2^30, purpose in {0, 1, 2}.

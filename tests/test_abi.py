@@ -50,6 +50,8 @@ def test_workspace_queries(lib):
     assert lib.dspark_schedule_workspace_bytes(512, 7) >= 512 * 7 * 8
     assert lib.dspark_schedule_workspace_bytes(512, 7) % 256 == 0
     assert lib.dspark_schedule_workspace_bytes(4096, 7) == 0
+    assert lib.dspark_acceptance_label_workspace_bytes(512, 7, 151936, 256) >= 512 * 7 * 2374 * 4
+    assert lib.dspark_acceptance_label_workspace_bytes(0, 7, 10, 0) == 0
 
 
 NULL = ctypes.c_void_p(0)
@@ -84,6 +86,24 @@ def test_schedule_async_argument_errors(lib):
     assert call(c=NULL) == -1
     assert call(ws=NULL) == -5
     assert call(wsb=ctypes.c_size_t(lib.dspark_schedule_workspace_bytes(4, 7) - 1)) == -5
+
+
+def test_acceptance_label_argument_errors(lib):
+    f = ctypes.c_float
+
+    def call(B=4, K=7, V=1024, r=16, T=1.0, P=FAKE, pt=0, D=FAKE, dt=0, W=FAKE, x0=FAKE, x=FAKE, lse=FAKE,
+             out=FAKE, wsp=FAKE, wsb=WS):
+        return lib.dspark_acceptance_label(B, K, V, f(T), P, pt, D, dt, W, W, r, x0, x, lse, out, wsp, wsb, NULL)
+    assert call(B=0) == -2
+    assert call(K=17) == -2
+    assert call(r=12) == -2
+    assert call(pt=7) == -3
+    assert call(T=-1.0) == -4
+    assert call(P=NULL) == -1
+    assert call(lse=NULL) == -1
+    assert call(T=0.0, lse=NULL, wsp=NULL) == -5     # lse_d not needed when greedy
+    assert call(W=NULL) == -1
+    assert call(wsb=ctypes.c_size_t(lib.dspark_acceptance_label_workspace_bytes(4, 7, 1024, 16) - 1)) == -5
 
 
 def test_draft_argument_errors(lib):

@@ -385,3 +385,75 @@ def test_gpu_emitted_token_follows_target_and_acceptance_is_one_minus_tv():
     assert abs((n_acc == 1).mean() - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / n)
     first = np.where(n_acc >= 1, x, tok)
     assert stats.chisquare(np.bincount(first, minlength=V), p * n).pvalue > 1e-6
+
+# ------------------------------------------------------- acceptance label
+def _label_case(P, U, W1, W2, x0, T, rows=None, seed=7):
+    """GPU label on the oracle's own draft (x, lse) of the checked requests
+    (the other requests get token 0 and are not checked), against the
+    oracle's label of those requests."""
+    f64 = lambda t: None if t is None else t.detach().to("cpu", torch.float64).numpy()
+    B, K, V = U.shape
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    sel = torch.as_tensor(rows)
+    W1n, W2n = f64(W1), (None if W2 is None else f64(W2).T.copy())
+    Us = f64(U[sel.to(U.device)])
+    x0n = x0.cpu().numpy()
+    d = oracle.draft_ref(Us, W1n, W2n, x0n[rows], T, seed, 0, request_ids=rows)
+    x = torch.zeros((B, K), dtype=torch.int32)
+    lse = torch.zeros((B, K), dtype=torch.float32)
+    x[sel] = torch.as_tensor(d["x"], dtype=torch.int32)
+    lse[sel] = torch.as_tensor(d["lse"], dtype=torch.float32)
+    got = ds().dspark_acceptance_label(P.to(DEV), U.to(DEV), None if W1 is None else W1.to(DEV),
+                                       None if W2 is None else W2.to(DEV), x0.to(DEV), x.to(DEV), lse.to(DEV), T)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()[rows]
+    ref = oracle.acceptance_label_ref(f64(P[sel.to(P.device)]), Us, W1n, W2n, x0n[rows], d["x"], T)
+    return got, ref
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_label_tiny(T):
+    w = wl().make("tiny", device="cpu")
+    P = w.t[:, :w.K].contiguous()
+    got, ref = _label_case(P, w.U, w.W1, w.W2, w.x0, T)
+    _say("label tiny T=%g max |diff| %.2e" % (T, np.abs(got - ref).max()))
+    if T == 0:
+        np.testing.assert_array_equal(got, ref)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_label_qwen_vocab(T):
+    w = wl().make("qwen_verify", device="cpu")
+    P = w.t[:, :w.K].contiguous()
+    got, ref = _label_case(P, w.U, None, None, w.x0, T, rows=np.arange(0, w.B, 4))
+    _say("label qwen T=%g max |diff| %.2e" % (T, np.abs(got - ref).max()))
+    if T == 0:
+        np.testing.assert_array_equal(got, ref)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
+
+
+def test_label_ragged_unaligned():
+    """V not a multiple of the vector width: the generic residual path."""
+    g = torch.Generator().manual_seed(404)
+    B, K, V, r = 3, 4, 999, 8
+    P = torch.randn((B, K, V), generator=g) * 2
+    U = P + torch.randn((B, K, V), generator=g)
+    W1 = (torch.randn((V, r), generator=g) * 0.1).to(torch.bfloat16)
+    W2 = (torch.randn((V, r), generator=g) * 0.1).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, dtype=torch.int32)
+    got, ref = _label_case(P, U, W1, W2, x0, 1.0)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
+
+
+def test_label_full_step_sampled():
+    """Full-size workload (B=512, K=7, V=151936, r=256, bf16), the launch the
+    bench times; the oracle checks 6 requests."""
+    w = wl().make("full_step", device=DEV)
+    P = w.t[:, :w.K].contiguous()
+    rows = np.array([0, 101, 255, 256, 400, 511])
+    got, ref = _label_case(P, w.U, w.W1, w.W2, w.x0, w.temperature, rows=rows)
+    _say("label full_step max |diff| %.2e" % np.abs(got - ref).max())
+    np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
