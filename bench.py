@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=512, help="requests in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle steps in the timed sample")
+    ap.add_argument("--no-next-rows", action="store_true", help="skip timing the rows beyond the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -164,6 +165,8 @@ def main():
                                    "GB/s": round(vb / (vus * 1e-6) / 1e9, 1),
                                    "frac": round(vb / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, args)
+
     value = verified * args.steps / (total_ms * 1e-3)
     out = {"metric": METRIC, "value": round(value, 1), "unit": "verified draft tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -174,10 +177,51 @@ def main():
                       "verified_drafts_per_step": verified, "accepted_drafts_last_step": accepted,
                       "emitted_tokens_last_step": accepted + B},
            "roofline": roof, "kernels_us": {k: round(v["mean_us"], 2) for k, v in kernels.items()}}
+    if next_rows:
+        out["next_rows"] = next_rows
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args, verified, B)
     print(json.dumps(out), flush=True)
+
+
+def measure_next_rows(ds, w, x, lse, sch, ws_s, args):
+    """The rows built beyond the step, timed on the same workload with HIP
+    events (library stream = torch's current stream), outside the step:
+    the acceptance label of every drafted position and the asynchronous
+    capacity schedule."""
+    import torch
+    B, K, V, r = w.B, w.K, w.V, w.r
+    Pk = w.t[:, :K].contiguous()           # target rows judging positions 1..K
+    c_lab = torch.empty((B, K), dtype=torch.float32, device=Pk.device)
+    ws_l = torch.empty(max(256, ds.dspark_acceptance_label_workspace_bytes(B, K, V, r)), dtype=torch.uint8,
+                       device=Pk.device)
+
+    def timed(fn, n=5):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / n
+
+    us_label = timed(lambda: ds.dspark_acceptance_label(Pk, w.U, w.W1, w.W2, w.x0, x, lse, w.temperature,
+                                                        out=c_lab, workspace=ws_l))
+    # algorithmic bytes: every target and draft row once, plus W2 once
+    lab_bytes = 2 * B * K * V * Pk.element_size() + (V * r * 2 if r else 0)
+    old = ds.dspark_schedule(w.c, w.sps, 1, 0, workspace=ws_s)    # capacity from the no-break search
+    async_out = {k: torch.empty_like(v) for k, v in sch.items()}
+    us_async = timed(lambda: ds.dspark_schedule_async(w.c, w.sps, old["n_admitted"], out=async_out,
+                                                      workspace=ws_s))
+    return {"acceptance_label": {"us": round(us_label, 1), "algorithmic_bytes": lab_bytes,
+                                 "GB/s": round(lab_bytes / (us_label * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round(lab_bytes / (us_label * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "mean_label": round(float(c_lab.mean()), 4)},
+            "schedule_async": {"us": round(us_async, 1), "capacity": int(old["n_admitted"].item())}}
 
 
 def cpu_baseline(w, args, verified, B):
