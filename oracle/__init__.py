@@ -44,6 +44,7 @@ from .schedule import (schedule_ref, schedule_async_ref, schedule_bruteforce, SC
                        SCHED_GLOBAL, SCHED_TOPK)
 from .verify import verify_ref
 from .label import acceptance_label_ref
+from .confidence import confidence_head_ref, confidence_logits_ref, ece_ref, sts_fit_ref
 from .step import run_step
 
 __all__ = [
@@ -52,4 +53,5 @@ __all__ = [
     "schedule_ref", "schedule_async_ref", "schedule_bruteforce", "SCHED_EARLY_STOP", "SCHED_GLOBAL",
     "SCHED_TOPK",
     "verify_ref", "run_step", "acceptance_label_ref",
+    "confidence_head_ref", "confidence_logits_ref", "ece_ref", "sts_fit_ref",
 ]
