@@ -66,6 +66,13 @@ def load_library():
     lib.dspark_acceptance_label.restype = c_int
     lib.dspark_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int, vp, vp,
                                             vp, vp, vp, c_size, vp]
+    lib.dspark_confidence_head.restype = c_int
+    lib.dspark_confidence_head.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, c_int, vp, vp, c_float, vp, vp, vp,
+                                           vp, vp, vp, vp]
+    lib.dspark_sts_fit_workspace_bytes.restype = c_size
+    lib.dspark_sts_fit_workspace_bytes.argtypes = [c_int] * 3
+    lib.dspark_sts_fit.restype = c_int
+    lib.dspark_sts_fit.argtypes = [c_int, c_int, vp, vp, c_int, vp, c_int, vp, vp, vp, c_size, vp]
     lib.dspark_uniforms.restype = c_int
     lib.dspark_uniforms.argtypes = [c_u64, c_u64, c_int, c_int, c_int, vp, vp]
     lib.dspark_profiler_enable.restype = c_int
@@ -301,6 +308,58 @@ def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, w
     if st != 0:
         raise DSparkError("dspark_acceptance_label", st)
     return out
+
+
+def dspark_confidence_head(H, w_h, w_e, bias, W1, x0, x, V, sts_temperature=None, out=None, logits_out=False):
+    """Confidence head c[r, k] = sigmoid((w_h . H[r, k] + w_e . W1[x_{k-1}] + bias) / T_k).
+
+    H [B, K, d] f32/bf16; w_h [d] f32; w_e [r] f32 and W1 [V, r] bf16 (or
+    None); x0 [B], x [B, K] int32; sts_temperature [K] f32 or None.
+    Returns c [B, K] f32, and the logits [B, K] when logits_out is set.
+    """
+    lib = load_library()
+    B, K, d = H.shape
+    _check(H, "H")
+    _check(w_h, "w_h", torch.float32, (d,))
+    r = 0
+    if W1 is not None:
+        r = W1.shape[1]
+        _check(W1, "W1", torch.bfloat16, (V, r))
+        _check(w_e, "w_e", torch.float32, (r,))
+    _check(x0, "x0", torch.int32, (B,))
+    _check(x, "x", torch.int32, (B, K))
+    if sts_temperature is not None:
+        _check(sts_temperature, "sts_temperature", torch.float32, (K,))
+    c = torch.empty((B, K), dtype=torch.float32, device=H.device) if out is None else out
+    z = torch.empty((B, K), dtype=torch.float32, device=H.device) if logits_out else None
+    st = lib.dspark_confidence_head(B, K, int(V), d, r, _ptr(H), _dtype_code(H), _ptr(w_h), _ptr(w_e),
+                                    float(bias), _ptr(W1), _ptr(x0), _ptr(x), _ptr(sts_temperature), _ptr(c),
+                                    _ptr(z), _stream())
+    if st != 0:
+        raise DSparkError("dspark_confidence_head", st)
+    return (c, z) if logits_out else c
+
+
+def dspark_sts_fit(logits, survived, grid, n_bins=10, workspace=None):
+    """Sequential Temperature Scaling on held-out logits [N, K] f32 and
+    prefix-survival labels [N, K] uint8 over the candidate temperatures
+    grid [G] f32.  Returns (T [K] f32, ece [K] f32) on the GPU."""
+    lib = load_library()
+    N, K = logits.shape
+    _check(logits, "logits", torch.float32)
+    _check(survived, "survived", torch.uint8, (N, K))
+    _check(grid, "grid", torch.float32)
+    G = grid.numel()
+    T = torch.empty(K, dtype=torch.float32, device=logits.device)
+    ece = torch.empty(K, dtype=torch.float32, device=logits.device)
+    need = lib.dspark_sts_fit_workspace_bytes(N, K, G)
+    if workspace is None:
+        workspace = _workspace(need, logits.device)
+    st = lib.dspark_sts_fit(N, K, _ptr(logits), _ptr(survived), G, _ptr(grid), int(n_bins), _ptr(T), _ptr(ece),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_sts_fit", st)
+    return T, ece
 
 
 def dspark_uniforms(seed, step, n, position, purpose, out=None):

@@ -20,6 +20,12 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
                  double* theta_out, void* workspace, hipStream_t stream);
 size_t verify_workspace_bytes(int R, int V, int N);
 size_t label_workspace_bytes(int B, int K, int V);
+int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h_bf16, const float* w_h,
+                        const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
+                        const float* T, float* c_out, float* logit_out, hipStream_t stream);
+size_t sts_workspace_bytes(int G);
+int run_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int G, const float* grid, int nbins,
+                float* T_out, float* ece_out, void* workspace, hipStream_t stream);
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
               const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
               float* c_out, void* workspace, hipStream_t stream);
@@ -227,6 +233,37 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
   return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
                                       W1, W2, r, x0, x, lse_d, c_out, workspace,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_confidence_head(int B, int K, int V, int d, int r, const void* H, int h_dtype, const float* w_h,
+                           const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
+                           const float* sts_temperature, float* c_out, float* logit_out, void* stream) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || d <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (!is_dtype(h_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * d * dtype_bytes(h_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!H || !w_h || !x0 || !x || !c_out) return DSPARK_E_NULL;
+  if (r > 0 && (!W1 || !w_e)) return DSPARK_E_NULL;
+  if (!std::isfinite(bias)) return DSPARK_E_RANGE;
+  return hip_status(dspark::run_confidence_head(B, K, d, r, V, H, h_dtype == DSPARK_BF16, w_h, w_e, bias, W1, x0,
+                                                x, sts_temperature, c_out, logit_out,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_sts_fit_workspace_bytes(int N, int K, int n_grid) {
+  if (N <= 0 || K <= 0 || n_grid <= 0) return 0;
+  return dspark::sts_workspace_bytes(n_grid);
+}
+
+int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int n_grid, const float* grid,
+                   int n_bins, float* T_out, float* ece_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (N <= 0 || K <= 0 || K > DSPARK_MAX_K || n_grid <= 0) return DSPARK_E_SHAPE;
+  if ((uint64_t)N * K * sizeof(float) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (n_bins < 1 || n_bins > DSPARK_STS_MAX_BINS) return DSPARK_E_RANGE;
+  if (!logits || !survived || !grid || !T_out) return DSPARK_E_NULL;
+  if (!workspace || workspace_bytes < dspark::sts_workspace_bytes(n_grid)) return DSPARK_E_WORKSPACE;
+  return hip_status(dspark::run_sts_fit(N, K, logits, survived, n_grid, grid, n_bins, T_out, ece_out, workspace,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, void* stream) {

@@ -77,6 +77,7 @@ enum dspark_sched_mode {
 #define DSPARK_MAX_K 16              /* draft positions per request */
 #define DSPARK_MAX_RANK 256          /* Markov rank r */
 #define DSPARK_MAX_CANDIDATES 16384  /* R * K for dspark_schedule */
+#define DSPARK_STS_MAX_BINS 32        /* ECE bins for dspark_sts_fit */
 
 /* Human-readable text for a status code (static storage). */
 const char* dspark_status_string(int status);
@@ -237,6 +238,55 @@ int dspark_acceptance_label(int B, int K, int V, float temperature,
                             const int32_t* x0, const int32_t* x,
                             const float* lse_d, float* c_out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Confidence head.  DSpark paper section 3.2.1 (Confidence Head: a linear
+ * projection of the backbone hidden state and the Markov embedding of the
+ * previous token, then a sigmoid; Post-hoc Calibration: one temperature per
+ * position); "Speculative decoding, from zero to DSpark", section 8 (The
+ * confidence head).
+ *
+ *   z[r, k] = w_h . H[r, k] + w_e . W1[x_{r,k-1}] + bias,  x_{r,0} = x0[r]
+ *   c_out[r, k] = sigmoid(z[r, k] / T_k)
+ * Inputs: H [B, K, d] (h_dtype) hidden states; w_h [d] f32; w_e [r] f32 and
+ * W1 [V, r] bf16 (unused when r == 0); x0 [B], x [B, K] int32 (the drafted
+ * tokens; x[r, K-1] is not used); sts_temperature [K] f32 from dspark_sts_fit,
+ * or NULL for T_k = 1.  Outputs: c_out [B, K] f32, the scheduler's c;
+ * logit_out [B, K] f32 (z, for calibration data) or NULL.
+ * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, d >= 1, H smaller than 4 GiB.
+ * Data errors: a previous token outside [0, V) gives NaN.  No workspace.
+ * ------------------------------------------------------------------------ */
+int dspark_confidence_head(int B, int K, int V, int d, int r,
+                           const void* H, int h_dtype,
+                           const float* w_h, const float* w_e, float bias,
+                           const void* W1, const int32_t* x0, const int32_t* x,
+                           const float* sts_temperature,
+                           float* c_out, float* logit_out, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Sequential Temperature Scaling.  DSpark paper section 3.2.1 (Post-hoc
+ * Calibration); "Speculative decoding, from zero to DSpark", Appendix A5.
+ *
+ * On held-out data, left to right over k = 1..K: T_out[k] is the first value
+ * of grid minimising the expected calibration error of the cumulative
+ * product prod_{i<=k} sigmoid(logits[n, i] / T_i) against survived[n, k]
+ * (1 where positions 1..k were all accepted), T_1..T_{k-1} already fixed.
+ * ECE: n_bins equal-width bins on [0, 1] (last one closed), sum over bins of
+ * |labels - predictions| / N; products and sums in fp64, reduced in a fixed
+ * order (deterministic).
+ * Inputs (device): logits [N, K] f32 (logit_out of dspark_confidence_head on
+ * held-out requests), survived [N, K] uint8, grid [n_grid] f32 (> 0).
+ * Outputs (device): T_out [K] f32; ece_out [K] f32 (the ECE at the chosen
+ * temperature) or NULL.
+ * Limits: N >= 1, 1 <= K <= DSPARK_MAX_K, n_grid >= 1,
+ * 1 <= n_bins <= DSPARK_STS_MAX_BINS.  Workspace:
+ * dspark_sts_fit_workspace_bytes(N, K, n_grid) bytes.
+ * ------------------------------------------------------------------------ */
+size_t dspark_sts_fit_workspace_bytes(int N, int K, int n_grid);
+int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived,
+                   int n_grid, const float* grid, int n_bins,
+                   float* T_out, float* ece_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * The per-decision uniforms themselves (the seeded counter-based stream the

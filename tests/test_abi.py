@@ -106,6 +106,30 @@ def test_acceptance_label_argument_errors(lib):
     assert call(wsb=ctypes.c_size_t(lib.dspark_acceptance_label_workspace_bytes(4, 7, 1024, 16) - 1)) == -5
 
 
+def test_confidence_and_sts_argument_errors(lib):
+    f = ctypes.c_float
+
+    def head(B=4, K=7, V=100, d=32, r=8, H=FAKE, ht=0, wh=FAKE, we=FAKE, b=0.0, W1=FAKE, x0=FAKE, x=FAKE, out=FAKE):
+        return lib.dspark_confidence_head(B, K, V, d, r, H, ht, wh, we, f(b), W1, x0, x, NULL, out, NULL, NULL)
+    assert head(B=0) == -2
+    assert head(d=0) == -2
+    assert head(r=12) == -2
+    assert head(ht=5) == -3
+    assert head(H=NULL) == -1
+    assert head(W1=NULL) == -1
+    assert head(b=float("inf")) == -4
+
+    def sts(N=100, K=7, lg=FAKE, sv=FAKE, G=9, grid=FAKE, nb=10, T=FAKE, ws=FAKE, wsb=WS):
+        return lib.dspark_sts_fit(N, K, lg, sv, G, grid, nb, T, NULL, ws, wsb, NULL)
+    assert sts(N=0) == -2
+    assert sts(G=0) == -2
+    assert sts(nb=0) == -4
+    assert sts(nb=33) == -4
+    assert sts(lg=NULL) == -1
+    assert sts(ws=NULL) == -5
+    assert lib.dspark_sts_fit_workspace_bytes(100, 7, 9) >= 9 * 8
+
+
 def test_draft_argument_errors(lib):
     f = ctypes.c_float
     ws = ctypes.c_size_t(1 << 30)

@@ -457,3 +457,65 @@ def test_label_full_step_sampled():
     got, ref = _label_case(P, w.U, w.W1, w.W2, w.x0, w.temperature, rows=rows)
     _say("label full_step max |diff| %.2e" % np.abs(got - ref).max())
     np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
+
+
+# ------------------------------------------- confidence head and STS
+@pytest.mark.parametrize("h_dtype", [torch.float32, torch.bfloat16])
+def test_confidence_head(h_dtype):
+    """Against the oracle on a drafted block: the head reads the hidden state
+    and the previous drafted token's Markov embedding (the anchor at k = 1)."""
+    w = wl().make("tiny", device="cpu")
+    g = torch.Generator().manual_seed(321)
+    B, K, V, r, d = w.B, w.K, w.V, w.r, 160
+    H = (torch.randn((B, K, d), generator=g)).to(h_dtype)
+    w_h = torch.randn(d, generator=g) * 0.1
+    w_e = torch.randn(r, generator=g) * 2.0
+    x = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    T = torch.tensor([0.5, 0.8, 1.0, 1.3, 2.0, 3.0, 0.7])[:K]
+    c, z = ds().dspark_confidence_head(H.to(DEV), w_h.to(DEV), w_e.to(DEV), 0.25, w.W1.to(DEV), w.x0.to(DEV),
+                                       x.to(DEV), V, sts_temperature=T.to(DEV), logits_out=True)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.to(torch.float64).numpy()
+    zr = oracle.confidence_logits_ref(f64(H), f64(w_h), f64(w_e), 0.25, f64(w.W1), w.x0.numpy(), x.numpy())
+    cr = oracle.confidence_head_ref(f64(H), f64(w_h), f64(w_e), 0.25, f64(w.W1), w.x0.numpy(), x.numpy(),
+                                    T.numpy())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(c.cpu().numpy(), cr, rtol=0, atol=2e-6)
+
+
+def test_confidence_head_bad_previous_token():
+    B, K, V, d = 2, 3, 10, 8
+    x = torch.tensor([[1, 2, 3], [4, 99, 5]], dtype=torch.int32)
+    c = ds().dspark_confidence_head(torch.ones((B, K, d), device=DEV), torch.ones(d, device=DEV),
+                                    torch.ones(8, device=DEV), 0.0,
+                                    torch.zeros((V, 8), dtype=torch.bfloat16, device=DEV),
+                                    torch.tensor([0, 1], dtype=torch.int32, device=DEV), x.to(DEV), V)
+    c = c.cpu().numpy()
+    assert np.isnan(c[1, 2]) and np.all(np.isfinite(np.delete(c.ravel(), 5)))
+
+
+def _sts_data(seed, N, K, T_true):
+    rng = np.random.default_rng(seed)
+    logits = rng.normal(1.5, 2.0, size=(N, K)).astype(np.float32)
+    p = 1.0 / (1.0 + np.exp(-logits.astype(np.float64) / T_true))
+    alive = np.ones(N, dtype=bool)
+    surv = np.zeros((N, K), dtype=np.uint8)
+    for k in range(K):
+        alive &= rng.uniform(size=N) < p[:, k]
+        surv[:, k] = alive
+    return logits, surv
+
+
+@pytest.mark.parametrize("n_bins", [10, 15, 32])
+def test_sts_fit_matches_oracle(n_bins):
+    N, K = 20000, 5
+    logits, surv = _sts_data(17 + n_bins, N, K, np.array([2.0, 1.5, 0.8, 1.2, 1.0]))
+    grid = np.exp(np.linspace(np.log(0.25), np.log(4.0), 97)).astype(np.float32)
+    T, ece = ds().dspark_sts_fit(torch.from_numpy(logits).to(DEV), torch.from_numpy(surv).to(DEV),
+                                 torch.from_numpy(grid).to(DEV), n_bins)
+    torch.cuda.synchronize()
+    Tr, er = oracle.sts_fit_ref(logits, surv, grid.astype(np.float64), n_bins)
+    _say("sts n_bins=%d T=%s ece=%s" % (n_bins, np.round(T.cpu().numpy(), 3), np.round(er, 4)))
+    np.testing.assert_array_equal(T.cpu().numpy(), Tr.astype(np.float32))
+    np.testing.assert_allclose(ece.cpu().numpy(), er, rtol=1e-5, atol=1e-7)
+
