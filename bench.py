@@ -217,7 +217,29 @@ def measure_next_rows(ds, w, x, lse, sch, ws_s, args):
     async_out = {k: torch.empty_like(v) for k, v in sch.items()}
     us_async = timed(lambda: ds.dspark_schedule_async(w.c, w.sps, old["n_admitted"], out=async_out,
                                                       workspace=ws_s))
-    return {"acceptance_label": {"us": round(us_label, 1), "algorithmic_bytes": lab_bytes,
+    # confidence head on the drafted block: synthetic hidden states of a
+    # 4096-wide backbone (bf16), head weights ~ N(0, 0.02^2)
+    g = torch.Generator(device=Pk.device)
+    g.manual_seed(2024)
+    d = 4096
+    H = (torch.randn((B, K, d), generator=g, device=Pk.device)).to(torch.bfloat16)
+    w_h = torch.randn(d, generator=g, device=Pk.device) * 0.02
+    w_e = torch.randn(max(r, 1), generator=g, device=Pk.device)[:r] * 0.02
+    T_sts = torch.ones(K, device=Pk.device)
+    c_head = torch.empty((B, K), dtype=torch.float32, device=Pk.device)
+    us_head = timed(lambda: ds.dspark_confidence_head(H, w_h, w_e if r else None, 0.5, w.W1 if r else None, w.x0, x,
+                                                      V, sts_temperature=T_sts, out=c_head))
+    head_bytes = B * K * d * 2 + B * K * r * 2
+    # STS over a held-out set of 100000 blocks, 121 temperatures, 15 bins
+    Nh = 100000
+    logits = torch.randn((Nh, K), generator=g, device=Pk.device) * 2.0 + 1.5
+    surv = (torch.rand((Nh, K), generator=g, device=Pk.device) < 0.8).to(torch.uint8).cumprod(dim=1).to(torch.uint8)
+    grid = torch.exp(torch.linspace(-1.386, 1.386, 121, device=Pk.device))
+    us_sts = timed(lambda: ds.dspark_sts_fit(logits, surv, grid, 15), n=2)
+    return {"confidence_head": {"us": round(us_head, 1), "d": d, "bytes": head_bytes,
+                                "GB/s": round(head_bytes / (us_head * 1e-6) / 1e9, 1)},
+            "sts_fit": {"us": round(us_sts, 1), "held_out": Nh, "grid": 121, "bins": 15},
+            "acceptance_label": {"us": round(us_label, 1), "algorithmic_bytes": lab_bytes,
                                  "GB/s": round(lab_bytes / (us_label * 1e-6) / 1e9, 1),
                                  "frac_hbm": round(lab_bytes / (us_label * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                  "mean_label": round(float(c_lab.mean()), 4)},

@@ -37,7 +37,7 @@ struct HeadArgs {
   float* logit_out;  // or null
 };
 
-template <typename HT>
+template <typename HT, bool VEC>
 __global__ __launch_bounds__(256) void confidence_head_kernel(HeadArgs a) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave_index();
@@ -46,11 +46,33 @@ __global__ __launch_bounds__(256) void confidence_head_kernel(HeadArgs a) {
   const int prev = k == 0 ? a.x0[r] : a.x[i - 1];
   const HT* h = reinterpret_cast<const HT*>(a.H) + (size_t)i * a.d;
   float s = 0.f;
-  for (int j = lane; j < a.d; j += 64) {
-    float hv;
-    if constexpr (sizeof(HT) == 2) hv = bf16_bits_to_f32(h[j]);
-    else hv = h[j];
-    s = fmaf(a.w_h[j], hv, s);
+  if constexpr (VEC) {
+    // 16-byte loads: lane takes 4 (f32) or 8 (bf16) consecutive elements per step
+    constexpr int E = 16 / sizeof(HT);
+    for (int j = lane * E; j < a.d; j += 64 * E) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(h + j);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(a.w_h + j);
+      if constexpr (sizeof(HT) == 2) {
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(a.w_h + j + 4);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          s = fmaf(w0[2 * e], __uint_as_float(v[e] << 16), s);
+          s = fmaf(w0[2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), s);
+          s = fmaf(w1[2 * e], __uint_as_float(v[e + 2] << 16), s);
+          s = fmaf(w1[2 * e + 1], __uint_as_float(v[e + 2] & 0xFFFF0000u), s);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(w0[e], __uint_as_float(v[e]), s);
+      }
+    }
+  } else {
+    for (int j = lane; j < a.d; j += 64) {
+      float hv;
+      if constexpr (sizeof(HT) == 2) hv = bf16_bits_to_f32(h[j]);
+      else hv = h[j];
+      s = fmaf(a.w_h[j], hv, s);
+    }
   }
   const bool ok = prev >= 0 && prev < a.V;
   if (a.r > 0 && ok) {
@@ -72,8 +94,14 @@ int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h
                         const float* T, float* c_out, float* logit_out, hipStream_t stream) {
   HeadArgs a{B, K, d, r, V, H, w_h, w_e, bias, reinterpret_cast<const uint16_t*>(W1), x0, x, T, c_out, logit_out};
   const dim3 grid((B * K + 3) / 4);
-  return h_bf16 ? launch_kernel("confidence_head", confidence_head_kernel<uint16_t>, grid, dim3(256), stream, a)
-                : launch_kernel("confidence_head", confidence_head_kernel<float>, grid, dim3(256), stream, a);
+  // vector path: rows and w_h 16-byte aligned
+  const bool vec = d % (h_bf16 ? 8 : 4) == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(w_h) % 16 == 0;
+  if (h_bf16)
+    return vec ? launch_kernel("confidence_head", confidence_head_kernel<uint16_t, true>, grid, dim3(256), stream, a)
+               : launch_kernel("confidence_head", confidence_head_kernel<uint16_t, false>, grid, dim3(256), stream, a);
+  return vec ? launch_kernel("confidence_head", confidence_head_kernel<float, true>, grid, dim3(256), stream, a)
+             : launch_kernel("confidence_head", confidence_head_kernel<float, false>, grid, dim3(256), stream, a);
 }
 
 // ------------------------------------------------------------------- STS --

@@ -460,13 +460,14 @@ def test_label_full_step_sampled():
 
 
 # ------------------------------------------- confidence head and STS
-@pytest.mark.parametrize("h_dtype", [torch.float32, torch.bfloat16])
-def test_confidence_head(h_dtype):
+@pytest.mark.parametrize("h_dtype,d", [(torch.float32, 160), (torch.bfloat16, 160), (torch.bfloat16, 4096),
+                                       (torch.bfloat16, 157)])
+def test_confidence_head(h_dtype, d):
     """Against the oracle on a drafted block: the head reads the hidden state
     and the previous drafted token's Markov embedding (the anchor at k = 1)."""
     w = wl().make("tiny", device="cpu")
     g = torch.Generator().manual_seed(321)
-    B, K, V, r, d = w.B, w.K, w.V, w.r, 160
+    B, K, V, r = w.B, w.K, w.V, w.r
     H = (torch.randn((B, K, d), generator=g)).to(h_dtype)
     w_h = torch.randn(d, generator=g) * 0.1
     w_e = torch.randn(r, generator=g) * 2.0
