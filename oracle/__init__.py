@@ -33,6 +33,7 @@ every categorical draw is an inverse-CDF draw in ascending token-id order.
 Modules:
   philox    -- Philox4x32-10 and the per-decision uniform
   draft     -- sequential Markov-head drafter (draft_ref, independent_draft_ref)
+  rnn       -- sequential RNN-head drafter (rnn_cell_ref, rnn_draft_ref)
   schedule  -- Algorithm 1 and its modes (schedule_ref), brute force
   verify    -- rejection-sampling verification (verify_ref)
   step      -- the composed step (run_step)
@@ -45,6 +46,7 @@ from .schedule import (schedule_ref, schedule_async_ref, schedule_bruteforce, SC
 from .verify import verify_ref
 from .label import acceptance_label_ref
 from .confidence import confidence_head_ref, confidence_logits_ref, ece_ref, sts_fit_ref
+from .rnn import rnn_cell_ref, rnn_draft_ref
 from .step import run_step
 
 __all__ = [
@@ -54,4 +56,5 @@ __all__ = [
     "SCHED_TOPK",
     "verify_ref", "run_step", "acceptance_label_ref",
     "confidence_head_ref", "confidence_logits_ref", "ece_ref", "sts_fit_ref",
+    "rnn_cell_ref", "rnn_draft_ref",
 ]

@@ -29,23 +29,33 @@ def _softmax_rows(z):
     return w / w.sum(axis=1, keepdims=True)
 
 
-def acceptance_label_ref(P, D, W1, W2, x0, x, temperature):
+def acceptance_label_ref(P, D, W1, W2, x0, x, temperature, O=None):
     """P: [R, K, V] target logits (row (r, k) judges draft position k+1);
     D: [R, K, V] draft base logits; W1 [V, r], W2 [r, V] or None; x0 [R];
-    x [R, K] drafted tokens.  Returns c* [R, K] (float64)."""
+    x [R, K] drafted tokens; O [R, K, r] or None (drafts of the RNN head: the
+    bias of position k is O[r, k] @ W2 and W1 is not used).  Returns c* [R, K]
+    (float64)."""
     P = np.asarray(P, dtype=np.float64)
     D = np.asarray(D, dtype=np.float64)
     x = np.asarray(x, dtype=np.int64)
     x0 = np.asarray(x0, dtype=np.int64)
     R, K, V = D.shape
-    have_bias = W1 is not None and W2 is not None and np.asarray(W1).shape[1] > 0
+    if O is not None:
+        O = np.asarray(O, dtype=np.float64)
+        W2 = np.asarray(W2, dtype=np.float64)
+        have_bias = False
+    else:
+        have_bias = W1 is not None and W2 is not None and np.asarray(W1).shape[1] > 0
     if have_bias:
         W1 = np.asarray(W1, dtype=np.float64)
         W2 = np.asarray(W2, dtype=np.float64)
     out = np.empty((R, K))
     for k in range(K):
         prev = x0 if k == 0 else x[:, k - 1]
-        z = D[:, k, :] + (W1[prev] @ W2 if have_bias else 0.0)
+        if O is not None:
+            z = D[:, k, :] + O[:, k, :] @ W2
+        else:
+            z = D[:, k, :] + (W1[prev] @ W2 if have_bias else 0.0)
         t = P[:, k, :]
         if temperature == 0:
             out[:, k] = (np.argmax(t, axis=1) == x[:, k]).astype(np.float64)

@@ -69,14 +69,16 @@ def _top2_gap(z, idx):
     return z[rows, idx] - other.max(axis=1)
 
 
-def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step, request_ids=None):
+def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step, request_ids=None, O=None):
     """Verify every request's scheduled prefix.
 
     P: [N, V] flat target logits (request r owns rows cu[r] .. cu[r+1]-1);
     cu_seqlens: [R+1]; D: [R, K, V] draft base logits; W1 [V, r] / W2 [r, V]
     or None; x0: [R] anchors; x: [R, K] draft tokens; temperature (0 = greedy);
     request_ids: the requests' indices in their batch, which address their
-    uniforms (default 0..R-1).
+    uniforms (default 0..R-1); O: [R, K, r] or None.  With O (drafts of the
+    RNN head) the draft row of position j carries the bias O[r, j-1] @ W2, the
+    head's output part in place of the Markov embedding, and W1 is not used.
 
     Returns dict: n_acc [R], tok [R] (correction or bonus token), mode [R]
     (0 = bonus, 1 = correction), p_x / q_x / ratio [R, K] (NaN where a position
@@ -89,9 +91,14 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step, request
     x = np.asarray(x, dtype=np.int64)
     x0 = np.asarray(x0, dtype=np.int64)
     R, K, V = D.shape
-    have_bias = W1 is not None and W2 is not None and np.asarray(W1).shape[1] > 0
+    if O is not None:
+        O = np.asarray(O, dtype=np.float64)
+        have_bias = True
+    else:
+        have_bias = W1 is not None and W2 is not None and np.asarray(W1).shape[1] > 0
     if have_bias:
-        W1 = np.asarray(W1, dtype=np.float64)
+        if O is None:
+            W1 = np.asarray(W1, dtype=np.float64)
         W2 = np.asarray(W2, dtype=np.float64)
     ell = cu[1:] - cu[:-1] - 1
     if np.any(ell < 0) or np.any(ell > K) or cu[0] != 0 or cu[-1] != P.shape[0]:
@@ -129,7 +136,9 @@ def verify_ref(P, cu_seqlens, D, W1, W2, x0, x, temperature, seed, step, request
             continue
         p = _softmax(t_rows / temperature)
         base = D[rs, j - 1, :].copy()
-        if have_bias:
+        if O is not None:
+            base += O[rs, j - 1, :] @ W2
+        elif have_bias:
             prev = x0[rs] if j == 1 else x[rs, j - 2]
             base += W1[prev, :] @ W2
         q = _softmax(base / temperature)
