@@ -165,7 +165,7 @@ def main():
                                    "GB/s": round(vb / (vus * 1e-6) / 1e9, 1),
                                    "frac": round(vb / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, args)
+    next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, P, args)
 
     value = verified * args.steps / (total_ms * 1e-3)
     out = {"metric": METRIC, "value": round(value, 1), "unit": "verified draft tokens/s", "n_gpus": 1,
@@ -185,11 +185,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_next_rows(ds, w, x, lse, sch, ws_s, args):
+def measure_next_rows(ds, w, x, lse, sch, ws_s, P, args):
     """The rows built beyond the step, timed on the same workload with HIP
     events (library stream = torch's current stream), outside the step:
-    the acceptance label of every drafted position and the asynchronous
-    capacity schedule."""
+    the acceptance label of every drafted position, the asynchronous
+    capacity schedule, the confidence head and STS, and the RNN head's draft
+    and verification."""
     import torch
     B, K, V, r = w.B, w.K, w.V, w.r
     Pk = w.t[:, :K].contiguous()           # target rows judging positions 1..K
@@ -236,7 +237,8 @@ def measure_next_rows(ds, w, x, lse, sch, ws_s, args):
     surv = (torch.rand((Nh, K), generator=g, device=Pk.device) < 0.8).to(torch.uint8).cumprod(dim=1).to(torch.uint8)
     grid = torch.exp(torch.linspace(-1.386, 1.386, 121, device=Pk.device))
     us_sts = timed(lambda: ds.dspark_sts_fit(logits, surv, grid, 15), n=2)
-    return {"confidence_head": {"us": round(us_head, 1), "d": d, "bytes": head_bytes,
+    rnn = measure_rnn_head(ds, w, P, sch, timed, d) if (r >= 32 and r % 32 == 0) else None
+    out = {"confidence_head": {"us": round(us_head, 1), "d": d, "bytes": head_bytes,
                                 "GB/s": round(head_bytes / (us_head * 1e-6) / 1e9, 1)},
             "sts_fit": {"us": round(us_sts, 1), "held_out": Nh, "grid": 121, "bins": 15},
             "acceptance_label": {"us": round(us_label, 1), "algorithmic_bytes": lab_bytes,
@@ -244,6 +246,57 @@ def measure_next_rows(ds, w, x, lse, sch, ws_s, args):
                                  "frac_hbm": round(lab_bytes / (us_label * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                  "mean_label": round(float(c_lab.mean()), 4)},
             "schedule_async": {"us": round(us_async, 1), "capacity": int(old["n_admitted"].item())}}
+    if rnn:
+        out["rnn_head"] = rnn
+    return out
+
+
+def measure_rnn_head(ds, w, P, sch, timed, d):
+    """The RNN head on the same workload (hidden states of a d-wide backbone):
+    one whole draft of the block per call (W2 to fp16, the hidden-state
+    projection, then per position the gated update, the fused bias + softmax
+    partials pass and the sampling), and verification of its drafts on the
+    step's schedule."""
+    import torch
+    from draft_verify_schedule_amd import workloads
+    B, K, V, r = w.B, w.K, w.V, w.r
+    dev = w.U.device
+    H, Wr = workloads.rnn_head(B, K, r, d, 1005, device=dev)
+    out = (torch.empty((B, K), dtype=torch.int32, device=dev), torch.empty((B, K), dtype=torch.float32, device=dev),
+           torch.empty((B, K), dtype=torch.float32, device=dev),
+           torch.empty((B, K, r), dtype=torch.float32, device=dev))
+    ws = torch.empty(ds.dspark_rnn_draft_workspace_bytes(B, K, V, r, d), dtype=torch.uint8, device=dev)
+    draft = lambda: ds.dspark_rnn_draft(w.U, H, Wr, w.W1, w.W2, w.x0, w.temperature, w.rng_seed, 0, out=out,
+                                        workspace=ws)
+    us_draft = timed(draft)
+    ds.dspark_profiler_reset()
+    ds.dspark_profiler_enable(True)
+    for _ in range(3):
+        draft()
+    torch.cuda.synchronize()
+    ds.dspark_profiler_enable(False)
+    kern = {k: {"launches": n // 3, "mean_us": round(1000.0 * ms / n, 2)} for k, (n, ms) in
+            ds.dspark_profiler_read().items() if n}
+    x, q, lse, O = out
+    N = P.shape[0]
+    ws_v = torch.empty(ds.dspark_rnn_verify_workspace_bytes(B, K, V, r, N), dtype=torch.uint8, device=dev)
+    vout = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    us_verify = timed(lambda: ds.dspark_rnn_verify(P, sch["cu_seqlens"], w.U, O, w.W2, w.x0, x, q, lse,
+                                                   w.temperature, w.rng_seed, 0, out=vout, workspace=ws_v))
+    # the fused pass of one position: U_k, the fp16 W2 and the output parts;
+    # its MFMA work is the bias with o split in two (2 x 2 B r V flops)
+    part_bytes = B * V * w.U.element_size() + V * r * 2 + B * r * 4
+    part_us = kern.get("draft_partials", {}).get("mean_us")
+    res = {"d": d, "draft_us": round(us_draft, 1), "drafted_tokens_per_s": round(B * K / (us_draft * 1e-6), 1),
+           "verify_us": round(us_verify, 1), "verify_rows": N, "kernels": kern}
+    if part_us:
+        res["draft_partials"] = {"algorithmic_bytes": part_bytes, "GB/s": round(part_bytes / (part_us * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round(part_bytes / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "mfma_TFLOP/s": round(4.0 * B * r * V / (part_us * 1e-6) / 1e12, 1)}
+    hp = kern.get("rnn_hproj", {}).get("mean_us")
+    if hp:
+        res["rnn_hproj_TFLOP/s"] = round(2.0 * B * K * d * 3 * r / (hp * 1e-6) / 1e12, 1)
+    return res
 
 
 def cpu_baseline(w, args, verified, B):

@@ -13,7 +13,9 @@ _BINDING_NAMES = {
     "dspark_markov_draft", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
     "dspark_markov_draft_workspace_bytes", "dspark_schedule_workspace_bytes", "dspark_verify_workspace_bytes",
     "dspark_acceptance_label", "dspark_acceptance_label_workspace_bytes",
-    "dspark_confidence_head", "dspark_sts_fit",
+    "dspark_confidence_head", "dspark_sts_fit", "dspark_sts_fit_workspace_bytes",
+    "dspark_rnn_draft", "dspark_rnn_draft_workspace_bytes", "dspark_rnn_verify", "dspark_rnn_acceptance_label",
+    "dspark_rnn_verify_workspace_bytes", "dspark_rnn_acceptance_label_workspace_bytes",
     "dspark_status_string", "dspark_version", "dspark_uniforms",
     "dspark_profiler_enable", "dspark_profiler_reset", "dspark_profiler_read",
     "DSparkError", "load_library", "library_path",

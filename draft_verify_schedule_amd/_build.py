@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libdspark.so"
-SOURCES = ["draft.hip", "schedule.hip", "verify.hip", "confidence.hip", "rng.hip", "api.cpp"]
+SOURCES = ["draft.hip", "schedule.hip", "verify.hip", "confidence.hip", "rnn.hip", "rng.hip", "api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 arithmetic.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=fast",

@@ -66,6 +66,21 @@ def load_library():
     lib.dspark_acceptance_label.restype = c_int
     lib.dspark_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int, vp, vp,
                                             vp, vp, vp, c_size, vp]
+    lib.dspark_rnn_draft_workspace_bytes.restype = c_size
+    lib.dspark_rnn_draft_workspace_bytes.argtypes = [c_int] * 5
+    lib.dspark_rnn_draft.restype = c_int
+    lib.dspark_rnn_draft.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, vp,
+                                     vp, c_u64, c_u64, vp, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_rnn_verify_workspace_bytes.restype = c_size
+    lib.dspark_rnn_verify_workspace_bytes.argtypes = [c_int] * 5
+    lib.dspark_rnn_acceptance_label_workspace_bytes.restype = c_size
+    lib.dspark_rnn_acceptance_label_workspace_bytes.argtypes = [c_int] * 4
+    lib.dspark_rnn_verify.restype = c_int
+    lib.dspark_rnn_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp,
+                                      c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, c_size, vp]
+    lib.dspark_rnn_acceptance_label.restype = c_int
+    lib.dspark_rnn_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int,
+                                                vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_confidence_head.restype = c_int
     lib.dspark_confidence_head.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, c_int, vp, vp, c_float, vp, vp, vp,
                                            vp, vp, vp, vp]
@@ -310,6 +325,121 @@ def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, w
     return out
 
 
+def dspark_rnn_draft_workspace_bytes(B, K, V, r, d):
+    return load_library().dspark_rnn_draft_workspace_bytes(B, K, V, r, d)
+
+
+def dspark_rnn_draft(U, H, W, W1, W2, x0, temperature, seed, step, out=None, workspace=None):
+    """Sequential RNN-head draft.
+
+    U [B, K, V] f32/bf16 base logits; H [B, K, d] bf16 hidden states; W
+    [3r, 2r + d] bf16 (gate, candidate, output rows); W1 [V, r] bf16; W2 the
+    r x V factor column-major ([V, r] bf16); x0 [B] int32.
+    Returns (x [B, K] int32, q_tok [B, K] f32, lse [B, K] f32, O [B, K, r] f32).
+    """
+    lib = load_library()
+    B, K, V = U.shape
+    _check(U, "U")
+    r = W1.shape[1]
+    d = H.shape[2]
+    _check(H, "H", torch.bfloat16, (B, K, d))
+    _check(W, "W", torch.bfloat16, (3 * r, 2 * r + d))
+    _check(W1, "W1", torch.bfloat16, (V, r))
+    _check(W2, "W2", torch.bfloat16, (V, r))
+    _check(x0, "x0", torch.int32, (B,))
+    dev = U.device
+    if out is None:
+        out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K, r), dtype=torch.float32, device=dev))
+    x, q, lse, O = out
+    need = lib.dspark_rnn_draft_workspace_bytes(B, K, V, r, d)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_rnn_draft(B, K, V, r, d, float(temperature), _ptr(U), _dtype_code(U), _ptr(H), DSPARK_BF16,
+                              _ptr(W), _ptr(W1), _ptr(W2), _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q),
+                              _ptr(lse), _ptr(O), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream())
+    if st != 0:
+        raise DSparkError("dspark_rnn_draft", st)
+    return x, q, lse, O
+
+
+def dspark_rnn_verify_workspace_bytes(R, K, V, r, N):
+    return load_library().dspark_rnn_verify_workspace_bytes(R, K, V, r, N)
+
+
+def dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r):
+    return load_library().dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r)
+
+
+def dspark_rnn_verify(P, cu_seqlens, D, O, W2, x0, x, q_tok, lse_d, temperature, seed, step, out=None,
+                      workspace=None):
+    """Verification of RNN-head drafts: as dspark_verify, with the draft rows'
+    bias rebuilt from the output parts O [R, K, r] f32 returned by
+    dspark_rnn_draft.  Returns (n_acc [R] int32, tok [R] int32)."""
+    lib = load_library()
+    N, V = P.shape
+    R, K, V2 = D.shape
+    if V2 != V:
+        raise ValueError("P and D disagree on V")
+    r = O.shape[2]
+    _check(P, "P")
+    _check(D, "D")
+    _check(O, "O", torch.float32, (R, K, r))
+    _check(W2, "W2", torch.bfloat16, (V, r))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (R + 1,))
+    _check(x0, "x0", torch.int32, (R,))
+    _check(x, "x", torch.int32, (R, K))
+    if q_tok is not None:
+        _check(q_tok, "q_tok", torch.float32, (R, K))
+    if lse_d is not None:
+        _check(lse_d, "lse_d", torch.float32, (R, K))
+    dev = P.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev))
+    n_acc, tok = out
+    need = lib.dspark_rnn_verify_workspace_bytes(R, K, V, r, N)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_rnn_verify(R, K, V, float(temperature), _ptr(P), _dtype_code(P), N, _ptr(cu_seqlens), _ptr(D),
+                               _dtype_code(D), _ptr(O), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(q_tok), _ptr(lse_d),
+                               int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_rnn_verify", st)
+    return n_acc, tok
+
+
+def dspark_rnn_acceptance_label(P, D, O, W2, x0, x, lse_d, temperature, out=None, workspace=None):
+    """Acceptance label of RNN-head drafts: as dspark_acceptance_label, with
+    the output parts O [B, K, r] f32 in place of the Markov embeddings."""
+    lib = load_library()
+    B, K, V = D.shape
+    r = O.shape[2]
+    _check(P, "P", shape=(B, K, V))
+    _check(D, "D")
+    _check(O, "O", torch.float32, (B, K, r))
+    _check(W2, "W2", torch.bfloat16, (V, r))
+    _check(x0, "x0", torch.int32, (B,))
+    _check(x, "x", torch.int32, (B, K))
+    _check(lse_d, "lse_d", torch.float32, (B, K))
+    dev = D.device
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.float32, device=dev)
+    need = lib.dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_rnn_acceptance_label(B, K, V, float(temperature), _ptr(P), _dtype_code(P), _ptr(D),
+                                         _dtype_code(D), _ptr(O), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(lse_d),
+                                         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream())
+    if st != 0:
+        raise DSparkError("dspark_rnn_acceptance_label", st)
+    return out
+
+
 def dspark_confidence_head(H, w_h, w_e, bias, W1, x0, x, V, sts_temperature=None, out=None, logits_out=False):
     """Confidence head c[r, k] = sigmoid((w_h . H[r, k] + w_e . W1[x_{k-1}] + bias) / T_k).
 
@@ -338,6 +468,10 @@ def dspark_confidence_head(H, w_h, w_e, bias, W1, x0, x, V, sts_temperature=None
     if st != 0:
         raise DSparkError("dspark_confidence_head", st)
     return (c, z) if logits_out else c
+
+
+def dspark_sts_fit_workspace_bytes(N, K, n_grid):
+    return load_library().dspark_sts_fit_workspace_bytes(N, K, n_grid)
 
 
 def dspark_sts_fit(logits, survived, grid, n_bins=10, workspace=None):

@@ -9,11 +9,13 @@
 #include <string>
 #include <vector>
 
+#include "rnn.hpp"
+
 namespace dspark {
 size_t draft_workspace_bytes(int B, int K, int V);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
               const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
-              float* lse_out, void* workspace, hipStream_t stream);
+              float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
 size_t schedule_workspace_bytes(int R, int K);
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
@@ -28,11 +30,12 @@ int run_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int 
                 float* T_out, float* ece_out, void* workspace, hipStream_t stream);
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
               const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
-              float* c_out, void* workspace, hipStream_t stream);
+              float* c_out, void* workspace, const float* O, const uint16_t* W2h, hipStream_t stream);
 int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N, const int32_t* cu,
                const void* D, bool d_bf16, const void* W1, const void* W2, int r, const int32_t* x0,
                const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed, uint64_t step,
-               int32_t* n_acc_out, int32_t* tok_out, void* workspace, hipStream_t stream);
+               int32_t* n_acc_out, int32_t* tok_out, void* workspace, const float* O, const uint16_t* W2h,
+               hipStream_t stream);
 int run_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, hipStream_t stream);
 
 // ---- kernel timer --------------------------------------------------------
@@ -97,6 +100,9 @@ uint64_t dtype_bytes(int d) { return d == DSPARK_BF16 ? 2 : 4; }
 // Kernels address each logit and factor buffer with 32-bit byte offsets.
 constexpr uint64_t kMaxBufferBytes = (uint64_t)1 << 32;
 bool rank_ok(int r) { return r >= 0 && r <= DSPARK_MAX_RANK && r % 8 == 0; }
+// RNN head: the state is tiled in 32-column chunks and 16-unit MFMA blocks
+bool rnn_rank_ok(int r) { return r >= 32 && r <= DSPARK_MAX_RANK && r % 32 == 0; }
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 int hip_status(int rc) { return rc == 0 ? DSPARK_OK : DSPARK_E_HIP; }
 }  // namespace
 
@@ -140,7 +146,51 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
   if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
     return DSPARK_E_RANGE;
   return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, x0, seed,
-                                      step, x_out, q_tok_out, lse_out, workspace,
+                                      step, x_out, q_tok_out, lse_out, workspace, nullptr,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d) {
+  (void)d;
+  if (B <= 0 || K <= 0 || V <= 0 || r <= 0) return 0;
+  const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  return base + dspark::rnn_workspace_bytes(B, K, V, r);
+}
+
+int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const void* U, int u_dtype,
+                     const void* H, int h_dtype, const void* W, const void* W1, const void* W2, const int32_t* x0,
+                     uint64_t seed, uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, float* o_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (d < 64 || d % 64 != 0) return DSPARK_E_SHAPE;
+  if (!is_dtype(u_dtype) || h_dtype != DSPARK_BF16) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)B * K * d * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)3 * r * (2 * r + d) * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!U || !H || !W || !W1 || !W2 || !x0 || !x_out || !q_tok_out || !lse_out || !o_out) return DSPARK_E_NULL;
+  const size_t need = dspark_rnn_draft_workspace_bytes(B, K, V, r, d);
+  if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(H) || !aligned16(W) || !aligned16(o_out)) return DSPARK_E_RANGE;
+  dspark::RnnParams p{};
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.r = r;
+  p.d = d;
+  p.H = reinterpret_cast<const uint16_t*>(H);
+  p.W = reinterpret_cast<const uint16_t*>(W);
+  p.W1 = reinterpret_cast<const uint16_t*>(W1);
+  p.x0 = x0;
+  p.x = x_out;
+  p.O = o_out;
+  p.W2 = reinterpret_cast<const uint16_t*>(W2);
+  const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  dspark::rnn_bind_workspace(p, reinterpret_cast<char*>(workspace) + base);
+  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, x0, seed, step,
+                                      x_out, q_tok_out, lse_out, workspace, &p,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -204,7 +254,40 @@ int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_d
     return DSPARK_E_RANGE;
   return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
                                        d_dtype == DSPARK_BF16, W1, W2, r, x0, x, q_tok, lse_d, seed, step,
-                                       n_acc_out, tok_out, workspace, reinterpret_cast<hipStream_t>(stream)));
+                                       n_acc_out, tok_out, workspace, nullptr, nullptr,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_rnn_verify_workspace_bytes(int R, int K, int V, int r, int N) {
+  (void)K;
+  if (R <= 0 || V <= 0 || N <= 0 || r <= 0) return 0;
+  return dspark::verify_workspace_bytes(R, V, N) + dspark::w2_f16_bytes(V, r);
+}
+
+int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int p_dtype, int N,
+                      const int32_t* cu_seqlens, const void* D, int d_dtype, const float* O, const void* W2, int r,
+                      const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
+                      uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
+  if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!P || !cu_seqlens || !D || !O || !W2 || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
+  if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
+  const size_t base = dspark::verify_workspace_bytes(R, V, N);
+  if (!workspace || workspace_bytes < base + dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
+  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, (size_t)V * r, s)) return DSPARK_E_HIP;
+  return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
+                                       d_dtype == DSPARK_BF16, nullptr, W2, r, x0, x, q_tok, lse_d, seed, step,
+                                       n_acc_out, tok_out, workspace, O, W2h, s));
 }
 
 size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
@@ -231,8 +314,36 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
   if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
     return DSPARK_E_RANGE;
   return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
-                                      W1, W2, r, x0, x, lse_d, c_out, workspace,
+                                      W1, W2, r, x0, x, lse_d, c_out, workspace, nullptr, nullptr,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || r <= 0) return 0;
+  return (dspark::label_workspace_bytes(B, K, V) + 255) / 256 * 256 + dspark::w2_f16_bytes(V, r);
+}
+
+int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
+                                int d_dtype, const float* O, const void* W2, int r, const int32_t* x0,
+                                const int32_t* x, const float* lse_d, float* c_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (!P || !D || !O || !W2 || !x0 || !x || !c_out) return DSPARK_E_NULL;
+  if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
+  const size_t base = (dspark::label_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  if (!workspace || workspace_bytes < base + dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
+  if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
+  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, (size_t)V * r, s)) return DSPARK_E_HIP;
+  return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
+                                      nullptr, W2, r, x0, x, lse_d, c_out, workspace, O, W2h, s));
 }
 
 int dspark_confidence_head(int B, int K, int V, int d, int r, const void* H, int h_dtype, const float* w_h,

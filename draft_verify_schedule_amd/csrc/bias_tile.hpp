@@ -26,9 +26,16 @@ constexpr int kTileCols = 256;   // columns per workgroup (4 waves)
 
 // LDS row pitch in bf16 elements for the E stage: 16 bytes of padding breaks
 // the power-of-two stride between the 16 rows a b128 read touches.
-template <int KC>
+// SPLIT: rows staged from fp32 values v (the RNN head's output parts) hold
+// hi = fp16(v) in columns [0, 32 KC) and lo = fp16(v - hi) in [32 KC, 64 KC);
+// both meet the same W2 fragment (converted to fp16, which holds every bf16
+// weight of magnitude 2^-14 .. 2^15 exactly), on the fp16 MFMA.  hi + lo
+// carries v to 2^-22 relative (plus 2^-25 absolute where lo is subnormal),
+// where one bf16 operand would keep 2^-8 and a bf16 pair 2^-16.
+template <int KC, bool SPLIT = false>
 struct EStage {
-  static constexpr int kPitch = 32 * KC + 8;
+  static constexpr int kLo = 32 * KC;  // column of the lo half (SPLIT)
+  static constexpr int kPitch = (SPLIT ? 64 : 32) * KC + 8;
   uint16_t e[kStageRows][kPitch];
 };
 
@@ -65,30 +72,31 @@ struct W2Frags {
     col_bytes = (uint32_t)r * 2u;
     lane_off = (uint32_t)(16 * (a >> 2) + (a & 3)) * col_bytes + (uint32_t)((lane >> 4) * 8) * 2u;
   }
-  template <int KC>
-  __device__ __forceinline__ void load(int n0, bf16x8 (&fr)[4][KC]) const {
+  // FT: bf16x8 (W2 as given) or f16x8 (its fp16 copy, for SPLIT stages)
+  template <int KC, typename FT>
+  __device__ __forceinline__ void load(int n0, FT (&fr)[4][KC]) const {
     load_from<KC>((uint32_t)n0 * col_bytes, fr);
   }
   // valid = false: every offset is past the resource, the registers read as
   // zero and no memory is touched (wave-uniform select, no branch)
-  template <int KC>
-  __device__ __forceinline__ void load_if(int n0, bool valid, bf16x8 (&fr)[4][KC]) const {
+  template <int KC, typename FT>
+  __device__ __forceinline__ void load_if(int n0, bool valid, FT (&fr)[4][KC]) const {
     load_from<KC>(valid ? (uint32_t)n0 * col_bytes : bytes, fr);
   }
-  template <int KC, int K0 = 0, int K1 = KC>
-  __device__ __forceinline__ void load_from(uint32_t base, bf16x8 (&fr)[4][KC]) const {
+  template <int KC, int K0 = 0, int K1 = KC, typename FT>
+  __device__ __forceinline__ void load_from(uint32_t base, FT (&fr)[4][KC]) const {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int kc = K0; kc < K1; ++kc) {
         const uint32_t soff = base + (uint32_t)(4 * b) * col_bytes + (uint32_t)(64 * kc);
-        fr[b][kc] = __builtin_bit_cast(bf16x8, buffer_load16(rsrc, lane_off, soff));
+        fr[b][kc] = __builtin_bit_cast(FT, buffer_load16(rsrc, lane_off, soff));
       }
     }
   }
   // k chunks [K0, K1) only (valid = false: zeros, no memory access)
-  template <int KC, int K0, int K1>
-  __device__ __forceinline__ void load_range_if(int n0, bool valid, bf16x8 (&fr)[4][KC]) const {
+  template <int KC, int K0, int K1, typename FT>
+  __device__ __forceinline__ void load_range_if(int n0, bool valid, FT (&fr)[4][KC]) const {
     load_from<KC, K0, K1>(valid ? (uint32_t)n0 * col_bytes : bytes, fr);
   }
 };
@@ -153,13 +161,65 @@ __device__ __forceinline__ void stage_e(EStage<KC>& st, const uint16_t* __restri
   ld.store(st, r);
 }
 
+// Round to nearest even, as raw bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp16 of f (round to nearest even) as raw bits.
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Stage fp32 rows (width r, row stride r; 16-byte aligned, r % 4 == 0) as
+// split hi/lo fp16 rows.  row_of(row) gives the source row or -1 (zeros);
+// columns past r are zero.  Each wave takes 32 rows, 8 at a time: one
+// 16-byte load per lane and row, 64 lanes per row.
+template <int KC, typename RowFn>
+__device__ __forceinline__ void stage_rows(EStage<KC, true>& st, const float* __restrict__ src, int r, int row0,
+                                           int nrows, RowFn row_of) {
+  static_assert(KC <= 8, "64 lanes x 4 values per row");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = 4 * lane;
+  const bool c_ok = c < r && c < 32 * KC;
+#pragma unroll
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = row0 + 32 * wave + i0 + i;
+      const int src_row = g < nrows ? row_of(g) : -1;
+      v[i] = (src_row >= 0 && c_ok) ? *reinterpret_cast<const f32x4*>(src + (size_t)src_row * r + c)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 32 * wave + i0 + i;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const _Float16 h = (_Float16)v[i][e];
+        hi[e] = (uint32_t)__builtin_bit_cast(uint16_t, h);
+        lo[e] = f16_bits(v[i][e] - (float)h);
+      }
+      if (c < 32 * KC) {
+        *reinterpret_cast<uint2*>(&st.e[row][c]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+        *reinterpret_cast<uint2*>(&st.e[row][EStage<KC, true>::kLo + c]) =
+            make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      }
+    }
+  }
+}
+
 // Byte offset of this lane's E fragment row within the stage (group 0,
 // chunk 0).  Callers that loop over column blocks pass it through
 // launder() once per block so that the compiler cannot hoist the (loop
 // invariant) LDS reads of all groups out of the loop and keep them live.
-template <int KC>
+template <int KC, bool SPLIT = false>
 __device__ __forceinline__ int e_lane_offset(int lane) {
-  return ((lane & 15) * EStage<KC>::kPitch + (lane >> 4) * 8) * 2;
+  return ((lane & 15) * EStage<KC, SPLIT>::kPitch + (lane >> 4) * 8) * 2;
 }
 
 __device__ __forceinline__ int launder(int v) {
@@ -173,16 +233,22 @@ __device__ __forceinline__ int launder(int v) {
 // same 16 x 64 tile, so the MFMAs leave base + bias in them directly.
 // Only the k chunks [K0, K1) (K0 = 0, K1 = KC: the whole contraction); ZERO
 // clears the accumulators first.
-template <int KC, bool ZERO = true, int K0 = 0, int K1 = KC>
-__device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane,
-                                           const bf16x8 (&w2)[4][KC], f32x4 (&acc)[4],
+// SPLIT stages (fp16 W2 fragments, w2 of type f16x8) add the lo half of each
+// chunk right after its hi half on the fp16 MFMA.
+template <int KC, bool ZERO = true, int K0 = 0, int K1 = KC, bool SPLIT, typename FT>
+__device__ __forceinline__ void mfma_group(const EStage<KC, SPLIT>& st, int g, int lane,
+                                           const FT (&w2)[4][KC], f32x4 (&acc)[4],
                                            int e_off = -1) {
-  bf16x8 e[KC];
-  if (e_off < 0) e_off = e_lane_offset<KC>(lane);
-  const char* base = reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC>::kPitch * 2;
+  FT e[KC];
+  FT el[SPLIT ? KC : 1];
+  if (e_off < 0) e_off = e_lane_offset<KC, SPLIT>(lane);
+  const char* base =
+      reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC, SPLIT>::kPitch * 2;
 #pragma unroll
-  for (int kc = K0; kc < K1; ++kc)
-    e[kc] = *reinterpret_cast<const bf16x8*>(base + 64 * kc);
+  for (int kc = K0; kc < K1; ++kc) {
+    e[kc] = *reinterpret_cast<const FT*>(base + 64 * kc);
+    if constexpr (SPLIT) el[kc] = *reinterpret_cast<const FT*>(base + 2 * EStage<KC, true>::kLo + 64 * kc);
+  }
   if constexpr (ZERO) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -190,8 +256,15 @@ __device__ __forceinline__ void mfma_group(const EStage<KC>& st, int g, int lane
 #pragma unroll
   for (int kc = K0; kc < K1; ++kc) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2[b][kc], e[kc], acc[b], 0, 0, 0);
+    for (int b = 0; b < 4; ++b) {
+      if constexpr (SPLIT) {
+        static_assert(sizeof(FT) == sizeof(f16x8), "fp16 fragments");
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w2[b][kc], e[kc], acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w2[b][kc], el[kc], acc[b], 0, 0, 0);
+      } else {
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2[b][kc], e[kc], acc[b], 0, 0, 0);
+      }
+    }
   }
 }
 
@@ -338,6 +411,35 @@ __device__ __forceinline__ float bias_chunk64(const uint16_t* __restrict__ w1row
   return s;
 }
 
+// The same over an fp32 row (the RNN head's output part o): lane l owns
+// column col and accumulates sum_k o[k] * W2[k, col] over k in [k0, k0 + 64)
+// in fp32 FMAs in index order.  Requires r % 8 == 0.
+__device__ __forceinline__ float bias_chunk64_rows(const float* __restrict__ orow,
+                                                  const uint16_t* __restrict__ w2col, int k0, int r) {
+  f32x4 av[16];
+  u32x4 bv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + 8 * i;
+    const bool ok = k < r;
+    av[2 * i] = ok ? *reinterpret_cast<const f32x4*>(orow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    av[2 * i + 1] = ok ? *reinterpret_cast<const f32x4*>(orow + k + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2col + k) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = av[2 * i + e / 2][2 * (e % 2)];
+      const float a1 = av[2 * i + e / 2][2 * (e % 2) + 1];
+      s = fmaf(a0, __uint_as_float(bv[i][e] << 16), s);
+      s = fmaf(a1, __uint_as_float(bv[i][e] & 0xFFFF0000u), s);
+    }
+  }
+  return s;
+}
+
 // One wave: the chunks of 64 in order, summed left to right.
 __device__ __forceinline__ float valu_bias(const uint16_t* __restrict__ w1row,
                                            const uint16_t* __restrict__ w2col, int r) {
@@ -346,13 +448,23 @@ __device__ __forceinline__ float valu_bias(const uint16_t* __restrict__ w1row,
   return s;
 }
 
+__device__ __forceinline__ float valu_bias_rows(const float* __restrict__ orow,
+                                                const uint16_t* __restrict__ w2col, int r) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < r; k0 += 64) s += bias_chunk64_rows(orow, w2col, k0, r);
+  return s;
+}
+
 // Four waves of a workgroup (r <= 256): wave w takes the chunk starting at
 // 64 w; the four chunk sums are combined in chunk order through LDS
 // (part[256], all waves must call it).  Returns the bias on every wave.
-__device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w1row,
+// With orow set, the bias input is that fp32 row instead of w1row.
+__device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w1row, const float* __restrict__ orow,
                                                   const uint16_t* __restrict__ w2col, int r, bool ok,
                                                   int wave, int lane, float* part) {
-  part[wave * 64 + lane] = ok ? bias_chunk64(w1row, w2col, 64 * wave, r) : 0.f;
+  float v = 0.f;
+  if (ok) v = orow ? bias_chunk64_rows(orow, w2col, 64 * wave, r) : bias_chunk64(w1row, w2col, 64 * wave, r);
+  part[wave * 64 + lane] = v;
   __syncthreads();
   return ((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane];
 }

@@ -12,10 +12,16 @@
 //   draft_locate    one wave per request: merges the slice partials into the
 //                   normaliser, finds the slice where the CDF crosses u * S,
 //                   re-evaluates that slice's 64 logits and picks the token.
+// With the RNN head (same paper, section 3.1, RNN head) a third launch comes
+// first at each position, rnn_step, which leaves the head's output part o_k
+// for every request; the bias is then o_k W2 (o_k staged as split bf16 rows)
+// instead of W1[x_{k-1}] W2.
 #include <algorithm>
+#include <type_traits>
 
 #include "bias_tile.hpp"
 #include "launch.hpp"
+#include "rnn.hpp"
 
 namespace dspark {
 
@@ -36,6 +42,8 @@ struct DraftArgs {
   int32_t* x_out;
   float* q_out;
   float* lse_out;
+  const float* O;          // RNN head: output parts [B, K, r] fp32, row b * K + k - 1 (else null)
+  const uint16_t* W2h;     // RNN head: fp16 copy of W2t
 };
 
 // Epilogue of one group: z = base logits + bias for 16 consecutive columns of
@@ -146,7 +154,9 @@ struct UAccess<UT, false> {
 // that have no block to read and the stores of lanes 16..63 get offsets past
 // their buffer resource (no memory access).  The block holding the column
 // tail (V not a multiple of 64) and partial stages take the plain path.
-template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL>
+// ROWS: the bias inputs are the fp32 rows a.O (RNN head) instead of gathered
+// W1 rows.
+template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL, bool ROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   static_assert(!FULL || VEC, "the pipelined sweep reads through buffer resources");
@@ -172,9 +182,9 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // gate the first MFMA through the LDS stage), then the first groups of
   // base logits and the first block's W2 fragments; the LDS stores of the E
   // stage wait for the W1 rows only.
-  __shared__ EStage<KCs> st;
+  __shared__ EStage<KCs, ROWS> st;
   EStageLoad<KCs> eld;
-  if constexpr (KC > 0) {
+  if constexpr (KC > 0 && !ROWS) {
     const int32_t* prev = a.prev;
     const int stride = a.prev_stride;
     eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
@@ -190,12 +200,17 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     for (int g = 0; g < kPrefetch; ++g) ua.load_if(buf[g], row0 + 16 * g, blk, blk < blk_stop);
   }
 
-  bf16x8 w2[4][KCs];
+  std::conditional_t<ROWS, f16x8, bf16x8> w2[4][KCs];
   W2Frags wf;
   if constexpr (KC > 0) {
-    wf.setup(a.W2t, a.r, a.V, lane);
+    wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
     if constexpr (FULL) wf.load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
-    eld.store(st, a.r);
+    if constexpr (ROWS) {
+      const int K = a.K, k = a.k;
+      stage_rows<KC>(st, a.O, a.r, row0, a.B, [&](int g) { return g * K + k - 1; });
+    } else {
+      eld.store(st, a.r);
+    }
     __syncthreads();
   }
 
@@ -212,7 +227,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       const int cbase = blk * kWaveCols + lane_col;
       const int nxt = blk + 4;
       const bool has_next = nxt < blk_stop;
-      const int e_off = launder(e_lane_offset<KCs>(lane));
+      const int e_off = launder(e_lane_offset<KCs, ROWS>(lane));
       auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
         if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
         else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
@@ -275,7 +290,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       one.unpack(z, cbase, a.V, row_live(g));
       if constexpr (KC > 0) {
         f32x4 acc[4];
-        mfma_group<KC>(st, g, lane, w2, acc, launder(e_lane_offset<KC>(lane)));
+        mfma_group<KC>(st, g, lane, w2, acc, launder(e_lane_offset<KC, ROWS>(lane)));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -476,8 +491,8 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   }
   float bias = 0.f;
   if (a.r > 0)
-    bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok,
-                            wave, lane, bias_part);
+    bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.O ? a.O + out * a.r : nullptr,
+                            a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok, wave, lane, bias_part);
   if (wave != 0) return;
   const float t_in = (float)((target - before) / (double)fast_exp2(m_s - M));
   const float z = col_ok ? base + bias : -INFINITY;
@@ -498,19 +513,19 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
 
 // Full 128-row stages and the trailing partial stage (B not a multiple of
 // 128) are separate launches of separately register-allocated variants.
-template <typename UT, bool VEC, int KC, bool GREEDY>
+template <typename UT, bool VEC, int KC, bool GREEDY, bool ROWS = false>
 static int launch_partials(const DraftArgs& a, hipStream_t stream) {
   const int full = VEC ? a.B / kStageRows : 0;  // unaligned rows: the plain variant throughout
   const int partial = a.nstages - full;
   if constexpr (VEC) {
     if (full > 0) {
-      const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true>,
+      const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true, ROWS>,
                                    dim3(xcd_grid(a.ncol_tiles, full)), dim3(256), stream, a, 0, full);
       if (rc) return rc;
     }
   }
   if (partial > 0) {
-    return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, false>,
+    return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, false, ROWS>,
                          dim3(xcd_grid(a.ncol_tiles, partial)), dim3(256), stream, a, full, partial);
   }
   return 0;
@@ -518,6 +533,8 @@ static int launch_partials(const DraftArgs& a, hipStream_t stream) {
 
 template <typename UT, bool VEC, bool GREEDY>
 static int dispatch_kc(const DraftArgs& a, hipStream_t stream) {
+  // RNN head: one variant, r <= 256 zero-padded to eight chunks
+  if (a.O) return launch_partials<UT, VEC, 8, GREEDY, true>(a, stream);
   switch ((a.r + 31) / 32) {
     case 0: return launch_partials<UT, VEC, 0, GREEDY>(a, stream);
     case 1: return launch_partials<UT, VEC, 1, GREEDY>(a, stream);
@@ -533,7 +550,13 @@ static int dispatch_kc(const DraftArgs& a, hipStream_t stream) {
 }
 
 template <typename UT, bool GREEDY>
-static int run_draft_typed(DraftArgs a, bool vec, hipStream_t stream) {
+static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStream_t stream) {
+  if (rnn) {
+    int rc = run_w2_to_f16(rnn->W2, rnn->W2h, (size_t)a.V * a.r, stream);
+    if (rc) return rc;
+    rc = run_rnn_hproj(*rnn, stream);
+    if (rc) return rc;
+  }
   for (int k = 1; k <= a.K; ++k) {
     a.k = k;
     if (k == 1) {
@@ -541,6 +564,10 @@ static int run_draft_typed(DraftArgs a, bool vec, hipStream_t stream) {
     } else {
       a.prev = a.x_out + (k - 2);
       a.prev_stride = a.K;
+    }
+    if (rnn) {
+      const int rc = run_rnn_step(*rnn, k, stream);
+      if (rc) return rc;
     }
     int rc = vec ? dispatch_kc<UT, true, GREEDY>(a, stream) : dispatch_kc<UT, false, GREEDY>(a, stream);
     if (rc) return rc;
@@ -558,7 +585,8 @@ size_t draft_workspace_bytes(int B, int K, int V) {
 
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16,
               const void* W1, const void* W2, const int32_t* x0, uint64_t seed, uint64_t step,
-              int32_t* x_out, float* q_out, float* lse_out, void* workspace, hipStream_t stream) {
+              int32_t* x_out, float* q_out, float* lse_out, void* workspace, const RnnParams* rnn,
+              hipStream_t stream) {
   DraftArgs a{};
   a.U = U;
   a.W1 = reinterpret_cast<const uint16_t*>(W1);
@@ -580,16 +608,19 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   a.x_out = x_out;
   a.q_out = q_out;
   a.lse_out = lse_out;
+  a.O = rnn ? rnn->O : nullptr;
+  a.W2h = rnn ? rnn->W2h : nullptr;
   const bool greedy = temperature == 0.f;
   a.c2 = greedy ? 1.f : kLog2e / temperature;
   const uintptr_t base = reinterpret_cast<uintptr_t>(U);
   if (u_bf16) {
     const bool vec = (V % 8 == 0) && (base % 16 == 0);
-    return greedy ? run_draft_typed<uint16_t, true>(a, vec, stream)
-                  : run_draft_typed<uint16_t, false>(a, vec, stream);
+    return greedy ? run_draft_typed<uint16_t, true>(a, vec, rnn, stream)
+                  : run_draft_typed<uint16_t, false>(a, vec, rnn, stream);
   }
   const bool vec = (V % 4 == 0) && (base % 16 == 0);
-  return greedy ? run_draft_typed<float, true>(a, vec, stream) : run_draft_typed<float, false>(a, vec, stream);
+  return greedy ? run_draft_typed<float, true>(a, vec, rnn, stream)
+                : run_draft_typed<float, false>(a, vec, rnn, stream);
 }
 
 }  // namespace dspark

@@ -1,0 +1,282 @@
+// RNN head of the sequential draft stage (DSpark paper, section 3.1, RNN
+// head; "Speculative decoding, from zero to DSpark", section 6).
+//
+// The head keeps a state s_k in R^r per request.  At position k it forms
+// z_k = [s_{k-1}; W1[x_{k-1}]; h_k] (s_0 = 0) and applies one projection W
+// whose 3r rows are the gate, candidate and output parts.  The page's update
+// equation did not survive; the reading taken is a GRU-style blend with no
+// additive bias:
+//   g = sigmoid(W_g z),  c~ = tanh(W_c z),  o = W_o z,  s_k = (1 - g) s_{k-1} + g c~.
+// o_k is the bias input in front of W2: the draft stages it where the Markov
+// head has W1[x_{k-1}].
+//
+// Launches:
+//   rnn_hproj  once per draft: the hidden-state part W[:, 2r:] h_k of every
+//              (request, position), an MFMA GEMM (B*K x d) x (d x 3r); h does
+//              not depend on the sampled tokens, so this leaves the
+//              sequential loop;
+//   rnn_step   once per position: the state and embedding parts on MFMA (the
+//              fp32 state split into three bf16 operands), then the gates;
+//   w2_to_f16  once per call: the fp16 copy of W2 that the output parts
+//              (staged as hi + lo fp16) meet in the draft's bias MFMA.
+#include <algorithm>
+
+#include "bias_tile.hpp"
+#include "launch.hpp"
+#include "rnn.hpp"
+
+namespace dspark {
+
+// ---------------------------------------------------------------- hproj --
+// 128 x 128 output tile per workgroup (n: projection rows, m: (request,
+// position) rows).  4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA blocks with
+// A = W rows (n) and B = h rows (m): lane l ends with 4 consecutive n of one
+// m, stored as one 16-byte vector.  The contraction runs in stages of 64
+// columns through double-buffered LDS; rows past M or N read as zero through
+// the buffer resources' range check.
+constexpr int kHpTile = 128;
+constexpr int kHpK = 64;
+constexpr int kHpPitch = kHpK + 8;  // bf16 per LDS row: 144 bytes
+
+__global__ __launch_bounds__(256) void rnn_hproj_kernel(RnnParams p, int mtiles, int ntiles) {
+  int mt, nt;
+  if (!xcd_tile(blockIdx.x, mtiles, ntiles, mt, nt)) return;
+  __shared__ uint16_t hs[2][kHpTile][kHpPitch];
+  __shared__ uint16_t ws[2][kHpTile][kHpPitch];
+  const int M = p.B * p.K, N = 3 * p.r, d = p.d;
+  const int ldw = 2 * p.r + d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int wn = wave >> 1, wm = wave & 1;
+  const int m0 = mt * kHpTile, n0 = nt * kHpTile;
+  const uint32_t hbytes = (uint32_t)((uint64_t)M * d * 2);
+  const uint32_t wbytes = (uint32_t)((uint64_t)N * ldw * 2);
+  const rsrc_t hr = make_rsrc(p.H, hbytes);
+  const rsrc_t wr = make_rsrc(p.W, wbytes);
+  // global -> LDS: four 16-byte chunks per thread and operand; chunk id / 8 is
+  // the tile row, id % 8 the 8-column group
+  uint32_t hoff[4], woff[4];
+  int lrow[4], lcol[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int id = tid + 256 * q;
+    lrow[q] = id >> 3;
+    lcol[q] = (id & 7) * 8;
+    const int m = m0 + lrow[q], n = n0 + lrow[q];
+    hoff[q] = m < M ? (uint32_t)(((uint64_t)m * d + lcol[q]) * 2) : hbytes;
+    woff[q] = n < N ? (uint32_t)(((uint64_t)n * ldw + 2 * p.r + lcol[q]) * 2) : wbytes;
+  }
+  u32x4 hv[4], wv[4];
+  auto gload = [&](int kt) {
+    const uint32_t so = (uint32_t)kt * (kHpK * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hv[q] = buffer_load16(hr, hoff[q], so);
+      wv[q] = buffer_load16(wr, woff[q], so);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<u32x4*>(&hs[buf][lrow[q]][lcol[q]]) = hv[q];
+      *reinterpret_cast<u32x4*>(&ws[buf][lrow[q]][lcol[q]]) = wv[q];
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = d / kHpK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kc = 0; kc < kHpK / 32; ++kc) {
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(&ws[buf][64 * wn + 16 * i + fr][32 * kc + fk]);
+        bf[i] = *reinterpret_cast<const bf16x8*>(&hs[buf][64 * wm + 16 * i + fr][32 * kc + fk]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nb], bf[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = n0 + 64 * wn + 16 * nb + 4 * (lane >> 4);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + 64 * wm + 16 * mb + fr;
+      if (m < M && n < N) *reinterpret_cast<f32x4*>(p.Hp + (size_t)m * N + n) = acc[nb][mb];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- step --
+// One workgroup per (16 state units j, 16 requests).  MFMA A operands are W
+// rows (gate, candidate, output row of unit j), B operands the z rows of the
+// requests, so lane l ends with units j0 + 4 (l / 16) + i of request
+// b0 + l % 16.  The four waves split the contraction by 32-column chunk
+// (chunk c on wave c % 4): state chunks as three bf16 terms (together the
+// fp32 value), embedding chunks as the bf16 W1 row itself.  Their partial sums meet in LDS in wave
+// order; wave 0 adds the hidden-state part and applies the gates.
+__global__ __launch_bounds__(256) void rnn_step_kernel(RnnParams p, int k, const float* __restrict__ s_prev,
+                                                       float* __restrict__ s_next) {
+  const int r = p.r, ldw = 2 * r + p.d;
+  const int jtiles = r / 16;
+  const int jt = blockIdx.x % jtiles, bt = blockIdx.x / jtiles;
+  const int j0 = 16 * jt, b0 = 16 * bt;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int b = b0 + (lane & 15);
+  const bool b_ok = b < p.B;
+  const int kq = 8 * (lane >> 4);
+  int prev = -1;
+  if (b_ok) prev = k == 1 ? p.x0[b] : p.x[(size_t)b * p.K + k - 2];
+  const bool e_ok = prev >= 0 && prev < p.V;
+  const uint16_t* wrow[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) wrow[c] = p.W + (size_t)(c * r + j0 + (lane & 15)) * ldw;
+  f32x4 acc[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = r / 32;
+  if (s_prev) {  // s_0 = 0 adds nothing
+    for (int c = wave; c < nch; c += 4) {
+      const int kk = 32 * c + kq;
+      f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+      if (b_ok) {
+        v0 = *reinterpret_cast<const f32x4*>(s_prev + (size_t)b * r + kk);
+        v1 = *reinterpret_cast<const f32x4*>(s_prev + (size_t)b * r + kk + 4);
+      }
+      // s = t0 + t1 + t2 in bf16 terms, each the rounded remainder of the
+      // previous: 24 significant bits, the fp32 state itself
+      u32x4 t[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float f0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
+        float f1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const uint32_t h0 = bf16_rne_bits(f0), h1 = bf16_rne_bits(f1);
+          t[q][e] = h0 | (h1 << 16);
+          f0 -= __uint_as_float(h0 << 16);
+          f1 -= __uint_as_float(h1 << 16);
+        }
+      }
+#pragma unroll
+      for (int comp = 0; comp < 3; ++comp) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow[comp] + kk);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          acc[comp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, t[q]), acc[comp], 0, 0, 0);
+      }
+    }
+  }
+  for (int c = wave; c < nch; c += 4) {
+    const int kk = 32 * c + kq;
+    const u32x4 ev = e_ok ? *reinterpret_cast<const u32x4*>(p.W1 + (size_t)prev * r + kk) : u32x4{0u, 0u, 0u, 0u};
+    const bf16x8 z = __builtin_bit_cast(bf16x8, ev);
+#pragma unroll
+    for (int comp = 0; comp < 3; ++comp) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow[comp] + r + kk);
+      acc[comp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, z, acc[comp], 0, 0, 0);
+    }
+  }
+  __shared__ f32x4 red[4][3][64];
+#pragma unroll
+  for (int comp = 0; comp < 3; ++comp) red[wave][comp][lane] = acc[comp];
+  __syncthreads();
+  if (wave != 0 || !b_ok) return;
+  f32x4 pre[3];
+#pragma unroll
+  for (int comp = 0; comp < 3; ++comp)
+    pre[comp] = ((red[0][comp][lane] + red[1][comp][lane]) + red[2][comp][lane]) + red[3][comp][lane];
+  const int jj = j0 + 4 * (lane >> 4);
+  const size_t row = (size_t)b * p.K + (k - 1);
+  const float* hp = p.Hp + row * (size_t)(3 * r);
+  const f32x4 hg = *reinterpret_cast<const f32x4*>(hp + jj);
+  const f32x4 hc = *reinterpret_cast<const f32x4*>(hp + r + jj);
+  const f32x4 ho = *reinterpret_cast<const f32x4*>(hp + 2 * r + jj);
+  f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (s_prev) sp = *reinterpret_cast<const f32x4*>(s_prev + (size_t)b * r + jj);
+  f32x4 sn, o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g = 1.f / (1.f + expf(-(pre[0][i] + hg[i])));
+    const float cand = tanhf(pre[1][i] + hc[i]);
+    sn[i] = (1.f - g) * sp[i] + g * cand;
+    o[i] = pre[2][i] + ho[i];
+  }
+  *reinterpret_cast<f32x4*>(s_next + (size_t)b * r + jj) = sn;
+  *reinterpret_cast<f32x4*>(p.O + row * r + jj) = o;
+}
+
+// ------------------------------------------------------------ W2 to fp16 --
+// bf16 -> fp32 is exact; fp32 -> fp16 rounds to nearest even, exact for every
+// bf16 of magnitude 2^-14 .. 2^15 (8 significant bits fit in 11), with at
+// most 2^-25 absolute error below that range.
+__global__ __launch_bounds__(256) void w2_to_f16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                        size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(in + 8 * i);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = f16_bits(__uint_as_float(v[e] << 16)) | (f16_bits(__uint_as_float(v[e] & 0xFFFF0000u)) << 16);
+    *reinterpret_cast<u32x4*>(out + 8 * i) = o;
+  }
+}
+
+// ------------------------------------------------------------------ host --
+static size_t align256_rnn(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t w2_f16_bytes(int V, int r) { return align256_rnn((size_t)V * r * sizeof(uint16_t)); }
+
+size_t rnn_workspace_bytes(int B, int K, int V, int r) {
+  return align256_rnn((size_t)B * K * 3 * r * sizeof(float)) + 2 * align256_rnn((size_t)B * r * sizeof(float)) +
+         w2_f16_bytes(V, r);
+}
+
+void rnn_bind_workspace(RnnParams& p, void* workspace) {
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.Hp = reinterpret_cast<float*>(ws);
+  ws += align256_rnn((size_t)p.B * p.K * 3 * p.r * sizeof(float));
+  p.s[0] = reinterpret_cast<float*>(ws);
+  ws += align256_rnn((size_t)p.B * p.r * sizeof(float));
+  p.s[1] = reinterpret_cast<float*>(ws);
+  ws += align256_rnn((size_t)p.B * p.r * sizeof(float));
+  p.W2h = reinterpret_cast<uint16_t*>(ws);
+}
+
+int run_w2_to_f16(const uint16_t* W2, uint16_t* out, size_t n, hipStream_t stream) {
+  const size_t n8 = n / 8;
+  const size_t blocks = std::min<size_t>((n8 + 255) / 256, 4096);
+  return launch_kernel("w2_to_f16", w2_to_f16_kernel, dim3((unsigned)std::max<size_t>(blocks, 1)), dim3(256), stream,
+                       W2, out, n8);
+}
+
+int run_rnn_hproj(const RnnParams& p, hipStream_t stream) {
+  const int mtiles = (p.B * p.K + kHpTile - 1) / kHpTile;
+  const int ntiles = (3 * p.r + kHpTile - 1) / kHpTile;
+  return launch_kernel("rnn_hproj", rnn_hproj_kernel, dim3(xcd_grid(mtiles, ntiles)), dim3(256), stream, p, mtiles,
+                       ntiles);
+}
+
+int run_rnn_step(const RnnParams& p, int k, hipStream_t stream) {
+  const float* s_prev = k == 1 ? nullptr : p.s[(k - 1) & 1];
+  float* s_next = p.s[k & 1];
+  const int grid = (p.r / 16) * ((p.B + 15) / 16);
+  return launch_kernel("rnn_step", rnn_step_kernel, dim3(grid), dim3(256), stream, p, k, s_prev, s_next);
+}
+
+}  // namespace dspark

@@ -1,0 +1,38 @@
+// RNN head of the sequential draft stage (DSpark paper, section 3.1, RNN
+// head): host-side parameters and launchers shared by the draft driver.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dspark {
+
+struct RnnParams {
+  int B, K, V, r, d;
+  const uint16_t* H;   // [B, K, d] bf16 backbone hidden states (h_k at [b, k-1])
+  const uint16_t* W;   // [3r, 2r + d] bf16: gate rows, candidate rows, output rows
+  const uint16_t* W1;  // [V, r] bf16 Markov embedding
+  const int32_t* x0;   // [B] anchors
+  const int32_t* x;    // [B, K] drafted tokens (x_{k-1} is read at position k)
+  float* Hp;           // workspace [B * K, 3r]: W[:, 2r:] h for every (request, position)
+  float* s[2];         // workspace [B, r] x 2: state of the odd / even positions
+  float* O;            // [B, K, r] output parts o_k (the caller's buffer)
+  uint16_t* W2h;       // workspace [V, r]: fp16 copy of the column-major W2
+  const uint16_t* W2;  // [V, r] bf16 column-major W2
+};
+
+size_t rnn_workspace_bytes(int B, int K, int V, int r);
+// Carves Hp, the two state buffers and W2h out of a workspace of rnn_workspace_bytes.
+void rnn_bind_workspace(RnnParams& p, void* workspace);
+// out[i] = fp16(W2[i]) for n bf16 values (n % 8 == 0, both 16-byte aligned):
+// the fp16 operand the split output parts meet on the MFMA.
+int run_w2_to_f16(const uint16_t* W2, uint16_t* out, size_t n, hipStream_t stream);
+size_t w2_f16_bytes(int V, int r);
+// Hp = h W[:, 2r:]^T for all B * K rows: one MFMA GEMM per call.
+int run_rnn_hproj(const RnnParams& p, hipStream_t stream);
+// The gated update of position k (1-based) for every request: writes s_k and o_k.
+int run_rnn_step(const RnnParams& p, int k, hipStream_t stream);
+
+}  // namespace dspark

@@ -20,7 +20,11 @@
 //   verify_sample     (T > 0) one wave per request: inverse-CDF draw of the
 //                     correction (residual partials, 64-column re-scan) or the
 //                     bonus (target partials, 256-column re-scan).
+// Drafts of the RNN head (DSpark paper, section 3.1, RNN head) pass their
+// output parts O [R, K, r] fp32: the draft row of position j then carries the
+// bias O[r, j-1] W2, staged as split hi/lo bf16 rows for the MFMA.
 #include <algorithm>
+#include <type_traits>
 
 #include "bias_tile.hpp"
 #include "launch.hpp"
@@ -43,6 +47,8 @@ struct VerifyArgs {
   const int32_t* x;         // [R, K]
   const float* q_tok;       // [R, K]
   const float* lse_d;       // [R, K]
+  const float* O;           // RNN head: output parts [R, K, r] fp32 (else null)
+  const uint16_t* W2h;      // RNN head: fp16 copy of W2t
   uint64_t seed, step;
   int32_t* n_acc_out;
   int32_t* tok_out;
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
 // columns, 128 requests (8 MFMA groups) per workgroup, W2 fragments held in
 // registers, the target and draft rows of group g+2 requested before the
 // epilogue of group g.  Requests that are not correcting take no loads.
-template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL = false>
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL = false, bool ROWS = false>
 __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
   int col_tile, stage;
   if (!xcd_tile(blockIdx.x, a.ncol_tiles, a.nstages, col_tile, stage)) return;
@@ -434,22 +440,30 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
     db1.load(drow(1, in1), cbase, a.V);
   }
 
-  __shared__ EStage<(KC > 0 ? KC : 1)> st;
-  bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  __shared__ EStage<(KC > 0 ? KC : 1), ROWS> st;
+  std::conditional_t<ROWS, f16x8, bf16x8> w2[4][(KC > 0 ? KC : 1)];
   if constexpr (KC > 0) {
     const int4* info = a.info;
     const int32_t* x0 = a.x0;
     const int32_t* x = a.x;
     const int K = a.K;
-    stage_e<KC>(st, a.W1, a.r, a.V, row0, nrow, [&](int g) {
-      if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
-      const int4 in = info[g];
-      if (in.x != 1) return -1;
-      return in.w == 0 ? x0[g] : x[(size_t)g * K + in.w - 1];
-    });
+    if constexpr (ROWS) {
+      stage_rows<KC>(st, a.O, a.r, row0, nrow, [&](int g) {
+        if constexpr (LABEL) return g;
+        const int4 in = info[g];
+        return in.x == 1 ? g * K + in.w : -1;
+      });
+    } else {
+      stage_e<KC>(st, a.W1, a.r, a.V, row0, nrow, [&](int g) {
+        if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
+        const int4 in = info[g];
+        if (in.x != 1) return -1;
+        return in.w == 0 ? x0[g] : x[(size_t)g * K + in.w - 1];
+      });
+    }
     if (col_live) {
       W2Frags wf;
-      wf.setup(a.W2t, a.r, a.V, lane);
+      wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
       wf.load<KC>(n0, w2);
     }
     __syncthreads();
@@ -526,7 +540,7 @@ struct ResidualRow {
   float lp, lq;           // log2-normalisers of p and q
 };
 
-template <typename PT, typename DT, int KC, bool LABEL = false>
+template <typename PT, typename DT, int KC, bool LABEL = false, bool ROWS = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void verify_residual_stream_kernel(VerifyArgs a) {
   // LABEL: one item per (request, position) pair, item i = r * K + k, with
@@ -550,7 +564,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   const int blk_end = (int)((int64_t)(split + 1) * nblocks / nsplit);
 
   __shared__ ResidualRow rows[kStageRows];
-  __shared__ EStage<(KC > 0 ? KC : 1)> st;
+  __shared__ EStage<(KC > 0 ? KC : 1), ROWS> st;
   if (threadIdx.x < kStageRows) {
     ResidualRow rr{0u, 0u, 0.f, 0.f};
     if ((int)threadIdx.x < nrows) {
@@ -566,7 +580,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     }
     rows[threadIdx.x] = rr;
   }
-  bf16x8 w2[4][(KC > 0 ? KC : 1)];
+  std::conditional_t<ROWS, f16x8, bf16x8> w2[4][(KC > 0 ? KC : 1)];
   W2Frags wf;
   if constexpr (KC > 0) {
     const int32_t* list = a.rej_list;
@@ -574,13 +588,21 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     const int32_t* x0 = a.x0;
     const int32_t* x = a.x;
     const int K = a.K;
-    stage_e<KC>(st, a.W1, a.r, a.V, row0, count, [&](int g) {
-      if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
-      const int r = list[g];
-      const int4 in = info[r];
-      return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
-    });
-    wf.setup(a.W2t, a.r, a.V, lane);
+    if constexpr (ROWS) {
+      stage_rows<KC>(st, a.O, a.r, row0, count, [&](int g) {
+        if constexpr (LABEL) return g;
+        const int r = list[g];
+        return r * K + info[r].w;
+      });
+    } else {
+      stage_e<KC>(st, a.W1, a.r, a.V, row0, count, [&](int g) {
+        if constexpr (LABEL) return (g % K == 0) ? x0[g / K] : x[g - 1];
+        const int r = list[g];
+        const int4 in = info[r];
+        return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
+      });
+    }
+    wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
   }
   __syncthreads();
 
@@ -594,7 +616,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
     if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
-    const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1)>(lane));
+    const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1), ROWS>(lane));
     GroupLogitsBuf<PT> pb;
     GroupLogitsBuf<DT> db;
     ResidualRow ri = row_info(0);
@@ -716,7 +738,8 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
         const int prev = in.w == 0 ? a.x0[r] : a.x[(size_t)r * a.K + in.w - 1];
         const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)r * a.K + in.w) * a.V;
         float zq = load_logit(drow, col);
-        if (a.r > 0) zq += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
+        if (a.O) zq += valu_bias_rows(a.O + ((size_t)r * a.K + in.w) * a.r, a.W2t + (size_t)col * a.r, a.r);
+        else if (a.r > 0) zq += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
         const float lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
         const float p = fast_exp2(fmaf(load_logit(prow, col), a.c2, -lp));
         const float q = fast_exp2(fmaf(zq, a.c2, -lq));
@@ -877,15 +900,17 @@ __global__ __launch_bounds__(256) void label_reduce_kernel(VerifyArgs a, float* 
   if (lane == 0) c_out[i] = ok ? (float)fmin(1.0, fmax(0.0, 1.0 - z)) : NAN;
 }
 
-template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL>
+template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual(const VerifyArgs& a, hipStream_t stream) {
   return launch_kernel(LABEL ? "label_residual" : "verify_residual",
-                       verify_residual_kernel<PT, DT, VEC_P, VEC_D, KC, LABEL>,
+                       verify_residual_kernel<PT, DT, VEC_P, VEC_D, KC, LABEL, ROWS>,
                        dim3(xcd_grid(a.ncol_tiles, a.nstages)), dim3(256), stream, a);
 }
 
 template <typename PT, typename DT, bool VEC_P, bool VEC_D, bool LABEL = false>
 static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
+  // RNN head: one variant, r <= 256 zero-padded to eight chunks
+  if (a.O) return launch_residual<PT, DT, VEC_P, VEC_D, 8, LABEL, true>(a, stream);
   switch ((a.r + 31) / 32) {
     case 0: return launch_residual<PT, DT, VEC_P, VEC_D, 0, LABEL>(a, stream);
     case 1: return launch_residual<PT, DT, VEC_P, VEC_D, 1, LABEL>(a, stream);
@@ -900,17 +925,18 @@ static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
   }
 }
 
-template <typename PT, typename DT, int KC, bool LABEL>
+template <typename PT, typename DT, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   // about two workgroups per CU, and enough 8-slot rows for every stage
   const int rows = LABEL ? a.R * a.K : a.R;
   const int slots = std::max(64, (rows + kStageRows - 1) / kStageRows);
-  return launch_kernel(LABEL ? "label_residual" : "verify_residual", verify_residual_stream_kernel<PT, DT, KC, LABEL>,
-                       dim3(8 * slots), dim3(256), stream, a);
+  return launch_kernel(LABEL ? "label_residual" : "verify_residual",
+                       verify_residual_stream_kernel<PT, DT, KC, LABEL, ROWS>, dim3(8 * slots), dim3(256), stream, a);
 }
 
 template <typename PT, typename DT, bool LABEL = false>
 static int dispatch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
+  if (a.O) return launch_residual_stream<PT, DT, 8, LABEL, true>(a, stream);
   switch ((a.r + 31) / 32) {
     case 0: return launch_residual_stream<PT, DT, 0, LABEL>(a, stream);
     case 1: return launch_residual_stream<PT, DT, 1, LABEL>(a, stream);
@@ -961,7 +987,7 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
                const int32_t* cu, const void* D, bool d_bf16, const void* W1, const void* W2, int r,
                const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d,
                uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
-               hipStream_t stream) {
+               const float* O, const uint16_t* W2h, hipStream_t stream) {
   const VerifyLayout l = verify_layout(R, V, N);
   char* ws = reinterpret_cast<char*>(workspace);
   VerifyArgs a{};
@@ -981,6 +1007,8 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   a.x = x;
   a.q_tok = q_tok;
   a.lse_d = lse_d;
+  a.O = O;
+  a.W2h = W2h;
   a.seed = seed;
   a.step = step;
   a.n_acc_out = n_acc_out;
@@ -1043,7 +1071,7 @@ static int run_label_typed(VerifyArgs& a, float* c_out, bool greedy, bool vec_p,
 
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
               const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
-              float* c_out, void* workspace, hipStream_t stream) {
+              float* c_out, void* workspace, const float* O, const uint16_t* W2h, hipStream_t stream) {
   const int N = B * K;
   char* ws = reinterpret_cast<char*>(workspace);
   VerifyArgs a{};
@@ -1061,6 +1089,8 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   a.x0 = x0;
   a.x = x;
   a.lse_d = lse_d;
+  a.O = O;
+  a.W2h = W2h;
   a.nsP = (V + kRowSlice - 1) / kRowSlice;
   a.ns64 = (V + kWaveCols - 1) / kWaveCols;
   a.nchunks = (V + kRowChunk - 1) / kRowChunk;

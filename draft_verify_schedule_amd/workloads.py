@@ -27,6 +27,11 @@ suffix decay of the DSpark paper's Figure 2):
               (k = 1..7, s = 2 sqrt(2) the standard deviation of U) and a bonus
               row t_8 = s eps; staircase SPS(B) = 1000 min(1, 2048 / (64 ceil(B/64))).
 
+RNN-head inputs (rnn_head): backbone hidden states H [B, K, d] ~ N(0, 1) and
+the head's projection W [3r, 2r + d] ~ N(0, 1 / (2r + d)), both bf16, so that
+gate, candidate and output pre-activations have about unit variance; the
+full-size case uses the full_step workload with r = 256 and d = 4096.
+
 Float values are drawn in float32 and rounded to nearest-even bfloat16 where
 the workload is bf16.  Randomness: a torch generator seeded with
 1000 + workload number drives the large logit tensors (on the requested
@@ -170,6 +175,15 @@ def make(name, device="cpu", B=None, V=None):
         return Workload(name, B, K, V, r, 1.0, U, t, W1, W2, x0, c, sps, rng_seed,
                         {"target": "correlated 0.85 with the base logits U"})
     raise KeyError(name)
+
+
+def rnn_head(B, K, r, d, seed, device="cpu"):
+    """Hidden states H [B, K, d] and the RNN head's projection W [3r, 2r + d]
+    (gate rows, candidate rows, output rows), bf16."""
+    g = _gen(seed, device)
+    H = _normal((B, K, d), g, device).to(torch.bfloat16)
+    W = _normal((3 * r, 2 * r + d), g, device, 1.0 / math.sqrt(2 * r + d)).to(torch.bfloat16)
+    return H.contiguous(), W.contiguous()
 
 
 def flat_target_rows(t, cu_seqlens):

@@ -240,6 +240,85 @@ int dspark_acceptance_label(int B, int K, int V, float temperature,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Sequential RNN-head draft.  DSpark paper section 3.1 ("RNN head");
+ * "Speculative decoding, from zero to DSpark", section 6.
+ *
+ * A state s_k in R^r per request, s_0 = 0.  For k = 1..K in order:
+ *   z_k = [s_{k-1}; W1[x_{k-1}]; h_k]            (length 2r + d, x_0 = x0[b])
+ *   g = sigmoid(W_g z_k), c~ = tanh(W_c z_k), o_k = W_o z_k
+ *   s_k = (1 - g) * s_{k-1} + g * c~
+ *   x_k = inverse-CDF draw from softmax((U[b,k-1,:] + o_k W2) / T)
+ * W_g, W_c, W_o are the row blocks [0, r), [r, 2r), [2r, 3r) of W.  The
+ * page gives z_k, the three parts of one projection and s_0 = 0; its update
+ * equation is lost, and the GRU-style blend above, with no additive bias, is
+ * this library's reading.  The output part o_k takes the place of the Markov
+ * embedding in front of W2 (with W_o = [0 | I | 0] the call is
+ * dspark_markov_draft).
+ * Inputs: U [B, K, V] (u_dtype f32 or bf16); H [B, K, d] bf16 (h_dtype must
+ * be DSPARK_BF16), h_k at [b, k-1]; W [3r, 2r + d] bf16 row-major; W1 [V, r]
+ * and W2 (column-major r x V) bf16 as for the Markov draft; x0 [B] int32.
+ * Outputs: x_out, q_tok_out, lse_out [B, K] as for dspark_markov_draft;
+ * o_out [B, K, r] f32, the output parts o_k, which dspark_rnn_verify and
+ * dspark_rnn_acceptance_label take to rebuild the draft distributions.
+ * The bias o_k W2 runs on the fp16 MFMA with o_k split into hi + lo fp16
+ * parts and W2 converted to fp16 (relative error 2^-22 on o_k): entries of
+ * o_k and W2 must be smaller than 2^15 in magnitude.
+ * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V, r a multiple of 32 in
+ * [32, DSPARK_MAX_RANK], d a positive multiple of 64; U, H, W, W1 each smaller
+ * than 4 GiB; H, W, W1, W2, o_out 16-byte aligned (else DSPARK_E_RANGE).
+ * Workspace: dspark_rnn_draft_workspace_bytes(B, K, V, r, d) bytes.
+ * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
+ * that request's remaining positions x = -1, q_tok = lse = NaN.
+ * ------------------------------------------------------------------------ */
+size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d);
+int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature,
+                     const void* U, int u_dtype,
+                     const void* H, int h_dtype,
+                     const void* W, const void* W1, const void* W2,
+                     const int32_t* x0,
+                     uint64_t seed, uint64_t step,
+                     int32_t* x_out, float* q_tok_out, float* lse_out, float* o_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Verification of RNN-head drafts: dspark_verify with the draft rows'
+ * bias rebuilt from the head's output parts, q_j = softmax((D[r,j-1] +
+ * O[r,j-1] W2) / T - lse_d) (DSpark paper section 3.1, RNN head, and the
+ * sources cited for dspark_verify).  O [R, K, r] f32 as returned in o_out by
+ * dspark_rnn_draft (16-byte aligned); W2 column-major bf16; r as for
+ * dspark_rnn_draft.  Workspace: dspark_rnn_verify_workspace_bytes(R, K, V, r,
+ * N) bytes (dspark_verify's, plus an fp16 copy of W2).  Everything else is as
+ * for dspark_verify.
+ * ------------------------------------------------------------------------ */
+size_t dspark_rnn_verify_workspace_bytes(int R, int K, int V, int r, int N);
+int dspark_rnn_verify(int R, int K, int V, float temperature,
+                      const void* P, int p_dtype, int N,
+                      const int32_t* cu_seqlens,
+                      const void* D, int d_dtype,
+                      const float* O, const void* W2, int r,
+                      const int32_t* x0, const int32_t* x,
+                      const float* q_tok, const float* lse_d,
+                      uint64_t seed, uint64_t step,
+                      int32_t* n_acc_out, int32_t* tok_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Acceptance label of RNN-head drafts: dspark_acceptance_label with
+ * q_{r,k} = softmax((D[r,k] + O[r,k] W2) / T) (DSpark paper sections 3.1 and
+ * 3.2.1).  O [B, K, r] f32 from dspark_rnn_draft; workspace:
+ * dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r) bytes; otherwise as
+ * for dspark_acceptance_label.
+ * ------------------------------------------------------------------------ */
+size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r);
+int dspark_rnn_acceptance_label(int B, int K, int V, float temperature,
+                                const void* P, int p_dtype,
+                                const void* D, int d_dtype,
+                                const float* O, const void* W2, int r,
+                                const int32_t* x0, const int32_t* x,
+                                const float* lse_d, float* c_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Confidence head.  DSpark paper section 3.2.1 (Confidence Head: a linear
  * projection of the backbone hidden state and the Markov embedding of the
  * previous token, then a sigmoid; Post-hoc Calibration: one temperature per

@@ -172,3 +172,61 @@ def test_uniforms_argument_errors(lib):
     assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 0, 1, 0, FAKE, NULL) == -2
     assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 3, FAKE, NULL) == -4
     assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 0, NULL, NULL) == -1
+
+
+def test_rnn_argument_errors(lib):
+    B, K, V, r, d = 4, 7, 1024, 64, 128
+    need = lib.dspark_rnn_draft_workspace_bytes(B, K, V, r, d)
+    assert need >= lib.dspark_markov_draft_workspace_bytes(B, K, V, r) + B * K * 3 * r * 4 + 2 * B * r * 4 + V * r * 2
+    assert lib.dspark_rnn_verify_workspace_bytes(4, K, V, r, 8) >= \
+        lib.dspark_verify_workspace_bytes(4, K, V, r, 8) + V * r * 2
+    assert lib.dspark_rnn_acceptance_label_workspace_bytes(4, K, V, r) >= \
+        lib.dspark_acceptance_label_workspace_bytes(4, K, V, r) + V * r * 2
+    assert need % 256 == 0
+
+    def draft(B=B, K=K, V=V, r=r, d=d, T=1.0, U=FAKE, ud=1, H=FAKE, hd=1, W=FAKE, W1=FAKE, W2=FAKE, x0=FAKE,
+              o=FAKE, ws=FAKE, wsb=WS):
+        return lib.dspark_rnn_draft(B, K, V, r, d, T, U, ud, H, hd, W, W1, W2, x0, 1, 2, FAKE, FAKE, FAKE, o,
+                                    ws, wsb, NULL)
+    assert draft(r=48) == -2          # not a multiple of 32
+    assert draft(r=0) == -2
+    assert draft(r=288) == -2
+    assert draft(d=100) == -2         # not a multiple of 64
+    assert draft(d=0) == -2
+    assert draft(K=17) == -2
+    assert draft(hd=0) == -3          # f32 hidden states are not taken
+    assert draft(ud=2) == -3
+    assert draft(T=-1.0) == -4
+    assert draft(H=NULL) == -1
+    assert draft(W=NULL) == -1
+    assert draft(o=NULL) == -1
+    assert draft(wsb=ctypes.c_size_t(need - 1)) == -5
+    assert draft(ws=ctypes.c_void_p(0x100010)) == -5     # not 256-byte aligned
+    assert draft(W=ctypes.c_void_p(0x100008)) == -4      # not 16-byte aligned
+
+    def verify(R=4, K=7, V=V, T=1.0, N=8, O=FAKE, W2=FAKE, r=r, wsb=WS):
+        return lib.dspark_rnn_verify(R, K, V, T, FAKE, 1, N, FAKE, FAKE, 1, O, W2, r, FAKE, FAKE, FAKE, FAKE, 1, 2,
+                                     FAKE, FAKE, FAKE, wsb, NULL)
+    assert verify(r=40) == -2
+    assert verify(N=3) == -2
+    assert verify(O=NULL) == -1
+    assert verify(W2=NULL) == -1
+    assert verify(O=ctypes.c_void_p(0x100004)) == -4
+    assert verify(wsb=ctypes.c_size_t(16)) == -5
+
+    def label(B=4, K=7, V=V, T=1.0, O=FAKE, r=r, wsb=WS):
+        return lib.dspark_rnn_acceptance_label(B, K, V, T, FAKE, 1, FAKE, 1, O, FAKE, r, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, wsb, NULL)
+    assert label(r=16) == -2
+    assert label(O=NULL) == -1
+    assert label(T=float("inf")) == -4
+    assert label(wsb=ctypes.c_size_t(16)) == -5
+
+
+def test_binding_exports_resolve(lib):
+    """Every name the package exports resolves to a binding function or constant."""
+    import draft_verify_schedule_amd as m
+    for name in m.__all__:
+        assert getattr(m, name) is not None, name
+    for name in declared_functions():
+        assert hasattr(m, name), name

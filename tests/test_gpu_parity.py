@@ -520,3 +520,174 @@ def test_sts_fit_matches_oracle(n_bins):
     np.testing.assert_array_equal(T.cpu().numpy(), Tr.astype(np.float32))
     np.testing.assert_allclose(ece.cpu().numpy(), er, rtol=1e-5, atol=1e-7)
 
+
+
+# ------------------------------------------------------------- RNN head
+def _rnn_inputs(B, K, V, r, d, dtype, seed, scale=3.0, wscale=0.3):
+    U, W1, W2, x0 = _random_draft_inputs(B, K, V, r, dtype, seed, scale, wscale)
+    H, W = wl().rnn_head(B, K, r, d, seed + 1)
+    return U, H, W, W1, W2, x0
+
+
+def _oracle_rnn(U, H, W, W1, W2, x0, T, seed, step=0, request_ids=None):
+    return oracle.rnn_draft_ref(f64(U), f64(H), f64(W), f64(W1), f64(W2).T, x0.cpu().numpy(), T, seed, step,
+                                request_ids)
+
+
+def _compare_rnn(rep, got, ref, bf16_inputs, greedy):
+    x, q, lse, O = got
+    same = compare_draft(rep, x, q, lse, ref, bf16_inputs=bf16_inputs, greedy=greedy)
+    # o_k depends on the tokens before k: compare it where those agree
+    ok = np.ones_like(same)
+    ok[:, 1:] = same[:, :-1]
+    rep.err("O", O[ok], ref["O"][ok])
+    np.testing.assert_allclose(O[ok], ref["O"][ok], rtol=1e-4, atol=2e-5)
+    return same
+
+
+@pytest.mark.parametrize("B,K,V,r,d,dtype,T", [
+    (4, 7, 1024, 32, 64, torch.float32, 1.0),      # the tiny workload's shape
+    (37, 3, 1000, 64, 128, torch.float32, 0.8),    # ragged rows and vocabulary tail
+    (5, 2, 1003, 32, 64, torch.bfloat16, 1.0),     # V not a multiple of 8: scalar path
+    (130, 3, 4096, 256, 256, torch.bfloat16, 1.0), # full rank, a full and a partial row stage
+    (17, 3, 2000, 96, 192, torch.bfloat16, 0.0),   # greedy, r below the padded eight chunks
+])
+def test_rnn_draft_shapes(B, K, V, r, d, dtype, T):
+    _say("rnn draft B=%d K=%d V=%d r=%d d=%d %s T=%g" % (B, K, V, r, d, dtype, T))
+    U, H, W, W1, W2, x0 = _rnn_inputs(B, K, V, r, d, dtype, seed=B * 100 + r)
+    out = ds().dspark_rnn_draft(U.to(DEV), H.to(DEV), W.to(DEV), W1.to(DEV), W2.to(DEV), x0.to(DEV), T, 77, 3)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in out]
+    ref = _oracle_rnn(U, H, W, W1, W2, x0, T, 77, 3)
+    rep = Report("rnn draft")
+    same = _compare_rnn(rep, got, ref, bf16_inputs=(dtype == torch.bfloat16), greedy=(T == 0))
+    rep.check_near_ties()
+    assert same.sum() >= 0.9 * same.size
+    _say(str(rep))
+
+
+def test_rnn_draft_markov_special_case():
+    """W_o = [0 | I | 0]: the RNN head's draft is the Markov head's, against
+    the Markov oracle."""
+    B, K, V, r, d = 9, 5, 2048, 64, 64
+    U, H, W, W1, W2, x0 = _rnn_inputs(B, K, V, r, d, torch.bfloat16, seed=808)
+    W = W.clone()
+    W[2 * r:] = 0
+    W[2 * r:, r:2 * r] = torch.eye(r, dtype=torch.bfloat16)
+    x, q, lse, O = ds().dspark_rnn_draft(U.to(DEV), H.to(DEV), W.to(DEV), W1.to(DEV), W2.to(DEV), x0.to(DEV), 1.0,
+                                         5, 1)
+    torch.cuda.synchronize()
+    ref = _oracle_draft(U, W1, W2, x0, 1.0, 5, 1)
+    rep = Report("rnn as markov")
+    same = compare_draft(rep, x.cpu().numpy(), q.cpu().numpy(), lse.cpu().numpy(), ref, bf16_inputs=True,
+                         greedy=False)
+    rep.check_near_ties()
+    prev = np.concatenate([x0.numpy()[:, None], ref["x"][:, :-1]], axis=1)
+    ok = np.ones_like(same)
+    ok[:, 1:] = same[:, :-1]
+    np.testing.assert_array_equal(O.cpu().numpy()[ok], f64(W1)[prev][ok])
+
+
+def test_rnn_draft_invalid_anchor_flags_request():
+    U, H, W, W1, W2, x0 = _rnn_inputs(4, 3, 256, 32, 64, torch.float32, seed=6)
+    x0[2] = 256
+    x, q, lse, O = ds().dspark_rnn_draft(U.to(DEV), H.to(DEV), W.to(DEV), W1.to(DEV), W2.to(DEV), x0.to(DEV), 1.0,
+                                         3, 0)
+    torch.cuda.synchronize()
+    x, q = x.cpu().numpy(), q.cpu().numpy()
+    assert np.all(x[2] == -1) and np.all(np.isnan(q[2]))
+    ref = _oracle_rnn(U, H, W, W1, W2, x0, 1.0, 3, 0)
+    np.testing.assert_array_equal(x, ref["x"])
+
+
+def _rnn_verify_case(B, K, V, r, d, dtype, T, seed, all_rows=True):
+    """The oracle's RNN draft (tokens, probabilities, output parts) verified on
+    the GPU and by the oracle, the same fp32 output parts on both sides."""
+    g = torch.Generator().manual_seed(seed)
+    U, H, W, W1, W2, x0 = _rnn_inputs(B, K, V, r, d, dtype, seed)
+    t = (0.8 * U.float() + 0.6 * torch.randn((B, K + 1, V), generator=g)[:, :K] * 3).to(dtype)
+    t = torch.cat([t, (torch.randn((B, 1, V), generator=g) * 3).to(dtype)], dim=1).contiguous()
+    d_ref = _oracle_rnn(U, H, W, W1, W2, x0, T, seed, 0)
+    O32 = torch.as_tensor(d_ref["O"], dtype=torch.float32)
+    if all_rows:
+        cu = np.arange(0, B * (K + 1) + 1, K + 1)
+    else:
+        ell = np.random.default_rng(seed).integers(0, K + 1, size=B)
+        cu = np.concatenate([[0], np.cumsum(ell + 1)])
+    cu_t = torch.as_tensor(cu, dtype=torch.int32)
+    P = wl().flat_target_rows(t, cu_t)
+    n_acc, tok = ds().dspark_rnn_verify(P.to(DEV), cu_t.to(DEV), U.to(DEV), O32.to(DEV), W2.to(DEV), x0.to(DEV),
+                                        torch.as_tensor(d_ref["x"], dtype=torch.int32).to(DEV),
+                                        torch.as_tensor(d_ref["q_tok"], dtype=torch.float32).to(DEV),
+                                        torch.as_tensor(d_ref["lse"], dtype=torch.float32).to(DEV), T, seed, 0)
+    torch.cuda.synchronize()
+    ref = oracle.verify_ref(f64(P), cu, f64(U), None, f64(W2).T, x0.numpy(), d_ref["x"], T, seed, 0,
+                            O=O32.double().numpy())
+    return n_acc.cpu().numpy(), tok.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("B,K,V,r,d,dtype,T,all_rows", [
+    (4, 7, 1024, 32, 64, torch.float32, 1.0, True),
+    (4, 7, 1024, 32, 64, torch.float32, 0.0, True),
+    (16, 7, 151936, 256, 256, torch.bfloat16, 1.0, True),   # aligned rows: the streaming residual pass
+    (9, 4, 999, 64, 64, torch.float32, 1.0, False),         # unaligned rows: the generic residual pass
+    (150, 3, 2048, 128, 128, torch.bfloat16, 0.7, False),   # two row stages of corrections
+])
+def test_rnn_verify(B, K, V, r, d, dtype, T, all_rows):
+    _say("rnn verify B=%d K=%d V=%d r=%d %s T=%g" % (B, K, V, r, dtype, T))
+    n_acc, tok, ref = _rnn_verify_case(B, K, V, r, d, dtype, T, seed=B + V, all_rows=all_rows)
+    rep = Report("rnn verify")
+    compare_verify(rep, n_acc, tok, ref)
+    rep.check_near_ties()
+    _say(str(rep) + " mean n_acc %.3f" % n_acc.mean())
+
+
+@pytest.mark.parametrize("B,K,V,r,d,dtype,T", [
+    (4, 7, 1024, 32, 64, torch.float32, 1.0),
+    (4, 7, 1024, 32, 64, torch.float32, 0.0),
+    (3, 4, 999, 64, 64, torch.float32, 0.8),                # generic residual pass
+    (24, 7, 151936, 256, 256, torch.bfloat16, 1.0),         # streaming residual pass
+])
+def test_rnn_label(B, K, V, r, d, dtype, T):
+    _say("rnn label B=%d V=%d T=%g" % (B, V, T))
+    seed = 31 + V
+    g = torch.Generator().manual_seed(seed)
+    U, H, W, W1, W2, x0 = _rnn_inputs(B, K, V, r, d, dtype, seed)
+    P = (0.8 * U.float() + 0.6 * torch.randn((B, K, V), generator=g) * 3).to(dtype).contiguous()
+    d_ref = _oracle_rnn(U, H, W, W1, W2, x0, T, seed, 0)
+    O32 = torch.as_tensor(d_ref["O"], dtype=torch.float32)
+    got = ds().dspark_rnn_acceptance_label(P.to(DEV), U.to(DEV), O32.to(DEV), W2.to(DEV), x0.to(DEV),
+                                           torch.as_tensor(d_ref["x"], dtype=torch.int32).to(DEV),
+                                           torch.as_tensor(d_ref["lse"], dtype=torch.float32).to(DEV), T)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ref = oracle.acceptance_label_ref(f64(P), f64(U), None, f64(W2).T, x0.numpy(), d_ref["x"], T,
+                                      O=O32.double().numpy())
+    _say("rnn label max |diff| %.2e" % np.abs(got - ref).max())
+    if T == 0:
+        np.testing.assert_array_equal(got, ref)
+    elif dtype == torch.bfloat16:
+        np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
+
+
+def test_rnn_draft_full_size_sampled():
+    """The full-step workload with the RNN head (r = 256, d = 4096), the
+    launch configuration the benchmark times: GPU on all 512 requests, the
+    oracle on a sample of them."""
+    w = wl().make("full_step", device=DEV)
+    H, W = wl().rnn_head(w.B, w.K, w.r, 4096, 1005, device=DEV)
+    _say("rnn full size generated")
+    x, q, lse, O = ds().dspark_rnn_draft(w.U, H, W, w.W1, w.W2, w.x0, 1.0, w.rng_seed, 0)
+    torch.cuda.synchronize()
+    _say("rnn full size gpu done")
+    sample = np.array([0, 1, 137, 256, 390, 511])
+    sel = torch.as_tensor(sample, device=DEV)
+    ref = oracle.rnn_draft_ref(f64(w.U[sel]), f64(H[sel]), f64(W), f64(w.W1), f64(w.W2).T,
+                               w.x0.cpu().numpy()[sample], 1.0, w.rng_seed, 0, request_ids=sample)
+    rep = Report("rnn full size sampled")
+    got = [t.cpu().numpy()[sample] for t in (x, q, lse, O)]
+    _compare_rnn(rep, got, ref, bf16_inputs=True, greedy=False)
+    rep.check_near_ties()
+    _say(str(rep))
