@@ -183,6 +183,14 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // base logits and the first block's W2 fragments; the LDS stores of the E
   // stage wait for the W1 rows only.
   __shared__ EStage<KCs, ROWS> st;
+  // Blocks of the pipelined sweep after each wave's first are handed out in
+  // order from this counter, so the four waves of the workgroup finish
+  // within a block of each other (a static split gives some waves one block
+  // more than others).
+  __shared__ int blk_next;
+  if constexpr (FULL) {
+    if (threadIdx.x == 0) blk_next = blk_begin + 4;
+  }
   EStageLoad<KCs> eld;
   if constexpr (KC > 0 && !ROWS) {
     const int32_t* prev = a.prev;
@@ -214,6 +222,8 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     __syncthreads();
   }
 
+  if constexpr (FULL && KC == 0) __syncthreads();  // blk_next
+
   if constexpr (FULL) {
     const uint32_t part_bytes = (uint32_t)((uint64_t)a.B * a.nslices * sizeof(float2));
     const int4v prs = raw_rsrc_words(a.part, part_bytes);
@@ -223,9 +233,16 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     // accumulators (one step before h's epilogue); the freed slot is refilled
     // kPrefetch groups ahead.
     static_assert(kGroupsPerWG % kPrefetch == 0, "ring");
-    for (; blk < blk_stop; blk += 4) {
+    // the next block is claimed at the start of the current one: its base
+    // logits and W2 fragments are requested during the current block
+    auto claim = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&blk_next, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    while (blk < blk_stop) {
       const int cbase = blk * kWaveCols + lane_col;
-      const int nxt = blk + 4;
+      const int nxt = claim();
       const bool has_next = nxt < blk_stop;
       const int e_off = launder(e_lane_offset<KCs, ROWS>(lane));
       auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
@@ -275,10 +292,13 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
         const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
         buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
       }
+      blk = nxt;
     }
   }
 
   // plain path: partial stages, and the column-tail block of a full stage
+  // (claimed by exactly one wave: blk_stop is the only block of the range
+  // past the pipelined ones)
   for (; blk < blk_end; blk += 4) {
     const int cbase = blk * kWaveCols + lane_col;
     float2* part = a.part + blk;
