@@ -551,6 +551,8 @@ def _compare_rnn(rep, got, ref, bf16_inputs, greedy):
     (5, 2, 1003, 32, 64, torch.bfloat16, 1.0),     # V not a multiple of 8: scalar path
     (130, 3, 4096, 256, 256, torch.bfloat16, 1.0), # full rank, a full and a partial row stage
     (17, 3, 2000, 96, 192, torch.bfloat16, 0.0),   # greedy, r below the padded eight chunks
+    (1, 1, 7, 32, 64, torch.float32, 1.0),         # one request, one position, V below one slice
+    (3, 16, 300, 64, 64, torch.float32, 0.5),      # the largest K: sixteen state updates
 ])
 def test_rnn_draft_shapes(B, K, V, r, d, dtype, T):
     _say("rnn draft B=%d K=%d V=%d r=%d d=%d %s T=%g" % (B, K, V, r, d, dtype, T))
