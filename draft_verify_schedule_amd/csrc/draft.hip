@@ -25,7 +25,8 @@
 
 namespace dspark {
 
-constexpr int kPersistentWGs = 512;  // 2 per CU on 256 CUs
+constexpr int kPersistentWGs = 256;  // one per CU on 256 CUs
+constexpr int kDraftWaves = 8;       // waves per draft workgroup: two per SIMD, one E stage per CU
 
 struct DraftArgs {
   const void* U;           // [B, K, V]
@@ -141,10 +142,14 @@ struct UAccess<UT, false> {
   }
 };
 
-// Persistent workgroups: 4 waves, 128 rows (8 MFMA groups of 16), and a
-// contiguous range of 64-column blocks.  The W1 rows of the 128 requests are
-// staged in LDS once; each wave then sweeps the blocks w, w+4, ... of the
-// range, holding one block's W2 fragments in registers for all 8 groups.
+// Persistent workgroups, one per CU: 8 waves (two per SIMD), 128 rows (8
+// MFMA groups of 16), and a contiguous range of 64-column blocks.  The W1
+// rows of the 128 requests are staged in LDS once (by waves 0..3) and shared
+// by all 8 waves; each wave sweeps blocks of the range (its first by index,
+// the rest claimed in order), holding one block's W2 fragments in registers
+// for all 8 groups.  One workgroup per CU rather than two of 4 waves: the CU
+// holds one E stage, so the split stages of the RNN head (133 KB) also run
+// two waves per SIMD.
 //
 // FULL (a stage of 128 live rows, 16-byte aligned rows): the complete blocks
 // are swept by a software pipeline with no branches: several groups of base
@@ -157,7 +162,7 @@ struct UAccess<UT, false> {
 // ROWS: the bias inputs are the fp32 rows a.O (RNN head) instead of gathered
 // W1 rows.
 template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL, bool ROWS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kDraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   static_assert(!FULL || VEC, "the pipelined sweep reads through buffer resources");
   constexpr int KCs = KC > 0 ? KC : 1;
@@ -189,13 +194,13 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // more than others).
   __shared__ int blk_next;
   if constexpr (FULL) {
-    if (threadIdx.x == 0) blk_next = blk_begin + 4;
+    if (threadIdx.x == 0) blk_next = blk_begin + kDraftWaves;
   }
   EStageLoad<KCs> eld;
   if constexpr (KC > 0 && !ROWS) {
     const int32_t* prev = a.prev;
     const int stride = a.prev_stride;
-    eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
+    if (wave < 4) eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
   }
 
   UAccess<UT, VEC> ua;
@@ -215,9 +220,9 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     if constexpr (FULL) wf.load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
     if constexpr (ROWS) {
       const int K = a.K, k = a.k;
-      stage_rows<KC>(st, a.O, a.r, row0, a.B, [&](int g) { return g * K + k - 1; });
+      if (wave < 4) stage_rows<KC>(st, a.O, a.r, row0, a.B, [&](int g) { return g * K + k - 1; });
     } else {
-      eld.store(st, a.r);
+      if (wave < 4) eld.store(st, a.r);
     }
     __syncthreads();
   }
@@ -299,7 +304,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // plain path: partial stages, and the column-tail block of a full stage
   // (claimed by exactly one wave: blk_stop is the only block of the range
   // past the pipelined ones)
-  for (; blk < blk_end; blk += 4) {
+  for (; blk < blk_end; blk += kDraftWaves) {
     const int cbase = blk * kWaveCols + lane_col;
     float2* part = a.part + blk;
     if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
@@ -540,13 +545,13 @@ static int launch_partials(const DraftArgs& a, hipStream_t stream) {
   if constexpr (VEC) {
     if (full > 0) {
       const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true, ROWS>,
-                                   dim3(xcd_grid(a.ncol_tiles, full)), dim3(256), stream, a, 0, full);
+                                   dim3(xcd_grid(a.ncol_tiles, full)), dim3(kDraftWaves * 64), stream, a, 0, full);
       if (rc) return rc;
     }
   }
   if (partial > 0) {
     return launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, false, ROWS>,
-                         dim3(xcd_grid(a.ncol_tiles, partial)), dim3(256), stream, a, full, partial);
+                         dim3(xcd_grid(a.ncol_tiles, partial)), dim3(kDraftWaves * 64), stream, a, full, partial);
   }
   return 0;
 }
