@@ -34,6 +34,7 @@ namespace dspark {
 constexpr int kRowChunk = 8192;   // columns per rowstats workgroup (2048 per wave)
 constexpr int kRowSlice = 256;    // columns per target-row partial
 constexpr int kRowstatsWGs = 2048;  // persistent rowstats grid: 8 workgroups per CU
+constexpr int kMaxPositions = 16;   // draft positions per request (the ABI's limit on K)
 
 struct VerifyArgs {
   int R, K, V, N, r;
@@ -307,6 +308,53 @@ __device__ __forceinline__ int owner_of(const int32_t* cu, int R, int i) {
   return lo;
 }
 
+// The same search by a whole wave in two rounds of loads (R <= 4096): 64
+// probes at stride ceil(R / 64) bracket i, then up to 64 probes inside the
+// bracket.  For non-decreasing cu it returns what owner_of returns.
+__device__ __forceinline__ int owner_of_wave(const int32_t* cu, int R, int i) {
+  if (R > 64 * 64) return owner_of(cu, R, i);
+  const int lane = threadIdx.x & 63;
+  const int step = (R + 63) / 64;
+  const int p1 = lane * step;
+  const bool in1 = p1 < R && cu[min(p1, R - 1)] <= i;
+  const unsigned long long m1 = __ballot(in1);
+  const int lo = m1 ? (63 - __clzll((long long)m1)) * step : 0;
+  const int p2 = lo + lane;
+  const bool in2 = lane < step && p2 < R && cu[min(p2, R - 1)] <= i;
+  const unsigned long long m2 = __ballot(in2);
+  return m2 ? lo + 63 - __clzll((long long)m2) : lo;
+}
+
+// Merge of one row's slice partials by a wave: lane l takes slices l, l + 64,
+// ... in that order (all loads requested together when the row has at most
+// 64 * kMergePer slices), then a butterfly over the lanes.
+constexpr int kMergePer = 16;
+template <bool GREEDY>
+__device__ __forceinline__ void merge_row(const float2* __restrict__ part, int ns, float& m, float& s, int& idx) {
+  const int lane = threadIdx.x & 63;
+  m = -INFINITY;
+  s = 0.f;
+  idx = -1;
+  if (ns <= 64 * kMergePer) {
+    float2 pv[kMergePer];
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) pv[j] = (lane + 64 * j < ns) ? part[lane + 64 * j] : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+      if (lane + 64 * j < ns) {
+        if constexpr (GREEDY) merge_argmax(m, idx, pv[j].x, __float_as_int(pv[j].y));
+        else merge_ms(m, s, pv[j].x, pv[j].y);
+      }
+    }
+  } else {
+    for (int k = lane; k < ns; k += 64) {
+      const float2 p = part[k];
+      if constexpr (GREEDY) merge_argmax(m, idx, p.x, __float_as_int(p.y));
+      else merge_ms(m, s, p.x, p.y);
+    }
+  }
+}
+
 template <typename PT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
@@ -314,13 +362,9 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.rej_count = 0;  // filled by the decide kernel
   if (i >= a.N) return;
   const float2* part = a.ppart + (size_t)i * a.nsP;
-  float m = -INFINITY, s = 0.f;
-  int idx = -1;
-  for (int k = lane; k < a.nsP; k += 64) {
-    const float2 p = part[k];
-    if constexpr (GREEDY) merge_argmax(m, idx, p.x, __float_as_int(p.y));
-    else merge_ms(m, s, p.x, p.y);
-  }
+  float m, s;
+  int idx;
+  merge_row<GREEDY>(part, a.nsP, m, s, idx);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off, 64);
@@ -332,10 +376,10 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
       merge_ms(m, s, m2, s2);
     }
   }
+  const int r = owner_of_wave(a.cu, a.R, i);
   if (lane != 0) return;
   a.rowms[i] = GREEDY ? make_float2(m, __int_as_float(idx)) : make_float2(m, s);
 
-  const int r = owner_of(a.cu, a.R, i);
   const int c0 = a.cu[r], c1 = a.cu[r + 1];
   if (!(c0 >= 0 && c0 <= i && i < c1 && c1 <= a.N && c1 - c0 <= a.K + 1)) {
     a.flag[i] = 2;
@@ -375,9 +419,18 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
   bool ok = c0 >= 0 && c1 > c0 && c1 <= a.N && c1 - c0 <= a.K + 1;
   int n = 0, L = 0;
   if (ok) {
-    L = c1 - c0 - 1;
-    for (int j = 0; j <= L; ++j)
-      if (a.flag[c0 + j] == 2) ok = false;
+    L = c1 - c0 - 1;  // <= K <= kMaxPositions
+    // the request's flags, loaded together
+    int f[kMaxPositions + 1];
+#pragma unroll
+    for (int j = 0; j <= kMaxPositions; ++j) f[j] = (j <= L) ? a.flag[c0 + j] : 1;
+    bool run = true;  // still in the leading run of accepted drafts
+#pragma unroll
+    for (int j = 0; j <= kMaxPositions; ++j) {
+      if (f[j] == 2) ok = false;
+      if (j < L && run && f[j] == 1) ++n;
+      else run = false;
+    }
     if (!GREEDY && a.r > 0 && (a.x0[r] < 0 || a.x0[r] >= a.V)) ok = false;
   }
   if (!ok) {
@@ -386,7 +439,6 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
     a.tok_out[r] = -1;
     return;
   }
-  while (n < L && a.flag[c0 + n] == 1) ++n;
   const int mode = (n < L) ? 1 : 0;  // 1: correction from the residual, 0: bonus
   a.info[r] = make_int4(mode, c0 + n, n + 1, n);
   if (!GREEDY && mode == 1) a.rej_list[atomicAdd(a.rej_count, 1)] = r;
@@ -666,6 +718,46 @@ struct SliceHit {
   double before;
 };
 
+// find_slice over weights held in registers: lane l's run is w[0..cnt) for
+// slices s_begin.. (fp32 values, summed in fp64 in slice order).  Every lane
+// walks its own run without branches; the owner's result is broadcast.
+template <int N>
+__device__ __forceinline__ SliceHit find_slice_regs(int ns, double target, double incl, double local, int s_begin,
+                                                    int cnt, const float (&w)[N]) {
+  int owner = wave_first_lane(incl > target);
+  if (owner < 0) {
+    const unsigned long long m = __ballot(local > 0.0);
+    owner = m ? 63 - __clzll((long long)m) : 0;
+  }
+  double acc = incl - local;
+  int s_star = -1, last = -1;
+  double before = 0.0, last_before = acc;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double wi = i < cnt ? (double)w[i] : 0.0;
+    if (wi > 0.0 && s_star < 0) {
+      last = s_begin + i;
+      last_before = acc;
+      if (acc + wi > target) {
+        s_star = s_begin + i;
+        before = acc;
+      }
+    }
+    acc += wi;
+  }
+  if (s_star < 0) {
+    s_star = last;
+    before = last_before;
+  }
+  SliceHit h;
+  h.slice = __shfl(s_star, owner, 64);
+  h.before = __shfl(before, owner, 64);
+  if (h.slice < 0 || h.slice >= ns) h.slice = 0;
+  return h;
+}
+
+constexpr int kSamPer = 40;  // slices per lane held in registers by the sample kernel
+
 template <typename WeightFn>
 __device__ __forceinline__ SliceHit find_slice(int ns, double target, double incl, double local, int s_begin,
                                                int s_end, WeightFn weight) {
@@ -725,13 +817,23 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     const int ns = a.ns64;
     const int per = (ns + 63) / 64;
     const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
+    const bool regs = per <= kSamPer;
+    float wv[kSamPer];
     double local = 0.0;
-    for (int s = s_begin; s < s_end; ++s) local += (double)rp[s];
+    if (regs) {
+#pragma unroll
+      for (int i = 0; i < kSamPer; ++i) wv[i] = (s_begin + i < s_end) ? rp[s_begin + i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kSamPer; ++i) local += (double)wv[i];
+    } else {
+      for (int s = s_begin; s < s_end; ++s) local += (double)rp[s];
+    }
     const double incl = wave_inclusive_scan(local);
     const double Z = __shfl(incl, 63, 64);
     if (Z > 0.0 && Z <= 2.0) {
       const double target = (double)u * Z;
-      const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return (double)rp[s]; });
+      const SliceHit h = regs ? find_slice_regs(ns, target, incl, local, s_begin, s_end - s_begin, wv)
+                              : find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return (double)rp[s]; });
       const int col = h.slice * kWaveCols + lane;
       float rho = 0.f;
       if (col < a.V) {
@@ -761,21 +863,40 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   // bonus (or fallback): target partials per 256-column slice
   const float2* pp = a.ppart + (size_t)in.y * a.nsP;
   const int ns = a.nsP;
+  const int per = (ns + 63) / 64;
+  const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
+  const bool regs = per <= kSamPer;
+  float2 pv[kSamPer];
   float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, pp[s].x);
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kSamPer; ++i) pv[i] = (s_begin + i < s_end) ? pp[s_begin + i] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int i = 0; i < kSamPer; ++i) M = fmaxf(M, pv[i].x);
+  } else {
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, pp[s].x);
+  }
   M = wave_max(M);
   auto weight = [&](int s) {
     const float2 p = pp[s];
     return (p.x == -INFINITY) ? 0.0 : (double)(p.y * fast_exp2(p.x - M));
   };
-  const int per = (ns + 63) / 64;
-  const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
   double local = 0.0;
-  for (int s = s_begin; s < s_end; ++s) local += weight(s);
+  float wv[kSamPer];
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kSamPer; ++i) {
+      wv[i] = (pv[i].x == -INFINITY) ? 0.f : pv[i].y * fast_exp2(pv[i].x - M);
+      local += (double)wv[i];
+    }
+  } else {
+    for (int s = s_begin; s < s_end; ++s) local += weight(s);
+  }
   const double incl = wave_inclusive_scan(local);
   const double S = __shfl(incl, 63, 64);
   const double target = (double)u * S;
-  const SliceHit h = find_slice(ns, target, incl, local, s_begin, s_end, weight);
+  const SliceHit h = regs ? find_slice_regs(ns, target, incl, local, s_begin, s_end - s_begin, wv)
+                          : find_slice(ns, target, incl, local, s_begin, s_end, weight);
   const float m_s = pp[h.slice].x;
   const float t_in = (float)((target - h.before) / (double)fast_exp2(m_s - M));
   // 256 columns, 4 consecutive per lane
@@ -858,13 +979,9 @@ __global__ __launch_bounds__(256) void label_merge_kernel(VerifyArgs a) {
   const int i = blockIdx.x * 4 + wave_index();
   if (i >= a.N) return;
   const float2* part = a.ppart + (size_t)i * a.nsP;
-  float m = -INFINITY, s = 0.f;
-  int idx = -1;
-  for (int k = lane; k < a.nsP; k += 64) {
-    const float2 p = part[k];
-    if constexpr (GREEDY) merge_argmax(m, idx, p.x, __float_as_int(p.y));
-    else merge_ms(m, s, p.x, p.y);
-  }
+  float m, s;
+  int idx;
+  merge_row<GREEDY>(part, a.nsP, m, s, idx);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off, 64);
