@@ -101,6 +101,7 @@ def test_draft_tiny_workload(T):
     (1, 1, 7, 0, torch.float32, 1.0),          # V smaller than a wave, no Markov head
     (17, 3, 2000, 64, torch.bfloat16, 0.0),    # greedy with bf16 ties
     (9, 2, 520, 0, torch.bfloat16, 0.0),       # greedy, no bias, ragged tail
+    (2, 16, 300, 32, torch.float32, 1.0),      # the largest K
 ])
 def test_draft_shapes(B, K, V, r, dtype, T):
     _say("draft shape B=%d K=%d V=%d r=%d %s T=%g" % (B, K, V, r, dtype, T))
@@ -693,3 +694,31 @@ def test_rnn_draft_full_size_sampled():
     _compare_rnn(rep, got, ref, bf16_inputs=True, greedy=False)
     rep.check_near_ties()
     _say(str(rep))
+
+
+def test_verify_largest_k():
+    """K = 16 (the ABI's limit): every position verified, and a ragged
+    schedule; the decide kernel's fixed flag window covers all 17 rows."""
+    g = torch.Generator().manual_seed(1616)
+    B, K, V, r = 6, 16, 500, 16
+    U = torch.randn((B, K, V), generator=g) * 2
+    t = (0.9 * torch.cat([U, torch.randn((B, 1, V), generator=g) * 2], dim=1)
+         + 0.4 * torch.randn((B, K + 1, V), generator=g)).contiguous()
+    W1 = (torch.randn((V, r), generator=g) * 0.1).to(torch.bfloat16)
+    W2 = (torch.randn((V, r), generator=g) * 0.1).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, dtype=torch.int32)
+    d = oracle.draft_ref(f64(U), f64(W1), f64(W2).T, x0.numpy(), 1.0, 77, 0)
+    for ell in (np.full(B, K), np.array([16, 0, 7, 15, 1, 16])):
+        cu = np.concatenate([[0], np.cumsum(ell + 1)])
+        cu_t = torch.as_tensor(cu, dtype=torch.int32)
+        P = wl().flat_target_rows(t, cu_t)
+        n_acc, tok = ds().dspark_verify(P.to(DEV), cu_t.to(DEV), U.to(DEV), W1.to(DEV), W2.to(DEV), x0.to(DEV),
+                                        torch.as_tensor(d["x"], dtype=torch.int32).to(DEV),
+                                        torch.as_tensor(d["q_tok"], dtype=torch.float32).to(DEV),
+                                        torch.as_tensor(d["lse"], dtype=torch.float32).to(DEV), 1.0, 77, 0)
+        torch.cuda.synchronize()
+        ref = oracle.verify_ref(f64(P), cu, f64(U), f64(W1), f64(W2).T, x0.numpy(), d["x"], 1.0, 77, 0)
+        rep = Report("verify K=16")
+        compare_verify(rep, n_acc.cpu().numpy(), tok.cpu().numpy(), ref)
+        rep.check_near_ties()
+        _say(str(rep) + " n_acc %s" % n_acc.cpu().numpy().tolist())
