@@ -134,11 +134,12 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
                         const void* W1, const void* W2, const int32_t* x0, uint64_t seed, uint64_t step,
                         int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
   if (!workspace || workspace_bytes < dspark::draft_workspace_bytes(B, K, V)) return DSPARK_E_WORKSPACE;
@@ -161,7 +162,7 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
                      const void* H, int h_dtype, const void* W, const void* W1, const void* W2, const int32_t* x0,
                      uint64_t seed, uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, float* o_out,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (d < 64 || d % 64 != 0) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype) || h_dtype != DSPARK_BF16) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
@@ -169,6 +170,7 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   if ((uint64_t)B * K * d * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)3 * r * (2 * r + d) * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !H || !W || !W1 || !W2 || !x0 || !x_out || !q_tok_out || !lse_out || !o_out) return DSPARK_E_NULL;
   const size_t need = dspark_rnn_draft_workspace_bytes(B, K, V, r, d);
   if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
@@ -202,11 +204,12 @@ size_t dspark_schedule_workspace_bytes(int R, int K) {
 int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len, int mode, int capacity,
                     float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out, int32_t* n_admitted_out,
                     double* theta_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
+  if (R < 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
   if (mode < DSPARK_SCHED_EARLY_STOP || mode > DSPARK_SCHED_TOPK) return DSPARK_E_RANGE;
   if (capacity < 0) return DSPARK_E_RANGE;
   if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
-  if (!c || !sps || !a_out || !ell_out || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
+  if (!sps || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
+  if (R > 0 && (!c || !a_out || !ell_out)) return DSPARK_E_NULL;
   if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
   return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_seqlens_out,
                                          n_admitted_out, theta_out, workspace,
@@ -216,10 +219,10 @@ int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len
 int dspark_schedule_async(int R, int K, const float* c, const double* sps, int sps_len, const int32_t* capacity,
                           float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out, int32_t* n_admitted_out,
                           double* theta_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
+  if (R < 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
   if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
-  if (!c || !sps || !capacity || !a_out || !ell_out || !cu_seqlens_out || !n_admitted_out || !theta_out)
-    return DSPARK_E_NULL;
+  if (!sps || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
+  if (R > 0 && (!c || !capacity || !a_out || !ell_out)) return DSPARK_E_NULL;
   if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
   return hip_status(dspark::run_schedule(R, K, c, sps, DSPARK_SCHED_TOPK, 0, capacity, a_out, ell_out,
                                          cu_seqlens_out, n_admitted_out, theta_out, workspace,
@@ -238,13 +241,14 @@ int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_d
                   const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
                   uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (R < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (R == 0) return DSPARK_OK;  // empty batch
   if (!P || !cu_seqlens || !D || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
   if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
@@ -269,13 +273,14 @@ int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int
                       const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
                       uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (R < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (R == 0) return DSPARK_OK;  // empty batch
   if (!P || !cu_seqlens || !D || !O || !W2 || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
   if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
   const size_t base = dspark::verify_workspace_bytes(R, V, N);
@@ -300,12 +305,13 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
                             int d_dtype, const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x,
                             const float* lse_d, float* c_out, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (B == 0) return DSPARK_OK;  // empty batch
   if (!P || !D || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
@@ -327,12 +333,13 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
                                 int d_dtype, const float* O, const void* W2, int r, const int32_t* x0,
                                 const int32_t* x, const float* lse_d, float* c_out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
+  if (B == 0) return DSPARK_OK;  // empty batch
   if (!P || !D || !O || !W2 || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
   const size_t base = (dspark::label_workspace_bytes(B, K, V) + 255) / 256 * 256;
@@ -349,12 +356,13 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
 int dspark_confidence_head(int B, int K, int V, int d, int r, const void* H, int h_dtype, const float* w_h,
                            const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
                            const float* sts_temperature, float* c_out, float* logit_out, void* stream) {
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || d <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || d <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(h_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * d * dtype_bytes(h_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!std::isfinite(bias)) return DSPARK_E_RANGE;
+  if (B == 0) return DSPARK_OK;  // empty batch
   if (!H || !w_h || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !w_e)) return DSPARK_E_NULL;
-  if (!std::isfinite(bias)) return DSPARK_E_RANGE;
   return hip_status(dspark::run_confidence_head(B, K, d, r, V, H, h_dtype == DSPARK_BF16, w_h, w_e, bias, W1, x0,
                                                 x, sts_temperature, c_out, logit_out,
                                                 reinterpret_cast<hipStream_t>(stream)));
@@ -378,8 +386,9 @@ int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived, i
 }
 
 int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, void* stream) {
-  if (n <= 0) return DSPARK_E_SHAPE;
+  if (n < 0) return DSPARK_E_SHAPE;
   if (position < 0 || position >= (1 << 30) || purpose < 0 || purpose > 2) return DSPARK_E_RANGE;
+  if (n == 0) return DSPARK_OK;
   if (!out) return DSPARK_E_NULL;
   return hip_status(dspark::run_uniforms(seed, step, n, position, purpose, out, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -327,9 +327,22 @@ size_t schedule_workspace_bytes(int R, int K) {
   return (((size_t)R * K * sizeof(uint64_t)) + 255) & ~(size_t)255;
 }
 
+// An empty batch (R = 0): no candidates, B = tau = 0, so the layout is
+// cu_seqlens = [0], nothing admitted, and Theta = 0 * SPS(0).
+__global__ void schedule_empty_kernel(const double* __restrict__ sps, int32_t* __restrict__ cu_out,
+                                      int32_t* __restrict__ n_out, double* __restrict__ theta_out) {
+  if (threadIdx.x == 0) {
+    cu_out[0] = 0;
+    n_out[0] = 0;
+    theta_out[0] = 0.0 * sps[0];
+  }
+}
+
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
                  double* theta_out, void* workspace, hipStream_t stream) {
+  if (R == 0)
+    return launch_kernel("schedule", schedule_empty_kernel, dim3(1), dim3(64), stream, sps, cu_out, n_out, theta_out);
   ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out, capacity_dev};
   uint64_t* sorted = reinterpret_cast<uint64_t*>(workspace);
   const int n = R * K;

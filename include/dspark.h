@@ -45,6 +45,11 @@
  *   - Each logit buffer (U, P, D) and each Markov factor must be smaller than
  *     4 GiB (kernels address them with 32-bit byte offsets); larger inputs
  *     return DSPARK_E_SHAPE.
+ *   - Empty batches: a call with no requests (B or R == 0; n == 0 for
+ *     dspark_uniforms) and otherwise valid sizes and scalars returns DSPARK_OK
+ *     without enqueuing anything; its array and workspace pointers are not
+ *     read and may be NULL.  dspark_schedule and dspark_schedule_async are the
+ *     exception: with R == 0 they still write the empty layout (see there).
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -99,7 +104,7 @@ int dspark_version(void);
  *   lse_out    log sum_v exp(z_k(v)) in natural-log units (when T == 0: the
  *              largest biased logit).
  * Inputs: U [B, K, V] (u_dtype f32 or bf16); W1 [V, r] and W2 (column-major
- * r x V) bf16; x0 [B] int32.  Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
+ * r x V) bf16; x0 [B] int32.  Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
  * r as in the header comment, U smaller than 4 GiB.
  * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
  * that request's remaining positions x = -1, q_tok = lse = NaN.
@@ -128,7 +133,10 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature,
  * Outputs: a_out [R, K] f32; ell_out [R] int32 (verify lengths l*_r);
  * cu_seqlens_out [R + 1] int32 (prefix sums of 1 + l*_r, the flattened verify
  * layout); n_admitted_out [1] int32; theta_out [1] f64 (Theta of the choice).
- * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R * K <= DSPARK_MAX_CANDIDATES.
+ * Limits: 0 <= R, 1 <= K <= DSPARK_MAX_K, R * K <= DSPARK_MAX_CANDIDATES.
+ * R == 0 (empty batch: nothing to admit, B = tau = 0): cu_seqlens_out[0] = 0,
+ * n_admitted = 0, theta = 0 * sps[0]; c, a_out, ell_out may be NULL and no
+ * workspace is needed.
  * Data errors: any c outside [0, 1] or NaN gives ell = 0, cu_seqlens[r] = r,
  * n_admitted = -1, theta = NaN (a valid no-draft layout).
  * Workspace: dspark_schedule_workspace_bytes(R, K) bytes (the sorted
@@ -158,7 +166,8 @@ int dspark_schedule(int R, int K, const float* c,
  * first min(max(capacity, 0), number of candidates) candidates of the
  * current a are admitted; a negative capacity (e.g. -1 from a call that saw
  * invalid confidences) admits nothing.  All other arguments, outputs, limits,
- * data errors and the workspace are those of dspark_schedule.
+ * data errors and the workspace are those of dspark_schedule (capacity may
+ * be NULL when R == 0).
  * ------------------------------------------------------------------------ */
 int dspark_schedule_async(int R, int K, const float* c,
                           const double* sps, int sps_len,
@@ -189,7 +198,7 @@ int dspark_schedule_async(int R, int K, const float* c,
  * dspark_markov_draft (q_tok, lse_d unused when T == 0).
  * Outputs: n_acc_out [R] accepted drafts; tok_out [R] the correction or bonus
  * token (emitted sequence: x_1..x_{n_acc}, tok).
- * Limits: 1 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), P and D each
+ * Limits: 0 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), P and D each
  * smaller than 4 GiB.
  * Data errors: a request whose cu_seqlens slice is inconsistent (length < 1 or
  * > K + 1, or outside [0, N]) or whose tokens are outside [0, V) gets
@@ -225,7 +234,7 @@ int dspark_verify(int R, int K, int V, float temperature,
  * the draft; x [B, K] the drafted tokens and lse_d [B, K] their
  * log-normalisers, as returned by dspark_markov_draft (lse_d unused when
  * T == 0).  Output: c_out [B, K] f32.
- * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, P and D each smaller than 4 GiB.
+ * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, P and D each smaller than 4 GiB.
  * Data errors: a position whose previous or own token is outside [0, V) gets
  * NaN.  Workspace: dspark_acceptance_label_workspace_bytes(B, K, V, r) bytes,
  * 256-byte aligned, contents need not be initialised.
@@ -263,7 +272,7 @@ int dspark_acceptance_label(int B, int K, int V, float temperature,
  * The bias o_k W2 runs on the fp16 MFMA with o_k split into hi + lo fp16
  * parts and W2 converted to fp16 (relative error 2^-22 on o_k): entries of
  * o_k and W2 must be smaller than 2^15 in magnitude.
- * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V, r a multiple of 32 in
+ * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V, r a multiple of 32 in
  * [32, DSPARK_MAX_RANK], d a positive multiple of 64; U, H, W, W1 each smaller
  * than 4 GiB; H, W, W1, W2, o_out 16-byte aligned (else DSPARK_E_RANGE).
  * Workspace: dspark_rnn_draft_workspace_bytes(B, K, V, r, d) bytes.
@@ -332,7 +341,7 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature,
  * tokens; x[r, K-1] is not used); sts_temperature [K] f32 from dspark_sts_fit,
  * or NULL for T_k = 1.  Outputs: c_out [B, K] f32, the scheduler's c;
  * logit_out [B, K] f32 (z, for calibration data) or NULL.
- * Limits: 1 <= B, 1 <= K <= DSPARK_MAX_K, d >= 1, H smaller than 4 GiB.
+ * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, d >= 1, H smaller than 4 GiB.
  * Data errors: a previous token outside [0, V) gives NaN.  No workspace.
  * ------------------------------------------------------------------------ */
 int dspark_confidence_head(int B, int K, int V, int d, int r,
@@ -370,7 +379,7 @@ int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived,
 /* ------------------------------------------------------------------------ *
  * The per-decision uniforms themselves (the seeded counter-based stream the
  * three calls consume): out[i] = u(seed, step, request i, position, purpose)
- * for i in [0, n).  Limits: n >= 1, 0 <= position < 2^30, purpose in {0, 1, 2}.
+ * for i in [0, n).  Limits: n >= 0, 0 <= position < 2^30, purpose in {0, 1, 2}.
  * ------------------------------------------------------------------------ */
 int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out,
                     void* stream);

@@ -60,8 +60,8 @@ WS = ctypes.c_size_t(1 << 30)
 
 
 def test_schedule_argument_errors(lib):
-    # R <= 0, K too large, too many candidates
-    assert lib.dspark_schedule(0, 7, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
+    # R < 0, K too large, too many candidates
+    assert lib.dspark_schedule(-1, 7, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
     assert lib.dspark_schedule(4, 17, FAKE, FAKE, 100, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
     assert lib.dspark_schedule(4096, 7, FAKE, FAKE, 10 ** 6, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -2
     # SPS table too short, bad mode, negative capacity
@@ -79,7 +79,7 @@ def test_schedule_argument_errors(lib):
 def test_schedule_async_argument_errors(lib):
     def call(R=4, K=7, c=FAKE, sps=FAKE, n=33, cap=FAKE, out=FAKE, ws=FAKE, wsb=WS):
         return lib.dspark_schedule_async(R, K, c, sps, n, cap, out, out, out, out, out, ws, wsb, NULL)
-    assert call(R=0) == -2
+    assert call(R=-1) == -2
     assert call(K=17) == -2
     assert call(n=32) == -4
     assert call(cap=NULL) == -1
@@ -94,7 +94,7 @@ def test_acceptance_label_argument_errors(lib):
     def call(B=4, K=7, V=1024, r=16, T=1.0, P=FAKE, pt=0, D=FAKE, dt=0, W=FAKE, x0=FAKE, x=FAKE, lse=FAKE,
              out=FAKE, wsp=FAKE, wsb=WS):
         return lib.dspark_acceptance_label(B, K, V, f(T), P, pt, D, dt, W, W, r, x0, x, lse, out, wsp, wsb, NULL)
-    assert call(B=0) == -2
+    assert call(B=-1) == -2
     assert call(K=17) == -2
     assert call(r=12) == -2
     assert call(pt=7) == -3
@@ -111,7 +111,7 @@ def test_confidence_and_sts_argument_errors(lib):
 
     def head(B=4, K=7, V=100, d=32, r=8, H=FAKE, ht=0, wh=FAKE, we=FAKE, b=0.0, W1=FAKE, x0=FAKE, x=FAKE, out=FAKE):
         return lib.dspark_confidence_head(B, K, V, d, r, H, ht, wh, we, f(b), W1, x0, x, NULL, out, NULL, NULL)
-    assert head(B=0) == -2
+    assert head(B=-1) == -2
     assert head(d=0) == -2
     assert head(r=12) == -2
     assert head(ht=5) == -3
@@ -169,7 +169,7 @@ def test_verify_argument_errors(lib):
 
 
 def test_uniforms_argument_errors(lib):
-    assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 0, 1, 0, FAKE, NULL) == -2
+    assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), -1, 1, 0, FAKE, NULL) == -2
     assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 3, FAKE, NULL) == -4
     assert lib.dspark_uniforms(ctypes.c_uint64(1), ctypes.c_uint64(0), 10, 1, 0, NULL, NULL) == -1
 
@@ -221,6 +221,47 @@ def test_rnn_argument_errors(lib):
     assert label(O=NULL) == -1
     assert label(T=float("inf")) == -4
     assert label(wsb=ctypes.c_size_t(16)) == -5
+
+
+def test_empty_batches_are_noops(lib):
+    """No requests: every call returns DSPARK_OK without enqueuing anything
+    and without reading its (NULL) array and workspace pointers; the shape and
+    scalar checks still apply.  The schedule calls are the exception: with
+    R = 0 they write the empty layout, so they still need those outputs."""
+    f = ctypes.c_float
+    u64 = ctypes.c_uint64
+    Z = ctypes.c_size_t(0)
+    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+                                   NULL, NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(-1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+                                   NULL, NULL, NULL, NULL, Z, NULL) == -4
+    assert lib.dspark_markov_draft(0, 17, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+                                   NULL, NULL, NULL, NULL, Z, NULL) == -2
+    assert lib.dspark_rnn_draft(0, 7, 1024, 64, 128, f(1.0), NULL, 1, NULL, 1, NULL, NULL, NULL, NULL, u64(1),
+                                u64(0), NULL, NULL, NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL, NULL,
+                             u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 1, NULL, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL, NULL,
+                             u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == -2     # rows without requests
+    assert lib.dspark_rnn_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, 64, NULL, NULL, NULL,
+                                 NULL, u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL,
+                                       NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_rnn_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, 64, NULL, NULL, NULL,
+                                           NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_confidence_head(0, 7, 100, 32, 8, NULL, 0, NULL, NULL, f(0.0), NULL, NULL, NULL, NULL, NULL,
+                                      NULL, NULL) == 0
+    assert lib.dspark_uniforms(u64(1), u64(0), 0, 1, 0, NULL, NULL) == 0
+    # the schedule writes cu_seqlens[0], n_admitted and theta even for R = 0
+    assert lib.dspark_schedule(0, 7, NULL, FAKE, 1, 0, 0, NULL, NULL, NULL, FAKE, FAKE, NULL, Z, NULL) == -1
+    assert lib.dspark_schedule(0, 7, NULL, NULL, 1, 0, 0, NULL, NULL, FAKE, FAKE, FAKE, NULL, Z, NULL) == -1
+    assert lib.dspark_schedule(0, 7, NULL, FAKE, 0, 0, 0, NULL, NULL, FAKE, FAKE, FAKE, NULL, Z, NULL) == -4
+    assert lib.dspark_schedule_async(0, 7, NULL, FAKE, 1, NULL, NULL, NULL, FAKE, NULL, FAKE, NULL, Z, NULL) == -1
+    for q in (lib.dspark_markov_draft_workspace_bytes(0, 7, 1024, 16), lib.dspark_schedule_workspace_bytes(0, 7),
+              lib.dspark_verify_workspace_bytes(0, 7, 1024, 16, 0),
+              lib.dspark_acceptance_label_workspace_bytes(0, 7, 1024, 16),
+              lib.dspark_rnn_draft_workspace_bytes(0, 7, 1024, 64, 128)):
+        assert q == 0
 
 
 def test_binding_exports_resolve(lib):

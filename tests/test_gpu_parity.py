@@ -215,6 +215,56 @@ def test_schedule_async_capacity_edges():
         np.testing.assert_array_equal(got["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
 
 
+def test_empty_batch_end_to_end():
+    """A step with no requests: every call succeeds and returns empty outputs;
+    the schedule overwrites its layout outputs with the empty layout the
+    oracle gives (cu_seqlens = [0], nothing admitted, Theta = 0)."""
+    _say("empty batch")
+    K, V, r, d = 5, 300, 32, 64
+    g = torch.Generator().manual_seed(11)
+    W1 = (0.1 * torch.randn(V, r, generator=g)).to(torch.bfloat16).to(DEV)
+    W2 = (0.1 * torch.randn(V, r, generator=g)).to(torch.bfloat16).to(DEV)
+    W = (0.1 * torch.randn(3 * r, 2 * r + d, generator=g)).to(torch.bfloat16).to(DEV)
+    U = torch.empty((0, K, V), dtype=torch.bfloat16, device=DEV)
+    x0 = torch.empty(0, dtype=torch.int32, device=DEV)
+    x, q, lse = ds().dspark_markov_draft(U, W1, W2, x0, 1.0, 5, 0)
+    assert x.shape == q.shape == lse.shape == (0, K)
+    H = torch.empty((0, K, d), dtype=torch.bfloat16, device=DEV)
+    xr, qr, lr, O = ds().dspark_rnn_draft(U, H, W, W1, W2, x0, 1.0, 5, 0)
+    assert xr.shape == (0, K) and O.shape == (0, K, r)
+    c = torch.empty((0, K), dtype=torch.float32, device=DEV)
+    sps = torch.tensor([4.0, 3.0], dtype=torch.float64, device=DEV)
+    ref = oracle.schedule_ref(np.zeros((0, K), dtype=np.float32), np.array([4.0, 3.0]), 0)
+    for call in ("sync", "async"):
+        out = {"a": torch.empty((0, K), dtype=torch.float32, device=DEV),
+               "ell": torch.empty(0, dtype=torch.int32, device=DEV),
+               "cu_seqlens": torch.full((1,), 77, dtype=torch.int32, device=DEV),
+               "n_admitted": torch.full((1,), 77, dtype=torch.int32, device=DEV),
+               "theta": torch.full((1,), 77.0, dtype=torch.float64, device=DEV)}
+        if call == "sync":
+            ds().dspark_schedule(c, sps, 0, out=out)
+        else:
+            ds().dspark_schedule_async(c, sps, torch.tensor([3], dtype=torch.int32, device=DEV), out=out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+        assert int(out["n_admitted"].cpu()[0]) == ref["n_admitted"] == 0
+        assert float(out["theta"].cpu()[0]) == ref["theta"] == 0.0
+    P = torch.empty((0, V), dtype=torch.bfloat16, device=DEV)
+    cu = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n_acc, tok = ds().dspark_verify(P, cu, U, W1, W2, x0, x, q, lse, 1.0, 5, 0)
+    assert n_acc.shape == tok.shape == (0,)
+    n_acc, tok = ds().dspark_rnn_verify(P, cu, U, O, W2, x0, xr, qr, lr, 1.0, 5, 0)
+    assert n_acc.shape == (0,)
+    P3 = torch.empty((0, K, V), dtype=torch.bfloat16, device=DEV)
+    assert ds().dspark_acceptance_label(P3, U, W1, W2, x0, x, lse, 1.0).shape == (0, K)
+    assert ds().dspark_rnn_acceptance_label(P3, U, O, W2, x0, xr, lr, 1.0).shape == (0, K)
+    w_h = torch.zeros(d, dtype=torch.float32, device=DEV)
+    w_e = torch.zeros(r, dtype=torch.float32, device=DEV)
+    assert ds().dspark_confidence_head(H, w_h, w_e, 0.0, W1, x0, x, V).shape == (0, K)
+    assert ds().dspark_uniforms(1, 0, 0, 1, 0).shape == (0,)
+    torch.cuda.synchronize()
+
+
 def test_schedule_invalid_confidence():
     c = torch.full((5, 3), 0.5)
     c[2, 1] = float("nan")

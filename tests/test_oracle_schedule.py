@@ -11,7 +11,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle.schedule import (schedule_ref, schedule_bruteforce, survival,
+from oracle.schedule import (schedule_ref, schedule_async_ref, schedule_bruteforce, survival,
                              SCHED_EARLY_STOP, SCHED_GLOBAL, SCHED_TOPK)
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -184,3 +184,17 @@ def test_invalid_confidence_rejected():
     for bad in (np.nan, -0.1, 1.5):
         with pytest.raises(ValueError):
             schedule_ref(np.array([[0.5, bad]], dtype=np.float32), sps)
+
+
+def test_empty_batch_admits_nothing():
+    """No requests (Algorithm 1 with R = 0): the pool is empty, B = tau = 0, so
+    nothing is admitted, the flat layout is [0] and Theta = 0 * SPS(0) = 0;
+    the asynchronous variant inherits a zero capacity."""
+    sps = np.array([3.0, 2.0])
+    for mode in (SCHED_EARLY_STOP, SCHED_GLOBAL, SCHED_TOPK):
+        out = schedule_ref(np.zeros((0, 4), dtype=np.float32), sps, mode, 5)
+        assert out["ell"].shape == (0,) and out["a"].shape == (0, 4)
+        assert list(out["cu_seqlens"]) == [0]
+        assert out["n_admitted"] == 0 and out["theta"] == 0.0
+    out = schedule_async_ref(np.zeros((0, 4), dtype=np.float32), np.zeros((0, 4), dtype=np.float32), sps)
+    assert out["capacity"] == 0 and out["n_admitted"] == 0 and list(out["cu_seqlens"]) == [0]
