@@ -189,7 +189,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // stage wait for the W1 rows only.
   __shared__ EStage<KCs, ROWS> st;
   // Blocks of the pipelined sweep after each wave's first are handed out in
-  // order from this counter, so the four waves of the workgroup finish
+  // order from this counter, so the eight waves of the workgroup finish
   // within a block of each other (a static split gives some waves one block
   // more than others).
   __shared__ int blk_next;
@@ -623,7 +623,7 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   a.V = V;
   a.r = r;
   a.nslices = (V + kWaveCols - 1) / kWaveCols;
-  // persistent grid: about two workgroups per CU; column ranges split the
+  // persistent grid: one 8-wave workgroup per CU; column ranges split the
   // 64-column blocks evenly, row stages of 128 requests
   a.nstages = (B + kStageRows - 1) / kStageRows;
   a.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / a.nstages));
