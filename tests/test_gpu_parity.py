@@ -416,6 +416,48 @@ def test_full_step_full_size_sampled():
     _say(str(rep) + " n_acc(sample)=%s" % g["n_acc"][sample].tolist())
 
 
+def test_offsets_near_the_4gib_limit():
+    """U, D and P just under 4 GiB, the limit of the kernels' 32-bit byte
+    offsets: draft and verify of 7000 requests (two positions, one draft row
+    judged per request), the oracle on the first and last requests, where the
+    offsets are smallest and largest."""
+    B, K, V, r, seed = 7000, 2, 151936, 64, 0xB16
+    assert B * K * V * 2 < 2 ** 32 and 2 * B * V * 2 < 2 ** 32
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    U = torch.empty((B, K, V), dtype=torch.bfloat16, device=DEV)
+    P = torch.empty((2 * B, V), dtype=torch.bfloat16, device=DEV)
+    for i in range(0, B, 1000):
+        U[i:i + 1000] = (2.0 * torch.randn((min(1000, B - i), K, V), generator=g, device=DEV)).to(torch.bfloat16)
+        P[2 * i:2 * i + 2000] = (2.0 * torch.randn((min(2000, 2 * B - 2 * i), V), generator=g,
+                                                   device=DEV)).to(torch.bfloat16)
+    W1 = (0.2 * torch.randn((V, r), generator=g, device=DEV)).to(torch.bfloat16)
+    W2 = (0.2 * torch.randn((V, r), generator=g, device=DEV)).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, device=DEV, dtype=torch.int32)
+    _say("near-4GiB inputs generated")
+    x, q, lse = ds().dspark_markov_draft(U, W1, W2, x0, 1.0, seed, 0)
+    cu = torch.arange(0, 2 * B + 1, 2, dtype=torch.int32, device=DEV)
+    n_acc, tok = ds().dspark_verify(P, cu, U, W1, W2, x0, x, q, lse, 1.0, seed, 0)
+    torch.cuda.synchronize()
+    _say("near-4GiB gpu done")
+    sample = np.array([0, 1, 3333, B - 2, B - 1])
+    sel = torch.as_tensor(sample, device=DEV)
+    W1f, W2f = f64(W1), f64(W2).T
+    Us = f64(U[sel])
+    ref_d = oracle.draft_ref(Us, W1f, W2f, x0.cpu().numpy()[sample], 1.0, seed, 0, request_ids=sample)
+    rep = Report("near 4 GiB")
+    same = compare_draft(rep, x.cpu().numpy()[sample], q.cpu().numpy()[sample], lse.cpu().numpy()[sample], ref_d,
+                         bf16_inputs=True, greedy=False)
+    rows = torch.stack([2 * sel, 2 * sel + 1], 1).reshape(-1)
+    Ps = f64(P[rows])
+    cu_s = np.arange(0, 2 * len(sample) + 1, 2)
+    ref_v = oracle.verify_ref(Ps, cu_s, Us, W1f, W2f, x0.cpu().numpy()[sample], ref_d["x"], 1.0, seed, 0,
+                              request_ids=sample)
+    whole = [i for i in range(len(sample)) if same[i].all()]
+    compare_verify(rep, n_acc.cpu().numpy()[sample], tok.cpu().numpy()[sample], ref_v, whole)
+    rep.check_near_ties()
+    _say(str(rep))
+
+
 # ------------------------------------------------------- statistics on GPU
 def test_gpu_emitted_token_follows_target_and_acceptance_is_one_minus_tv():
     n, V = 1_000_000, 8
