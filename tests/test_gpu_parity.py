@@ -418,9 +418,9 @@ def test_full_step_full_size_sampled():
 
 def test_offsets_near_the_4gib_limit():
     """U, D and P just under 4 GiB, the limit of the kernels' 32-bit byte
-    offsets: draft and verify of 7000 requests (two positions, one draft row
-    judged per request), the oracle on the first and last requests, where the
-    offsets are smallest and largest."""
+    offsets: draft, verify (two positions, one draft row judged per request)
+    and acceptance label of 7000 requests, the oracle on the first and last
+    requests, where the offsets are smallest and largest."""
     B, K, V, r, seed = 7000, 2, 151936, 64, 0xB16
     assert B * K * V * 2 < 2 ** 32 and 2 * B * V * 2 < 2 ** 32
     g = torch.Generator(device=DEV).manual_seed(seed)
@@ -456,6 +456,10 @@ def test_offsets_near_the_4gib_limit():
     compare_verify(rep, n_acc.cpu().numpy()[sample], tok.cpu().numpy()[sample], ref_v, whole)
     rep.check_near_ties()
     _say(str(rep))
+    # the acceptance label over the same buffers, P read as [B, K, V]
+    got, ref = _label_case(P.view(B, K, V), U, W1, W2, x0, 1.0, rows=sample, seed=seed)
+    _say("near-4GiB label max |diff| %.2e" % np.abs(got - ref).max())
+    np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
 
 
 # ------------------------------------------------------- statistics on GPU
