@@ -5,7 +5,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <deque>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -49,10 +52,13 @@ struct KernelTotal {
   int64_t launches = 0;
   double ms = 0.0;
 };
-bool g_prof = false;
-std::vector<KernelTotal> g_totals;
+// The timer may be driven from several host threads: the open bracket is
+// per thread, the totals and the pending events are under one lock.
+std::atomic<bool> g_prof{false};
+std::mutex g_lock;
+std::deque<KernelTotal> g_totals;  // a deque keeps each name's storage in place as it grows
 std::vector<Pending> g_pending;
-Pending g_open{-1, nullptr, nullptr};
+thread_local Pending g_open{-1, nullptr, nullptr};
 
 int kernel_index(const char* name) {
   for (size_t i = 0; i < g_totals.size(); ++i)
@@ -75,10 +81,13 @@ void drain_pending() {
 }
 }  // namespace
 
-bool profiler_on() { return g_prof; }
+bool profiler_on() { return g_prof.load(std::memory_order_relaxed); }
 
 void profiler_begin(const char* name, hipStream_t stream) {
-  g_open.kernel = kernel_index(name);
+  {
+    std::lock_guard<std::mutex> hold(g_lock);
+    g_open.kernel = kernel_index(name);
+  }
   if (hipEventCreate(&g_open.start) != hipSuccess || hipEventCreate(&g_open.stop) != hipSuccess) {
     g_open.kernel = -1;
     return;
@@ -89,7 +98,10 @@ void profiler_begin(const char* name, hipStream_t stream) {
 void profiler_end(hipStream_t stream) {
   if (g_open.kernel < 0) return;
   (void)hipEventRecord(g_open.stop, stream);
-  g_pending.push_back(g_open);
+  {
+    std::lock_guard<std::mutex> hold(g_lock);
+    g_pending.push_back(g_open);
+  }
   g_open.kernel = -1;
 }
 }  // namespace dspark
@@ -394,17 +406,19 @@ int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpo
 }
 
 int dspark_profiler_enable(int on) {
-  dspark::g_prof = on != 0;
+  dspark::g_prof.store(on != 0);
   return DSPARK_OK;
 }
 
 int dspark_profiler_reset(void) {
+  std::lock_guard<std::mutex> hold(dspark::g_lock);
   dspark::drain_pending();
   dspark::g_totals.clear();
   return DSPARK_OK;
 }
 
 int dspark_profiler_read(int index, const char** name, int64_t* launches, double* total_ms) {
+  std::lock_guard<std::mutex> hold(dspark::g_lock);
   dspark::drain_pending();
   if (!name) return (int)dspark::g_totals.size();
   if (index < 0 || index >= (int)dspark::g_totals.size()) return DSPARK_E_RANGE;

@@ -389,7 +389,9 @@ int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpo
  * every kernel the calls above launch is bracketed by a pair of HIP events
  * recorded on the caller's stream.  dspark_profiler_read waits for the
  * recorded events and reports, per kernel name, the number of launches and the
- * summed event time.  Host-side state, not thread-safe.
+ * summed event time.  Host-side state shared by every thread of the process
+ * (calls from several threads are safe); a name returned by
+ * dspark_profiler_read stays valid until the next dspark_profiler_reset.
  * ------------------------------------------------------------------------ */
 int dspark_profiler_enable(int on);
 int dspark_profiler_reset(void);

@@ -264,6 +264,15 @@ def test_empty_batches_are_noops(lib):
         assert q == 0
 
 
+def test_profiler_without_launches(lib):
+    """The kernel timer's host side: nothing recorded reads as no kernels."""
+    assert lib.dspark_profiler_enable(1) == 0
+    assert lib.dspark_profiler_reset() == 0
+    assert lib.dspark_profiler_read(0, None, None, None) == 0
+    assert lib.dspark_profiler_read(0, ctypes.byref(ctypes.c_char_p()), None, None) == -4
+    assert lib.dspark_profiler_enable(0) == 0
+
+
 def test_binding_exports_resolve(lib):
     """Every name the package exports resolves to a binding function or constant."""
     import draft_verify_schedule_amd as m

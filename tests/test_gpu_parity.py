@@ -462,6 +462,47 @@ def test_offsets_near_the_4gib_limit():
     np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
 
 
+def test_kernel_timer_from_several_threads():
+    """Draft calls from four host threads, each on its own stream, with the
+    kernel timer on: every launch is counted once and every thread's draft
+    equals the one-thread result."""
+    import threading
+    w = wl().make("tiny", device=DEV)
+    ref = [t.cpu() for t in ds().dspark_markov_draft(w.U, w.W1, w.W2, w.x0, 1.0, w.rng_seed, 0)]
+    torch.cuda.synchronize()
+    ds().dspark_profiler_reset()
+    ds().dspark_profiler_enable(True)
+    results, errors = [None] * 4, []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    out = ds().dspark_markov_draft(w.U, w.W1, w.W2, w.x0, 1.0, w.rng_seed, 0)
+                s.synchronize()
+            results[i] = [t.cpu() for t in out]
+        except Exception as e:  # reported after the join
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    ds().dspark_profiler_enable(False)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    totals = ds().dspark_profiler_read()
+    ds().dspark_profiler_reset()
+    K = w.U.shape[1]
+    assert totals["draft_locate"][0] == 4 * 3 * K
+    assert totals["draft_partials"][0] >= 4 * 3 * K
+    for res in results:
+        for a, b in zip(res, ref):
+            np.testing.assert_array_equal(a.numpy(), b.numpy())
+
+
 # ------------------------------------------------------- statistics on GPU
 def test_gpu_emitted_token_follows_target_and_acceptance_is_one_minus_tv():
     n, V = 1_000_000, 8
