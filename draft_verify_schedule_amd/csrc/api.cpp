@@ -16,6 +16,7 @@
 
 namespace dspark {
 size_t draft_workspace_bytes(int B, int K, int V);
+size_t w2_swizzle_bytes(int V, int r);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
               const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
               float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
@@ -136,10 +137,9 @@ const char* dspark_status_string(int status) {
 int dspark_version(void) { return 100; }
 
 size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
-  (void)K;
-  (void)r;
-  if (B <= 0 || V <= 0) return 0;
-  return dspark::draft_workspace_bytes(B, K, V);
+  if (B <= 0 || V <= 0 || r < 0) return 0;
+  // slice partials, then (Markov head) W2 in MFMA fragment order
+  return dspark::draft_workspace_bytes(B, K, V) + dspark::w2_swizzle_bytes(V, r);
 }
 
 int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
@@ -150,11 +150,12 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
   if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_swizzle_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::draft_workspace_bytes(B, K, V)) return DSPARK_E_WORKSPACE;
+  if (!workspace || workspace_bytes < dspark_markov_draft_workspace_bytes(B, K, V, r)) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
     return DSPARK_E_RANGE;

@@ -101,6 +101,47 @@ struct W2Frags {
   }
 };
 
+// The same A-operand fragments from a copy of W2 rearranged once per call
+// (w2_swizzle_kernel): for 64-column block blk, fragment f = b * KC + kc is
+// 1 KB holding lane l's 16 bytes at 16 l, in the order the MFMA reads them.
+// A wave's fragment load is then one contiguous kilobyte (8 cache lines)
+// where the column-major W2 puts each lane's 16 bytes 16 lanes away from its
+// neighbours in the same line (every lane a separate cache access).
+struct W2SwzFrags {
+  rsrc_t rsrc;
+  uint32_t lane_off;   // 16 * lane
+  uint32_t blk_bytes;  // 4 * KC * 1024
+  uint32_t bytes;      // resource size
+  __device__ __forceinline__ void setup(const uint16_t* W2s, int kc_count, int V, int lane) {
+    blk_bytes = (uint32_t)(4 * kc_count) * 1024u;
+    bytes = (uint32_t)((V + 63) / 64) * blk_bytes;
+    rsrc = make_rsrc(W2s, bytes);
+    lane_off = (uint32_t)lane * 16u;
+  }
+  template <int KC, int K0 = 0, int K1 = KC, typename FT>
+  __device__ __forceinline__ void load_from(uint32_t base, FT (&fr)[4][KC]) const {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int kc = K0; kc < K1; ++kc)
+        fr[b][kc] = __builtin_bit_cast(FT, buffer_load16(rsrc, lane_off, base + (uint32_t)(b * KC + kc) * 1024u));
+    }
+  }
+  // n0: first column of the block (a multiple of 64)
+  template <int KC, typename FT>
+  __device__ __forceinline__ void load(int n0, FT (&fr)[4][KC]) const {
+    load_from<KC>((uint32_t)(n0 / 64) * blk_bytes, fr);
+  }
+  template <int KC, typename FT>
+  __device__ __forceinline__ void load_if(int n0, bool valid, FT (&fr)[4][KC]) const {
+    load_from<KC>(valid ? (uint32_t)(n0 / 64) * blk_bytes : bytes, fr);
+  }
+  template <int KC, int K0, int K1, typename FT>
+  __device__ __forceinline__ void load_range_if(int n0, bool valid, FT (&fr)[4][KC]) const {
+    load_from<KC, K0, K1>(valid ? (uint32_t)(n0 / 64) * blk_bytes : bytes, fr);
+  }
+};
+
 // Stage E rows W1[prev(row)] of rows [row0, row0 + kStageRows) into LDS (zeros
 // for rows past nrows, invalid previous tokens, or k >= r).  prev_of(row)
 // returns the previous token of that row or -1.  The 256 threads (4 waves)

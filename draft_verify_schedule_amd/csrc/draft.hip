@@ -45,6 +45,7 @@ struct DraftArgs {
   float* lse_out;
   const float* O;          // RNN head: output parts [B, K, r] fp32, row b * K + k - 1 (else null)
   const uint16_t* W2h;     // RNN head: fp16 copy of W2t
+  const uint16_t* W2s;     // Markov head: W2t rearranged into MFMA fragment order (w2_swizzle_kernel)
 };
 
 // Epilogue of one group: z = base logits + bias for 16 consecutive columns of
@@ -214,10 +215,12 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   }
 
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][KCs];
-  W2Frags wf;
+  // the RNN head's split stages read the fp16 copy; the Markov head the fragment-ordered copy
+  std::conditional_t<ROWS, W2Frags, W2SwzFrags> wf;
   if constexpr (KC > 0) {
-    wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
-    if constexpr (FULL) wf.load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
+    if constexpr (ROWS) wf.setup(a.W2h, a.r, a.V, lane);
+    else wf.setup(a.W2s, KC, a.V, lane);
+    if constexpr (FULL) wf.template load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
     if constexpr (ROWS) {
       const int K = a.K, k = a.k;
       if (wave < 4) stage_rows<KC>(st, a.O, a.r, row0, a.B, [&](int g) { return g * K + k - 1; });
@@ -286,13 +289,13 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
               constexpr int KH = KC / 2;
               mfma_group<KC, false, 0, KH>(st, g + 1, lane, w2, acc, e_off);
               __builtin_amdgcn_sched_barrier(0);
-              wf.load_range_if<KC, 0, KH>(nxt * kWaveCols, has_next, w2);
+              wf.template load_range_if<KC, 0, KH>(nxt * kWaveCols, has_next, w2);
               __builtin_amdgcn_sched_barrier(0);
               mfma_group<KC, false, KH, KC>(st, g + 1, lane, w2, acc, e_off);
             }
           }
         } else if constexpr (KC > 0) {
-          wf.load_range_if<KC, KC / 2, KC>(nxt * kWaveCols, has_next, w2);
+          wf.template load_range_if<KC, KC / 2, KC>(nxt * kWaveCols, has_next, w2);
         }
         const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
         buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
@@ -307,7 +310,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   for (; blk < blk_end; blk += kDraftWaves) {
     const int cbase = blk * kWaveCols + lane_col;
     float2* part = a.part + blk;
-    if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
+    if constexpr (KC > 0) wf.template load<KC>(blk * kWaveCols, w2);
     for (int g = 0; g < ngroups; ++g) {
       typename UAccess<UT, VEC>::Buf one;
       ua.load(one, row0 + 16 * g, blk);
@@ -574,8 +577,42 @@ static int dispatch_kc(const DraftArgs& a, hipStream_t stream) {
   }
 }
 
+// W2 (column-major, V x r bf16) into fragment order for KC = ceil(r / 32)
+// chunks: entry (blk, f = b * KC + kc, lane l) holds the 8 weights of column
+// 64 blk + 16 (a / 4) + a % 4 + 4 b (a = l % 16) at k = 32 kc + 8 (l / 16) ..
+// +7, or zeros past V or past r.  One thread per 16-byte entry; the writes
+// are contiguous.
+__global__ __launch_bounds__(256) void w2_swizzle_kernel(const uint16_t* __restrict__ W2, u32x4* __restrict__ out,
+                                                         int V, int r, int KC, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int lane = (int)(i & 63);
+    const size_t fi = i >> 6;
+    const int f = (int)(fi % (size_t)(4 * KC));
+    const size_t blk = fi / (size_t)(4 * KC);
+    const int b = f / KC, kc = f % KC;
+    const int a = lane & 15;
+    const size_t col = blk * 64 + (size_t)(16 * (a >> 2) + (a & 3) + 4 * b);
+    const int k = 32 * kc + 8 * (lane >> 4);
+    out[i] = (col < (size_t)V && k < r) ? *reinterpret_cast<const u32x4*>(W2 + col * r + k) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+size_t w2_swizzle_bytes(int V, int r) {
+  if (r <= 0) return 0;
+  const size_t kc = (size_t)(r + 31) / 32;
+  return (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 1024;
+}
+
 template <typename UT, bool GREEDY>
 static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStream_t stream) {
+  if (!rnn && a.r > 0) {
+    const int kc = (a.r + 31) / 32;
+    const size_t n = w2_swizzle_bytes(a.V, a.r) / 16;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+    const int rc = launch_kernel("w2_swizzle", w2_swizzle_kernel, dim3((unsigned)blocks), dim3(256), stream, a.W2t,
+                                 const_cast<u32x4*>(reinterpret_cast<const u32x4*>(a.W2s)), a.V, a.r, kc, n);
+    if (rc) return rc;
+  }
   if (rnn) {
     int rc = run_w2_to_f16(rnn->W2, rnn->W2h, (size_t)a.V * a.r, stream);
     if (rc) return rc;
@@ -628,6 +665,10 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   a.nstages = (B + kStageRows - 1) / kStageRows;
   a.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / a.nstages));
   a.part = reinterpret_cast<float2*>(workspace);
+  // Markov head: the fragment-ordered W2 follows the slice partials
+  a.W2s = (!rnn && r > 0) ? reinterpret_cast<const uint16_t*>(reinterpret_cast<char*>(workspace) +
+                                                              draft_workspace_bytes(B, K, V))
+                          : nullptr;
   a.seed = seed;
   a.step = step;
   a.x_out = x_out;

@@ -108,6 +108,11 @@ int dspark_version(void);
  * r as in the header comment, U smaller than 4 GiB.
  * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
  * that request's remaining positions x = -1, q_tok = lse = NaN.
+ * Workspace: dspark_markov_draft_workspace_bytes(B, K, V, r) bytes, 256-byte
+ * aligned, contents need not be initialised: the per-slice softmax partials
+ * and, when r > 0, a copy of W2 in the order the bias MFMAs read it
+ * (ceil(V / 64) x 4 x ceil(r / 32) KB, written by the call itself before the
+ * first position; it must be smaller than 4 GiB).
  * ------------------------------------------------------------------------ */
 size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r);
 int dspark_markov_draft(int B, int K, int V, int r, float temperature,

@@ -45,6 +45,11 @@ def test_status_strings(lib):
 def test_workspace_queries(lib):
     assert lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 256) >= 512 * 2374 * 8
     assert lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 256) % 256 == 0
+    # the Markov head adds W2 in MFMA fragment order: ceil(V / 64) blocks of 4 x ceil(r / 32) KB
+    for r in (8, 24, 64, 256):
+        extra = lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, r) - \
+            lib.dspark_markov_draft_workspace_bytes(512, 7, 151936, 0)
+        assert extra == 2374 * 4 * ((r + 31) // 32) * 1024
     assert lib.dspark_verify_workspace_bytes(512, 7, 151936, 256, 4096) > 0
     assert lib.dspark_verify_workspace_bytes(0, 7, 10, 0, 1) == 0
     assert lib.dspark_schedule_workspace_bytes(512, 7) >= 512 * 7 * 8
@@ -177,7 +182,8 @@ def test_uniforms_argument_errors(lib):
 def test_rnn_argument_errors(lib):
     B, K, V, r, d = 4, 7, 1024, 64, 128
     need = lib.dspark_rnn_draft_workspace_bytes(B, K, V, r, d)
-    assert need >= lib.dspark_markov_draft_workspace_bytes(B, K, V, r) + B * K * 3 * r * 4 + 2 * B * r * 4 + V * r * 2
+    # the RNN head reuses the slice partials of the draft (the Markov head's W2 copy is not needed)
+    assert need >= lib.dspark_markov_draft_workspace_bytes(B, K, V, 0) + B * K * 3 * r * 4 + 2 * B * r * 4 + V * r * 2
     assert lib.dspark_rnn_verify_workspace_bytes(4, K, V, r, 8) >= \
         lib.dspark_verify_workspace_bytes(4, K, V, r, 8) + V * r * 2
     assert lib.dspark_rnn_acceptance_label_workspace_bytes(4, K, V, r) >= \
