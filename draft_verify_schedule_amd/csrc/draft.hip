@@ -143,6 +143,33 @@ struct UAccess<UT, false> {
   }
 };
 
+// bf16 base logits of one 16-row group read coalesced: lane l takes the 16
+// bytes at 16 (l % 8) of row l / 8 (w[0], rows 0..7 of the group) and of row
+// 8 + l / 8 (w[1]), so each load instruction covers 8 whole 128-byte row
+// segments.  The MFMA layout instead wants lane l to hold 32 bytes of row
+// l % 16, which puts a row segment's four pieces 16 lanes apart and makes
+// every lane a separate cache access; the sweep moves the data between the
+// two layouts through LDS.  Offsets past the resource read as zero.
+struct UCoal {
+  rsrc_t rsrc;
+  uint32_t lane_off;
+  uint32_t bytes;
+  uint64_t row_bytes;
+  __device__ __forceinline__ void setup(const DraftArgs& a, int lane) {
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(a.U) + (size_t)(a.k - 1) * a.V;
+    bytes = (uint32_t)(((uint64_t)a.B * a.K * a.V - (uint64_t)(a.k - 1) * a.V) * 2u);
+    rsrc = make_rsrc(base, bytes);
+    row_bytes = (uint64_t)a.K * a.V * 2u;
+    lane_off = (uint32_t)((uint64_t)(lane >> 3) * row_bytes + (uint64_t)(lane & 7) * 16u);
+  }
+  __device__ __forceinline__ void load_if(GroupLogitsBuf<uint16_t>& b, int row, int blk, bool valid) const {
+    const uint32_t off = (uint32_t)((uint64_t)row * row_bytes + (uint64_t)blk * kWaveCols * 2u);
+    const uint32_t off8 = (uint32_t)((uint64_t)(row + 8) * row_bytes + (uint64_t)blk * kWaveCols * 2u);
+    b.w[0] = buffer_load16(rsrc, lane_off, valid ? off : bytes);
+    b.w[1] = buffer_load16(rsrc, lane_off, valid ? off8 : bytes);
+  }
+};
+
 // Persistent workgroups, one per CU: 8 waves (two per SIMD), 128 rows (8
 // MFMA groups of 16), and a contiguous range of 64-column blocks.  The W1
 // rows of the 128 requests are staged in LDS once (by waves 0..3) and shared
@@ -209,9 +236,19 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // groups of base logits in flight per wave: 8 registers per packed bf16 group, 16 per fp32
   constexpr int kPrefetch = (FULL && sizeof(UT) == 2) ? 4 : 1;
   typename UAccess<UT, VEC>::Buf buf[kPrefetch];
+  // UX: full bf16 stages of the Markov head load their base logits coalesced
+  // (UCoal) and pass each group through this wave's LDS tile (row pitch 144
+  // bytes, conflict-free for the MFMA-layout reads) two groups ahead of use
+  constexpr bool UX = FULL && !ROWS && std::is_same_v<UT, uint16_t>;
+  __shared__ u32x4 utile[UX ? kDraftWaves : 1][2][16 * 9];
+  UCoal uc;
   if constexpr (FULL) {
+    if constexpr (UX) uc.setup(a, lane);
 #pragma unroll
-    for (int g = 0; g < kPrefetch; ++g) ua.load_if(buf[g], row0 + 16 * g, blk, blk < blk_stop);
+    for (int g = 0; g < kPrefetch; ++g) {
+      if constexpr (UX) uc.load_if(buf[g], row0 + 16 * g, blk, blk < blk_stop);
+      else ua.load_if(buf[g], row0 + 16 * g, blk, blk < blk_stop);
+    }
   }
 
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][KCs];
@@ -248,20 +285,54 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       if (lane == 0) v = atomicAdd(&blk_next, 1);
       return __builtin_amdgcn_readfirstlane(v);
     };
+    // UX: group h (of the block, h >= 8: of the next one) goes from ring slot
+    // h % kPrefetch into tile h % 2 two steps before its MFMAs (xwrite), and
+    // comes back in the MFMA layout one step before them (xread); the slot is
+    // refilled with group h + kPrefetch as soon as it is written out.  LDS
+    // operations of one wave complete in order, so no barrier is needed.
+    auto xwrite = [&](int h) {
+      if constexpr (UX) {
+        utile[wave][h & 1][(lane >> 3) * 9 + (lane & 7)] = buf[h % kPrefetch].w[0];
+        utile[wave][h & 1][(8 + (lane >> 3)) * 9 + (lane & 7)] = buf[h % kPrefetch].w[1];
+      }
+    };
+    auto xread = [&](int h, float (&u)[16]) {
+      if constexpr (UX) {
+        GroupLogitsBuf<uint16_t> t;
+        t.w[0] = utile[wave][h & 1][(lane & 15) * 9 + 2 * (lane >> 4)];
+        t.w[1] = utile[wave][h & 1][(lane & 15) * 9 + 2 * (lane >> 4) + 1];
+        t.unpack(u);
+      }
+    };
+    if constexpr (UX) {
+      xwrite(0);
+      uc.load_if(buf[0], row0 + 16 * kPrefetch, blk, blk < blk_stop);
+      xwrite(1);
+      uc.load_if(buf[1], row0 + 16 * (kPrefetch + 1), blk, blk < blk_stop);
+    }
     while (blk < blk_stop) {
       const int cbase = blk * kWaveCols + lane_col;
       const int nxt = claim();
       const bool has_next = nxt < blk_stop;
       const int e_off = launder(e_lane_offset<KCs, ROWS>(lane));
       auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
-        if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
-        else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
+        if constexpr (UX) {
+          if (h < kGroupsPerWG) uc.load_if(buf[h % kPrefetch], row0 + 16 * h, blk, true);
+          else uc.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
+        } else {
+          if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
+          else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
+        }
       };
       f32x4 acc[4];
       {
         float u[16];
-        buf[0].unpack(u);
-        refill(kPrefetch);
+        if constexpr (UX) {
+          xread(0, u);
+        } else {
+          buf[0].unpack(u);
+          refill(kPrefetch);
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
         if constexpr (KC > 0) mfma_group<KC, false>(st, 0, lane, w2, acc, e_off);
@@ -275,8 +346,12 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
           for (int i = 0; i < 4; ++i) z[4 * b + i] = acc[b][i];
         if (g + 1 < kGroupsPerWG) {
           float u[16];
-          buf[(g + 1) % kPrefetch].unpack(u);
-          refill(g + 1 + kPrefetch);
+          if constexpr (UX) {
+            xread(g + 1, u);
+          } else {
+            buf[(g + 1) % kPrefetch].unpack(u);
+            refill(g + 1 + kPrefetch);
+          }
 #pragma unroll
           for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
           if constexpr (KC > 0) {
@@ -296,6 +371,10 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
           }
         } else if constexpr (KC > 0) {
           wf.template load_range_if<KC, KC / 2, KC>(nxt * kWaveCols, has_next, w2);
+        }
+        if constexpr (UX) {
+          xwrite(g + 2);
+          refill(g + 2 + kPrefetch);
         }
         const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
         buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
