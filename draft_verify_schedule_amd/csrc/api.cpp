@@ -25,7 +25,7 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
                  double* theta_out, void* workspace, hipStream_t stream);
 size_t verify_workspace_bytes(int R, int V, int N);
-size_t label_workspace_bytes(int B, int K, int V);
+size_t label_workspace_bytes(int B, int K, int V, int r);
 int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h_bf16, const float* w_h,
                         const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
                         const float* T, float* c_out, float* logit_out, hipStream_t stream);
@@ -309,9 +309,8 @@ int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int
 }
 
 size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
-  (void)r;
-  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0) return 0;
-  return dspark::label_workspace_bytes(B, K, V);
+  if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || r < 0) return 0;
+  return dspark::label_workspace_bytes(B, K, V, r);
 }
 
 int dspark_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
@@ -323,12 +322,13 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_swizzle_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!P || !D || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::label_workspace_bytes(B, K, V)) return DSPARK_E_WORKSPACE;
+  if (!workspace || workspace_bytes < dspark::label_workspace_bytes(B, K, V, r)) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
     return DSPARK_E_RANGE;
@@ -339,7 +339,7 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
 
 size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
   if (B <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || r <= 0) return 0;
-  return (dspark::label_workspace_bytes(B, K, V) + 255) / 256 * 256 + dspark::w2_f16_bytes(V, r);
+  return (dspark::label_workspace_bytes(B, K, V, 0) + 255) / 256 * 256 + dspark::w2_f16_bytes(V, r);
 }
 
 int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
@@ -355,7 +355,7 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!P || !D || !O || !W2 || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
-  const size_t base = (dspark::label_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  const size_t base = (dspark::label_workspace_bytes(B, K, V, 0) + 255) / 256 * 256;
   if (!workspace || workspace_bytes < base + dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;

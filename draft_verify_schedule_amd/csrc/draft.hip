@@ -682,14 +682,19 @@ size_t w2_swizzle_bytes(int V, int r) {
   return (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 1024;
 }
 
+// W2 (column-major) into fragment order at out (w2_swizzle_bytes(V, r) bytes).
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, hipStream_t stream) {
+  const int kc = (r + 31) / 32;
+  const size_t n = w2_swizzle_bytes(V, r) / 16;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+  return launch_kernel("w2_swizzle", w2_swizzle_kernel, dim3((unsigned)std::max<size_t>(blocks, 1)), dim3(256), stream,
+                       W2, reinterpret_cast<u32x4*>(out), V, r, kc, n);
+}
+
 template <typename UT, bool GREEDY>
 static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStream_t stream) {
   if (!rnn && a.r > 0) {
-    const int kc = (a.r + 31) / 32;
-    const size_t n = w2_swizzle_bytes(a.V, a.r) / 16;
-    const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
-    const int rc = launch_kernel("w2_swizzle", w2_swizzle_kernel, dim3((unsigned)blocks), dim3(256), stream, a.W2t,
-                                 const_cast<u32x4*>(reinterpret_cast<const u32x4*>(a.W2s)), a.V, a.r, kc, n);
+    const int rc = run_w2_swizzle(a.W2t, const_cast<uint16_t*>(a.W2s), a.V, a.r, stream);
     if (rc) return rc;
   }
   if (rnn) {

@@ -50,6 +50,7 @@ struct VerifyArgs {
   const float* lse_d;       // [R, K]
   const float* O;           // RNN head: output parts [R, K, r] fp32 (else null)
   const uint16_t* W2h;      // RNN head: fp16 copy of W2t
+  const uint16_t* W2s;      // acceptance label, Markov head: W2t in MFMA fragment order
   uint64_t seed, step;
   int32_t* n_acc_out;
   int32_t* tok_out;
@@ -633,7 +634,11 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     rows[threadIdx.x] = rr;
   }
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][(KC > 0 ? KC : 1)];
-  W2Frags wf;
+  // the label's Markov pass reads the fragment-ordered copy of W2 (one
+  // contiguous KB per fragment load); verification and the RNN head the
+  // column-major W2 (or its fp16 copy)
+  constexpr bool SWZ = LABEL && !ROWS;
+  std::conditional_t<SWZ, W2SwzFrags, W2Frags> wf;
   if constexpr (KC > 0) {
     const int32_t* list = a.rej_list;
     const int4* info = a.info;
@@ -654,7 +659,8 @@ void verify_residual_stream_kernel(VerifyArgs a) {
         return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
       });
     }
-    wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
+    if constexpr (SWZ) wf.setup(a.W2s, KC, a.V, lane);
+    else wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
   }
   __syncthreads();
 
@@ -667,7 +673,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
-    if constexpr (KC > 0) wf.load<KC>(blk * kWaveCols, w2);
+    if constexpr (KC > 0) wf.template load<KC>(blk * kWaveCols, w2);
     const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1), ROWS>(lane));
     GroupLogitsBuf<PT> pb;
     GroupLogitsBuf<DT> db;
@@ -1151,10 +1157,15 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   return run_verify_typed<float, float>(a, greedy, vec_p, vec_d, stream);
 }
 
-size_t label_workspace_bytes(int B, int K, int V) {
+size_t w2_swizzle_bytes(int V, int r);
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, hipStream_t stream);
+
+// r > 0 (Markov head): plus W2 in fragment order for the residual pass
+size_t label_workspace_bytes(int B, int K, int V, int r) {
   const size_t N = (size_t)B * K;
   const size_t nsP = (V + kRowSlice - 1) / kRowSlice, ns64 = (V + kWaveCols - 1) / kWaveCols;
-  return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(N * ns64 * sizeof(float));
+  return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(N * ns64 * sizeof(float)) +
+         w2_swizzle_bytes(V, r);
 }
 
 template <typename PT, typename DT>
@@ -1219,9 +1230,15 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   a.rowms = reinterpret_cast<float2*>(ws + off);
   off += align256((size_t)N * sizeof(float2));
   a.rpart = reinterpret_cast<float*>(ws + off);
+  off += align256((size_t)N * a.ns64 * sizeof(float));
   const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
   const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
+  if (!O && r > 0 && temperature != 0.f && vec_p && vec_d) {  // the streamed residual pass reads it
+    a.W2s = reinterpret_cast<const uint16_t*>(ws + off);
+    const int rc = run_w2_swizzle(a.W2t, ws + off, V, r, stream);
+    if (rc) return rc;
+  }
   if (p_bf16 && d_bf16) return run_label_typed<uint16_t, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);
   if (p_bf16) return run_label_typed<uint16_t, float>(a, c_out, greedy, vec_p, vec_d, stream);
   if (d_bf16) return run_label_typed<float, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);

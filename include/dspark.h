@@ -242,7 +242,8 @@ int dspark_verify(int R, int K, int V, float temperature,
  * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, P and D each smaller than 4 GiB.
  * Data errors: a position whose previous or own token is outside [0, V) gets
  * NaN.  Workspace: dspark_acceptance_label_workspace_bytes(B, K, V, r) bytes,
- * 256-byte aligned, contents need not be initialised.
+ * 256-byte aligned, contents need not be initialised (with r > 0 it holds a
+ * copy of W2 in MFMA fragment order, written by the call, as for the draft).
  * ------------------------------------------------------------------------ */
 size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r);
 int dspark_acceptance_label(int B, int K, int V, float temperature,
