@@ -180,6 +180,7 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   if (!is_dtype(u_dtype) || h_dtype != DSPARK_BF16) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_f16_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * d * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)3 * r * (2 * r + d) * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
@@ -292,6 +293,7 @@ int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int
   if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_f16_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (R == 0) return DSPARK_OK;  // empty batch
   if (!P || !cu_seqlens || !D || !O || !W2 || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
@@ -302,7 +304,7 @@ int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int
   if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
-  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, (size_t)V * r, s)) return DSPARK_E_HIP;
+  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, V, r, s)) return DSPARK_E_HIP;
   return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
                                        d_dtype == DSPARK_BF16, nullptr, W2, r, x0, x, q_tok, lse_d, seed, step,
                                        n_acc_out, tok_out, workspace, O, W2h, s));
@@ -351,6 +353,7 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_f16_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!P || !D || !O || !W2 || !x0 || !x || !c_out) return DSPARK_E_NULL;
@@ -361,7 +364,7 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
   if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
-  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, (size_t)V * r, s)) return DSPARK_E_HIP;
+  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, V, r, s)) return DSPARK_E_HIP;
   return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
                                       nullptr, W2, r, x0, x, lse_d, c_out, workspace, O, W2h, s));
 }

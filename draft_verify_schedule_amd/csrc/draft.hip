@@ -252,11 +252,10 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   }
 
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][KCs];
-  // the RNN head's split stages read the fp16 copy; the Markov head the fragment-ordered copy
-  std::conditional_t<ROWS, W2Frags, W2SwzFrags> wf;
+  // fragment-ordered W2: its fp16 copy for the RNN head's split stages
+  W2SwzFrags wf;
   if constexpr (KC > 0) {
-    if constexpr (ROWS) wf.setup(a.W2h, a.r, a.V, lane);
-    else wf.setup(a.W2s, KC, a.V, lane);
+    wf.setup(ROWS ? a.W2h : a.W2s, KC, a.V, lane);
     if constexpr (FULL) wf.template load_if<KC>(blk * kWaveCols, blk < blk_stop, w2);
     if constexpr (ROWS) {
       const int K = a.K, k = a.k;
@@ -659,8 +658,10 @@ static int dispatch_kc(const DraftArgs& a, hipStream_t stream) {
 // W2 (column-major, V x r bf16) into fragment order for KC = ceil(r / 32)
 // chunks: entry (blk, f = b * KC + kc, lane l) holds the 8 weights of column
 // 64 blk + 16 (a / 4) + a % 4 + 4 b (a = l % 16) at k = 32 kc + 8 (l / 16) ..
-// +7, or zeros past V or past r.  One thread per 16-byte entry; the writes
-// are contiguous.
+// +7, or zeros past V or past r.  F16: the weights converted to fp16 (the
+// RNN head's split stages; exact for bf16 magnitudes 2^-14 .. 2^15).  One
+// thread per 16-byte entry; the writes are contiguous.
+template <bool F16>
 __global__ __launch_bounds__(256) void w2_swizzle_kernel(const uint16_t* __restrict__ W2, u32x4* __restrict__ out,
                                                          int V, int r, int KC, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
@@ -672,7 +673,13 @@ __global__ __launch_bounds__(256) void w2_swizzle_kernel(const uint16_t* __restr
     const int a = lane & 15;
     const size_t col = blk * 64 + (size_t)(16 * (a >> 2) + (a & 3) + 4 * b);
     const int k = 32 * kc + 8 * (lane >> 4);
-    out[i] = (col < (size_t)V && k < r) ? *reinterpret_cast<const u32x4*>(W2 + col * r + k) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 v = (col < (size_t)V && k < r) ? *reinterpret_cast<const u32x4*>(W2 + col * r + k) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (F16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = f16_bits(__uint_as_float(v[e] << 16)) | (f16_bits(__uint_as_float(v[e] & 0xFFFF0000u)) << 16);
+    }
+    out[i] = v;
   }
 }
 
@@ -682,23 +689,24 @@ size_t w2_swizzle_bytes(int V, int r) {
   return (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 1024;
 }
 
-// W2 (column-major) into fragment order at out (w2_swizzle_bytes(V, r) bytes).
-int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, hipStream_t stream) {
-  const int kc = (r + 31) / 32;
-  const size_t n = w2_swizzle_bytes(V, r) / 16;
-  const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
-  return launch_kernel("w2_swizzle", w2_swizzle_kernel, dim3((unsigned)std::max<size_t>(blocks, 1)), dim3(256), stream,
-                       W2, reinterpret_cast<u32x4*>(out), V, r, kc, n);
+// W2 (column-major) into fragment order for kc chunks of 32 (zeros past r)
+// at out, ceil(V / 64) * 4 * kc KB; f16: as fp16 values.
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream) {
+  const size_t n = (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 64;
+  const dim3 grid((unsigned)std::max<size_t>(std::min<size_t>((n + 255) / 256, 8192), 1));
+  u32x4* o = reinterpret_cast<u32x4*>(out);
+  return f16 ? launch_kernel("w2_to_f16", w2_swizzle_kernel<true>, grid, dim3(256), stream, W2, o, V, r, kc, n)
+             : launch_kernel("w2_swizzle", w2_swizzle_kernel<false>, grid, dim3(256), stream, W2, o, V, r, kc, n);
 }
 
 template <typename UT, bool GREEDY>
 static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStream_t stream) {
   if (!rnn && a.r > 0) {
-    const int rc = run_w2_swizzle(a.W2t, const_cast<uint16_t*>(a.W2s), a.V, a.r, stream);
+    const int rc = run_w2_swizzle(a.W2t, const_cast<uint16_t*>(a.W2s), a.V, a.r, (a.r + 31) / 32, false, stream);
     if (rc) return rc;
   }
   if (rnn) {
-    int rc = run_w2_to_f16(rnn->W2, rnn->W2h, (size_t)a.V * a.r, stream);
+    int rc = run_w2_to_f16(rnn->W2, rnn->W2h, a.V, a.r, stream);
     if (rc) return rc;
     rc = run_rnn_hproj(*rnn, stream);
     if (rc) return rc;

@@ -225,22 +225,18 @@ __global__ __launch_bounds__(256) void rnn_step_kernel(RnnParams p, int k, const
 // bf16 -> fp32 is exact; fp32 -> fp16 rounds to nearest even, exact for every
 // bf16 of magnitude 2^-14 .. 2^15 (8 significant bits fit in 11), with at
 // most 2^-25 absolute error below that range.
-__global__ __launch_bounds__(256) void w2_to_f16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                        size_t n8) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(in + 8 * i);
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = f16_bits(__uint_as_float(v[e] << 16)) | (f16_bits(__uint_as_float(v[e] & 0xFFFF0000u)) << 16);
-    *reinterpret_cast<u32x4*>(out + 8 * i) = o;
-  }
-}
-
 // ------------------------------------------------------------------ host --
 static size_t align256_rnn(size_t n) { return (n + 255) / 256 * 256; }
 
-size_t w2_f16_bytes(int V, int r) { return align256_rnn((size_t)V * r * sizeof(uint16_t)); }
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
+
+// The RNN head's kernels run with eight k chunks for every r (zero-padded),
+// so its fp16 fragment-ordered copy holds eight chunks per block.
+constexpr int kRnnChunks = 8;
+size_t w2_f16_bytes(int V, int r) {
+  (void)r;
+  return (size_t)((V + 63) / 64) * 4 * kRnnChunks * 1024;
+}
 
 size_t rnn_workspace_bytes(int B, int K, int V, int r) {
   return align256_rnn((size_t)B * K * 3 * r * sizeof(float)) + 2 * align256_rnn((size_t)B * r * sizeof(float)) +
@@ -258,11 +254,8 @@ void rnn_bind_workspace(RnnParams& p, void* workspace) {
   p.W2h = reinterpret_cast<uint16_t*>(ws);
 }
 
-int run_w2_to_f16(const uint16_t* W2, uint16_t* out, size_t n, hipStream_t stream) {
-  const size_t n8 = n / 8;
-  const size_t blocks = std::min<size_t>((n8 + 255) / 256, 4096);
-  return launch_kernel("w2_to_f16", w2_to_f16_kernel, dim3((unsigned)std::max<size_t>(blocks, 1)), dim3(256), stream,
-                       W2, out, n8);
+int run_w2_to_f16(const uint16_t* W2, uint16_t* out, int V, int r, hipStream_t stream) {
+  return run_w2_swizzle(W2, out, V, r, kRnnChunks, true, stream);
 }
 
 int run_rnn_hproj(const RnnParams& p, hipStream_t stream) {

@@ -19,16 +19,16 @@ struct RnnParams {
   float* Hp;           // workspace [B * K, 3r]: W[:, 2r:] h for every (request, position)
   float* s[2];         // workspace [B, r] x 2: state of the odd / even positions
   float* O;            // [B, K, r] output parts o_k (the caller's buffer)
-  uint16_t* W2h;       // workspace [V, r]: fp16 copy of the column-major W2
+  uint16_t* W2h;       // workspace: fp16 copy of W2 in MFMA fragment order
   const uint16_t* W2;  // [V, r] bf16 column-major W2
 };
 
 size_t rnn_workspace_bytes(int B, int K, int V, int r);
 // Carves Hp, the two state buffers and W2h out of a workspace of rnn_workspace_bytes.
 void rnn_bind_workspace(RnnParams& p, void* workspace);
-// out[i] = fp16(W2[i]) for n bf16 values (n % 8 == 0, both 16-byte aligned):
-// the fp16 operand the split output parts meet on the MFMA.
-int run_w2_to_f16(const uint16_t* W2, uint16_t* out, size_t n, hipStream_t stream);
+// fp16 copy of the column-major bf16 W2 in MFMA fragment order (the layout
+// W2SwzFrags reads): the operand the split output parts meet on the MFMA.
+int run_w2_to_f16(const uint16_t* W2, uint16_t* out, int V, int r, hipStream_t stream);
 size_t w2_f16_bytes(int V, int r);
 // Hp = h W[:, 2r:]^T for all B * K rows: one MFMA GEMM per call.
 int run_rnn_hproj(const RnnParams& p, hipStream_t stream);

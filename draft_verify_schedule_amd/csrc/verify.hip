@@ -515,9 +515,11 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
       });
     }
     if (col_live) {
-      W2Frags wf;
-      wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
-      wf.load<KC>(n0, w2);
+      // the RNN head's fp16 copy of W2 is in fragment order
+      std::conditional_t<ROWS, W2SwzFrags, W2Frags> wf;
+      if constexpr (ROWS) wf.setup(a.W2h, KC, a.V, lane);
+      else wf.setup(a.W2t, a.r, a.V, lane);
+      wf.template load<KC>(n0, w2);
     }
     __syncthreads();
   }
@@ -634,10 +636,10 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     rows[threadIdx.x] = rr;
   }
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][(KC > 0 ? KC : 1)];
-  // the label's Markov pass reads the fragment-ordered copy of W2 (one
-  // contiguous KB per fragment load); verification and the RNN head the
-  // column-major W2 (or its fp16 copy)
-  constexpr bool SWZ = LABEL && !ROWS;
+  // fragment-ordered W2 (one contiguous KB per fragment load): the label's
+  // Markov pass and the RNN head's fp16 copy; Markov verification reads the
+  // column-major W2
+  constexpr bool SWZ = LABEL || ROWS;
   std::conditional_t<SWZ, W2SwzFrags, W2Frags> wf;
   if constexpr (KC > 0) {
     const int32_t* list = a.rej_list;
@@ -659,8 +661,8 @@ void verify_residual_stream_kernel(VerifyArgs a) {
         return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
       });
     }
-    if constexpr (SWZ) wf.setup(a.W2s, KC, a.V, lane);
-    else wf.setup(ROWS ? a.W2h : a.W2t, a.r, a.V, lane);
+    if constexpr (SWZ) wf.setup(ROWS ? a.W2h : a.W2s, KC, a.V, lane);
+    else wf.setup(a.W2t, a.r, a.V, lane);
   }
   __syncthreads();
 
@@ -1158,7 +1160,7 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
 }
 
 size_t w2_swizzle_bytes(int V, int r);
-int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, hipStream_t stream);
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
 
 // r > 0 (Markov head): plus W2 in fragment order for the residual pass
 size_t label_workspace_bytes(int B, int K, int V, int r) {
@@ -1236,7 +1238,7 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
   if (!O && r > 0 && temperature != 0.f && vec_p && vec_d) {  // the streamed residual pass reads it
     a.W2s = reinterpret_cast<const uint16_t*>(ws + off);
-    const int rc = run_w2_swizzle(a.W2t, ws + off, V, r, stream);
+    const int rc = run_w2_swizzle(a.W2t, ws + off, V, r, (r + 31) / 32, false, stream);
     if (rc) return rc;
   }
   if (p_bf16 && d_bf16) return run_label_typed<uint16_t, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);

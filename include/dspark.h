@@ -277,7 +277,9 @@ int dspark_acceptance_label(int B, int K, int V, float temperature,
  * dspark_rnn_acceptance_label take to rebuild the draft distributions.
  * The bias o_k W2 runs on the fp16 MFMA with o_k split into hi + lo fp16
  * parts and W2 converted to fp16 (relative error 2^-22 on o_k): entries of
- * o_k and W2 must be smaller than 2^15 in magnitude.
+ * o_k and W2 must be smaller than 2^15 in magnitude.  The fp16 copy of W2,
+ * made by each RNN call in its workspace, is laid out in MFMA fragment order
+ * (ceil(V / 64) x 32 KB, which must be smaller than 4 GiB).
  * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V, r a multiple of 32 in
  * [32, DSPARK_MAX_RANK], d a positive multiple of 64; U, H, W, W1 each smaller
  * than 4 GiB; H, W, W1, W2, o_out 16-byte aligned (else DSPARK_E_RANGE).
