@@ -452,6 +452,37 @@ __device__ __forceinline__ float bias_chunk64(const uint16_t* __restrict__ w1row
   return s;
 }
 
+// bias_chunk64 with W2 read from its fragment-ordered copy (W2SwzFrags
+// layout): w2blk is the slice's 64-column block, c the lane's column in it
+// (0..63).  Same products in the same order; for a wave the loads of one k
+// step are four runs of 16 consecutive 16-byte entries instead of 64
+// scattered ones.
+__device__ __forceinline__ float bias_chunk64_swz(const uint16_t* __restrict__ w1row, const char* __restrict__ w2blk,
+                                                 int c, int k0, int r, int kc_count) {
+  const int a = 4 * (c >> 4) + (c & 3);  // MFMA A-row of column c ...
+  const int b = (c >> 2) & 3;            // ... in block b
+  u32x4 av[8], bv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + 8 * i;
+    const bool ok = k < r;
+    const int f = b * kc_count + (k >> 5);
+    av[i] = ok ? *reinterpret_cast<const u32x4*>(w1row + k) : u32x4{0u, 0u, 0u, 0u};
+    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2blk + (size_t)f * 1024 + (16 * ((k >> 3) & 3) + a) * 16)
+               : u32x4{0u, 0u, 0u, 0u};
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(__uint_as_float(av[i][e] << 16), __uint_as_float(bv[i][e] << 16), s);
+      s = fmaf(__uint_as_float(av[i][e] & 0xFFFF0000u), __uint_as_float(bv[i][e] & 0xFFFF0000u), s);
+    }
+  }
+  return s;
+}
+
 // The same over an fp32 row (the RNN head's output part o): lane l owns
 // column col and accumulates sum_k o[k] * W2[k, col] over k in [k0, k0 + 64)
 // in fp32 FMAs in index order.  Requires r % 8 == 0.
@@ -500,11 +531,18 @@ __device__ __forceinline__ float valu_bias_rows(const float* __restrict__ orow,
 // 64 w; the four chunk sums are combined in chunk order through LDS
 // (part[256], all waves must call it).  Returns the bias on every wave.
 // With orow set, the bias input is that fp32 row instead of w1row.
+// w2blk (Markov head only): the slice's block of the fragment-ordered W2,
+// read instead of w2col.
 __device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w1row, const float* __restrict__ orow,
                                                   const uint16_t* __restrict__ w2col, int r, bool ok,
-                                                  int wave, int lane, float* part) {
+                                                  int wave, int lane, float* part,
+                                                  const char* __restrict__ w2blk = nullptr) {
   float v = 0.f;
-  if (ok) v = orow ? bias_chunk64_rows(orow, w2col, 64 * wave, r) : bias_chunk64(w1row, w2col, 64 * wave, r);
+  if (ok) {
+    if (orow) v = bias_chunk64_rows(orow, w2col, 64 * wave, r);
+    else if (w2blk) v = bias_chunk64_swz(w1row, w2blk, lane, 64 * wave, r, (r + 31) / 32);
+    else v = bias_chunk64(w1row, w2col, 64 * wave, r);
+  }
   part[wave * 64 + lane] = v;
   __syncthreads();
   return ((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane];

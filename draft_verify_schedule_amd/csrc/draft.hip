@@ -598,7 +598,9 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
   float bias = 0.f;
   if (a.r > 0)
     bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.O ? a.O + out * a.r : nullptr,
-                            a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok, wave, lane, bias_part);
+                            a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok, wave, lane, bias_part,
+                            a.W2s ? reinterpret_cast<const char*>(a.W2s) + (size_t)s_star * 4 * ((a.r + 31) / 32) * 1024
+                                  : nullptr);
   if (wave != 0) return;
   const float t_in = (float)((target - before) / (double)fast_exp2(m_s - M));
   const float z = col_ok ? base + bias : -INFINITY;
