@@ -146,6 +146,8 @@ def test_draft_argument_errors(lib):
     assert call(K=0) == -2
     assert call(K=17) == -2
     assert call(r=12) == -2          # not a multiple of 8
+    # W2 itself fits (1.1 GB) but its fragment-ordered copy (4 KB per 64 columns at r = 8) would not
+    assert call(B=1, K=1, V=70_000_000, r=8) == -2
     assert call(r=264) == -2         # above DSPARK_MAX_RANK
     assert call(dt=5) == -3
     assert call(T=-1.0) == -4
