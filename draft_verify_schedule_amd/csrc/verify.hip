@@ -671,33 +671,54 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   const uint32_t lane_col = (uint32_t)(16 * (lane >> 4));
   auto row_info = [&](int g) { return rows[16 * g + (lane & 15)]; };
   auto live = [&](int g) { return 16 * g + (lane & 15) < nrows; };
+  // CX: bf16 target and draft rows are read coalesced: lane l takes the 16
+  // bytes at 16 (l % 8) of the block's 128-byte segment of rows l / 8 (w[0])
+  // and 8 + l / 8 (w[1]) of the group, so one load instruction covers eight
+  // whole segments, and the group goes into the MFMA layout (lane l: 32
+  // bytes of row l % 16) through this wave's LDS tile (row pitch 144 bytes).
+  // The lanes end up with the bytes the MFMA-layout loads would have read.
+  // One tile serves both rows: LDS operations of a wave complete in order.
+  constexpr bool CX = std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>;
+  __shared__ u32x4 xtile[CX ? 4 : 1][16 * 9];
+  auto cload = [&](GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db, int g, int blk) {
+    if constexpr (CX) {
+      const ResidualRow r0 = rows[16 * g + (lane >> 3)], r1 = rows[16 * g + 8 + (lane >> 3)];
+      const uint32_t c = (uint32_t)blk * kWaveCols * 2u + 16u * (uint32_t)(lane & 7);
+      pb.w[0] = buffer_load16(prs, r0.p_off + c, 0u);
+      pb.w[1] = buffer_load16(prs, r1.p_off + c, 0u);
+      db.w[0] = buffer_load16(drs, r0.d_off + c, 0u);
+      db.w[1] = buffer_load16(drs, r1.d_off + c, 0u);
+    }
+  };
+  auto xpose = [&](auto& b) {
+    if constexpr (CX) {
+      xtile[wave][(lane >> 3) * 9 + (lane & 7)] = b.w[0];
+      xtile[wave][(8 + (lane >> 3)) * 9 + (lane & 7)] = b.w[1];
+      b.w[0] = xtile[wave][(lane & 15) * 9 + 2 * (lane >> 4)];
+      b.w[1] = xtile[wave][(lane & 15) * 9 + 2 * (lane >> 4) + 1];
+    }
+  };
 
   for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
     if constexpr (KC > 0) wf.template load<KC>(blk * kWaveCols, w2);
     const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1), ROWS>(lane));
-    GroupLogitsBuf<PT> pb;
-    GroupLogitsBuf<DT> db;
-    ResidualRow ri = row_info(0);
-    pb.load(prs, ri.p_off + pcol, 0u);
-    db.load(drs, ri.d_off + dcol, 0u);
-    f32x4 acc[4];
-    for (int g = 0; g < ngroups; ++g) {
-      const ResidualRow cur = ri;
+    // one group in the MFMA layout: the draft rows seed the accumulators, the
+    // MFMAs add the bias, and the residual mass of the 64 columns is stored;
+    // refill requests a later group's rows into the freed buffers before the
+    // epilogue
+    auto group = [&](int g, const ResidualRow& cur, GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db, auto refill) {
       const bool lv = live(g);
       float u[16];
       db.unpack(u, cbase, a.V, lv);
+      f32x4 acc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
       if constexpr (KC > 0) mfma_group<KC, false>(st, g, lane, w2, acc, e_off);
       float t[16];
       pb.unpack(t, cbase, a.V, lv);
-      if (g + 1 < ngroups) {  // next group's rows are requested before this epilogue
-        ri = row_info(g + 1);
-        pb.load(prs, ri.p_off + pcol, 0u);
-        db.load(drs, ri.d_off + dcol, 0u);
-      }
+      refill(pb, db);
       float s = 0.f;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -712,6 +733,40 @@ void verify_residual_stream_kernel(VerifyArgs a) {
       if (lv && lane < 16) {
         const int item = row0 + 16 * g + lane;
         a.rpart[(size_t)(LABEL ? item : a.rej_list[item]) * a.ns64 + blk] = s;
+      }
+    };
+    if constexpr (CX) {
+      // two groups in flight: group g + 2 is requested into g's buffers
+      GroupLogitsBuf<PT> pb0, pb1;
+      GroupLogitsBuf<DT> db0, db1;
+      cload(pb0, db0, 0, blk);
+      if (ngroups > 1) cload(pb1, db1, 1, blk);
+      auto step = [&](int g, GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db) {
+        xpose(db);
+        xpose(pb);
+        group(g, row_info(g), pb, db, [&](GroupLogitsBuf<PT>& np, GroupLogitsBuf<DT>& nd) {
+          if (g + 2 < ngroups) cload(np, nd, g + 2, blk);
+        });
+      };
+      for (int g = 0; g < ngroups; g += 2) {
+        step(g, pb0, db0);
+        if (g + 1 < ngroups) step(g + 1, pb1, db1);
+      }
+    } else {
+      GroupLogitsBuf<PT> pb;
+      GroupLogitsBuf<DT> db;
+      ResidualRow ri = row_info(0);
+      pb.load(prs, ri.p_off + pcol, 0u);
+      db.load(drs, ri.d_off + dcol, 0u);
+      for (int g = 0; g < ngroups; ++g) {
+        const ResidualRow cur = ri;
+        group(g, cur, pb, db, [&](GroupLogitsBuf<PT>& np, GroupLogitsBuf<DT>& nd) {
+          if (g + 1 < ngroups) {  // the next group's rows
+            ri = row_info(g + 1);
+            np.load(prs, ri.p_off + pcol, 0u);
+            nd.load(drs, ri.d_off + dcol, 0u);
+          }
+        });
       }
     }
   }
