@@ -699,23 +699,55 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     }
   };
 
+  // CX: two groups in flight (group g + 2 is requested into g's buffers).
+  // PF (the label, whose waves sweep tens of blocks; verification's sweep a
+  // few and measured slower with it): also across blocks when the group
+  // count is even (group 0 / 1 of the next block go into the buffers of the
+  // last two), and the next block's W2 fragments are requested during the
+  // last group's MFMAs
+  constexpr bool PF = CX && LABEL;
+  GroupLogitsBuf<PT> pb0, pb1;
+  GroupLogitsBuf<DT> db0, db1;
+  const bool xpf = PF && ngroups % 2 == 0;
+  bool first = true;
   for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
+    const int nxt = blk + 4;
+    const bool has_next = nxt < blk_end;
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
-    if constexpr (KC > 0) wf.template load<KC>(blk * kWaveCols, w2);
+    if constexpr (KC > 0) {
+      if (!PF || first) wf.template load<KC>(blk * kWaveCols, w2);
+    }
     const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1), ROWS>(lane));
     // one group in the MFMA layout: the draft rows seed the accumulators, the
     // MFMAs add the bias, and the residual mass of the 64 columns is stored;
     // refill requests a later group's rows into the freed buffers before the
-    // epilogue
-    auto group = [&](int g, const ResidualRow& cur, GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db, auto refill) {
+    // epilogue; pf: the block's last group, whose MFMAs are split in two
+    // halves so that each half's W2 registers take the next block's
+    // fragments as soon as the MFMAs reading them have issued
+    auto group = [&](int g, const ResidualRow& cur, GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db, auto refill,
+                     bool pf) {
       const bool lv = live(g);
       float u[16];
       db.unpack(u, cbase, a.V, lv);
       f32x4 acc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
-      if constexpr (KC > 0) mfma_group<KC, false>(st, g, lane, w2, acc, e_off);
+      if constexpr (KC > 0) {
+        if (!pf) {
+          mfma_group<KC, false>(st, g, lane, w2, acc, e_off);
+        } else {
+          constexpr int KH = KC / 2;
+          mfma_group<KC, false, 0, KH>(st, g, lane, w2, acc, e_off);
+          __builtin_amdgcn_sched_barrier(0);
+          wf.template load_range_if<KC, 0, KH>(nxt * kWaveCols, has_next, w2);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_group<KC, false, KH, KC>(st, g, lane, w2, acc, e_off);
+          __builtin_amdgcn_sched_barrier(0);
+          wf.template load_range_if<KC, KH, KC>(nxt * kWaveCols, has_next, w2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       float t[16];
       pb.unpack(t, cbase, a.V, lv);
       refill(pb, db);
@@ -736,39 +768,38 @@ void verify_residual_stream_kernel(VerifyArgs a) {
       }
     };
     if constexpr (CX) {
-      // two groups in flight: group g + 2 is requested into g's buffers
-      GroupLogitsBuf<PT> pb0, pb1;
-      GroupLogitsBuf<DT> db0, db1;
-      cload(pb0, db0, 0, blk);
-      if (ngroups > 1) cload(pb1, db1, 1, blk);
+      if (first || !xpf) {
+        cload(pb0, db0, 0, blk);
+        if (ngroups > 1) cload(pb1, db1, 1, blk);
+      }
       auto step = [&](int g, GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db) {
         xpose(db);
         xpose(pb);
         group(g, row_info(g), pb, db, [&](GroupLogitsBuf<PT>& np, GroupLogitsBuf<DT>& nd) {
           if (g + 2 < ngroups) cload(np, nd, g + 2, blk);
-        });
+          else if (xpf && has_next) cload(np, nd, g + 2 - ngroups, nxt);
+        }, PF && g + 1 == ngroups);
       };
       for (int g = 0; g < ngroups; g += 2) {
         step(g, pb0, db0);
         if (g + 1 < ngroups) step(g + 1, pb1, db1);
       }
     } else {
-      GroupLogitsBuf<PT> pb;
-      GroupLogitsBuf<DT> db;
       ResidualRow ri = row_info(0);
-      pb.load(prs, ri.p_off + pcol, 0u);
-      db.load(drs, ri.d_off + dcol, 0u);
+      pb0.load(prs, ri.p_off + pcol, 0u);
+      db0.load(drs, ri.d_off + dcol, 0u);
       for (int g = 0; g < ngroups; ++g) {
         const ResidualRow cur = ri;
-        group(g, cur, pb, db, [&](GroupLogitsBuf<PT>& np, GroupLogitsBuf<DT>& nd) {
+        group(g, cur, pb0, db0, [&](GroupLogitsBuf<PT>& np, GroupLogitsBuf<DT>& nd) {
           if (g + 1 < ngroups) {  // the next group's rows
             ri = row_info(g + 1);
             np.load(prs, ri.p_off + pcol, 0u);
             nd.load(drs, ri.d_off + dcol, 0u);
           }
-        });
+        }, false);
       }
     }
+    first = false;
   }
 }
 
