@@ -586,6 +586,24 @@ def test_label_ragged_unaligned():
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
 
 
+def test_label_bf16_odd_groups():
+    """bf16 rows, 37 requests x 7 positions = 259 items: stages of 128, 128
+    and 3 items, so the last stage has one 16-row group (an odd count: the
+    next block's rows are not requested early there, its W2 still is) and
+    every wave sweeps several 64-column blocks of the full vocabulary; the
+    oracle checks requests 0, 18 and 36 (36 holds the last stage's items)."""
+    g = torch.Generator().manual_seed(4242)
+    B, K, V, r = 37, 7, 151936, 256
+    P = (torch.randn((B, K, V), generator=g) * 2).to(torch.bfloat16)
+    U = (P.float() + torch.randn((B, K, V), generator=g)).to(torch.bfloat16)
+    W1 = (torch.randn((V, r), generator=g) * 0.05).to(torch.bfloat16)
+    W2 = (torch.randn((V, r), generator=g) * 0.05).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, dtype=torch.int32)
+    got, ref = _label_case(P, U, W1, W2, x0, 1.0, rows=np.array([0, 18, 36]))
+    _say("label bf16 odd groups max |diff| %.2e" % np.abs(got - ref).max())
+    np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
+
+
 def test_label_full_step_sampled():
     """Full-size workload (B=512, K=7, V=151936, r=256, bf16), the launch the
     bench times; the oracle checks 6 requests."""
