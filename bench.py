@@ -6,15 +6,20 @@ early-stopping scheduler on a staircase SPS table (see
 draft_verify_schedule_amd/workloads.py for the value laws).  A step is the
 whole hot path: dspark_markov_draft (K sequential positions), dspark_schedule
 and dspark_verify over the flattened batch the schedule chose.  Inputs are
-resident in HBM before timing starts.  The target model's pass is out of
-scope: its output rows (the flat [N, V] batch) are gathered once before the
-timed loop; the confidences are inputs, so the schedule, and hence the flat
-layout, is the same every step (checked after the timed loop).
+resident in HBM before timing starts; W2's fragment-ordered copy is made once
+per weight load (dspark_markov_prepare_w2) before timing, as a server would
+at start-up.  The target model's pass is out of scope: its output rows (the
+flat [N, V] batch) are gathered once before the timed loop; the confidences
+are inputs, so the schedule, and hence the flat layout, is the same every
+step (checked after the timed loop).
 
 Prints one JSON line: verified draft tokens/s (sum of l_r per step / step
 time), the dominant kernel's roofline (algorithmic bytes per launch / mean
-launch time from HIP events on the library's stream), and the CPU oracle
-timed on a bounded sample of the same workload.
+launch time from HIP events on the library's stream), the other workloads'
+rows (tiny step latency, the verify-only Qwen3-vocabulary workload, the
+DeepSeek-vocabulary and scheduler-stress workloads), a measured device copy
+bandwidth, a cold-cache step time, and the CPU oracle timed on the same
+workload with a process pool over requests.
 """
 import argparse
 import hashlib
@@ -23,11 +28,14 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "verified draft tokens/sec/GPU at V=151936, K=7; HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15       # dense bf16 MFMA, FLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_step.json")
 KERNEL_SOURCES = ["draft.hip", "bias_tile.hpp", "common.hpp", "verify.hip"]
 
@@ -38,6 +46,17 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "draft_verify_schedule_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -51,6 +70,7 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=512, help="requests in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle steps in the timed sample")
     ap.add_argument("--no-next-rows", action="store_true", help="skip timing the rows beyond the step")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' rows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -63,7 +83,6 @@ def main():
               "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import __graft_entry__
@@ -88,7 +107,9 @@ def main():
            "cu_seqlens": torch.empty(B + 1, dtype=torch.int32, device=dev),
            "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
            "theta": torch.empty(1, dtype=torch.float64, device=dev)}
-    ws_d = torch.empty(max(256, ds.dspark_markov_draft_workspace_bytes(B, K, V, r)), dtype=torch.uint8, device=dev)
+    # W2's fragment-ordered copy: made once per weight load, outside the step
+    w2f = ds.dspark_markov_prepare_w2(W2) if r else None
+    ws_d = torch.empty(max(256, ds.dspark_markov_draft_workspace_bytes(B, K, V, 0)), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(max(256, ds.dspark_schedule_workspace_bytes(B, K)), dtype=torch.uint8, device=dev)
     ds.dspark_schedule(c, sps, args.mode, 0, out=sch, workspace=ws_s)
     cu0 = sch["cu_seqlens"].clone()
@@ -101,10 +122,10 @@ def main():
     torch.cuda.synchronize()
 
     def step(s):
-        ds.dspark_markov_draft(U, W1, W2, x0, T, w.rng_seed, s, out=(x, q, lse), workspace=ws_d)
+        ds.dspark_markov_draft(U, W1, W2, x0, T, w.rng_seed, s, out=(x, q, lse), workspace=ws_d, w2f=w2f)
         ds.dspark_schedule(c, sps, args.mode, 0, out=sch, workspace=ws_s)
         ds.dspark_verify(P, sch["cu_seqlens"], U, W1, W2, x0, x, q, lse, T, w.rng_seed, s, out=(n_acc, tok),
-                         workspace=ws_v)
+                         workspace=ws_v, w2f=w2f)
 
     print("warmup %d steps (N=%d verify rows, %d verified drafts/step)" % (args.warmup, N, verified),
           file=sys.stderr, flush=True)
@@ -137,12 +158,28 @@ def main():
     kt = ds.dspark_profiler_read()
     kernels = {k: {"launches": n, "mean_us": 1000.0 * ms / n} for k, (n, ms) in kt.items() if n}
 
-    if args.calibrate_copy:
-        a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
+    # cold caches: a 512 MB write between steps evicts U, W2 and the partials
+    # from the 256 MB MALL and the L2s, and each step is timed alone
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for s_ in range(5):
+        flush.fill_(s_ & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(2000 + s_)
+        e1.record()
         torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    warm = []
+    for s_ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(3000 + s_)
+        e1.record()
+        torch.cuda.synchronize()
+        warm.append(e0.elapsed_time(e1))
+    del flush
+    copy_gbs = copy_bandwidth(torch, dev, calibrate=args.calibrate_copy)
 
     # roofline of the dominant kernel: the fused bias-GEMM + softmax-partials pass
     dom = "draft_partials"
@@ -157,7 +194,11 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-            "algorithmic_bytes_per_launch": per_launch_bytes, "mean_launch_us": round(mean_us, 2)}
+            "algorithmic_bytes_per_launch": per_launch_bytes, "mean_launch_us": round(mean_us, 2),
+            "measured_copy_GB/s": copy_gbs,
+            # the bias GEMM inside the same launch: 2 B r V flops against the dense bf16 MFMA peak
+            "bias_gemm_TFLOP/s": round(2.0 * B * r * V / (mean_us * 1e-6) / 1e12, 1),
+            "bias_gemm_frac_of_bf16_peak": round(2.0 * B * r * V / (mean_us * 1e-6) / MFMA_BF16_PEAK, 4)}
     if "verify_rowstats" in kernels:
         vb = N * V * P.element_size()
         vus = kernels["verify_rowstats"]["mean_us"]
@@ -165,7 +206,7 @@ def main():
                                    "GB/s": round(vb / (vus * 1e-6) / 1e9, 1),
                                    "frac": round(vb / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, P, args)
+    next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, P, args, w2f)
 
     value = verified * args.steps / (total_ms * 1e-3)
     out = {"metric": METRIC, "value": round(value, 1), "unit": "verified draft tokens/s", "n_gpus": 1,
@@ -176,16 +217,164 @@ def main():
                       "sched_mode": ["early_stop", "global", "topk"][args.mode], "verify_rows": N,
                       "verified_drafts_per_step": verified, "accepted_drafts_last_step": accepted,
                       "emitted_tokens_last_step": accepted + B},
-           "roofline": roof, "kernels_us": {k: round(v["mean_us"], 2) for k, v in kernels.items()}}
+           "roofline": roof, "kernels_us": {k: round(v["mean_us"], 2) for k, v in kernels.items()},
+           "cold_cache_step_ms": round(sorted(cold)[len(cold) // 2], 4),
+           "warm_single_step_ms": round(sorted(warm)[len(warm) // 2], 4),
+           "library_build_id": ds.dspark_build_id()}
     if next_rows:
         out["next_rows"] = next_rows
+    if not args.no_configs and args.workload == "full_step":
+        out["configs"] = measure_configs(ds, wl, torch, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args, verified, B)
     print(json.dumps(out), flush=True)
 
 
-def measure_next_rows(ds, w, x, lse, sch, ws_s, P, args):
+def copy_bandwidth(torch, dev, calibrate=False):
+    """Measured device-to-device copy bandwidth (1 GiB read + 1 GiB written
+    per copy), beside the 8 TB/s specification."""
+    a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3 if calibrate else 2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    del a, b
+    return round(2.0 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+
+
+def _event_time_us(torch, fn, n=10, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / n
+
+
+def _kernel_means(ds, torch, fn, n=5):
+    ds.dspark_profiler_reset()
+    ds.dspark_profiler_enable(True)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    ds.dspark_profiler_enable(False)
+    return {k: round(1000.0 * ms / c, 2) for k, (c, ms) in ds.dspark_profiler_read().items() if c}
+
+
+def measure_configs(ds, wl, torch, dev):
+    """The other workloads, each timed on its own inputs:
+    tiny (B=4, K=7, V=1024, r=16, fp32): latency of each call and of one
+      position of the sequential draft loop;
+    qwen_verify (B=64, K=7, V=151936, bf16): verification alone from the
+      logits (the draft's normalisers not given), T = 1 and T = 0, every
+      position verified;
+    ds_stepped (B=256, K=5, V=129280, bf16): the schedule (early stop and no
+      break) and verification of the early-stop layout;
+    sched_stress (B=1024, K=7, V=32768, fp32): the schedule over 7168
+      candidates and verification of its layout."""
+    res = {}
+    # tiny: latency-bound
+    w = wl.make("tiny", device=dev)
+    w2f = ds.dspark_markov_prepare_w2(w.W2)
+    out = (torch.empty((w.B, w.K), dtype=torch.int32, device=dev),
+           torch.empty((w.B, w.K), dtype=torch.float32, device=dev),
+           torch.empty((w.B, w.K), dtype=torch.float32, device=dev))
+    draft = lambda: ds.dspark_markov_draft(w.U, w.W1, w.W2, w.x0, 1.0, w.rng_seed, 0, out=out, w2f=w2f)
+    sch = ds.dspark_schedule(w.c, w.sps)
+    cu = sch["cu_seqlens"]
+    P = wl.flat_target_rows(w.t, cu)
+    x, q, lse = draft()
+    us_draft = _event_time_us(torch, draft)
+    us_sched = _event_time_us(torch, lambda: ds.dspark_schedule(w.c, w.sps, out=sch))
+    us_verify = _event_time_us(torch, lambda: ds.dspark_verify(P, cu, w.U, w.W1, w.W2, w.x0, x, q, lse, 1.0,
+                                                               w.rng_seed, 0, w2f=w2f))
+    res["tiny"] = {"B": w.B, "K": w.K, "V": w.V, "r": w.r, "dtype": "f32", "draft_us": round(us_draft, 1),
+                   "draft_us_per_position": round(us_draft / w.K, 2), "schedule_us": round(us_sched, 1),
+                   "verify_us": round(us_verify, 1), "step_us": round(us_draft + us_sched + us_verify, 1),
+                   "bound": "launch latency (about 0.25 MB touched)"}
+    # qwen_verify: verification alone from the logits
+    w = wl.make("qwen_verify", device=dev)
+    B, K, V = w.B, w.K, w.V
+    cu = torch.arange(0, B * (K + 1) + 1, K + 1, dtype=torch.int32, device=dev)
+    P = wl.flat_target_rows(w.t, cu)
+    row = V * 2
+    for T in (1.0, 0.0):
+        x, _, _ = ds.dspark_markov_draft(w.U, None, None, w.x0, T, w.rng_seed, 0)   # untimed
+        n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+        tok = torch.empty(B, dtype=torch.int32, device=dev)
+        ws = torch.empty(ds.dspark_verify_workspace_bytes(B, K, V, 0, P.shape[0]), dtype=torch.uint8, device=dev)
+        fn = lambda: ds.dspark_verify(P, cu, w.U, None, None, w.x0, x, None, None, T, w.rng_seed, 0,
+                                      out=(n_acc, tok), workspace=ws)
+        us = _event_time_us(torch, fn, n=20)
+        kern = _kernel_means(ds, torch, fn)
+        n_corr = int((n_acc < K).sum().item()) if T > 0 else 0
+        # target rows + draft rows once each; T > 0: plus the rejected position's
+        # target and draft rows again (residual pass) for each correcting request
+        nbytes = B * (K + 1) * row + (B * K * row + 2 * n_corr * row if T > 0 else 0)
+        verified = B * K
+        key = "qwen_verify_T%g" % T
+        res[key] = {"B": B, "K": K, "V": V, "T": T, "dtype": "bf16", "verify_us": round(us, 2),
+                    "verified_draft_tokens_per_s": round(verified / (us * 1e-6), 1),
+                    "accepted_drafts": int(n_acc.sum().item()), "correcting_requests": n_corr,
+                    "normalisers": "recomputed from the draft rows" if T > 0 else "not needed (greedy)",
+                    "roofline": {"bound": "hbm", "algorithmic_bytes": nbytes,
+                                 "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                    "kernels_us": kern}
+    del P
+    # ds_stepped and sched_stress: schedule latency and verification of the layout
+    for name in ("ds_stepped", "sched_stress"):
+        w = wl.make(name, device=dev)
+        B, K, V = w.B, w.K, w.V
+        x, q, lse = ds.dspark_markov_draft(w.U, None, None, w.x0, w.temperature, w.rng_seed, 0)   # untimed
+        ws_s = torch.empty(max(256, ds.dspark_schedule_workspace_bytes(B, K)), dtype=torch.uint8, device=dev)
+        entry = {"B": B, "K": K, "V": V, "dtype": "bf16" if w.U.dtype == torch.bfloat16 else "f32",
+                 "candidates": B * K}
+        for mode, label in ((0, "early_stop"), (1, "global")):
+            sch = ds.dspark_schedule(w.c, w.sps, mode, workspace=ws_s)
+            entry["schedule_%s_us" % label] = round(_event_time_us(
+                torch, lambda: ds.dspark_schedule(w.c, w.sps, mode, out=sch, workspace=ws_s), n=20), 2)
+            entry["admitted_%s" % label] = int(sch["n_admitted"].item())
+        sch = ds.dspark_schedule(w.c, w.sps, 0, workspace=ws_s)
+        cu = sch["cu_seqlens"]
+        N = int(cu[-1].item())
+        P = wl.flat_target_rows(w.t, cu)
+        n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+        tok = torch.empty(B, dtype=torch.int32, device=dev)
+        fn = lambda: ds.dspark_verify(P, cu, w.U, None, None, w.x0, x, q, lse, w.temperature, w.rng_seed, 0,
+                                      out=(n_acc, tok))
+        us = _event_time_us(torch, fn)
+        n_corr = int((n_acc < (cu[1:] - cu[:-1] - 1)).sum().item())
+        row = V * w.U.element_size()
+        nbytes = N * row + 2 * n_corr * row
+        verified = N - B
+        entry.update({"verify_rows": N, "verified_drafts": verified, "verify_us": round(us, 2),
+                      "verified_draft_tokens_per_s": round(verified / (us * 1e-6), 1),
+                      "correcting_requests": n_corr,
+                      "roofline": {"bound": "hbm", "algorithmic_bytes": nbytes,
+                                   "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                      "kernels_us": _kernel_means(ds, torch, fn)})
+        res[name] = entry
+        del P, w
+        torch.cuda.empty_cache()
+    return res
+
+
+def measure_next_rows(ds, w, x, lse, sch, ws_s, P, args, w2f):
     """The rows built beyond the step, timed on the same workload with HIP
     events (library stream = torch's current stream), outside the step:
     the acceptance label of every drafted position, the asynchronous
@@ -211,9 +400,10 @@ def measure_next_rows(ds, w, x, lse, sch, ws_s, P, args):
         return e0.elapsed_time(e1) * 1000.0 / n
 
     us_label = timed(lambda: ds.dspark_acceptance_label(Pk, w.U, w.W1, w.W2, w.x0, x, lse, w.temperature,
-                                                        out=c_lab, workspace=ws_l))
-    # algorithmic bytes: every target and draft row once, plus W2 once
-    lab_bytes = 2 * B * K * V * Pk.element_size() + (V * r * 2 if r else 0)
+                                                        out=c_lab, workspace=ws_l, w2f=w2f))
+    # algorithmic bytes: the target rows twice (their normalisers must be known
+    # before the residual pass), the draft rows once, plus W2 once
+    lab_bytes = 3 * B * K * V * Pk.element_size() + (V * r * 2 if r else 0)
     old = ds.dspark_schedule(w.c, w.sps, 1, 0, workspace=ws_s)    # capacity from the no-break search
     async_out = {k: torch.empty_like(v) for k, v in sch.items()}
     us_async = timed(lambda: ds.dspark_schedule_async(w.c, w.sps, old["n_admitted"], out=async_out,
@@ -266,8 +456,9 @@ def measure_rnn_head(ds, w, P, sch, timed, d):
            torch.empty((B, K), dtype=torch.float32, device=dev),
            torch.empty((B, K, r), dtype=torch.float32, device=dev))
     ws = torch.empty(ds.dspark_rnn_draft_workspace_bytes(B, K, V, r, d), dtype=torch.uint8, device=dev)
+    w2h = ds.dspark_rnn_prepare_w2(w.W2)   # made once per weight load
     draft = lambda: ds.dspark_rnn_draft(w.U, H, Wr, w.W1, w.W2, w.x0, w.temperature, w.rng_seed, 0, out=out,
-                                        workspace=ws)
+                                        workspace=ws, w2h=w2h)
     us_draft = timed(draft)
     ds.dspark_profiler_reset()
     ds.dspark_profiler_enable(True)
@@ -282,7 +473,7 @@ def measure_rnn_head(ds, w, P, sch, timed, d):
     ws_v = torch.empty(ds.dspark_rnn_verify_workspace_bytes(B, K, V, r, N), dtype=torch.uint8, device=dev)
     vout = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
     us_verify = timed(lambda: ds.dspark_rnn_verify(P, sch["cu_seqlens"], w.U, O, w.W2, w.x0, x, q, lse,
-                                                   w.temperature, w.rng_seed, 0, out=vout, workspace=ws_v))
+                                                   w.temperature, w.rng_seed, 0, out=vout, workspace=ws_v, w2h=w2h))
     # the fused pass of one position: U_k, the fp16 W2 and the output parts;
     # its MFMA work is the bias with o split in two (2 x 2 B r V flops)
     part_bytes = B * V * w.U.element_size() + V * r * 2 + B * r * 4
@@ -299,51 +490,75 @@ def measure_rnn_head(ds, w, P, sch, timed, d):
     return res
 
 
+_ORACLE = {}
+
+
+def _oracle_requests(task):
+    """One worker's share of an oracle step: draft + verify of its requests
+    (arrays inherited from the parent at fork)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    ids, step = task
+    g = _ORACLE
+    with threadpool_limits(1):
+        req = g["req"][ids]     # the requests' indices in the batch address their uniforms
+        d = oracle.draft_ref(g["U"][ids], g["W1"], g["W2"], g["x0"][ids], g["T"], g["seed"], step, request_ids=req)
+        ell = g["ell"][ids]
+        cu = np.concatenate([[0], np.cumsum(ell + 1)])
+        rows = np.concatenate([np.arange(g["cu"][i], g["cu"][i + 1]) for i in ids])
+        oracle.verify_ref(g["P"][rows], cu, g["U"][ids], g["W1"], g["W2"], g["x0"][ids], d["x"], g["T"], g["seed"],
+                          step, request_ids=req)
+    return len(ids)
+
+
 def cpu_baseline(w, args, verified, B):
-    """The oracle (float64 NumPy, as it stands) on a bounded sample of the same
-    workload: `cpu_steps` whole steps (schedule of all requests, draft + verify
-    of `cpu_sample` requests, scaled linearly to all B when fewer), reported in
-    the same unit as the GPU figure."""
-    import numpy as np
+    """The oracle (float64 NumPy, as it stands) on the same workload, on the
+    host's cores: the schedule of all requests in one process, then draft +
+    verify of the requests split over a process pool of one worker per core
+    the process may run on (one BLAS thread each); `cpu_steps` whole steps,
+    reported in the same unit as the GPU figure."""
+    import multiprocessing as mp
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores = len(os.sched_getaffinity(0))
     n = min(args.cpu_sample, B)
     sample = np.linspace(0, B - 1, n).round().astype(np.int64)
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
-    Us = f64(w.U[torch.as_tensor(sample, device=w.U.device)])
-    W1 = f64(w.W1) if w.W1 is not None else None
-    W2 = f64(w.W2).T.copy() if w.W2 is not None else None
-    x0 = w.x0.cpu().numpy()[sample]
     c = w.c.cpu().numpy()
     sps = w.sps.cpu().numpy()
+    sch = oracle.schedule_ref(c, sps, args.mode)
+    ell = sch["ell"][sample]
+    cu = np.concatenate([[0], np.cumsum(ell + 1)])
     tf = w.t[torch.as_tensor(sample, device=w.t.device)].cpu()
-    print("cpu baseline: oracle, %d step(s) on %d of %d requests" % (args.cpu_steps, n, B), file=sys.stderr, flush=True)
+    _ORACLE.update({"U": f64(w.U[torch.as_tensor(sample, device=w.U.device)]),
+                    "W1": f64(w.W1) if w.W1 is not None else None,
+                    "W2": f64(w.W2).T.copy() if w.W2 is not None else None,
+                    "x0": w.x0.cpu().numpy()[sample], "req": sample, "T": w.temperature, "seed": w.rng_seed, "ell": ell, "cu": cu,
+                    "P": torch.cat([tf[i, :ell[i] + 1] for i in range(n)]).to(torch.float64).numpy()})
+    del tf
+    print("cpu baseline: oracle, %d step(s) on %d of %d requests, %d worker processes (%s)"
+          % (args.cpu_steps, n, B, cores, cpu_model()), file=sys.stderr, flush=True)
+    chunks = [np.arange(i, min(n, i + 8)) for i in range(0, n, 8)]
     t_sched = t_req = 0.0
-    for s in range(args.cpu_steps):
-        t0 = time.perf_counter()
-        sch = oracle.schedule_ref(c, sps, args.mode)
-        t1 = time.perf_counter()
-        d = oracle.draft_ref(Us, W1, W2, x0, w.temperature, w.rng_seed, s, request_ids=sample)
-        t2 = time.perf_counter()
-        ell = sch["ell"][sample]
-        cu = np.concatenate([[0], np.cumsum(ell + 1)])
-        P = torch.cat([tf[i, :ell[i] + 1] for i in range(n)]).to(torch.float64).numpy()
-        t3 = time.perf_counter()
-        oracle.verify_ref(P, cu, Us, W1, W2, x0, d["x"], w.temperature, w.rng_seed, s, request_ids=sample)
-        t4 = time.perf_counter()
-        t_sched += t1 - t0
-        t_req += (t2 - t1) + (t4 - t3)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        for s in range(args.cpu_steps):
+            t0 = time.perf_counter()
+            oracle.schedule_ref(c, sps, args.mode)
+            t1 = time.perf_counter()
+            done = sum(pool.map(_oracle_requests, [(ch, s) for ch in chunks], chunksize=1))
+            t2 = time.perf_counter()
+            assert done == n
+            t_sched += t1 - t0
+            t_req += t2 - t1
+    _ORACLE.clear()
     step_s = (t_sched + t_req * B / n) / args.cpu_steps
     scaled = "" if n == B else ", scaled linearly to %d" % B
     return {"value": round(verified / step_s, 2), "unit": "verified draft tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "%d oracle step(s) of the same workload: schedule of all %d requests, draft + verify of %d%s; "
-                      "%.1f s of oracle time, %.2f s per step" % (args.cpu_steps, B, n, scaled, t_sched + t_req, step_s)}
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "%d oracle step(s) of the same workload: schedule of all %d requests (one process), draft + "
+                      "verify of %d requests%s over a pool of %d single-threaded worker processes; %.1f s of "
+                      "wall time, %.2f s per step" % (args.cpu_steps, B, n, scaled, cores, t_sched + t_req, step_s)}
 
 
 if __name__ == "__main__":

@@ -16,7 +16,8 @@ _BINDING_NAMES = {
     "dspark_confidence_head", "dspark_sts_fit", "dspark_sts_fit_workspace_bytes",
     "dspark_rnn_draft", "dspark_rnn_draft_workspace_bytes", "dspark_rnn_verify", "dspark_rnn_acceptance_label",
     "dspark_rnn_verify_workspace_bytes", "dspark_rnn_acceptance_label_workspace_bytes",
-    "dspark_status_string", "dspark_version", "dspark_uniforms",
+    "dspark_status_string", "dspark_version", "dspark_build_id", "dspark_uniforms",
+    "dspark_markov_prepare_w2", "dspark_markov_w2_frag_bytes", "dspark_rnn_prepare_w2", "dspark_rnn_w2_f16_bytes",
     "dspark_profiler_enable", "dspark_profiler_reset", "dspark_profiler_read",
     "DSparkError", "load_library", "library_path",
     "DSPARK_F32", "DSPARK_BF16",

@@ -45,11 +45,20 @@ def load_library():
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_status_string.argtypes = [c_int]
     lib.dspark_version.restype = c_int
+    lib.dspark_build_id.restype = ctypes.c_char_p
     lib.dspark_markov_draft_workspace_bytes.restype = c_size
     lib.dspark_markov_draft_workspace_bytes.argtypes = [c_int] * 4
     lib.dspark_markov_draft.restype = c_int
-    lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp,
+    lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp, vp,
                                         c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_markov_w2_frag_bytes.restype = c_size
+    lib.dspark_markov_w2_frag_bytes.argtypes = [c_int, c_int]
+    lib.dspark_markov_prepare_w2.restype = c_int
+    lib.dspark_markov_prepare_w2.argtypes = [c_int, c_int, vp, vp, c_size, vp]
+    lib.dspark_rnn_w2_f16_bytes.restype = c_size
+    lib.dspark_rnn_w2_f16_bytes.argtypes = [c_int, c_int]
+    lib.dspark_rnn_prepare_w2.restype = c_int
+    lib.dspark_rnn_prepare_w2.argtypes = [c_int, c_int, vp, vp, c_size, vp]
     lib.dspark_schedule.restype = c_int
     lib.dspark_schedule_workspace_bytes.restype = c_size
     lib.dspark_schedule_workspace_bytes.argtypes = [c_int] * 2
@@ -59,28 +68,28 @@ def load_library():
     lib.dspark_verify_workspace_bytes.restype = c_size
     lib.dspark_verify_workspace_bytes.argtypes = [c_int] * 5
     lib.dspark_verify.restype = c_int
-    lib.dspark_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp,
-                                  c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, c_size, vp]
+    lib.dspark_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp,
+                                  c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
     lib.dspark_acceptance_label_workspace_bytes.restype = c_size
     lib.dspark_acceptance_label_workspace_bytes.argtypes = [c_int] * 4
     lib.dspark_acceptance_label.restype = c_int
-    lib.dspark_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int, vp, vp,
-                                            vp, vp, vp, c_size, vp]
+    lib.dspark_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, vp, c_int,
+                                            vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_rnn_draft_workspace_bytes.restype = c_size
     lib.dspark_rnn_draft_workspace_bytes.argtypes = [c_int] * 5
     lib.dspark_rnn_draft.restype = c_int
     lib.dspark_rnn_draft.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, vp,
-                                     vp, c_u64, c_u64, vp, vp, vp, vp, vp, c_size, vp]
+                                     vp, vp, c_u64, c_u64, vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_rnn_verify_workspace_bytes.restype = c_size
     lib.dspark_rnn_verify_workspace_bytes.argtypes = [c_int] * 5
     lib.dspark_rnn_acceptance_label_workspace_bytes.restype = c_size
     lib.dspark_rnn_acceptance_label_workspace_bytes.argtypes = [c_int] * 4
     lib.dspark_rnn_verify.restype = c_int
-    lib.dspark_rnn_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp,
-                                      c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, c_size, vp]
+    lib.dspark_rnn_verify.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, c_int, vp, vp, c_int, vp, vp, vp,
+                                      c_int, vp, vp, vp, vp, c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
     lib.dspark_rnn_acceptance_label.restype = c_int
-    lib.dspark_rnn_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, c_int,
-                                                vp, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_rnn_acceptance_label.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, vp, vp, vp,
+                                                c_int, vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_confidence_head.restype = c_int
     lib.dspark_confidence_head.argtypes = [c_int, c_int, c_int, c_int, c_int, vp, c_int, vp, vp, c_float, vp, vp, vp,
                                            vp, vp, vp, vp]
@@ -140,6 +149,11 @@ def dspark_version():
     return load_library().dspark_version()
 
 
+def dspark_build_id():
+    """Hash of the sources the loaded library was built from."""
+    return load_library().dspark_build_id().decode()
+
+
 def dspark_markov_draft_workspace_bytes(B, K, V, r):
     return load_library().dspark_markov_draft_workspace_bytes(B, K, V, r)
 
@@ -148,12 +162,52 @@ def dspark_verify_workspace_bytes(R, K, V, r, N):
     return load_library().dspark_verify_workspace_bytes(R, K, V, r, N)
 
 
-def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, workspace=None):
+def dspark_markov_w2_frag_bytes(V, r):
+    return load_library().dspark_markov_w2_frag_bytes(V, r)
+
+
+def dspark_markov_prepare_w2(W2, out=None):
+    """The fragment-ordered copy of W2 ([V, r] bf16, column-major r x V) that
+    the bias MFMAs read, made once per weight load; pass it as w2f to the
+    draft, verify and label calls.  Returns a uint8 GPU tensor."""
+    lib = load_library()
+    V, r = W2.shape
+    _check(W2, "W2", torch.bfloat16)
+    nbytes = lib.dspark_markov_w2_frag_bytes(V, r)
+    if out is None:
+        out = _workspace(nbytes, W2.device)
+    st = lib.dspark_markov_prepare_w2(V, r, _ptr(W2), _ptr(out), out.numel() * out.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_markov_prepare_w2", st)
+    return out
+
+
+def dspark_rnn_w2_f16_bytes(V, r):
+    return load_library().dspark_rnn_w2_f16_bytes(V, r)
+
+
+def dspark_rnn_prepare_w2(W2, out=None):
+    """The RNN head's fp16 fragment-ordered copy of W2 ([V, r] bf16), made once;
+    pass it as w2h to the RNN calls.  Returns a uint8 GPU tensor."""
+    lib = load_library()
+    V, r = W2.shape
+    _check(W2, "W2", torch.bfloat16)
+    nbytes = lib.dspark_rnn_w2_f16_bytes(V, r)
+    if out is None:
+        out = _workspace(nbytes, W2.device)
+    st = lib.dspark_rnn_prepare_w2(V, r, _ptr(W2), _ptr(out), out.numel() * out.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_rnn_prepare_w2", st)
+    return out
+
+
+def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, workspace=None, w2f=None):
     """Sequential Markov-head draft.
 
     U [B, K, V] f32/bf16; W1 [V, r] bf16; W2 the r x V factor in column-major
     storage, i.e. a [V, r] bf16 tensor whose row v produces logit v; x0 [B]
-    int32.  W1 = W2 = None means no Markov head (r = 0).
+    int32.  W1 = W2 = None means no Markov head (r = 0).  w2f: the copy made
+    by dspark_markov_prepare_w2 (else the call makes one in its workspace).
     Returns (x [B, K] int32, q_tok [B, K] f32, lse [B, K] f32).
     """
     lib = load_library()
@@ -175,7 +229,8 @@ def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, worksp
     if workspace is None:
         workspace = _workspace(need, dev)
     st = lib.dspark_markov_draft(B, K, V, r, float(temperature), _ptr(U), _dtype_code(U), _ptr(W1), _ptr(W2),
-                                 _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q), _ptr(lse), _ptr(workspace),
+                                 _ptr(w2f), _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q), _ptr(lse),
+                                 _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise DSparkError("dspark_markov_draft", st)
@@ -245,13 +300,26 @@ def dspark_schedule_async(c, sps, capacity, out=None, workspace=None):
     return out
 
 
+def _margin_out(min_margin, R, dev):
+    if min_margin is None or min_margin is False:
+        return None
+    if min_margin is True:
+        return torch.empty(R, dtype=torch.float32, device=dev)
+    _check(min_margin, "min_margin", torch.float32, (R,))
+    return min_margin
+
+
 def dspark_verify(P, cu_seqlens, D, W1, W2, x0, x, q_tok, lse_d, temperature, seed, step, out=None,
-                  workspace=None):
+                  workspace=None, w2f=None, min_margin=None):
     """Rejection-sampling verification over the flat batch.
 
     P [N, V] target logits; cu_seqlens [R+1] int32; D [R, K, V] draft base
-    logits; W1 / W2 as for dspark_markov_draft (or None); x0 [R]; x, q_tok,
-    lse_d [R, K] from the draft.  Returns (n_acc [R] int32, tok [R] int32).
+    logits; W1 / W2 as for dspark_markov_draft (or None); x0 [R]; x [R, K]
+    the drafted tokens; q_tok, lse_d [R, K] from the draft, or None (then
+    recomputed from D and the bias); w2f as for dspark_markov_draft.
+    min_margin: True (or an [R] f32 tensor) to also get each request's
+    smallest decision margin.
+    Returns (n_acc [R] int32, tok [R] int32), plus the margins when asked.
     """
     lib = load_library()
     N, V = P.shape
@@ -276,23 +344,24 @@ def dspark_verify(P, cu_seqlens, D, W1, W2, x0, x, q_tok, lse_d, temperature, se
     if out is None:
         out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev))
     n_acc, tok = out
+    mm = _margin_out(min_margin, R, dev)
     need = lib.dspark_verify_workspace_bytes(R, K, V, r, N)
     if workspace is None:
         workspace = _workspace(need, dev)
     st = lib.dspark_verify(R, K, V, float(temperature), _ptr(P), _dtype_code(P), N, _ptr(cu_seqlens), _ptr(D),
-                           _dtype_code(D), _ptr(W1), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(q_tok), _ptr(lse_d),
-                           int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(workspace),
+                           _dtype_code(D), _ptr(W1), _ptr(W2), _ptr(w2f), r, _ptr(x0), _ptr(x), _ptr(q_tok),
+                           _ptr(lse_d), int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(mm), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise DSparkError("dspark_verify", st)
-    return n_acc, tok
+    return (n_acc, tok) if mm is None else (n_acc, tok, mm)
 
 
 def dspark_acceptance_label_workspace_bytes(B, K, V, r):
     return load_library().dspark_acceptance_label_workspace_bytes(B, K, V, r)
 
 
-def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, workspace=None):
+def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, workspace=None, w2f=None):
     """Analytic acceptance probability c*[r, k] = 1 - TV(q_{r,k}, p_{r,k}).
 
     P [B, K, V] target logits (row (r, k) judges draft position k+1); D
@@ -318,7 +387,7 @@ def dspark_acceptance_label(P, D, W1, W2, x0, x, lse_d, temperature, out=None, w
     if workspace is None:
         workspace = _workspace(need, dev)
     st = lib.dspark_acceptance_label(B, K, V, float(temperature), _ptr(P), _dtype_code(P), _ptr(D), _dtype_code(D),
-                                     _ptr(W1), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(lse_d), _ptr(out),
+                                     _ptr(W1), _ptr(W2), _ptr(w2f), r, _ptr(x0), _ptr(x), _ptr(lse_d), _ptr(out),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise DSparkError("dspark_acceptance_label", st)
@@ -329,7 +398,7 @@ def dspark_rnn_draft_workspace_bytes(B, K, V, r, d):
     return load_library().dspark_rnn_draft_workspace_bytes(B, K, V, r, d)
 
 
-def dspark_rnn_draft(U, H, W, W1, W2, x0, temperature, seed, step, out=None, workspace=None):
+def dspark_rnn_draft(U, H, W, W1, W2, x0, temperature, seed, step, out=None, workspace=None, w2h=None):
     """Sequential RNN-head draft.
 
     U [B, K, V] f32/bf16 base logits; H [B, K, d] bf16 hidden states; W
@@ -358,7 +427,7 @@ def dspark_rnn_draft(U, H, W, W1, W2, x0, temperature, seed, step, out=None, wor
     if workspace is None:
         workspace = _workspace(need, dev)
     st = lib.dspark_rnn_draft(B, K, V, r, d, float(temperature), _ptr(U), _dtype_code(U), _ptr(H), DSPARK_BF16,
-                              _ptr(W), _ptr(W1), _ptr(W2), _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q),
+                              _ptr(W), _ptr(W1), _ptr(W2), _ptr(w2h), _ptr(x0), int(seed), int(step), _ptr(x), _ptr(q),
                               _ptr(lse), _ptr(O), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream())
     if st != 0:
@@ -375,7 +444,7 @@ def dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r):
 
 
 def dspark_rnn_verify(P, cu_seqlens, D, O, W2, x0, x, q_tok, lse_d, temperature, seed, step, out=None,
-                      workspace=None):
+                      workspace=None, w2h=None, min_margin=None):
     """Verification of RNN-head drafts: as dspark_verify, with the draft rows'
     bias rebuilt from the output parts O [R, K, r] f32 returned by
     dspark_rnn_draft.  Returns (n_acc [R] int32, tok [R] int32)."""
@@ -403,16 +472,17 @@ def dspark_rnn_verify(P, cu_seqlens, D, O, W2, x0, x, q_tok, lse_d, temperature,
     need = lib.dspark_rnn_verify_workspace_bytes(R, K, V, r, N)
     if workspace is None:
         workspace = _workspace(need, dev)
+    mm = _margin_out(min_margin, R, dev)
     st = lib.dspark_rnn_verify(R, K, V, float(temperature), _ptr(P), _dtype_code(P), N, _ptr(cu_seqlens), _ptr(D),
-                               _dtype_code(D), _ptr(O), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(q_tok), _ptr(lse_d),
-                               int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(workspace),
+                               _dtype_code(D), _ptr(O), _ptr(W2), _ptr(w2h), r, _ptr(x0), _ptr(x), _ptr(q_tok),
+                               _ptr(lse_d), int(seed), int(step), _ptr(n_acc), _ptr(tok), _ptr(mm), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise DSparkError("dspark_rnn_verify", st)
-    return n_acc, tok
+    return (n_acc, tok) if mm is None else (n_acc, tok, mm)
 
 
-def dspark_rnn_acceptance_label(P, D, O, W2, x0, x, lse_d, temperature, out=None, workspace=None):
+def dspark_rnn_acceptance_label(P, D, O, W2, x0, x, lse_d, temperature, out=None, workspace=None, w2h=None):
     """Acceptance label of RNN-head drafts: as dspark_acceptance_label, with
     the output parts O [B, K, r] f32 in place of the Markov embeddings."""
     lib = load_library()
@@ -432,7 +502,8 @@ def dspark_rnn_acceptance_label(P, D, O, W2, x0, x, lse_d, temperature, out=None
     if workspace is None:
         workspace = _workspace(need, dev)
     st = lib.dspark_rnn_acceptance_label(B, K, V, float(temperature), _ptr(P), _dtype_code(P), _ptr(D),
-                                         _dtype_code(D), _ptr(O), _ptr(W2), r, _ptr(x0), _ptr(x), _ptr(lse_d),
+                                         _dtype_code(D), _ptr(O), _ptr(W2), _ptr(w2h), r, _ptr(x0), _ptr(x),
+                                         _ptr(lse_d),
                                          _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream())
     if st != 0:

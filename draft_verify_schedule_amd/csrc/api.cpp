@@ -18,13 +18,16 @@ namespace dspark {
 size_t draft_workspace_bytes(int B, int K, int V);
 size_t w2_swizzle_bytes(int V, int r);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
-              const void* W2, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_out,
-              float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
+              const void* W2, const void* W2f, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out,
+              float* q_out, float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
 size_t schedule_workspace_bytes(int R, int K);
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
                  double* theta_out, void* workspace, hipStream_t stream);
-size_t verify_workspace_bytes(int R, int V, int N);
+size_t verify_workspace_bytes(int R, int K, int V, int r, int N);
+size_t verify_workspace_need(int R, int K, int V, int r, int N, bool lse_given, bool w2f_given, bool margins,
+                             float temperature);
 size_t label_workspace_bytes(int B, int K, int V, int r);
 int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h_bf16, const float* w_h,
                         const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
@@ -33,13 +36,14 @@ size_t sts_workspace_bytes(int G);
 int run_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int G, const float* grid, int nbins,
                 float* T_out, float* ece_out, void* workspace, hipStream_t stream);
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
-              const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
-              float* c_out, void* workspace, const float* O, const uint16_t* W2h, hipStream_t stream);
+              const void* W1, const void* W2, const void* W2f, int r, const int32_t* x0, const int32_t* x,
+              const float* lse_d, float* c_out, void* workspace, const float* O, const uint16_t* W2h,
+              hipStream_t stream);
 int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N, const int32_t* cu,
-               const void* D, bool d_bf16, const void* W1, const void* W2, int r, const int32_t* x0,
-               const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed, uint64_t step,
-               int32_t* n_acc_out, int32_t* tok_out, void* workspace, const float* O, const uint16_t* W2h,
-               hipStream_t stream);
+               const void* D, bool d_bf16, const void* W1, const void* W2, const void* W2f, int r,
+               const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
+               uint64_t step, int32_t* n_acc_out, int32_t* tok_out, float* min_margin_out, void* workspace,
+               const float* O, const uint16_t* W2h, hipStream_t stream);
 int run_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpose, float* out, hipStream_t stream);
 
 // ---- kernel timer --------------------------------------------------------
@@ -134,7 +138,31 @@ const char* dspark_status_string(int status) {
   }
 }
 
-int dspark_version(void) { return 100; }
+int dspark_version(void) { return 200; }
+
+#ifndef DSPARK_BUILD_ID
+#define DSPARK_BUILD_ID "unknown-sources!"
+#endif
+// The marker lets a loader read the id from the file without loading it.
+static const char kBuildTag[] = "dspark-build-id:" DSPARK_BUILD_ID;
+const char* dspark_build_id(void) { return kBuildTag + 16; }
+
+size_t dspark_markov_w2_frag_bytes(int V, int r) {
+  if (V <= 0 || !rank_ok(r)) return 0;
+  return dspark::w2_swizzle_bytes(V, r);
+}
+
+int dspark_markov_prepare_w2(int V, int r, const void* W2, void* W2f, size_t W2f_bytes, void* stream) {
+  if (V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_swizzle_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (r == 0) return DSPARK_OK;
+  if (!W2 || !W2f) return DSPARK_E_NULL;
+  if (W2f_bytes < dspark::w2_swizzle_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  if (!aligned16(W2) || !aligned16(W2f)) return DSPARK_E_RANGE;
+  return hip_status(dspark::run_w2_swizzle(reinterpret_cast<const uint16_t*>(W2), W2f, V, r, (r + 31) / 32, false,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
 
 size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
   if (B <= 0 || V <= 0 || r < 0) return 0;
@@ -143,8 +171,8 @@ size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
 }
 
 int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
-                        const void* W1, const void* W2, const int32_t* x0, uint64_t seed, uint64_t step,
-                        int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
+                        const void* W1, const void* W2, const void* W2f, const int32_t* x0, uint64_t seed,
+                        uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
@@ -155,13 +183,29 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature, const voi
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark_markov_draft_workspace_bytes(B, K, V, r)) return DSPARK_E_WORKSPACE;
+  const size_t need = dspark::draft_workspace_bytes(B, K, V) + (W2f ? 0 : dspark::w2_swizzle_bytes(V, r));
+  if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
-    return DSPARK_E_RANGE;
-  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, x0, seed,
-                                      step, x_out, q_tok_out, lse_out, workspace, nullptr,
+  if (r > 0 && (!aligned16(W1) || !aligned16(W2) || !aligned16(W2f))) return DSPARK_E_RANGE;
+  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr,
+                                      x0, seed, step, x_out, q_tok_out, lse_out, workspace, nullptr,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t dspark_rnn_w2_f16_bytes(int V, int r) {
+  if (V <= 0 || !rnn_rank_ok(r)) return 0;
+  return dspark::w2_f16_bytes(V, r);
+}
+
+int dspark_rnn_prepare_w2(int V, int r, const void* W2, void* W2h, size_t W2h_bytes, void* stream) {
+  if (V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
+  if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_f16_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!W2 || !W2h) return DSPARK_E_NULL;
+  if (W2h_bytes < dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  if (!aligned16(W2) || !aligned16(W2h)) return DSPARK_E_RANGE;
+  return hip_status(dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), reinterpret_cast<uint16_t*>(W2h),
+                                          V, r, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d) {
@@ -172,9 +216,9 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d) {
 }
 
 int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const void* U, int u_dtype,
-                     const void* H, int h_dtype, const void* W, const void* W1, const void* W2, const int32_t* x0,
-                     uint64_t seed, uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, float* o_out,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     const void* H, int h_dtype, const void* W, const void* W1, const void* W2, const void* W2h,
+                     const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out, float* q_tok_out,
+                     float* lse_out, float* o_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (d < 64 || d % 64 != 0) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype) || h_dtype != DSPARK_BF16) return DSPARK_E_DTYPE;
@@ -186,10 +230,12 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !H || !W || !W1 || !W2 || !x0 || !x_out || !q_tok_out || !lse_out || !o_out) return DSPARK_E_NULL;
-  const size_t need = dspark_rnn_draft_workspace_bytes(B, K, V, r, d);
+  const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  const size_t need = base + dspark::rnn_workspace_bytes(B, K, V, r, W2h == nullptr);
   if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (!aligned16(W1) || !aligned16(W2) || !aligned16(H) || !aligned16(W) || !aligned16(o_out)) return DSPARK_E_RANGE;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(H) || !aligned16(W) || !aligned16(o_out) || !aligned16(W2h))
+    return DSPARK_E_RANGE;
   dspark::RnnParams p{};
   p.B = B;
   p.K = K;
@@ -203,10 +249,11 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   p.x = x_out;
   p.O = o_out;
   p.W2 = reinterpret_cast<const uint16_t*>(W2);
-  const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
+  p.w2h_ready = W2h != nullptr;
+  p.W2h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(W2h));
   dspark::rnn_bind_workspace(p, reinterpret_cast<char*>(workspace) + base);
-  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, x0, seed, step,
-                                      x_out, q_tok_out, lse_out, workspace, &p,
+  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, nullptr, x0, seed,
+                                      step, x_out, q_tok_out, lse_out, workspace, &p,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -244,49 +291,48 @@ int dspark_schedule_async(int R, int K, const float* c, const double* sps, int s
 }
 
 size_t dspark_verify_workspace_bytes(int R, int K, int V, int r, int N) {
-  (void)K;
-  (void)r;
-  if (R <= 0 || V <= 0 || N <= 0) return 0;
-  return dspark::verify_workspace_bytes(R, V, N);
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || N <= 0 || !rank_ok(r)) return 0;
+  return dspark::verify_workspace_bytes(R, K, V, r, N);
 }
 
 int dspark_verify(int R, int K, int V, float temperature, const void* P, int p_dtype, int N,
-                  const int32_t* cu_seqlens, const void* D, int d_dtype, const void* W1, const void* W2, int r,
-                  const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
-                  uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  const int32_t* cu_seqlens, const void* D, int d_dtype, const void* W1, const void* W2,
+                  const void* W2f, int r, const int32_t* x0, const int32_t* x, const float* q_tok,
+                  const float* lse_d, uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out,
+                  float* min_margin_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (R < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)N * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)R * K * V * dtype_bytes(d_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)dspark::w2_swizzle_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (R == 0) return DSPARK_OK;  // empty batch
   if (!P || !cu_seqlens || !D || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
-  if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::verify_workspace_bytes(R, V, N)) return DSPARK_E_WORKSPACE;
+  const size_t need = dspark::verify_workspace_need(R, K, V, r, N, lse_d != nullptr, W2f != nullptr,
+                                                    min_margin_out != nullptr, temperature);
+  if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
-    return DSPARK_E_RANGE;
+  if (r > 0 && (!aligned16(W1) || !aligned16(W2) || !aligned16(W2f))) return DSPARK_E_RANGE;
   return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
-                                       d_dtype == DSPARK_BF16, W1, W2, r, x0, x, q_tok, lse_d, seed, step,
-                                       n_acc_out, tok_out, workspace, nullptr, nullptr,
+                                       d_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr, r, x0, x, q_tok, lse_d,
+                                       seed, step, n_acc_out, tok_out, min_margin_out, workspace, nullptr, nullptr,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t dspark_rnn_verify_workspace_bytes(int R, int K, int V, int r, int N) {
-  (void)K;
-  if (R <= 0 || V <= 0 || N <= 0 || r <= 0) return 0;
-  return dspark::verify_workspace_bytes(R, V, N) + dspark::w2_f16_bytes(V, r);
+  if (R <= 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || N <= 0 || !rnn_rank_ok(r)) return 0;
+  return (dspark::verify_workspace_need(R, K, V, 0, N, true, true, true, 1.f) + 255) / 256 * 256 +
+         dspark::w2_f16_bytes(V, r);
 }
 
 int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int p_dtype, int N,
-                      const int32_t* cu_seqlens, const void* D, int d_dtype, const float* O, const void* W2, int r,
-                      const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d, uint64_t seed,
-                      uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      const int32_t* cu_seqlens, const void* D, int d_dtype, const float* O, const void* W2,
+                      const void* W2h, int r, const int32_t* x0, const int32_t* x, const float* q_tok,
+                      const float* lse_d, uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out,
+                      float* min_margin_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (R < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (N < R || (int64_t)N > (int64_t)R * (K + 1)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
@@ -298,16 +344,21 @@ int dspark_rnn_verify(int R, int K, int V, float temperature, const void* P, int
   if (R == 0) return DSPARK_OK;  // empty batch
   if (!P || !cu_seqlens || !D || !O || !W2 || !x0 || !x || !n_acc_out || !tok_out) return DSPARK_E_NULL;
   if (temperature > 0.f && (!q_tok || !lse_d)) return DSPARK_E_NULL;
-  const size_t base = dspark::verify_workspace_bytes(R, V, N);
-  if (!workspace || workspace_bytes < base + dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  // the verify passes see r = 0 (the bias comes from O); margins sized always
+  const size_t base = (dspark::verify_workspace_need(R, K, V, 0, N, true, true, true, 1.f) + 255) / 256 * 256;
+  if (!workspace || workspace_bytes < base + (W2h ? 0 : dspark::w2_f16_bytes(V, r))) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
+  if (!aligned16(O) || !aligned16(W2) || !aligned16(W2h)) return DSPARK_E_RANGE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
-  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, V, r, s)) return DSPARK_E_HIP;
+  const uint16_t* W2hp = reinterpret_cast<const uint16_t*>(W2h);
+  if (!W2hp) {
+    uint16_t* own = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
+    if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), own, V, r, s)) return DSPARK_E_HIP;
+    W2hp = own;
+  }
   return hip_status(dspark::run_verify(R, K, V, temperature, P, p_dtype == DSPARK_BF16, N, cu_seqlens, D,
-                                       d_dtype == DSPARK_BF16, nullptr, W2, r, x0, x, q_tok, lse_d, seed, step,
-                                       n_acc_out, tok_out, workspace, O, W2h, s));
+                                       d_dtype == DSPARK_BF16, nullptr, W2, nullptr, r, x0, x, q_tok, lse_d, seed,
+                                       step, n_acc_out, tok_out, min_margin_out, workspace, O, W2hp, s));
 }
 
 size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
@@ -316,9 +367,9 @@ size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
 }
 
 int dspark_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
-                            int d_dtype, const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x,
-                            const float* lse_d, float* c_out, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            int d_dtype, const void* W1, const void* W2, const void* W2f, int r, const int32_t* x0,
+                            const int32_t* x, const float* lse_d, float* c_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
@@ -330,13 +381,13 @@ int dspark_acceptance_label(int B, int K, int V, float temperature, const void* 
   if (!P || !D || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::label_workspace_bytes(B, K, V, r)) return DSPARK_E_WORKSPACE;
+  const size_t need = dspark::label_workspace_bytes(B, K, V, W2f ? 0 : r);
+  if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (r > 0 && (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(W2) % 16))
-    return DSPARK_E_RANGE;
+  if (r > 0 && (!aligned16(W1) || !aligned16(W2) || !aligned16(W2f))) return DSPARK_E_RANGE;
   return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
-                                      W1, W2, r, x0, x, lse_d, c_out, workspace, nullptr, nullptr,
-                                      reinterpret_cast<hipStream_t>(stream)));
+                                      W1, W2, r > 0 ? W2f : nullptr, r, x0, x, lse_d, c_out, workspace, nullptr,
+                                      nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
@@ -345,9 +396,9 @@ size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r) {
 }
 
 int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const void* P, int p_dtype, const void* D,
-                                int d_dtype, const float* O, const void* W2, int r, const int32_t* x0,
-                                const int32_t* x, const float* lse_d, float* c_out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int d_dtype, const float* O, const void* W2, const void* W2h, int r,
+                                const int32_t* x0, const int32_t* x, const float* lse_d, float* c_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rnn_rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(p_dtype) || !is_dtype(d_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(p_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
@@ -359,14 +410,18 @@ int dspark_rnn_acceptance_label(int B, int K, int V, float temperature, const vo
   if (!P || !D || !O || !W2 || !x0 || !x || !c_out) return DSPARK_E_NULL;
   if (temperature > 0.f && !lse_d) return DSPARK_E_NULL;
   const size_t base = (dspark::label_workspace_bytes(B, K, V, 0) + 255) / 256 * 256;
-  if (!workspace || workspace_bytes < base + dspark::w2_f16_bytes(V, r)) return DSPARK_E_WORKSPACE;
+  if (!workspace || workspace_bytes < base + (W2h ? 0 : dspark::w2_f16_bytes(V, r))) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
-  if (!aligned16(O) || !aligned16(W2)) return DSPARK_E_RANGE;
+  if (!aligned16(O) || !aligned16(W2) || !aligned16(W2h)) return DSPARK_E_RANGE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint16_t* W2h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
-  if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), W2h, V, r, s)) return DSPARK_E_HIP;
+  const uint16_t* W2hp = reinterpret_cast<const uint16_t*>(W2h);
+  if (!W2hp) {
+    uint16_t* own = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + base);
+    if (dspark::run_w2_to_f16(reinterpret_cast<const uint16_t*>(W2), own, V, r, s)) return DSPARK_E_HIP;
+    W2hp = own;
+  }
   return hip_status(dspark::run_label(B, K, V, temperature, P, p_dtype == DSPARK_BF16, D, d_dtype == DSPARK_BF16,
-                                      nullptr, W2, r, x0, x, lse_d, c_out, workspace, O, W2h, s));
+                                      nullptr, W2, nullptr, r, x0, x, lse_d, c_out, workspace, O, W2hp, s));
 }
 
 int dspark_confidence_head(int B, int K, int V, int d, int r, const void* H, int h_dtype, const float* w_h,

@@ -142,6 +142,54 @@ struct W2SwzFrags {
   }
 };
 
+// Either layout chosen at run time: the fragment-ordered copy when the
+// caller supplied one, else the column-major W2.  Both place fragment
+// (b, kc) of the block starting at column n0 at a per-lane offset plus a
+// wave-uniform offset linear in (n0 / 64, b, kc); only the strides differ.
+struct W2AnyFrags {
+  rsrc_t rsrc;
+  uint32_t lane_off, blk_stride, b_stride, kc_stride, bytes;
+  __device__ __forceinline__ void setup(const uint16_t* W2t, const uint16_t* W2s, int r, int V, int lane) {
+    const int kc_count = (r + 31) / 32;
+    if (W2s) {
+      blk_stride = (uint32_t)(4 * kc_count) * 1024u;
+      bytes = (uint32_t)((V + 63) / 64) * blk_stride;
+      rsrc = make_rsrc(W2s, bytes);
+      lane_off = (uint32_t)lane * 16u;
+      b_stride = (uint32_t)kc_count * 1024u;
+      kc_stride = 1024u;
+    } else {
+      const uint32_t col_bytes = (uint32_t)r * 2u;
+      bytes = (uint32_t)V * col_bytes;
+      rsrc = make_rsrc(W2t, bytes);
+      const int a = lane & 15;
+      lane_off = (uint32_t)(16 * (a >> 2) + (a & 3)) * col_bytes + (uint32_t)((lane >> 4) * 8) * 2u;
+      blk_stride = 64u * col_bytes;
+      b_stride = 4u * col_bytes;
+      kc_stride = 64u;
+    }
+  }
+  template <int KC, int K0 = 0, int K1 = KC, typename FT>
+  __device__ __forceinline__ void load_from(uint32_t base, FT (&fr)[4][KC]) const {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int kc = K0; kc < K1; ++kc)
+        fr[b][kc] = __builtin_bit_cast(FT, buffer_load16(rsrc, lane_off, base + (uint32_t)b * b_stride +
+                                                                             (uint32_t)kc * kc_stride));
+    }
+  }
+  // n0: first column of the block (a multiple of 64)
+  template <int KC, typename FT>
+  __device__ __forceinline__ void load(int n0, FT (&fr)[4][KC]) const {
+    load_from<KC>((uint32_t)(n0 / 64) * blk_stride, fr);
+  }
+  template <int KC, int K0, int K1, typename FT>
+  __device__ __forceinline__ void load_range_if(int n0, bool valid, FT (&fr)[4][KC]) const {
+    load_from<KC, K0, K1>(valid ? (uint32_t)(n0 / 64) * blk_stride : bytes, fr);
+  }
+};
+
 // Stage E rows W1[prev(row)] of rows [row0, row0 + kStageRows) into LDS (zeros
 // for rows past nrows, invalid previous tokens, or k >= r).  prev_of(row)
 // returns the previous token of that row or -1.  The 256 threads (4 waves)

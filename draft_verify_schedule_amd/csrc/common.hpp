@@ -111,6 +111,10 @@ __device__ __forceinline__ void buffer_store8_untracked(int4v r, float2 v, uint3
   asm volatile("buffer_store_dwordx2 %0, %1, %2, %3 offen" : : "v"(d), "v"(voffset), "s"(r), "s"(soffset));
 }
 
+__device__ __forceinline__ void buffer_store4_untracked(int4v r, float v, uint32_t voffset, uint32_t soffset) {
+  asm volatile("buffer_store_dword %0, %1, %2, %3 offen" : : "v"(v), "v"(voffset), "s"(r), "s"(soffset));
+}
+
 // Hardware exp2 / log2 (v_exp_f32, v_log_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -215,6 +219,27 @@ __device__ __forceinline__ void merge_argmax(float& m, int& idx, float m2, int i
   if (idx < 0 || m2 > m || (m2 == m && idx2 < idx)) {
     m = m2;
     idx = idx2;
+  }
+}
+
+// (max, first index, second largest value) triples: the greedy statistics
+// with the gap to the runner-up.  A value equal to the max at another index
+// is a runner-up equal to the max (gap 0).  An index of -1 marks an empty
+// partial.
+__device__ __forceinline__ void merge_top2(float& m, int& idx, float& m2, float om, int oidx, float om2) {
+  if (oidx < 0) return;
+  if (idx < 0) {
+    m = om;
+    idx = oidx;
+    m2 = om2;
+    return;
+  }
+  if (om > m || (om == m && oidx < idx)) {
+    m2 = fmaxf(m, om2);
+    m = om;
+    idx = oidx;
+  } else {
+    m2 = fmaxf(m2, om);
   }
 }
 

@@ -702,13 +702,13 @@ int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16
 }
 
 template <typename UT, bool GREEDY>
-static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStream_t stream) {
-  if (!rnn && a.r > 0) {
+static int run_draft_typed(DraftArgs a, bool vec, bool make_w2s, const RnnParams* rnn, hipStream_t stream) {
+  if (make_w2s) {
     const int rc = run_w2_swizzle(a.W2t, const_cast<uint16_t*>(a.W2s), a.V, a.r, (a.r + 31) / 32, false, stream);
     if (rc) return rc;
   }
   if (rnn) {
-    int rc = run_w2_to_f16(rnn->W2, rnn->W2h, a.V, a.r, stream);
+    int rc = rnn->w2h_ready ? 0 : run_w2_to_f16(rnn->W2, rnn->W2h, a.V, a.r, stream);
     if (rc) return rc;
     rc = run_rnn_hproj(*rnn, stream);
     if (rc) return rc;
@@ -733,6 +733,70 @@ static int run_draft_typed(DraftArgs a, bool vec, const RnnParams* rnn, hipStrea
   return 0;
 }
 
+// Log-normaliser of every request's draft row at position a.k from its
+// slice partials (one wave per request): lse = (M + log2 S) ln 2 with
+// M = max of the slices' scaled maxima, S = sum_s s_s 2^(m_s - M).
+__global__ __launch_bounds__(256) void draft_lse_kernel(DraftArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + wave_index();
+  if (b >= a.B) return;
+  const float2* part = a.part + (size_t)b * a.nslices;
+  float m = -INFINITY, s = 0.f;
+  for (int i = lane; i < a.nslices; i += 64) {
+    const float2 p = part[i];
+    merge_ms(m, s, p.x, p.y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    merge_ms(m, s, m2, s2);
+  }
+  if (lane == 0) a.lse_out[(size_t)b * a.K + (a.k - 1)] = (m + fast_log2(s)) * kLn2;
+}
+
+// The draft rows' log-normalisers lse[r, k-1] = log sum_v exp((D[r, k-1, v] +
+// W1[x_{k-1}] W2[:, v]) / T), x_0 = x0, for every request and position (T > 0):
+// the draft's fused bias pass at each position, then the merge above.
+// W2s: the fragment-ordered copy of W2 (required when r > 0); part: slice
+// partials [R, ceil(V / 64)] (draft_workspace_bytes(R, K, V)).
+int run_markov_lse(int R, int K, int V, int r, float temperature, const void* D, bool d_bf16, const void* W1,
+                   const void* W2, const void* W2s, const int32_t* x0, const int32_t* x, float* lse_out,
+                   void* part, hipStream_t stream) {
+  DraftArgs a{};
+  a.U = D;
+  a.W1 = reinterpret_cast<const uint16_t*>(W1);
+  a.W2t = reinterpret_cast<const uint16_t*>(W2);
+  a.W2s = reinterpret_cast<const uint16_t*>(W2s);
+  a.B = R;
+  a.K = K;
+  a.V = V;
+  a.r = r;
+  a.nslices = (V + kWaveCols - 1) / kWaveCols;
+  a.nstages = (R + kStageRows - 1) / kStageRows;
+  a.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / a.nstages));
+  a.part = reinterpret_cast<float2*>(part);
+  a.c2 = kLog2e / temperature;
+  a.lse_out = lse_out;
+  // prev of position k: the anchors at k = 1, then x[:, k-2]
+  const uintptr_t base = reinterpret_cast<uintptr_t>(D);
+  const bool vec = (base % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
+  auto run = [&](auto tag) -> int {
+    using UT = decltype(tag);
+    for (int k = 1; k <= K; ++k) {
+      a.k = k;
+      a.prev = k == 1 ? x0 : x + (k - 2);
+      a.prev_stride = k == 1 ? 1 : K;
+      int rc = vec ? dispatch_kc<UT, true, false>(a, stream) : dispatch_kc<UT, false, false>(a, stream);
+      if (rc) return rc;
+      rc = launch_kernel("draft_lse", draft_lse_kernel, dim3((R + 3) / 4), dim3(256), stream, a);
+      if (rc) return rc;
+    }
+    return 0;
+  };
+  return d_bf16 ? run(uint16_t{}) : run(float{});
+}
+
 size_t draft_workspace_bytes(int B, int K, int V) {
   (void)K;
   const size_t ns = (size_t)(V + kWaveCols - 1) / kWaveCols;
@@ -740,7 +804,7 @@ size_t draft_workspace_bytes(int B, int K, int V) {
 }
 
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16,
-              const void* W1, const void* W2, const int32_t* x0, uint64_t seed, uint64_t step,
+              const void* W1, const void* W2, const void* W2f, const int32_t* x0, uint64_t seed, uint64_t step,
               int32_t* x_out, float* q_out, float* lse_out, void* workspace, const RnnParams* rnn,
               hipStream_t stream) {
   DraftArgs a{};
@@ -759,9 +823,12 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   a.nstages = (B + kStageRows - 1) / kStageRows;
   a.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / a.nstages));
   a.part = reinterpret_cast<float2*>(workspace);
-  // Markov head: the fragment-ordered W2 follows the slice partials
-  a.W2s = (!rnn && r > 0) ? reinterpret_cast<const uint16_t*>(reinterpret_cast<char*>(workspace) +
-                                                              draft_workspace_bytes(B, K, V))
+  // Markov head: the caller's fragment-ordered W2, else a copy made here
+  // after the slice partials
+  const bool make_w2s = !rnn && r > 0 && !W2f;
+  a.W2s = (!rnn && r > 0) ? (W2f ? reinterpret_cast<const uint16_t*>(W2f)
+                                 : reinterpret_cast<const uint16_t*>(reinterpret_cast<char*>(workspace) +
+                                                                     draft_workspace_bytes(B, K, V)))
                           : nullptr;
   a.seed = seed;
   a.step = step;
@@ -775,12 +842,12 @@ int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool
   const uintptr_t base = reinterpret_cast<uintptr_t>(U);
   if (u_bf16) {
     const bool vec = (V % 8 == 0) && (base % 16 == 0);
-    return greedy ? run_draft_typed<uint16_t, true>(a, vec, rnn, stream)
-                  : run_draft_typed<uint16_t, false>(a, vec, rnn, stream);
+    return greedy ? run_draft_typed<uint16_t, true>(a, vec, make_w2s, rnn, stream)
+                  : run_draft_typed<uint16_t, false>(a, vec, make_w2s, rnn, stream);
   }
   const bool vec = (V % 4 == 0) && (base % 16 == 0);
-  return greedy ? run_draft_typed<float, true>(a, vec, rnn, stream)
-                : run_draft_typed<float, false>(a, vec, rnn, stream);
+  return greedy ? run_draft_typed<float, true>(a, vec, make_w2s, rnn, stream)
+                : run_draft_typed<float, false>(a, vec, make_w2s, rnn, stream);
 }
 
 }  // namespace dspark

@@ -238,9 +238,9 @@ size_t w2_f16_bytes(int V, int r) {
   return (size_t)((V + 63) / 64) * 4 * kRnnChunks * 1024;
 }
 
-size_t rnn_workspace_bytes(int B, int K, int V, int r) {
+size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h) {
   return align256_rnn((size_t)B * K * 3 * r * sizeof(float)) + 2 * align256_rnn((size_t)B * r * sizeof(float)) +
-         w2_f16_bytes(V, r);
+         (with_w2h ? w2_f16_bytes(V, r) : 0);
 }
 
 void rnn_bind_workspace(RnnParams& p, void* workspace) {
@@ -251,7 +251,7 @@ void rnn_bind_workspace(RnnParams& p, void* workspace) {
   ws += align256_rnn((size_t)p.B * p.r * sizeof(float));
   p.s[1] = reinterpret_cast<float*>(ws);
   ws += align256_rnn((size_t)p.B * p.r * sizeof(float));
-  p.W2h = reinterpret_cast<uint16_t*>(ws);
+  if (!p.w2h_ready) p.W2h = reinterpret_cast<uint16_t*>(ws);
 }
 
 int run_w2_to_f16(const uint16_t* W2, uint16_t* out, int V, int r, hipStream_t stream) {

@@ -19,12 +19,15 @@ struct RnnParams {
   float* Hp;           // workspace [B * K, 3r]: W[:, 2r:] h for every (request, position)
   float* s[2];         // workspace [B, r] x 2: state of the odd / even positions
   float* O;            // [B, K, r] output parts o_k (the caller's buffer)
-  uint16_t* W2h;       // workspace: fp16 copy of W2 in MFMA fragment order
+  uint16_t* W2h;       // fp16 copy of W2 in MFMA fragment order (caller's, or in the workspace)
+  bool w2h_ready;      // W2h was made by the caller: the call does not rebuild it
   const uint16_t* W2;  // [V, r] bf16 column-major W2
 };
 
-size_t rnn_workspace_bytes(int B, int K, int V, int r);
-// Carves Hp, the two state buffers and W2h out of a workspace of rnn_workspace_bytes.
+// with_w2h: room for the fp16 copy of W2 (absent when the caller made it)
+size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h = true);
+// Carves Hp, the two state buffers and W2h out of a workspace of
+// rnn_workspace_bytes; a caller-made copy (p.w2h_ready) is kept.
 void rnn_bind_workspace(RnnParams& p, void* workspace);
 // fp16 copy of the column-major bf16 W2 in MFMA fragment order (the layout
 // W2SwzFrags reads): the operand the split output parts meet on the MFMA.

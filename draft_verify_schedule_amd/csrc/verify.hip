@@ -64,7 +64,24 @@ struct VerifyArgs {
   int32_t* rej_count;       // [1]
   int nsP, ns64, nchunks;
   int ncol_tiles, nstages;
+  // rows of a rowstats pass over the draft rows D [R * K, V]: row r * K + j is
+  // streamed only when j < l_r (cu_seqlens of the verify layout); else null
+  const int32_t* row_cu;
+  int row_K;
+  float* ppart2;            // greedy: runner-up value per slice [N, nsP] (else null)
+  float* margin;            // [N]  decision margin of each flat row (else null)
+  float* rmin;              // [R]  smallest accept margin of each request (T > 0)
+  float* min_margin_out;    // [R]  or null
 };
+
+// Whether row q of a pass over the draft rows is judged by the layout
+// (request q / K, position q % K < l_r); every row when no filter is set.
+__device__ __forceinline__ bool drow_judged(const VerifyArgs& a, int q) {
+  if (!a.row_cu) return true;
+  const int r = q / a.row_K;
+  const int j = q - r * a.row_K;
+  return j < a.row_cu[r + 1] - a.row_cu[r] - 1;
+}
 
 // ---------------------------------------------------------------- rowstats --
 template <typename PT, bool VEC, bool GREEDY>
@@ -74,9 +91,10 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const int wbase = chunk * kRowChunk + wave * (kRowChunk / 4);
-  if (wbase >= a.V) return;
+  if (wbase >= a.V || !drow_judged(a, row)) return;
   const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)row * a.V;
   float2* out = a.ppart + (size_t)row * a.nsP;
+  float* out2 = a.ppart2 ? a.ppart2 + (size_t)row * a.nsP : nullptr;
 
   if constexpr (VEC) {
     constexpr int EPL = 16 / sizeof(PT);          // elements per 16-byte load
@@ -110,21 +128,22 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
       const int c = wbase + it * COLS + lane * EPL;
       const int slice = (wbase + it * COLS) / kRowSlice + lane / LPS;
       if constexpr (GREEDY) {
-        float m = -INFINITY;
+        float m = -INFINITY, m2 = -INFINITY;
         int idx = -1;
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-          if (c + e < a.V && (idx < 0 || v[it][e] > m)) {
-            m = v[it][e];
-            idx = c + e;
-          }
+          if (c + e < a.V) merge_top2(m, idx, m2, v[it][e], c + e, -INFINITY);
 #pragma unroll
         for (int off = 1; off < LPS; off <<= 1) {
-          const float m2 = __shfl_xor(m, off, 64);
-          const int i2 = __shfl_xor(idx, off, 64);
-          merge_argmax(m, idx, m2, i2);
+          const float om = __shfl_xor(m, off, 64);
+          const int oi = __shfl_xor(idx, off, 64);
+          const float om2 = __shfl_xor(m2, off, 64);
+          merge_top2(m, idx, m2, om, oi, om2);
         }
-        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) out[slice] = make_float2(m, __int_as_float(idx));
+        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) {
+          out[slice] = make_float2(m, __int_as_float(idx));
+          if (out2) out2[slice] = m2;
+        }
       } else {
         float m = -INFINITY;
 #pragma unroll
@@ -157,20 +176,24 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
       }
       const int slice = sbase / kRowSlice;
       if constexpr (GREEDY) {
-        float m = -INFINITY;
+        float m = -INFINITY, m2 = -INFINITY;
         int idx = -1;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int c = sbase + 64 * t + lane;
-          if (c < a.V) merge_argmax(m, idx, v[t], c);
+          if (c < a.V) merge_top2(m, idx, m2, v[t], c, -INFINITY);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-          const float m2 = __shfl_xor(m, off, 64);
-          const int i2 = __shfl_xor(idx, off, 64);
-          merge_argmax(m, idx, m2, i2);
+          const float om = __shfl_xor(m, off, 64);
+          const int oi = __shfl_xor(idx, off, 64);
+          const float om2 = __shfl_xor(m2, off, 64);
+          merge_top2(m, idx, m2, om, oi, om2);
         }
-        if (lane == 0) out[slice] = make_float2(m, __int_as_float(idx));
+        if (lane == 0) {
+          out[slice] = make_float2(m, __int_as_float(idx));
+          if (out2) out2[slice] = m2;
+        }
       } else {
         float m = -INFINITY;
 #pragma unroll
@@ -217,8 +240,10 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
   const int4v ors = raw_rsrc_words(a.ppart, obytes);
   const bool leader = (lane % LPS) == 0;
 
+  const uint32_t o2bytes = a.ppart2 ? obytes / 2u : 0u;
+  const int4v o2rs = raw_rsrc_words(a.ppart2, o2bytes);
   auto issue = [&](int item, u32x4 (&w)[LOADS]) {
-    const bool live = item < items;
+    const bool live = item < items && drow_judged(a, item / a.nchunks);
     const int row = live ? item / a.nchunks : 0;
     const int chunk = live ? item - row * a.nchunks : 0;
     const int wbase = chunk * kRowChunk + wave * kWaveColsR;
@@ -247,22 +272,22 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
       }
     }
     float2 res;
+    float runner_up = 0.f;
     if constexpr (GREEDY) {
-      float m = -INFINITY;
+      float m = -INFINITY, m2 = -INFINITY;
       int idx = -1;
 #pragma unroll
       for (int e = 0; e < CPL; ++e)
-        if (c0 + e < a.V && (idx < 0 || v[e] > m)) {
-          m = v[e];
-          idx = c0 + e;
-        }
+        if (c0 + e < a.V) merge_top2(m, idx, m2, v[e], c0 + e, -INFINITY);
 #pragma unroll
       for (int off = 1; off < LPS; off <<= 1) {
-        const float m2 = __shfl_xor(m, off, 64);
-        const int i2 = __shfl_xor(idx, off, 64);
-        merge_argmax(m, idx, m2, i2);
+        const float om = __shfl_xor(m, off, 64);
+        const int oi = __shfl_xor(idx, off, 64);
+        const float om2 = __shfl_xor(m2, off, 64);
+        merge_top2(m, idx, m2, om, oi, om2);
       }
       res = make_float2(m, __int_as_float(idx));
+      runner_up = m2;
     } else {
       float m = v[0];
 #pragma unroll
@@ -282,6 +307,9 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
     const uint32_t voff = (leader && slice < a.nsP) ? (uint32_t)(((uint64_t)row * a.nsP + slice) * sizeof(float2))
                                                     : obytes;
     buffer_store8_untracked(ors, res, voff, 0u);
+    if constexpr (GREEDY) {
+      if (a.ppart2) buffer_store4_untracked(o2rs, runner_up, voff / 2u, 0u);  // offsets past the resource drop
+    }
   };
 
   int item = blockIdx.x;
@@ -356,59 +384,122 @@ __device__ __forceinline__ void merge_row(const float2* __restrict__ part, int n
   }
 }
 
-template <typename PT, bool GREEDY>
+// The draft logit z_q(x) = D[r, j, x] + W1[prev] . W2[:, x] of one column
+// by a whole wave (lane l takes the weights k = 8 l .. 8 l + 7, fp32
+// products, wave sum); used when the caller gives no q_tok.
+template <typename DT>
+__device__ __forceinline__ float draft_logit_wave(const VerifyArgs& a, int r, int j, int xcol) {
+  const int lane = threadIdx.x & 63;
+  const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)r * a.K + j) * a.V;
+  float bias = 0.f;
+  if (a.r > 0) {
+    const int prev = j == 0 ? a.x0[r] : a.x[(size_t)r * a.K + j - 1];
+    const int pv = (prev >= 0 && prev < a.V) ? prev : 0;  // an invalid token flags the request elsewhere
+    const int k = 8 * lane;
+    if (k < a.r) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(a.W1 + (size_t)pv * a.r + k);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(a.W2t + (size_t)xcol * a.r + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bias = fmaf(__uint_as_float(e[i] << 16), __uint_as_float(w[i] << 16), bias);
+        bias = fmaf(__uint_as_float(e[i] & 0xFFFF0000u), __uint_as_float(w[i] & 0xFFFF0000u), bias);
+      }
+    }
+    bias = wave_sum(bias);
+  }
+  return load_logit(drow, xcol) + bias;
+}
+
+template <typename PT, typename DT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_accept_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave_index();
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.rej_count = 0;  // filled by the decide kernel
   if (i >= a.N) return;
   const float2* part = a.ppart + (size_t)i * a.nsP;
-  float m, s;
+  float m, s = 0.f, m2 = -INFINITY;
   int idx;
-  merge_row<GREEDY>(part, a.nsP, m, s, idx);
+  if constexpr (GREEDY) {
+    // (max, first argmax, runner-up): lane l merges slices l, l + 64, ...
+    m = -INFINITY;
+    idx = -1;
+    const float* part2 = a.ppart2 ? a.ppart2 + (size_t)i * a.nsP : nullptr;
+    for (int k0 = 0; k0 < a.nsP; k0 += 64 * kMergePer) {
+      float2 pv[kMergePer];
+      float p2[kMergePer];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, 64);
-    if constexpr (GREEDY) {
-      const int i2 = __shfl_xor(idx, off, 64);
-      merge_argmax(m, idx, m2, i2);
-    } else {
-      const float s2 = __shfl_xor(s, off, 64);
-      merge_ms(m, s, m2, s2);
+      for (int t = 0; t < kMergePer; ++t) {
+        const int k = k0 + lane + 64 * t;
+        pv[t] = k < a.nsP ? part[k] : make_float2(-INFINITY, __int_as_float(-1));
+        p2[t] = (part2 && k < a.nsP) ? part2[k] : -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < kMergePer; ++t) merge_top2(m, idx, m2, pv[t].x, __float_as_int(pv[t].y), p2[t]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(m, off, 64);
+      const int oi = __shfl_xor(idx, off, 64);
+      const float om2 = __shfl_xor(m2, off, 64);
+      merge_top2(m, idx, m2, om, oi, om2);
+    }
+  } else {
+    merge_row<false>(part, a.nsP, m, s, idx);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(m, off, 64);
+      const float os = __shfl_xor(s, off, 64);
+      merge_ms(m, s, om, os);
     }
   }
   const int r = owner_of_wave(a.cu, a.R, i);
-  if (lane != 0) return;
-  a.rowms[i] = GREEDY ? make_float2(m, __int_as_float(idx)) : make_float2(m, s);
+  if (lane == 0) a.rowms[i] = GREEDY ? make_float2(m, __int_as_float(idx)) : make_float2(m, s);
 
   const int c0 = a.cu[r], c1 = a.cu[r + 1];
-  if (!(c0 >= 0 && c0 <= i && i < c1 && c1 <= a.N && c1 - c0 <= a.K + 1)) {
-    a.flag[i] = 2;
-    return;
-  }
   const int j = i - c0;             // this row judges draft position j + 1
-  if (j >= c1 - c0 - 1) {
-    a.flag[i] = 3;                  // bonus row
-    return;
-  }
-  const int xj = a.x[(size_t)r * a.K + j];
-  if (xj < 0 || xj >= a.V) {
-    a.flag[i] = 2;
-    return;
-  }
-  bool accept;
-  if constexpr (GREEDY) {
-    accept = (idx == xj);
+  int state;                        // 2 bad row, 3 bonus row, else a draft to judge
+  int xj = 0;
+  if (!(c0 >= 0 && c0 <= i && i < c1 && c1 <= a.N && c1 - c0 <= a.K + 1)) {
+    state = 2;
+  } else if (j >= c1 - c0 - 1) {
+    state = 3;
   } else {
-    const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)i * a.V;
-    const float t = load_logit(prow, xj) * a.c2;
-    const float p = exp2f(t - m) / s;
-    const float q = a.q_tok[(size_t)r * a.K + j];
-    const float ratio = (q > 0.f) ? p / q : INFINITY;
-    const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept);
-    accept = u < ratio;
+    xj = a.x[(size_t)r * a.K + j];
+    state = (xj < 0 || xj >= a.V) ? 2 : 0;
   }
-  a.flag[i] = accept ? 1 : 0;
+  // the decision margin: the target's top-2 gap (greedy), else |u - ratio|
+  const float gap = m - m2;
+  if (state != 0) {
+    if (lane == 0) {
+      a.flag[i] = state;
+      if (a.margin) a.margin[i] = (state == 3 && GREEDY) ? gap : NAN;
+    }
+    return;
+  }
+  if constexpr (GREEDY) {
+    if (lane == 0) {
+      a.flag[i] = (idx == xj) ? 1 : 0;
+      if (a.margin) a.margin[i] = gap;
+    }
+  } else {
+    float q;
+    if (a.q_tok) {
+      q = a.q_tok[(size_t)r * a.K + j];
+    } else {
+      // q_j(x_j) = exp((z_q(x_j) - lse) / T), lse from the caller or the pass over the draft rows
+      const float zq = draft_logit_wave<DT>(a, r, j, xj);
+      q = fast_exp2(fmaf(zq, a.c2, -a.lse_d[(size_t)r * a.K + j] * kLog2e));
+    }
+    if (lane == 0) {
+      const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)i * a.V;
+      const float t = load_logit(prow, xj) * a.c2;
+      const float p = exp2f(t - m) / s;
+      const float ratio = (q > 0.f) ? p / q : INFINITY;
+      const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)(j + 1), kPurposeAccept);
+      a.flag[i] = (u < ratio) ? 1 : 0;
+      if (a.margin) a.margin[i] = fabsf(u - ratio);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ decide --
@@ -438,6 +529,7 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
     a.info[r] = make_int4(-1, 0, 0, 0);
     a.n_acc_out[r] = -1;
     a.tok_out[r] = -1;
+    if (a.min_margin_out) a.min_margin_out[r] = NAN;
     return;
   }
   const int mode = (n < L) ? 1 : 0;  // 1: correction from the residual, 0: bonus
@@ -445,6 +537,19 @@ __global__ __launch_bounds__(256) void verify_decide_kernel(VerifyArgs a) {
   if (!GREEDY && mode == 1) a.rej_list[atomicAdd(a.rej_count, 1)] = r;
   a.n_acc_out[r] = n;
   if constexpr (GREEDY) a.tok_out[r] = __float_as_int(a.rowms[c0 + n].y);
+  if (a.min_margin_out) {
+    // rows examined: the accept tests j = 0 .. min(n, L - 1); when greedy
+    // also the row whose argmax is emitted (row n: the rejected or the bonus row)
+    const int last = GREEDY ? n : min(n, L - 1);
+    float mg[kMaxPositions + 1];
+#pragma unroll
+    for (int j = 0; j <= kMaxPositions; ++j) mg[j] = (j <= last) ? a.margin[c0 + j] : INFINITY;
+    float mm = INFINITY;
+#pragma unroll
+    for (int j = 0; j <= kMaxPositions; ++j) mm = fminf(mm, mg[j]);
+    if constexpr (GREEDY) a.min_margin_out[r] = mm;
+    else a.rmin[r] = mm;  // the draw's own margin is added by the sample kernel
+  }
 }
 
 // ---------------------------------------------------------------- residual --
@@ -638,9 +743,9 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   std::conditional_t<ROWS, f16x8, bf16x8> w2[4][(KC > 0 ? KC : 1)];
   // fragment-ordered W2 (one contiguous KB per fragment load): the label's
   // Markov pass and the RNN head's fp16 copy; Markov verification reads the
-  // column-major W2
+  // caller's fragment-ordered copy when given, else the column-major W2
   constexpr bool SWZ = LABEL || ROWS;
-  std::conditional_t<SWZ, W2SwzFrags, W2Frags> wf;
+  std::conditional_t<SWZ, W2SwzFrags, W2AnyFrags> wf;
   if constexpr (KC > 0) {
     const int32_t* list = a.rej_list;
     const int4* info = a.info;
@@ -662,7 +767,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
       });
     }
     if constexpr (SWZ) wf.setup(ROWS ? a.W2h : a.W2s, KC, a.V, lane);
-    else wf.setup(a.W2t, a.r, a.V, lane);
+    else wf.setup(a.W2t, a.W2s, a.r, a.V, lane);
   }
   __syncthreads();
 
@@ -944,11 +1049,21 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
       const float t_in = (float)(target - h.before);
       const float cum = wave_inclusive_scan(rho);
       int pick = wave_first_lane(cum > t_in && rho > 0.f);
-      if (pick < 0) {
+      // the draw's margin: distance of the target from the nearer CDF edge of
+      // the drawn column, over the total mass (0 when rounding picked it)
+      float edge = INFINITY;
+      if (pick >= 0) {
+        const float hi = __shfl(cum, pick, 64), w = __shfl(rho, pick, 64);
+        edge = fminf(hi - t_in, t_in - (hi - w));
+      } else {
         const unsigned long long m = __ballot(rho > 0.f);
         pick = m ? 63 - __clzll((long long)m) : 0;
+        edge = 0.f;
       }
-      if (lane == 0) a.tok_out[r] = h.slice * kWaveCols + pick;
+      if (lane == 0) {
+        a.tok_out[r] = h.slice * kWaveCols + pick;
+        if (a.min_margin_out) a.min_margin_out[r] = fminf(a.rmin[r], (float)((double)edge / Z));
+      }
       return;
     }
     use_p = true;  // zero residual mass (rounding only): draw from p
@@ -1012,11 +1127,13 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   if (lane == owner) {
     float acc = incl2 - lsum;
     int last = 0;
+    float edge = 0.f;  // distance of the target from the drawn column's CDF edges (0: picked by rounding)
     for (int k = 0; k < 4; ++k) {
       if (e[k] > 0.f) {
         last = k;
         if (acc + e[k] > t_in) {
           pick = k;
+          edge = fminf(acc + e[k] - t_in, t_in - acc);
           break;
         }
       }
@@ -1024,6 +1141,11 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     }
     if (pick < 0) pick = last;
     a.tok_out[r] = h.slice * kRowSlice + 4 * lane + pick;
+    if (a.min_margin_out) {
+      // the slice's values are scaled by 2^(M - m_s) against the masses summing to S
+      const float mg = S > 0.0 ? (float)((double)edge * (double)fast_exp2(m_s - M) / S) : 0.f;
+      a.min_margin_out[r] = fminf(a.rmin[r], mg);
+    }
   }
 }
 
@@ -1031,31 +1153,70 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct VerifyLayout {
-  size_t ppart, rowms, flag, info, rpart, rej, total;
+  size_t ppart, rowms, flag, info, rpart, rej, margin, rmin, ppart2, lse, dpart, w2s, total;
 };
 
-static VerifyLayout verify_layout(int R, int V, int N) {
+size_t draft_workspace_bytes(int B, int K, int V);
+size_t w2_swizzle_bytes(int V, int r);
+int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
+
+// lse_pass: room to recompute the draft rows' log-normalisers (r == 0: the
+// rowstats partials of the R * K draft rows; r > 0: the draft's slice
+// partials of one position, plus the fragment-ordered W2 when make_w2s).
+// margins: the per-row decision margins and the greedy runner-ups.
+static VerifyLayout verify_layout(int R, int K, int V, int N, int r, bool lse_pass, bool make_w2s, bool margins) {
   VerifyLayout l{};
   const size_t nsP = (V + kRowSlice - 1) / kRowSlice;
   const size_t ns64 = (V + kWaveCols - 1) / kWaveCols;
   size_t off = 0;
-  l.ppart = off;
-  off += align256((size_t)N * nsP * sizeof(float2));
-  l.rowms = off;
-  off += align256((size_t)N * sizeof(float2));
-  l.flag = off;
-  off += align256((size_t)N * sizeof(int32_t));
-  l.info = off;
-  off += align256((size_t)R * sizeof(int4));
-  l.rpart = off;
-  off += align256((size_t)R * ns64 * sizeof(float));
-  l.rej = off;
-  off += align256((size_t)(R + 1) * sizeof(int32_t));
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off += align256(bytes);
+  };
+  take(l.ppart, (size_t)N * nsP * sizeof(float2));
+  take(l.rowms, (size_t)N * sizeof(float2));
+  take(l.flag, (size_t)N * sizeof(int32_t));
+  take(l.info, (size_t)R * sizeof(int4));
+  take(l.rpart, (size_t)R * ns64 * sizeof(float));
+  take(l.rej, (size_t)(R + 1) * sizeof(int32_t));
+  take(l.margin, margins ? (size_t)N * sizeof(float) : 0);
+  take(l.rmin, margins ? (size_t)R * sizeof(float) : 0);
+  take(l.ppart2, margins ? (size_t)N * nsP * sizeof(float) : 0);
+  take(l.lse, lse_pass ? (size_t)R * K * sizeof(float) : 0);
+  take(l.dpart, !lse_pass ? 0 : r == 0 ? (size_t)R * K * nsP * sizeof(float2) : draft_workspace_bytes(R, K, V));
+  take(l.w2s, (lse_pass && r > 0 && make_w2s) ? w2_swizzle_bytes(V, r) : 0);
   l.total = off;
   return l;
 }
 
-size_t verify_workspace_bytes(int R, int V, int N) { return verify_layout(R, V, N).total; }
+// The query: enough for every combination of optional inputs and outputs.
+size_t verify_workspace_bytes(int R, int K, int V, int r, int N) {
+  return verify_layout(R, K, V, N, r, true, true, true).total;
+}
+size_t verify_workspace_need(int R, int K, int V, int r, int N, bool lse_given, bool w2f_given, bool margins,
+                             float temperature) {
+  const bool lse_pass = !lse_given && temperature > 0.f;
+  return verify_layout(R, K, V, N, r, lse_pass, !w2f_given, margins).total;
+}
+
+// Log-normaliser of each row from its 256-column rowstats partials (one wave
+// per row): lse = (M + log2 S) ln 2, the draft's convention.
+__global__ __launch_bounds__(256) void row_lse_kernel(const float2* __restrict__ part, int nrows, int ns,
+                                                      float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave_index();
+  if (i >= nrows) return;
+  float m, s;
+  int idx;
+  merge_row<false>(part + (size_t)i * ns, ns, m, s, idx);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float om = __shfl_xor(m, off, 64);
+    const float os = __shfl_xor(s, off, 64);
+    merge_ms(m, s, om, os);
+  }
+  if (lane == 0) lse[i] = (m + fast_log2(s)) * kLn2;
+}
 
 // ------------------------------------------------------- acceptance label --
 // c*_i = 1 - 1/2 ||q_i - p_i||_1 for every (request, position) item
@@ -1162,6 +1323,10 @@ static int dispatch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   }
 }
 
+int run_markov_lse(int R, int K, int V, int r, float temperature, const void* D, bool d_bf16, const void* W1,
+                   const void* W2, const void* W2s, const int32_t* x0, const int32_t* x, float* lse_out,
+                   void* part, hipStream_t stream);
+
 template <typename PT, typename DT>
 static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, hipStream_t stream) {
   int rc;
@@ -1173,7 +1338,7 @@ static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, 
                : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, true>,
                                dim3(a.N * a.nchunks), b256, stream, a);
     if (rc) return rc;
-    rc = launch_kernel("verify_accept", verify_accept_kernel<PT, true>, dim3((a.N + 3) / 4), b256, stream, a);
+    rc = launch_kernel("verify_accept", verify_accept_kernel<PT, DT, true>, dim3((a.N + 3) / 4), b256, stream, a);
     if (rc) return rc;
     return launch_kernel("verify_decide", verify_decide_kernel<true>, dim3((a.R + 255) / 256), b256, stream, a);
   }
@@ -1182,7 +1347,7 @@ static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, 
              : launch_kernel("verify_rowstats", verify_rowstats_kernel<PT, false, false>,
                              dim3(a.N * a.nchunks), b256, stream, a);
   if (rc) return rc;
-  rc = launch_kernel("verify_accept", verify_accept_kernel<PT, false>, dim3((a.N + 3) / 4), b256, stream, a);
+  rc = launch_kernel("verify_accept", verify_accept_kernel<PT, DT, false>, dim3((a.N + 3) / 4), b256, stream, a);
   if (rc) return rc;
   rc = launch_kernel("verify_decide", verify_decide_kernel<false>, dim3((a.R + 255) / 256), b256, stream, a);
   if (rc) return rc;
@@ -1194,12 +1359,40 @@ static int run_verify_typed(VerifyArgs& a, bool greedy, bool vec_p, bool vec_d, 
   return launch_kernel("verify_sample", verify_sample_kernel<PT, DT>, dim3((a.R + 3) / 4), b256, stream, a);
 }
 
+// The draft rows' log-normalisers when the caller has none (T > 0), into
+// lse [R * K]: r == 0 (no bias) one rowstats pass over the judged draft rows
+// and a merge; with a Markov head the draft's fused bias pass per position.
+template <typename DT>
+static int run_draft_row_lse(const VerifyArgs& a, bool d_bf16, bool vec_d, float temperature, float* lse,
+                             void* dpart, hipStream_t stream) {
+  if (a.r > 0)
+    return run_markov_lse(a.R, a.K, a.V, a.r, temperature, a.D, d_bf16, a.W1, a.W2t, a.W2s, a.x0, a.x, lse, dpart,
+                          stream);
+  VerifyArgs d = a;
+  d.P = a.D;
+  d.N = a.R * a.K;
+  d.ppart = reinterpret_cast<float2*>(dpart);
+  d.ppart2 = nullptr;
+  d.row_cu = a.cu;
+  d.row_K = a.K;
+  int rc = vec_d ? launch_kernel("verify_rowstats", verify_rowstats_stream_kernel<DT, false>,
+                                 dim3(std::min(d.N * d.nchunks, kRowstatsWGs)), dim3(256), stream, d)
+                 : launch_kernel("verify_rowstats", verify_rowstats_kernel<DT, false, false>,
+                                 dim3(d.N * d.nchunks), dim3(256), stream, d);
+  if (rc) return rc;
+  return launch_kernel("verify_row_lse", row_lse_kernel, dim3((d.N + 3) / 4), dim3(256), stream,
+                       reinterpret_cast<const float2*>(dpart), d.N, d.nsP, lse);
+}
+
 int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf16, int N,
-               const int32_t* cu, const void* D, bool d_bf16, const void* W1, const void* W2, int r,
-               const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d,
-               uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out, void* workspace,
-               const float* O, const uint16_t* W2h, hipStream_t stream) {
-  const VerifyLayout l = verify_layout(R, V, N);
+               const int32_t* cu, const void* D, bool d_bf16, const void* W1, const void* W2, const void* W2f,
+               int r, const int32_t* x0, const int32_t* x, const float* q_tok, const float* lse_d,
+               uint64_t seed, uint64_t step, int32_t* n_acc_out, int32_t* tok_out, float* min_margin_out,
+               void* workspace, const float* O, const uint16_t* W2h, hipStream_t stream) {
+  const bool greedy = temperature == 0.f;
+  const bool lse_pass = !greedy && !lse_d;
+  const bool margins = min_margin_out != nullptr;
+  const VerifyLayout l = verify_layout(R, K, V, N, r, lse_pass, !W2f, margins);
   char* ws = reinterpret_cast<char*>(workspace);
   VerifyArgs a{};
   a.R = R;
@@ -1207,13 +1400,13 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   a.V = V;
   a.N = N;
   a.r = r;
-  const bool greedy = temperature == 0.f;
   a.c2 = greedy ? 1.f : kLog2e / temperature;
   a.P = P;
   a.cu = cu;
   a.D = D;
   a.W1 = reinterpret_cast<const uint16_t*>(W1);
   a.W2t = reinterpret_cast<const uint16_t*>(W2);
+  a.W2s = (!O && r > 0) ? reinterpret_cast<const uint16_t*>(W2f) : nullptr;
   a.x0 = x0;
   a.x = x;
   a.q_tok = q_tok;
@@ -1231,6 +1424,12 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   a.rpart = reinterpret_cast<float*>(ws + l.rpart);
   a.rej_count = reinterpret_cast<int32_t*>(ws + l.rej);
   a.rej_list = a.rej_count + 1;
+  if (margins) {
+    a.margin = reinterpret_cast<float*>(ws + l.margin);
+    a.rmin = reinterpret_cast<float*>(ws + l.rmin);
+    a.ppart2 = greedy ? reinterpret_cast<float*>(ws + l.ppart2) : nullptr;
+    a.min_margin_out = min_margin_out;
+  }
   a.nsP = (V + kRowSlice - 1) / kRowSlice;
   a.ns64 = (V + kWaveCols - 1) / kWaveCols;
   a.nchunks = (V + kRowChunk - 1) / kRowChunk;
@@ -1239,14 +1438,23 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
   const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
   const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
+  if (lse_pass) {
+    float* lse = reinterpret_cast<float*>(ws + l.lse);
+    if (r > 0 && !W2f) {  // the fused bias pass reads the fragment-ordered W2
+      const int rc = run_w2_swizzle(a.W2t, ws + l.w2s, V, r, (r + 31) / 32, false, stream);
+      if (rc) return rc;
+      a.W2s = reinterpret_cast<const uint16_t*>(ws + l.w2s);
+    }
+    const int rc = d_bf16 ? run_draft_row_lse<uint16_t>(a, true, vec_d, temperature, lse, ws + l.dpart, stream)
+                          : run_draft_row_lse<float>(a, false, vec_d, temperature, lse, ws + l.dpart, stream);
+    if (rc) return rc;
+    a.lse_d = lse;
+  }
   if (p_bf16 && d_bf16) return run_verify_typed<uint16_t, uint16_t>(a, greedy, vec_p, vec_d, stream);
   if (p_bf16) return run_verify_typed<uint16_t, float>(a, greedy, vec_p, vec_d, stream);
   if (d_bf16) return run_verify_typed<float, uint16_t>(a, greedy, vec_p, vec_d, stream);
   return run_verify_typed<float, float>(a, greedy, vec_p, vec_d, stream);
 }
-
-size_t w2_swizzle_bytes(int V, int r);
-int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
 
 // r > 0 (Markov head): plus W2 in fragment order for the residual pass
 size_t label_workspace_bytes(int B, int K, int V, int r) {
@@ -1286,8 +1494,9 @@ static int run_label_typed(VerifyArgs& a, float* c_out, bool greedy, bool vec_p,
 }
 
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
-              const void* W1, const void* W2, int r, const int32_t* x0, const int32_t* x, const float* lse_d,
-              float* c_out, void* workspace, const float* O, const uint16_t* W2h, hipStream_t stream) {
+              const void* W1, const void* W2, const void* W2f, int r, const int32_t* x0, const int32_t* x,
+              const float* lse_d, float* c_out, void* workspace, const float* O, const uint16_t* W2h,
+              hipStream_t stream) {
   const int N = B * K;
   char* ws = reinterpret_cast<char*>(workspace);
   VerifyArgs a{};
@@ -1323,9 +1532,13 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
   if (!O && r > 0 && temperature != 0.f && vec_p && vec_d) {  // the streamed residual pass reads it
-    a.W2s = reinterpret_cast<const uint16_t*>(ws + off);
-    const int rc = run_w2_swizzle(a.W2t, ws + off, V, r, (r + 31) / 32, false, stream);
-    if (rc) return rc;
+    if (W2f) {
+      a.W2s = reinterpret_cast<const uint16_t*>(W2f);
+    } else {
+      a.W2s = reinterpret_cast<const uint16_t*>(ws + off);
+      const int rc = run_w2_swizzle(a.W2t, ws + off, V, r, (r + 31) / 32, false, stream);
+      if (rc) return rc;
+    }
   }
   if (p_bf16 && d_bf16) return run_label_typed<uint16_t, uint16_t>(a, c_out, greedy, vec_p, vec_d, stream);
   if (p_bf16) return run_label_typed<uint16_t, float>(a, c_out, greedy, vec_p, vec_d, stream);

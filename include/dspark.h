@@ -90,6 +90,28 @@ const char* dspark_status_string(int status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int dspark_version(void);
 
+/* The 16 hex digits identifying the sources the library was built from
+ * (SHA-256 over the source files and compiler flags); static storage. */
+const char* dspark_build_id(void);
+
+/* ------------------------------------------------------------------------ *
+ * W2 in MFMA fragment order, made once per weight load.  DSpark paper
+ * section 3.1 ("Markov head": W2 is the r x V logit projection every
+ * position multiplies by).
+ *
+ * The bias MFMAs read W2 in 1 KB fragments, each the 16-byte pieces of 64
+ * lanes in lane order; dspark_markov_prepare_w2 writes that copy of the
+ * column-major W2 into caller memory W2f (W2f_bytes >=
+ * dspark_markov_w2_frag_bytes(V, r) = ceil(V / 64) * 4 * ceil(r / 32) KB,
+ * 16-byte aligned), zeros past V and past r.  The copy depends on W2 only:
+ * made once, it serves every dspark_markov_draft, dspark_verify and
+ * dspark_acceptance_label call on the same W2 (argument W2f), which then
+ * neither rebuild it nor need workspace for it.  The copy must be smaller
+ * than 4 GiB.  r == 0: nothing to prepare (0 bytes, no launch).
+ * ------------------------------------------------------------------------ */
+size_t dspark_markov_w2_frag_bytes(int V, int r);
+int dspark_markov_prepare_w2(int V, int r, const void* W2, void* W2f, size_t W2f_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Sequential Markov-head draft.  DSpark paper section 3.1 ("Sequential
  * stage", "Markov head"); "Speculative decoding, from zero to DSpark",
@@ -104,20 +126,21 @@ int dspark_version(void);
  *   lse_out    log sum_v exp(z_k(v)) in natural-log units (when T == 0: the
  *              largest biased logit).
  * Inputs: U [B, K, V] (u_dtype f32 or bf16); W1 [V, r] and W2 (column-major
- * r x V) bf16; x0 [B] int32.  Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
+ * r x V) bf16; W2f the copy of W2 made by dspark_markov_prepare_w2, or NULL
+ * (the call then makes it in its workspace, about 27 us at V = 151936,
+ * r = 256); x0 [B] int32.  Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V,
  * r as in the header comment, U smaller than 4 GiB.
  * Data errors: an anchor (or the previous drawn token) outside [0, V) makes
  * that request's remaining positions x = -1, q_tok = lse = NaN.
- * Workspace: dspark_markov_draft_workspace_bytes(B, K, V, r) bytes, 256-byte
- * aligned, contents need not be initialised: the per-slice softmax partials
- * and, when r > 0, a copy of W2 in the order the bias MFMAs read it
- * (ceil(V / 64) x 4 x ceil(r / 32) KB, written by the call itself before the
- * first position; it must be smaller than 4 GiB).
+ * Workspace: 256-byte aligned, contents need not be initialised: the
+ * per-slice softmax partials (dspark_markov_draft_workspace_bytes(B, K, V, 0)
+ * bytes) and, when r > 0 and W2f is NULL, the fragment-ordered copy of W2
+ * after them (dspark_markov_draft_workspace_bytes(B, K, V, r) bytes in all).
  * ------------------------------------------------------------------------ */
 size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r);
 int dspark_markov_draft(int B, int K, int V, int r, float temperature,
                         const void* U, int u_dtype,
-                        const void* W1, const void* W2,
+                        const void* W1, const void* W2, const void* W2f,
                         const int32_t* x0,
                         uint64_t seed, uint64_t step,
                         int32_t* x_out, float* q_tok_out, float* lse_out,
@@ -191,34 +214,50 @@ int dspark_schedule_async(int R, int K, const float* c,
  *
  * Request r owns flat target rows cu_seqlens[r] .. cu_seqlens[r+1]-1 of P
  * (l_r = cu_seqlens[r+1] - cu_seqlens[r] - 1 drafts, then the bonus row).
- * For j = 1..l_r: p_j = softmax(P[cu[r]+j-1] / T); accept x_j iff
- * u(r, j, accept) < p_j(x_j) / q_tok[r, j-1] (q_tok == 0 accepts).  At the first
- * rejection the correction is drawn from norm(max(0, p_j - q_j)) with
- * u(r, j, resample), q_j = softmax((D[r,j-1] + W1[x_{j-1}] W2) / T - lse_d),
- * x_0 = x0[r]; if that mass is zero, from p_j.  If all l_r drafts survive the
- * bonus is drawn from p_{l_r+1} with u(r, l_r + 1, resample).
+ * For j = 1..l_r: p_j = softmax(P[cu[r]+j-1] / T),
+ * q_j = softmax((D[r,j-1] + W1[x_{j-1}] W2) / T), x_0 = x0[r]; accept x_j iff
+ * u(r, j, accept) < p_j(x_j) / q_j(x_j) (q_j(x_j) == 0 accepts).  At the
+ * first rejection the correction is drawn from norm(max(0, p_j - q_j)) with
+ * u(r, j, resample); if that mass is zero, from p_j.  If all l_r drafts
+ * survive the bonus is drawn from p_{l_r+1} with u(r, l_r + 1, resample).
  * Inputs: P [N, V] (p_dtype), cu_seqlens [R+1] int32 with cu[0] = 0 and
- * cu[R] = N; D [R, K, V] (d_dtype) draft base logits; W1/W2/r/x0 as for the
- * draft (r == 0: no bias); x, q_tok, lse_d [R, K] as returned by
- * dspark_markov_draft (q_tok, lse_d unused when T == 0).
+ * cu[R] = N; D [R, K, V] (d_dtype) draft base logits; W1/W2/W2f/r/x0 as for
+ * the draft (r == 0: no bias; W2f NULL: W2 read column-major); x [R, K] the
+ * drafted tokens.
+ * The draft's exact probabilities (both [R, K], both unused when T == 0):
+ *   q_tok  q_j(x_j) as returned by dspark_markov_draft, or NULL: computed
+ *          from D, the bias and the normaliser;
+ *   lse_d  the draft rows' log-normalisers as returned by
+ *          dspark_markov_draft, or NULL: recomputed from D (plus the bias)
+ *          in an extra pass over the judged draft rows (r == 0: one
+ *          streaming pass over the rows j <= l_r; r > 0: the draft's fused
+ *          bias pass at every position).
  * Outputs: n_acc_out [R] accepted drafts; tok_out [R] the correction or bonus
- * token (emitted sequence: x_1..x_{n_acc}, tok).
+ * token (emitted sequence: x_1..x_{n_acc}, tok); min_margin_out [R] or NULL:
+ * the smallest margin of the request's decisions, i.e. |u - p_j(x_j)/q_j(x_j)|
+ * over the accept tests made (j <= min(n_acc + 1, l_r)) and the distance of
+ * the final draw's target u * Z from the nearer CDF edge of the drawn token,
+ * divided by the total mass Z; when T == 0 the gap between the largest and
+ * the second largest target logit of each examined row (ties give 0).
  * Limits: 0 <= R, 1 <= K <= DSPARK_MAX_K, R <= N <= R * (K + 1), P and D each
  * smaller than 4 GiB.
  * Data errors: a request whose cu_seqlens slice is inconsistent (length < 1 or
  * > K + 1, or outside [0, N]) or whose tokens are outside [0, V) gets
- * n_acc = tok = -1.
+ * n_acc = tok = -1 and min_margin = NaN.
+ * Workspace: dspark_verify_workspace_bytes(R, K, V, r, N) bytes (enough for
+ * NULL q_tok / lse_d and W2f); 256-byte aligned; contents need not be
+ * initialised.
  * ------------------------------------------------------------------------ */
 size_t dspark_verify_workspace_bytes(int R, int K, int V, int r, int N);
 int dspark_verify(int R, int K, int V, float temperature,
                   const void* P, int p_dtype, int N,
                   const int32_t* cu_seqlens,
                   const void* D, int d_dtype,
-                  const void* W1, const void* W2, int r,
+                  const void* W1, const void* W2, const void* W2f, int r,
                   const int32_t* x0, const int32_t* x,
                   const float* q_tok, const float* lse_d,
                   uint64_t seed, uint64_t step,
-                  int32_t* n_acc_out, int32_t* tok_out,
+                  int32_t* n_acc_out, int32_t* tok_out, float* min_margin_out,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
@@ -235,24 +274,36 @@ int dspark_verify(int R, int K, int V, float temperature,
  * T == 0: c_out = 1 where the first argmax of P[r, k] is x[r, k], else 0.
  *
  * Inputs: P [B, K, V] (p_dtype) target logits, row (r, k) judging draft
- * position k + 1; D [B, K, V] (d_dtype) draft base logits; W1/W2/r/x0 as for
- * the draft; x [B, K] the drafted tokens and lse_d [B, K] their
+ * position k + 1; D [B, K, V] (d_dtype) draft base logits; W1/W2/W2f/r/x0 as
+ * for the draft; x [B, K] the drafted tokens and lse_d [B, K] their
  * log-normalisers, as returned by dspark_markov_draft (lse_d unused when
  * T == 0).  Output: c_out [B, K] f32.
  * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, P and D each smaller than 4 GiB.
  * Data errors: a position whose previous or own token is outside [0, V) gets
  * NaN.  Workspace: dspark_acceptance_label_workspace_bytes(B, K, V, r) bytes,
- * 256-byte aligned, contents need not be initialised (with r > 0 it holds a
- * copy of W2 in MFMA fragment order, written by the call, as for the draft).
+ * 256-byte aligned, contents need not be initialised (with r > 0 and W2f
+ * NULL it holds a copy of W2 in MFMA fragment order, written by the call, as
+ * for the draft; with W2f the size for r = 0 suffices).
  * ------------------------------------------------------------------------ */
 size_t dspark_acceptance_label_workspace_bytes(int B, int K, int V, int r);
 int dspark_acceptance_label(int B, int K, int V, float temperature,
                             const void* P, int p_dtype,
                             const void* D, int d_dtype,
-                            const void* W1, const void* W2, int r,
+                            const void* W1, const void* W2, const void* W2f, int r,
                             const int32_t* x0, const int32_t* x,
                             const float* lse_d, float* c_out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * The fp16 copy of W2 in MFMA fragment order that the RNN head's bias
+ * passes read (DSpark paper section 3.1, RNN head: the output part meets the
+ * same W2 as the Markov embedding).  Written into caller memory W2h
+ * (W2h_bytes >= dspark_rnn_w2_f16_bytes(V, r) = ceil(V / 64) * 32 KB,
+ * 16-byte aligned) from the column-major bf16 W2, r a multiple of 32 in
+ * [32, DSPARK_MAX_RANK]; made once, it serves every RNN call on that W2.
+ * ------------------------------------------------------------------------ */
+size_t dspark_rnn_w2_f16_bytes(int V, int r);
+int dspark_rnn_prepare_w2(int V, int r, const void* W2, void* W2h, size_t W2h_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Sequential RNN-head draft.  DSpark paper section 3.1 ("RNN head");
@@ -277,9 +328,10 @@ int dspark_acceptance_label(int B, int K, int V, float temperature,
  * dspark_rnn_acceptance_label take to rebuild the draft distributions.
  * The bias o_k W2 runs on the fp16 MFMA with o_k split into hi + lo fp16
  * parts and W2 converted to fp16 (relative error 2^-22 on o_k): entries of
- * o_k and W2 must be smaller than 2^15 in magnitude.  The fp16 copy of W2,
- * made by each RNN call in its workspace, is laid out in MFMA fragment order
- * (ceil(V / 64) x 32 KB, which must be smaller than 4 GiB).
+ * o_k and W2 must be smaller than 2^15 in magnitude.  The fp16 copy of W2 is
+ * laid out in MFMA fragment order (ceil(V / 64) x 32 KB, which must be
+ * smaller than 4 GiB): W2h, made once by dspark_rnn_prepare_w2, or NULL, and
+ * each RNN call then makes it in its workspace.
  * Limits: 0 <= B, 1 <= K <= DSPARK_MAX_K, 1 <= V, r a multiple of 32 in
  * [32, DSPARK_MAX_RANK], d a positive multiple of 64; U, H, W, W1 each smaller
  * than 4 GiB; H, W, W1, W2, o_out 16-byte aligned (else DSPARK_E_RANGE).
@@ -291,7 +343,7 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d);
 int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature,
                      const void* U, int u_dtype,
                      const void* H, int h_dtype,
-                     const void* W, const void* W1, const void* W2,
+                     const void* W, const void* W1, const void* W2, const void* W2h,
                      const int32_t* x0,
                      uint64_t seed, uint64_t step,
                      int32_t* x_out, float* q_tok_out, float* lse_out, float* o_out,
@@ -302,35 +354,37 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature,
  * bias rebuilt from the head's output parts, q_j = softmax((D[r,j-1] +
  * O[r,j-1] W2) / T - lse_d) (DSpark paper section 3.1, RNN head, and the
  * sources cited for dspark_verify).  O [R, K, r] f32 as returned in o_out by
- * dspark_rnn_draft (16-byte aligned); W2 column-major bf16; r as for
- * dspark_rnn_draft.  Workspace: dspark_rnn_verify_workspace_bytes(R, K, V, r,
- * N) bytes (dspark_verify's, plus an fp16 copy of W2).  Everything else is as
- * for dspark_verify.
+ * dspark_rnn_draft (16-byte aligned); W2 column-major bf16; W2h as for
+ * dspark_rnn_draft; r as for dspark_rnn_draft.  q_tok and lse_d are required
+ * when T > 0 (the draft returns them).  Workspace:
+ * dspark_rnn_verify_workspace_bytes(R, K, V, r, N) bytes (dspark_verify's,
+ * plus an fp16 copy of W2 unless W2h is given).  Everything else is as for
+ * dspark_verify.
  * ------------------------------------------------------------------------ */
 size_t dspark_rnn_verify_workspace_bytes(int R, int K, int V, int r, int N);
 int dspark_rnn_verify(int R, int K, int V, float temperature,
                       const void* P, int p_dtype, int N,
                       const int32_t* cu_seqlens,
                       const void* D, int d_dtype,
-                      const float* O, const void* W2, int r,
+                      const float* O, const void* W2, const void* W2h, int r,
                       const int32_t* x0, const int32_t* x,
                       const float* q_tok, const float* lse_d,
                       uint64_t seed, uint64_t step,
-                      int32_t* n_acc_out, int32_t* tok_out,
+                      int32_t* n_acc_out, int32_t* tok_out, float* min_margin_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Acceptance label of RNN-head drafts: dspark_acceptance_label with
  * q_{r,k} = softmax((D[r,k] + O[r,k] W2) / T) (DSpark paper sections 3.1 and
- * 3.2.1).  O [B, K, r] f32 from dspark_rnn_draft; workspace:
- * dspark_rnn_acceptance_label_workspace_bytes(B, K, V, r) bytes; otherwise as
- * for dspark_acceptance_label.
+ * 3.2.1).  O [B, K, r] f32 from dspark_rnn_draft; W2h as for
+ * dspark_rnn_draft; workspace: dspark_rnn_acceptance_label_workspace_bytes(B,
+ * K, V, r) bytes; otherwise as for dspark_acceptance_label.
  * ------------------------------------------------------------------------ */
 size_t dspark_rnn_acceptance_label_workspace_bytes(int B, int K, int V, int r);
 int dspark_rnn_acceptance_label(int B, int K, int V, float temperature,
                                 const void* P, int p_dtype,
                                 const void* D, int d_dtype,
-                                const float* O, const void* W2, int r,
+                                const float* O, const void* W2, const void* W2h, int r,
                                 const int32_t* x0, const int32_t* x,
                                 const float* lse_d, float* c_out,
                                 void* workspace, size_t workspace_bytes, void* stream);

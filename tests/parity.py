@@ -8,11 +8,21 @@
   the counted fraction must stay below MAX_NEAR_TIE_FRACTION.
 * Probabilities agree within 1e-5 absolute for float32 inputs and 2e-3
   relative for bfloat16 inputs.
+
+The near-tie rate is asserted on a pooled count, not waived per test: every
+parity test adds its decisions and counted near-ties to POOL, and the last
+GPU test (tests/test_zy_pooled_near_ties.py) asserts the pooled fraction is
+below MAX_NEAR_TIE_FRACTION.  A test with at least 1 / MAX_NEAR_TIE_FRACTION
+decisions of its own must also meet the rate alone (no floor of one tie);
+smaller tests are held to the rule through the pool only.
 """
 import numpy as np
 
 MARGIN = 1e-5
 MAX_NEAR_TIE_FRACTION = 1e-4
+
+# session totals over every parity test that called check_near_ties
+POOL = {"tests": 0, "decisions": 0, "near_ties": 0, "excluded": 0}
 
 
 class Report:
@@ -35,8 +45,12 @@ class Report:
         self.max_rel[key] = max(self.max_rel.get(key, 0.0), float(rel.max()))
 
     def check_near_ties(self):
-        assert self.near_ties <= max(1, MAX_NEAR_TIE_FRACTION * self.decisions) or \
-            self.near_ties / max(self.decisions, 1) < MAX_NEAR_TIE_FRACTION, str(self)
+        POOL["tests"] += 1
+        POOL["decisions"] += self.decisions
+        POOL["near_ties"] += self.near_ties
+        POOL["excluded"] += self.excluded
+        if self.decisions * MAX_NEAR_TIE_FRACTION >= 1:
+            assert self.near_ties < MAX_NEAR_TIE_FRACTION * self.decisions, str(self)
 
     def __str__(self):
         return ("%s: decisions=%d near_ties=%d excluded=%d max_abs=%s max_rel=%s"
@@ -96,3 +110,27 @@ def compare_verify(rep, n_acc_gpu, tok_gpu, ref, requests=None):
             assert margin < MARGIN, ("emitted token mismatch at request %d: gpu %d oracle %d (mode %d), "
                                      "oracle margin %.3g" % (r, tok_gpu[r], ref["tok"][r], ref["mode"][r], margin))
             rep.near_ties += 1
+
+
+def oracle_min_margin(ref, r):
+    """A request's smallest decision margin from the oracle's verification:
+    the accept tests it made (NaN where a position was not examined) and the
+    final draw's margin."""
+    am = np.asarray(ref["accept_margin"][r], dtype=np.float64)
+    vals = [float(ref["sample_margin"][r])] + [float(v) for v in am if not np.isnan(v)]
+    return min(vals)
+
+
+def compare_margins(gpu_margin, n_acc_gpu, ref, atol, rtol, requests=None):
+    """min_margin_out against the oracle's margins, on the requests whose
+    accepted count matches (the others already counted as near-ties)."""
+    gpu_margin = np.asarray(gpu_margin, dtype=np.float64)
+    rs = range(len(gpu_margin)) if requests is None else requests
+    got, exp = [], []
+    for r in rs:
+        if int(n_acc_gpu[r]) != int(ref["n_acc"][r]):
+            continue
+        got.append(gpu_margin[r])
+        exp.append(oracle_min_margin(ref, r))
+    np.testing.assert_allclose(np.array(got), np.array(exp), rtol=rtol, atol=atol)
+    return len(got)

@@ -14,8 +14,7 @@ HEADER = os.path.join(ROOT, "include", "dspark.h")
 def lib():
     import __graft_entry__  # noqa: F401  (build helper)
     from draft_verify_schedule_amd import binding
-    if not os.path.exists(binding.library_path()):
-        __graft_entry__.build()
+    __graft_entry__._ensure_built()
     return binding.load_library()
 
 
@@ -39,7 +38,15 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     for st in range(-6, 1):
         assert lib.dspark_status_string(st)
-    assert lib.dspark_version() >= 100
+    assert lib.dspark_version() >= 200
+
+
+def test_build_id_matches_the_sources(lib):
+    """The library carries the hash of the sources it was built from, the one
+    the build helper computes from the tree (a stale library would differ)."""
+    from draft_verify_schedule_amd import _build
+    bid = lib.dspark_build_id().decode()
+    assert len(bid) == 16 and bid == _build.built_id() == _build.source_hash()
 
 
 def test_workspace_queries(lib):
@@ -98,7 +105,8 @@ def test_acceptance_label_argument_errors(lib):
 
     def call(B=4, K=7, V=1024, r=16, T=1.0, P=FAKE, pt=0, D=FAKE, dt=0, W=FAKE, x0=FAKE, x=FAKE, lse=FAKE,
              out=FAKE, wsp=FAKE, wsb=WS):
-        return lib.dspark_acceptance_label(B, K, V, f(T), P, pt, D, dt, W, W, r, x0, x, lse, out, wsp, wsb, NULL)
+        return lib.dspark_acceptance_label(B, K, V, f(T), P, pt, D, dt, W, W, NULL, r, x0, x, lse, out, wsp, wsb,
+                                           NULL)
     assert call(B=-1) == -2
     assert call(K=17) == -2
     assert call(r=12) == -2
@@ -109,6 +117,9 @@ def test_acceptance_label_argument_errors(lib):
     assert call(T=0.0, lse=NULL, wsp=NULL) == -5     # lse_d not needed when greedy
     assert call(W=NULL) == -1
     assert call(wsb=ctypes.c_size_t(lib.dspark_acceptance_label_workspace_bytes(4, 7, 1024, 16) - 1)) == -5
+    # with a prepared W2 copy the label needs no room for its own
+    assert lib.dspark_acceptance_label(4, 7, 1024, f(1.0), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.c_void_p(0x100008),
+                                       16, FAKE, FAKE, FAKE, FAKE, FAKE, WS, NULL) == -4   # W2f not 16-byte aligned
 
 
 def test_confidence_and_sts_argument_errors(lib):
@@ -140,9 +151,10 @@ def test_draft_argument_errors(lib):
     ws = ctypes.c_size_t(1 << 30)
     base = dict(B=4, K=7, V=1024, r=16)
 
-    def call(B=4, K=7, V=1024, r=16, T=1.0, U=FAKE, dt=1, W1=FAKE, W2=FAKE, x0=FAKE, out=FAKE, wsp=FAKE, wsb=ws):
-        return lib.dspark_markov_draft(B, K, V, r, f(T), U, dt, W1, W2, x0, ctypes.c_uint64(1), ctypes.c_uint64(0),
-                                       out, out, out, wsp, wsb, NULL)
+    def call(B=4, K=7, V=1024, r=16, T=1.0, U=FAKE, dt=1, W1=FAKE, W2=FAKE, W2f=NULL, x0=FAKE, out=FAKE, wsp=FAKE,
+             wsb=ws):
+        return lib.dspark_markov_draft(B, K, V, r, f(T), U, dt, W1, W2, W2f, x0, ctypes.c_uint64(1),
+                                       ctypes.c_uint64(0), out, out, out, wsp, wsb, NULL)
     assert call(K=0) == -2
     assert call(K=17) == -2
     assert call(r=12) == -2          # not a multiple of 8
@@ -156,23 +168,49 @@ def test_draft_argument_errors(lib):
     assert call(W1=NULL) == -1
     assert call(wsb=ctypes.c_size_t(16)) == -5
     assert call(wsp=NULL) == -5
+    # the partials alone are enough workspace when the caller brings the W2 copy
+    part = lib.dspark_markov_draft_workspace_bytes(4, 7, 1024, 0)
+    assert call(wsb=ctypes.c_size_t(part), W2f=ctypes.c_void_p(0x100008)) == -4    # W2f not 16-byte aligned
+    assert call(wsb=ctypes.c_size_t(part)) == -5                                    # without it: too small
+
+
+def test_prepare_w2_argument_errors(lib):
+    V, r = 1000, 64
+    need = lib.dspark_markov_w2_frag_bytes(V, r)
+    assert need == 16 * 4 * 2 * 1024 == lib.dspark_markov_draft_workspace_bytes(4, 7, V, r) - \
+        lib.dspark_markov_draft_workspace_bytes(4, 7, V, 0)
+    assert lib.dspark_markov_w2_frag_bytes(V, 12) == 0
+    assert lib.dspark_markov_prepare_w2(V, 12, FAKE, FAKE, need, NULL) == -2
+    assert lib.dspark_markov_prepare_w2(V, r, NULL, FAKE, need, NULL) == -1
+    assert lib.dspark_markov_prepare_w2(V, r, FAKE, NULL, need, NULL) == -1
+    assert lib.dspark_markov_prepare_w2(V, r, FAKE, FAKE, need - 1, NULL) == -5
+    assert lib.dspark_markov_prepare_w2(V, r, FAKE, ctypes.c_void_p(0x100008), need, NULL) == -4
+    assert lib.dspark_markov_prepare_w2(V, 0, NULL, NULL, 0, NULL) == 0       # nothing to prepare
+    need_h = lib.dspark_rnn_w2_f16_bytes(V, r)
+    assert need_h == 16 * 32 * 1024
+    assert lib.dspark_rnn_w2_f16_bytes(V, 48) == 0
+    assert lib.dspark_rnn_prepare_w2(V, 48, FAKE, FAKE, need_h, NULL) == -2
+    assert lib.dspark_rnn_prepare_w2(V, r, FAKE, NULL, need_h, NULL) == -1
+    assert lib.dspark_rnn_prepare_w2(V, r, FAKE, FAKE, need_h - 1, NULL) == -5
 
 
 def test_verify_argument_errors(lib):
     f = ctypes.c_float
     ws = ctypes.c_size_t(1 << 30)
 
-    def call(R=4, K=7, V=1024, T=1.0, N=32, pdt=0, ddt=0, r=0, P=FAKE, q=FAKE, wsp=FAKE, wsb=ws):
-        return lib.dspark_verify(R, K, V, f(T), P, pdt, N, FAKE, FAKE, ddt, NULL, NULL, r, FAKE, FAKE, q, q,
-                                 ctypes.c_uint64(1), ctypes.c_uint64(0), FAKE, FAKE, wsp, wsb, NULL)
+    def call(R=4, K=7, V=1024, T=1.0, N=32, pdt=0, ddt=0, r=0, P=FAKE, q=FAKE, mm=NULL, wsp=FAKE, wsb=ws):
+        return lib.dspark_verify(R, K, V, f(T), P, pdt, N, FAKE, FAKE, ddt, NULL, NULL, NULL, r, FAKE, FAKE, q, q,
+                                 ctypes.c_uint64(1), ctypes.c_uint64(0), FAKE, FAKE, mm, wsp, wsb, NULL)
     assert call(N=3) == -2           # fewer rows than requests
     assert call(N=33) == -2          # more than R (K + 1)
     assert call(pdt=7) == -3
     assert call(T=-0.5) == -4
     assert call(P=NULL) == -1
-    assert call(q=NULL) == -1        # T > 0 needs q_tok and lse_d
     assert call(r=16) == -1          # Markov bias without factors
     assert call(wsb=ctypes.c_size_t(0)) == -5
+    # the query covers recomputed draft normalisers and the margins; one byte less is refused
+    full = lib.dspark_verify_workspace_bytes(4, 7, 1024, 0, 32)
+    assert call(q=NULL, mm=FAKE, wsb=ctypes.c_size_t(full - 1)) == -5
 
 
 def test_uniforms_argument_errors(lib):
@@ -193,9 +231,9 @@ def test_rnn_argument_errors(lib):
         lib.dspark_acceptance_label_workspace_bytes(4, K, V, 0) + V * r * 2
     assert need % 256 == 0
 
-    def draft(B=B, K=K, V=V, r=r, d=d, T=1.0, U=FAKE, ud=1, H=FAKE, hd=1, W=FAKE, W1=FAKE, W2=FAKE, x0=FAKE,
-              o=FAKE, ws=FAKE, wsb=WS):
-        return lib.dspark_rnn_draft(B, K, V, r, d, T, U, ud, H, hd, W, W1, W2, x0, 1, 2, FAKE, FAKE, FAKE, o,
+    def draft(B=B, K=K, V=V, r=r, d=d, T=1.0, U=FAKE, ud=1, H=FAKE, hd=1, W=FAKE, W1=FAKE, W2=FAKE, W2h=NULL,
+              x0=FAKE, o=FAKE, ws=FAKE, wsb=WS):
+        return lib.dspark_rnn_draft(B, K, V, r, d, T, U, ud, H, hd, W, W1, W2, W2h, x0, 1, 2, FAKE, FAKE, FAKE, o,
                                     ws, wsb, NULL)
     assert draft(r=48) == -2          # not a multiple of 32
     assert draft(r=0) == -2
@@ -212,20 +250,23 @@ def test_rnn_argument_errors(lib):
     assert draft(wsb=ctypes.c_size_t(need - 1)) == -5
     assert draft(ws=ctypes.c_void_p(0x100010)) == -5     # not 256-byte aligned
     assert draft(W=ctypes.c_void_p(0x100008)) == -4      # not 16-byte aligned
+    assert draft(W2h=ctypes.c_void_p(0x100008)) == -4    # the prepared copy too
+    assert draft(W2h=FAKE, wsb=ctypes.c_size_t(need - lib.dspark_rnn_w2_f16_bytes(V, r) - 1)) == -5
 
-    def verify(R=4, K=7, V=V, T=1.0, N=8, O=FAKE, W2=FAKE, r=r, wsb=WS):
-        return lib.dspark_rnn_verify(R, K, V, T, FAKE, 1, N, FAKE, FAKE, 1, O, W2, r, FAKE, FAKE, FAKE, FAKE, 1, 2,
-                                     FAKE, FAKE, FAKE, wsb, NULL)
+    def verify(R=4, K=7, V=V, T=1.0, N=8, O=FAKE, W2=FAKE, r=r, q=FAKE, wsb=WS):
+        return lib.dspark_rnn_verify(R, K, V, T, FAKE, 1, N, FAKE, FAKE, 1, O, W2, NULL, r, FAKE, FAKE, q, q, 1, 2,
+                                     FAKE, FAKE, NULL, FAKE, wsb, NULL)
     assert verify(r=40) == -2
     assert verify(N=3) == -2
     assert verify(O=NULL) == -1
     assert verify(W2=NULL) == -1
+    assert verify(q=NULL) == -1       # the RNN head's verification takes the draft's q_tok and lse_d
     assert verify(O=ctypes.c_void_p(0x100004)) == -4
     assert verify(wsb=ctypes.c_size_t(16)) == -5
 
     def label(B=4, K=7, V=V, T=1.0, O=FAKE, r=r, wsb=WS):
-        return lib.dspark_rnn_acceptance_label(B, K, V, T, FAKE, 1, FAKE, 1, O, FAKE, r, FAKE, FAKE, FAKE, FAKE,
-                                               FAKE, wsb, NULL)
+        return lib.dspark_rnn_acceptance_label(B, K, V, T, FAKE, 1, FAKE, 1, O, FAKE, NULL, r, FAKE, FAKE, FAKE,
+                                               FAKE, FAKE, wsb, NULL)
     assert label(r=16) == -2
     assert label(O=NULL) == -1
     assert label(T=float("inf")) == -4
@@ -240,24 +281,24 @@ def test_empty_batches_are_noops(lib):
     f = ctypes.c_float
     u64 = ctypes.c_uint64
     Z = ctypes.c_size_t(0)
-    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, NULL, u64(1), u64(0),
                                    NULL, NULL, NULL, NULL, Z, NULL) == 0
-    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(-1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+    assert lib.dspark_markov_draft(0, 7, 1024, 16, f(-1.0), NULL, 1, NULL, NULL, NULL, NULL, u64(1), u64(0),
                                    NULL, NULL, NULL, NULL, Z, NULL) == -4
-    assert lib.dspark_markov_draft(0, 17, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, u64(1), u64(0),
+    assert lib.dspark_markov_draft(0, 17, 1024, 16, f(1.0), NULL, 1, NULL, NULL, NULL, NULL, u64(1), u64(0),
                                    NULL, NULL, NULL, NULL, Z, NULL) == -2
-    assert lib.dspark_rnn_draft(0, 7, 1024, 64, 128, f(1.0), NULL, 1, NULL, 1, NULL, NULL, NULL, NULL, u64(1),
+    assert lib.dspark_rnn_draft(0, 7, 1024, 64, 128, f(1.0), NULL, 1, NULL, 1, NULL, NULL, NULL, NULL, NULL, u64(1),
                                 u64(0), NULL, NULL, NULL, NULL, NULL, Z, NULL) == 0
-    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL, NULL,
-                             u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == 0
-    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 1, NULL, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL, NULL,
-                             u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == -2     # rows without requests
-    assert lib.dspark_rnn_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, 64, NULL, NULL, NULL,
-                                 NULL, u64(1), u64(0), NULL, NULL, NULL, Z, NULL) == 0
-    assert lib.dspark_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, 16, NULL, NULL, NULL,
+    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, NULL, 16, NULL, NULL, NULL,
+                             NULL, u64(1), u64(0), NULL, NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_verify(0, 7, 1024, f(1.0), NULL, 1, 1, NULL, NULL, 1, NULL, NULL, NULL, 16, NULL, NULL, NULL,
+                             NULL, u64(1), u64(0), NULL, NULL, NULL, NULL, Z, NULL) == -2     # rows without requests
+    assert lib.dspark_rnn_verify(0, 7, 1024, f(1.0), NULL, 1, 0, NULL, NULL, 1, NULL, NULL, NULL, 64, NULL, NULL,
+                                 NULL, NULL, u64(1), u64(0), NULL, NULL, NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, NULL, 16, NULL, NULL, NULL,
                                        NULL, NULL, Z, NULL) == 0
-    assert lib.dspark_rnn_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, 64, NULL, NULL, NULL,
-                                           NULL, NULL, Z, NULL) == 0
+    assert lib.dspark_rnn_acceptance_label(0, 7, 1024, f(1.0), NULL, 1, NULL, 1, NULL, NULL, NULL, 64, NULL, NULL,
+                                           NULL, NULL, NULL, Z, NULL) == 0
     assert lib.dspark_confidence_head(0, 7, 100, 32, 8, NULL, 0, NULL, NULL, f(0.0), NULL, NULL, NULL, NULL, NULL,
                                       NULL, NULL) == 0
     assert lib.dspark_uniforms(u64(1), u64(0), 0, 1, 0, NULL, NULL) == 0

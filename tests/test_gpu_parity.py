@@ -11,7 +11,7 @@ import torch
 from scipy import stats
 
 import oracle
-from tests.parity import Report, compare_draft, compare_verify
+from tests.parity import Report, compare_draft, compare_margins, compare_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -388,32 +388,33 @@ def test_full_step_tiny():
         rep.check_near_ties()
 
 
-def test_full_step_full_size_sampled():
-    """The full-step workload at its real shape (the benchmark's launch
-    configuration), GPU on all 512 requests; the oracle on a sample."""
+def test_full_step_full_size():
+    """The full-step workload at its real shape (B=512, K=7, V=151936,
+    r=256, bf16), in the launch configuration the benchmark times: draft,
+    schedule and verification of every request against the oracle, over
+    three RNG steps."""
     w = wl().make("full_step", device=DEV)
     _say("full step generated")
-    g = _gpu_step(w, step=0, dev_inputs=(w.U, w.W1, w.W2, w.x0, w.c, w.sps, w.t))
-    _say("full step gpu done: N=%d" % g["cu"][-1])
     s = oracle.schedule_ref(w.c.cpu().numpy(), w.sps.cpu().numpy(), 0)
-    np.testing.assert_array_equal(g["cu"], s["cu_seqlens"])
-    sample = np.array([0, 1, 137, 256, 390, 511])
     W1f, W2f = f64(w.W1), f64(w.W2).T
-    Us = f64(w.U[sample])
-    ref_d = oracle.draft_ref(Us, W1f, W2f, w.x0.cpu().numpy()[sample], 1.0, w.rng_seed, 0, request_ids=sample)
-    rep = Report("full step sampled")
-    same = compare_draft(rep, g["x"][sample], g["q"][sample], g["lse"][sample], ref_d, bf16_inputs=True,
-                         greedy=False)
-    ell = s["ell"][sample]
-    cu_s = np.concatenate([[0], np.cumsum(ell + 1)])
-    tf = w.t[sample].cpu()
-    P = torch.cat([tf[i, :ell[i] + 1] for i in range(len(sample))]).to(torch.float64).numpy()
-    ref_v = oracle.verify_ref(P, cu_s, Us, W1f, W2f, w.x0.cpu().numpy()[sample], ref_d["x"], 1.0, w.rng_seed, 0,
-                              request_ids=sample)
-    whole = [i for i in range(len(sample)) if same[i].all()]
-    compare_verify(rep, g["n_acc"][sample], g["tok"][sample], ref_v, whole)
+    Uf = f64(w.U)
+    x0 = w.x0.cpu().numpy()
+    cu_t = torch.as_tensor(s["cu_seqlens"], dtype=torch.int32)
+    P = f64(wl().flat_target_rows(w.t, cu_t.to(DEV)))
+    rep = Report("full step, all requests, 3 steps")
+    for step in range(3):
+        g = _gpu_step(w, step=step, dev_inputs=(w.U, w.W1, w.W2, w.x0, w.c, w.sps, w.t))
+        _say("full step %d gpu done: N=%d" % (step, g["cu"][-1]))
+        np.testing.assert_array_equal(g["cu"], s["cu_seqlens"])
+        np.testing.assert_array_equal(g["ell"], s["ell"])
+        ref_d = oracle.draft_ref(Uf, W1f, W2f, x0, 1.0, w.rng_seed, step)
+        same = compare_draft(rep, g["x"], g["q"], g["lse"], ref_d, bf16_inputs=True, greedy=False)
+        ref_v = oracle.verify_ref(P, s["cu_seqlens"], Uf, W1f, W2f, x0, ref_d["x"], 1.0, w.rng_seed, step)
+        whole = [r for r in range(w.B) if same[r].all()]
+        compare_verify(rep, g["n_acc"], g["tok"], ref_v, whole)
+        _say("  %s" % rep)
     rep.check_near_ties()
-    _say(str(rep) + " n_acc(sample)=%s" % g["n_acc"][sample].tolist())
+    assert rep.decisions >= 10 ** 4
 
 
 def test_offsets_near_the_4gib_limit():
@@ -604,14 +605,13 @@ def test_label_bf16_odd_groups():
     np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
 
 
-def test_label_full_step_sampled():
+def test_label_full_step():
     """Full-size workload (B=512, K=7, V=151936, r=256, bf16), the launch the
-    bench times; the oracle checks 6 requests."""
+    bench times: all 3584 positions against the oracle."""
     w = wl().make("full_step", device=DEV)
     P = w.t[:, :w.K].contiguous()
-    rows = np.array([0, 101, 255, 256, 400, 511])
-    got, ref = _label_case(P, w.U, w.W1, w.W2, w.x0, w.temperature, rows=rows)
-    _say("label full_step max |diff| %.2e" % np.abs(got - ref).max())
+    got, ref = _label_case(P, w.U, w.W1, w.W2, w.x0, w.temperature)
+    _say("label full_step (all %d positions) max |diff| %.2e" % (got.size, np.abs(got - ref).max()))
     np.testing.assert_allclose(got, ref, rtol=2e-3, atol=1e-6)
 
 
@@ -830,22 +830,20 @@ def test_rnn_label(B, K, V, r, d, dtype, T):
         np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
 
 
-def test_rnn_draft_full_size_sampled():
+def test_rnn_draft_full_size():
     """The full-step workload with the RNN head (r = 256, d = 4096), the
-    launch configuration the benchmark times: GPU on all 512 requests, the
-    oracle on a sample of them."""
+    launch configuration the benchmark times: every request against the
+    oracle."""
     w = wl().make("full_step", device=DEV)
     H, W = wl().rnn_head(w.B, w.K, w.r, 4096, 1005, device=DEV)
     _say("rnn full size generated")
     x, q, lse, O = ds().dspark_rnn_draft(w.U, H, W, w.W1, w.W2, w.x0, 1.0, w.rng_seed, 0)
     torch.cuda.synchronize()
     _say("rnn full size gpu done")
-    sample = np.array([0, 1, 137, 256, 390, 511])
-    sel = torch.as_tensor(sample, device=DEV)
-    ref = oracle.rnn_draft_ref(f64(w.U[sel]), f64(H[sel]), f64(W), f64(w.W1), f64(w.W2).T,
-                               w.x0.cpu().numpy()[sample], 1.0, w.rng_seed, 0, request_ids=sample)
-    rep = Report("rnn full size sampled")
-    got = [t.cpu().numpy()[sample] for t in (x, q, lse, O)]
+    ref = oracle.rnn_draft_ref(f64(w.U), f64(H), f64(W), f64(w.W1), f64(w.W2).T, w.x0.cpu().numpy(), 1.0,
+                               w.rng_seed, 0)
+    rep = Report("rnn full size")
+    got = [t.cpu().numpy() for t in (x, q, lse, O)]
     _compare_rnn(rep, got, ref, bf16_inputs=True, greedy=False)
     rep.check_near_ties()
     _say(str(rep))
