@@ -63,6 +63,8 @@ def load_library():
     lib.dspark_schedule_workspace_bytes.restype = c_size
     lib.dspark_schedule_workspace_bytes.argtypes = [c_int] * 2
     lib.dspark_schedule.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_schedule_noalloc.restype = c_int
+    lib.dspark_schedule_noalloc.argtypes = [c_int, c_int, vp, vp, c_int, c_int, c_int, vp, vp, vp, vp, vp, vp]
     lib.dspark_schedule_async.restype = c_int
     lib.dspark_schedule_async.argtypes = [c_int, c_int, vp, vp, c_int, vp, vp, vp, vp, vp, vp, vp, c_size, vp]
     lib.dspark_verify_workspace_bytes.restype = c_size
@@ -267,6 +269,30 @@ def dspark_schedule(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None, 
                              _stream())
     if st != 0:
         raise DSparkError("dspark_schedule", st)
+    return out
+
+
+def dspark_schedule_noalloc(c, sps, mode=DSPARK_SCHED_EARLY_STOP, capacity=0, out=None):
+    """dspark_schedule with the sorted keys in the library's own device array
+    (no workspace, nothing allocated by the library; pass `out` to allocate
+    nothing here either).  Same results as dspark_schedule; calls that
+    overlap on one GPU race on the shared array."""
+    lib = load_library()
+    R, K = c.shape
+    _check(c, "c", torch.float32)
+    _check(sps, "sps", torch.float64)
+    dev = c.device
+    if out is None:
+        out = {"a": torch.empty((R, K), dtype=torch.float32, device=dev),
+               "ell": torch.empty(R, dtype=torch.int32, device=dev),
+               "cu_seqlens": torch.empty(R + 1, dtype=torch.int32, device=dev),
+               "n_admitted": torch.empty(1, dtype=torch.int32, device=dev),
+               "theta": torch.empty(1, dtype=torch.float64, device=dev)}
+    st = lib.dspark_schedule_noalloc(R, K, _ptr(c), _ptr(sps), sps.numel(), int(mode), int(capacity), _ptr(out["a"]),
+                                     _ptr(out["ell"]), _ptr(out["cu_seqlens"]), _ptr(out["n_admitted"]),
+                                     _ptr(out["theta"]), _stream())
+    if st != 0:
+        raise DSparkError("dspark_schedule_noalloc", st)
     return out
 
 

@@ -25,6 +25,9 @@ size_t schedule_workspace_bytes(int R, int K);
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
                  const int32_t* capacity_dev, float* a_out, int32_t* ell_out, int32_t* cu_out, int32_t* n_out,
                  double* theta_out, void* workspace, hipStream_t stream);
+int run_schedule_noalloc(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
+                         int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, hipStream_t stream);
+int schedule_scratch_keys();
 size_t verify_workspace_bytes(int R, int K, int V, int r, int N);
 size_t verify_workspace_need(int R, int K, int V, int r, int N, bool lse_given, bool w2f_given, bool margins,
                              float temperature);
@@ -275,6 +278,21 @@ int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len
   return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_seqlens_out,
                                          n_admitted_out, theta_out, workspace,
                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_schedule_noalloc(int R, int K, const float* c, const double* sps, int sps_len, int mode, int capacity,
+                            float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out, int32_t* n_admitted_out,
+                            double* theta_out, void* stream) {
+  if (R < 0 || K <= 0 || K > DSPARK_MAX_K || (int64_t)R * K > DSPARK_MAX_CANDIDATES) return DSPARK_E_SHAPE;
+  if ((int64_t)R * K > DSPARK_NOALLOC_MAX_CANDIDATES || (int64_t)R * K > dspark::schedule_scratch_keys())
+    return DSPARK_E_SHAPE;
+  if (mode < DSPARK_SCHED_EARLY_STOP || mode > DSPARK_SCHED_TOPK) return DSPARK_E_RANGE;
+  if (capacity < 0) return DSPARK_E_RANGE;
+  if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
+  if (!sps || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
+  if (R > 0 && (!c || !a_out || !ell_out)) return DSPARK_E_NULL;
+  return hip_status(dspark::run_schedule_noalloc(R, K, c, sps, mode, capacity, a_out, ell_out, cu_seqlens_out,
+                                                 n_admitted_out, theta_out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int dspark_schedule_async(int R, int K, const float* c, const double* sps, int sps_len, const int32_t* capacity,

@@ -24,6 +24,8 @@
 //     3. l_r = number of r's candidates whose key lies below the n*-th sorted
 //        key (a prefix of positions by construction), and cu_seqlens by a
 //        block scan.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -355,6 +357,49 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
   if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a, cs);
   if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a, cs);
   return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+}
+
+// ---- the schedule without a caller workspace --------------------------------
+// The sorted candidate keys live in this library-owned device array instead
+// of a workspace: every GPU the library runs on holds its own copy (128 KB)
+// until the process ends, and every call on that GPU shares it.  In host
+// code the name is a host-side stand-in, not a device address: kernels get
+// the address hipGetSymbolAddress returns for the current device.
+constexpr int kScratchKeys = kSchedMaxKeys;
+static __device__ __align__(256) uint64_t scratch[kScratchKeys];
+
+constexpr int kScratchMaxDevices = 64;
+static std::mutex g_scratch_lock;
+static void* g_scratch_ptr[kScratchMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current); nullptr on failure.
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> hold(g_scratch_lock);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+int schedule_scratch_keys() { return kScratchKeys; }
+
+// dspark_schedule's launches with the sorted keys in the scratch array (no
+// allocation, no workspace).  Returns -1 when R * K exceeds the array or its
+// address cannot be had.  Nothing in the array needs to start at zero: the
+// rank kernel writes every key the admission kernel reads.
+int run_schedule_noalloc(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
+                         int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, hipStream_t stream) {
+  if ((int64_t)R * K > kScratchKeys) return -1;
+  if (R == 0) return run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_out, n_out, theta_out,
+                                  nullptr, stream);
+  void* ptr = scratch_address();
+  if (!ptr) return -1;
+  return run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_out, n_out, theta_out, ptr, stream);
 }
 
 }  // namespace dspark

@@ -182,6 +182,28 @@ int dspark_schedule(int R, int K, const float* c,
                     void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * dspark_schedule without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, outputs, limits, data
+ * errors and results as dspark_schedule, minus the workspace: the sorted
+ * candidate keys go to a library-owned device array of
+ * DSPARK_NOALLOC_MAX_CANDIDATES 64-bit keys (128 KB on each GPU the library
+ * runs on, held until the process ends).  The call allocates nothing and
+ * calls no allocating routine; R * K above DSPARK_NOALLOC_MAX_CANDIDATES
+ * returns DSPARK_E_SHAPE.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race on
+ * it and must be ordered by the caller.  Nothing in the array needs to start
+ * at zero (each call writes every key it reads).
+ * ------------------------------------------------------------------------ */
+#define DSPARK_NOALLOC_MAX_CANDIDATES 16384
+int dspark_schedule_noalloc(int R, int K, const float* c,
+                            const double* sps, int sps_len,
+                            int mode, int capacity,
+                            float* a_out, int32_t* ell_out, int32_t* cu_seqlens_out,
+                            int32_t* n_admitted_out, double* theta_out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Asynchronous capacity.  DSpark paper section 5.2 (the scheduler run
  * asynchronously: capacity from the confidences of two steps earlier, fresh
  * candidates ranked and cut to it); "Speculative decoding, from zero to
