@@ -32,11 +32,13 @@ constexpr int kTileCols = 256;   // columns per workgroup (4 waves)
 // weight of magnitude 2^-14 .. 2^15 exactly), on the fp16 MFMA.  hi + lo
 // carries v to 2^-22 relative (plus 2^-25 absolute where lo is subnormal),
 // where one bf16 operand would keep 2^-8 and a bf16 pair 2^-16.
-template <int KC, bool SPLIT = false>
+// NR: rows of the stage (128, or 256 for the draft's two-stage sweep).
+template <int KC, bool SPLIT = false, int NR = kStageRows>
 struct EStage {
   static constexpr int kLo = 32 * KC;  // column of the lo half (SPLIT)
   static constexpr int kPitch = (SPLIT ? 64 : 32) * KC + 8;
-  uint16_t e[kStageRows][kPitch];
+  static constexpr int kRows = NR;
+  uint16_t e[NR][kPitch];
 };
 
 // Workgroup -> (column tile, row stage), XCD-aware: workgroups are dealt to
@@ -190,10 +192,10 @@ struct W2AnyFrags {
   }
 };
 
-// Stage E rows W1[prev(row)] of rows [row0, row0 + kStageRows) into LDS (zeros
+// Stage E rows W1[prev(row)] of rows [row0, row0 + 32 * waves) into LDS (zeros
 // for rows past nrows, invalid previous tokens, or k >= r).  prev_of(row)
-// returns the previous token of that row or -1.  The 256 threads (4 waves)
-// take 32 rows per wave; each load instruction covers two whole rows, 32
+// returns the previous token of that row or -1.  Waves 0, 1, .. take 32 rows
+// each (4 waves for a 128-row stage, 8 for a 256-row one); each load instruction covers two whole rows, 32
 // lanes x 16 contiguous bytes per row, so one instruction touches 8 cache
 // lines instead of 64.  Lane j reads the previous token of row j of its
 // wave's 32 once; the token of each loaded row comes by a lane shuffle.
@@ -203,7 +205,6 @@ struct W2AnyFrags {
 // complete in order, so the stores then wait for the W1 rows only.
 template <int KC>
 struct EStageLoad {
-  static_assert(kStageRows == 128, "4 waves x 32 rows");
   static constexpr int kChunks = 4 * KC;  // 16-byte vectors per padded row, <= 32
   static constexpr int kLoads = 16;       // two rows per load instruction
   u32x4 vals[kLoads];
@@ -228,7 +229,8 @@ struct EStageLoad {
       vals[i] = *reinterpret_cast<const u32x4*>(W1 + (size_t)(ok ? prev : 0) * r + (k_ok ? k : 0));
     }
   }
-  __device__ __forceinline__ void store(EStage<KC>& st, int r) const {
+  template <int NR>
+  __device__ __forceinline__ void store(EStage<KC, false, NR>& st, int r) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = lane & 31;
@@ -308,7 +310,7 @@ __device__ __forceinline__ void stage_rows(EStage<KC, true>& st, const float* __
 // invariant) LDS reads of all groups out of the loop and keep them live.
 template <int KC, bool SPLIT = false>
 __device__ __forceinline__ int e_lane_offset(int lane) {
-  return ((lane & 15) * EStage<KC, SPLIT>::kPitch + (lane >> 4) * 8) * 2;
+  return ((lane & 15) * EStage<KC, SPLIT>::kPitch + (lane >> 4) * 8) * 2;  // the pitch does not depend on NR
 }
 
 __device__ __forceinline__ int launder(int v) {
@@ -324,15 +326,15 @@ __device__ __forceinline__ int launder(int v) {
 // clears the accumulators first.
 // SPLIT stages (fp16 W2 fragments, w2 of type f16x8) add the lo half of each
 // chunk right after its hi half on the fp16 MFMA.
-template <int KC, bool ZERO = true, int K0 = 0, int K1 = KC, bool SPLIT, typename FT>
-__device__ __forceinline__ void mfma_group(const EStage<KC, SPLIT>& st, int g, int lane,
+template <int KC, bool ZERO = true, int K0 = 0, int K1 = KC, bool SPLIT, int NR, typename FT>
+__device__ __forceinline__ void mfma_group(const EStage<KC, SPLIT, NR>& st, int g, int lane,
                                            const FT (&w2)[4][KC], f32x4 (&acc)[4],
                                            int e_off = -1) {
   FT e[KC];
   FT el[SPLIT ? KC : 1];
   if (e_off < 0) e_off = e_lane_offset<KC, SPLIT>(lane);
   const char* base =
-      reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC, SPLIT>::kPitch * 2;
+      reinterpret_cast<const char*>(&st.e[0][0]) + e_off + g * 16 * EStage<KC, SPLIT, NR>::kPitch * 2;
 #pragma unroll
   for (int kc = K0; kc < K1; ++kc) {
     e[kc] = *reinterpret_cast<const FT*>(base + 64 * kc);

@@ -189,18 +189,24 @@ struct UCoal {
 // tail (V not a multiple of 64) and partial stages take the plain path.
 // ROWS: the bias inputs are the fp32 rows a.O (RNN head) instead of gathered
 // W1 rows.
-template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL, bool ROWS>
+// G: 16-row groups per stage (8, or 16 for the bf16 Markov sweep of full
+// stage pairs: 256 rows share each W2 block loaded into a wave's registers,
+// halving the W2 reloads per base logit; the E stage then takes 135 KB of
+// LDS and the wave's base-logit tile is single-buffered).
+template <typename UT, bool VEC, int KC, bool GREEDY, bool FULL, bool ROWS, int G = kGroupsPerWG>
 __global__ __launch_bounds__(kDraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   static_assert(!FULL || VEC, "the pipelined sweep reads through buffer resources");
+  static_assert(G == kGroupsPerWG || (FULL && !ROWS && KC > 0), "256-row stages: full bf16 Markov stages only");
   constexpr int KCs = KC > 0 ? KC : 1;
+  constexpr int kRows = 16 * G;
   int split, stage;
   if (!xcd_tile(blockIdx.x, a.ncol_tiles, nstages, split, stage)) return;
   stage += stage0;
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const int row0 = stage * kStageRows;
-  const int ngroups = min(kGroupsPerWG, (a.B - row0 + 15) / 16);
+  const int row0 = stage * kRows;
+  const int ngroups = min(G, (a.B - row0 + 15) / 16);
   const int nblocks = (a.V + kWaveCols - 1) / kWaveCols;
   const int blk_begin = (int)((int64_t)split * nblocks / a.ncol_tiles);
   const int blk_end = (int)((int64_t)(split + 1) * nblocks / a.ncol_tiles);
@@ -215,7 +221,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   // gate the first MFMA through the LDS stage), then the first groups of
   // base logits and the first block's W2 fragments; the LDS stores of the E
   // stage wait for the W1 rows only.
-  __shared__ EStage<KCs, ROWS> st;
+  __shared__ EStage<KCs, ROWS, kRows> st;
   // Blocks of the pipelined sweep after each wave's first are handed out in
   // order from this counter, so the eight waves of the workgroup finish
   // within a block of each other (a static split gives some waves one block
@@ -225,10 +231,11 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     if (threadIdx.x == 0) blk_next = blk_begin + kDraftWaves;
   }
   EStageLoad<KCs> eld;
+  constexpr int kStageWaves = kRows / 32;  // 32 rows gathered per wave
   if constexpr (KC > 0 && !ROWS) {
     const int32_t* prev = a.prev;
     const int stride = a.prev_stride;
-    if (wave < 4) eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
+    if (wave < kStageWaves) eld.load(a.W1, a.r, a.V, row0, a.B, [&](int g) { return prev[(size_t)g * stride]; });
   }
 
   UAccess<UT, VEC> ua;
@@ -238,9 +245,13 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   typename UAccess<UT, VEC>::Buf buf[kPrefetch];
   // UX: full bf16 stages of the Markov head load their base logits coalesced
   // (UCoal) and pass each group through this wave's LDS tile (row pitch 144
-  // bytes, conflict-free for the MFMA-layout reads) two groups ahead of use
+  // bytes, conflict-free for the MFMA-layout reads): two tiles, two groups
+  // ahead of use (128-row stages), or one tile, one group ahead (256-row
+  // stages, whose E stage leaves room for one)
   constexpr bool UX = FULL && !ROWS && std::is_same_v<UT, uint16_t>;
-  __shared__ u32x4 utile[UX ? kDraftWaves : 1][2][16 * 9];
+  constexpr int NT = G == kGroupsPerWG ? 2 : 1;
+  static_assert(UX || NT == 2, "single-tile pipeline: coalesced bf16 loads only");
+  __shared__ u32x4 utile[UX ? kDraftWaves : 1][NT][16 * 9];
   UCoal uc;
   if constexpr (FULL) {
     if constexpr (UX) uc.setup(a, lane);
@@ -261,7 +272,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       const int K = a.K, k = a.k;
       if (wave < 4) stage_rows<KC>(st, a.O, a.r, row0, a.B, [&](int g) { return g * K + k - 1; });
     } else {
-      if (wave < 4) eld.store(st, a.r);
+      if (wave < kStageWaves) eld.store(st, a.r);
     }
     __syncthreads();
   }
@@ -276,7 +287,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
     // Group h's base logits sit in buf[h % kPrefetch] until they seed h's
     // accumulators (one step before h's epilogue); the freed slot is refilled
     // kPrefetch groups ahead.
-    static_assert(kGroupsPerWG % kPrefetch == 0, "ring");
+    static_assert(G % kPrefetch == 0, "ring");
     // the next block is claimed at the start of the current one: its base
     // logits and W2 fragments are requested during the current block
     auto claim = [&]() {
@@ -284,30 +295,33 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       if (lane == 0) v = atomicAdd(&blk_next, 1);
       return __builtin_amdgcn_readfirstlane(v);
     };
-    // UX: group h (of the block, h >= 8: of the next one) goes from ring slot
-    // h % kPrefetch into tile h % 2 two steps before its MFMAs (xwrite), and
-    // comes back in the MFMA layout one step before them (xread); the slot is
-    // refilled with group h + kPrefetch as soon as it is written out.  LDS
-    // operations of one wave complete in order, so no barrier is needed.
+    // UX: group h (of the block, h >= G: of the next one) goes from ring slot
+    // h % kPrefetch into tile h % NT before its MFMAs (xwrite), and comes back
+    // in the MFMA layout one step before them (xread); the slot is refilled
+    // with group h + kPrefetch as soon as it is written out.  LDS operations
+    // of one wave complete in order, so no barrier is needed, and with one
+    // tile a group is written only after the previous one has been read.
     auto xwrite = [&](int h) {
       if constexpr (UX) {
-        utile[wave][h & 1][(lane >> 3) * 9 + (lane & 7)] = buf[h % kPrefetch].w[0];
-        utile[wave][h & 1][(8 + (lane >> 3)) * 9 + (lane & 7)] = buf[h % kPrefetch].w[1];
+        utile[wave][h % NT][(lane >> 3) * 9 + (lane & 7)] = buf[h % kPrefetch].w[0];
+        utile[wave][h % NT][(8 + (lane >> 3)) * 9 + (lane & 7)] = buf[h % kPrefetch].w[1];
       }
     };
     auto xread = [&](int h, float (&u)[16]) {
       if constexpr (UX) {
         GroupLogitsBuf<uint16_t> t;
-        t.w[0] = utile[wave][h & 1][(lane & 15) * 9 + 2 * (lane >> 4)];
-        t.w[1] = utile[wave][h & 1][(lane & 15) * 9 + 2 * (lane >> 4) + 1];
+        t.w[0] = utile[wave][h % NT][(lane & 15) * 9 + 2 * (lane >> 4)];
+        t.w[1] = utile[wave][h % NT][(lane & 15) * 9 + 2 * (lane >> 4) + 1];
         t.unpack(u);
       }
     };
     if constexpr (UX) {
       xwrite(0);
       uc.load_if(buf[0], row0 + 16 * kPrefetch, blk, blk < blk_stop);
-      xwrite(1);
-      uc.load_if(buf[1], row0 + 16 * (kPrefetch + 1), blk, blk < blk_stop);
+      if constexpr (NT == 2) {
+        xwrite(1);
+        uc.load_if(buf[1], row0 + 16 * (kPrefetch + 1), blk, blk < blk_stop);
+      }
     }
     while (blk < blk_stop) {
       const int cbase = blk * kWaveCols + lane_col;
@@ -316,11 +330,11 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
       const int e_off = launder(e_lane_offset<KCs, ROWS>(lane));
       auto refill = [&](int h) {  // slot h % kPrefetch now takes group h (maybe of the next block)
         if constexpr (UX) {
-          if (h < kGroupsPerWG) uc.load_if(buf[h % kPrefetch], row0 + 16 * h, blk, true);
-          else uc.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
+          if (h < G) uc.load_if(buf[h % kPrefetch], row0 + 16 * h, blk, true);
+          else uc.load_if(buf[h % kPrefetch], row0 + 16 * (h - G), nxt, has_next);
         } else {
-          if (h < kGroupsPerWG) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
-          else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - kGroupsPerWG), nxt, has_next);
+          if (h < G) ua.load(buf[h % kPrefetch], row0 + 16 * h, blk);
+          else ua.load_if(buf[h % kPrefetch], row0 + 16 * (h - G), nxt, has_next);
         }
       };
       f32x4 acc[4];
@@ -328,6 +342,10 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
         float u[16];
         if constexpr (UX) {
           xread(0, u);
+          if constexpr (NT == 1) {  // one tile: group 1 goes in once group 0 is out
+            xwrite(1);
+            refill(1 + kPrefetch);
+          }
         } else {
           buf[0].unpack(u);
           refill(kPrefetch);
@@ -337,13 +355,13 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
         if constexpr (KC > 0) mfma_group<KC, false>(st, 0, lane, w2, acc, e_off);
       }
 #pragma unroll
-      for (int g = 0; g < kGroupsPerWG; ++g) {
+      for (int g = 0; g < G; ++g) {
         float z[16];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) z[4 * b + i] = acc[b][i];
-        if (g + 1 < kGroupsPerWG) {
+        if (g + 1 < G) {
           float u[16];
           if constexpr (UX) {
             xread(g + 1, u);
@@ -354,7 +372,7 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) acc[b] = f32x4{u[4 * b], u[4 * b + 1], u[4 * b + 2], u[4 * b + 3]};
           if constexpr (KC > 0) {
-            if (g + 2 < kGroupsPerWG) {
+            if (g + 2 < G) {
               mfma_group<KC, false>(st, g + 1, lane, w2, acc, e_off);
             } else {
               // last group of the block: the first half of the next block's W2
@@ -372,8 +390,10 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
           wf.template load_range_if<KC, KC / 2, KC>(nxt * kWaveCols, has_next, w2);
         }
         if constexpr (UX) {
-          xwrite(g + 2);
-          refill(g + 2 + kPrefetch);
+          if (NT == 2 || g + 2 <= G) {  // one tile: the next block's group 1 waits for its group 0's read
+            xwrite(g + 2);
+            refill(g + 2 + kPrefetch);
+          }
         }
         const float2 v = slice_values<GREEDY, false>(z, cbase, a.V, a.c2);
         buffer_store8_untracked(prs, v, st_voff, (uint32_t)(row0 + 16 * g) * row_bytes + (uint32_t)blk * 8u);
@@ -621,14 +641,31 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
 
 // Full 128-row stages and the trailing partial stage (B not a multiple of
 // 128) are separate launches of separately register-allocated variants.
+// bf16 base logits with a Markov head sweep pairs of full stages as 256-row
+// stages (each pair one stage of the 256-row variant, over the whole grid).
 template <typename UT, bool VEC, int KC, bool GREEDY, bool ROWS = false>
 static int launch_partials(const DraftArgs& a, hipStream_t stream) {
   const int full = VEC ? a.B / kStageRows : 0;  // unaligned rows: the plain variant throughout
   const int partial = a.nstages - full;
   if constexpr (VEC) {
-    if (full > 0) {
+    int done = 0;
+    if constexpr (!ROWS && KC > 0 && std::is_same_v<UT, uint16_t>) {
+      const int pairs = full / 2;
+      if (pairs > 0) {
+        DraftArgs b = a;
+        b.ncol_tiles = std::max(1, std::min(a.nslices, kPersistentWGs / pairs));
+        const int rc = launch_kernel("draft_partials",
+                                     draft_partials_kernel<UT, VEC, KC, GREEDY, true, false, 2 * kGroupsPerWG>,
+                                     dim3(xcd_grid(b.ncol_tiles, pairs)), dim3(kDraftWaves * 64), stream, b, 0,
+                                     pairs);
+        if (rc) return rc;
+        done = 2 * pairs;
+      }
+    }
+    if (full > done) {
       const int rc = launch_kernel("draft_partials", draft_partials_kernel<UT, VEC, KC, GREEDY, true, ROWS>,
-                                   dim3(xcd_grid(a.ncol_tiles, full)), dim3(kDraftWaves * 64), stream, a, 0, full);
+                                   dim3(xcd_grid(a.ncol_tiles, full - done)), dim3(kDraftWaves * 64), stream, a,
+                                   done, full - done);
       if (rc) return rc;
     }
   }

@@ -102,6 +102,9 @@ def test_draft_tiny_workload(T):
     (17, 3, 2000, 64, torch.bfloat16, 0.0),    # greedy with bf16 ties
     (9, 2, 520, 0, torch.bfloat16, 0.0),       # greedy, no bias, ragged tail
     (2, 16, 300, 32, torch.float32, 1.0),      # the largest K
+    (384, 2, 4096, 256, torch.bfloat16, 1.0),  # a 256-row stage pair and a leftover full 128-row stage
+    (300, 2, 2048, 64, torch.bfloat16, 0.8),   # a 256-row stage pair and a partial stage
+    (272, 3, 2048, 128, torch.bfloat16, 0.0),  # greedy over a 256-row stage pair
 ])
 def test_draft_shapes(B, K, V, r, dtype, T):
     _say("draft shape B=%d K=%d V=%d r=%d %s T=%g" % (B, K, V, r, dtype, T))
