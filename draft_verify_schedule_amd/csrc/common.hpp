@@ -172,6 +172,26 @@ __device__ __forceinline__ float rows_sum(float v) {
   return a + b;
 }
 
+// Exchanges within groups of 8 lanes on the DPP path (no LDS): xor 1 and
+// xor 2 inside each quad, then lane i <-> 7 - i (the two quads of an 8-lane
+// row half).  Three combining steps leave the 8-lane reduction in all 8 lanes.
+__device__ __forceinline__ int dpp_q1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_q2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_hm(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ float dpp_q1(float v) { return __int_as_float(dpp_q1(__float_as_int(v))); }
+__device__ __forceinline__ float dpp_q2(float v) { return __int_as_float(dpp_q2(__float_as_int(v))); }
+__device__ __forceinline__ float dpp_hm(float v) { return __int_as_float(dpp_hm(__float_as_int(v))); }
+__device__ __forceinline__ float lanes8_max(float v) {
+  v = fmaxf(v, dpp_q1(v));
+  v = fmaxf(v, dpp_q2(v));
+  return fmaxf(v, dpp_hm(v));
+}
+__device__ __forceinline__ float lanes8_sum(float v) {
+  v += dpp_q1(v);
+  v += dpp_q2(v);
+  return v + dpp_hm(v);
+}
+
 // Inclusive prefix sum across the 64 lanes in lane order.
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
   const int lane = threadIdx.x & (kWave - 1);

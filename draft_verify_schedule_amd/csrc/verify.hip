@@ -251,15 +251,16 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) w[l] = buffer_load16(rs, lane_off + (uint32_t)(16 * l), soff);
   };
-  auto reduce = [&](int item, const u32x4 (&w)[LOADS]) {
-    const int row = item / a.nchunks;
-    const int chunk = item - row * a.nchunks;
-    const int wbase = chunk * kRowChunk + wave * kWaveColsR;
+  // one item's statistics; MASK: the wave's 2048 columns pass the end of the
+  // row (only then are values masked: V is a multiple of EPL, so whole
+  // vectors are in or out)
+  auto reduce_as = [&](auto mask_tag, int row, int wbase, const u32x4 (&w)[LOADS]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int c0 = wbase + lane * CPL;
     float v[CPL];
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      const bool ok = c0 + l * EPL < a.V;  // V is a multiple of EPL: whole vectors are in or out
+      const bool ok = !MASK || c0 + l * EPL < a.V;
       if constexpr (sizeof(PT) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -276,14 +277,31 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
     if constexpr (GREEDY) {
       float m = -INFINITY, m2 = -INFINITY;
       int idx = -1;
+      if constexpr (MASK) {
 #pragma unroll
-      for (int e = 0; e < CPL; ++e)
-        if (c0 + e < a.V) merge_top2(m, idx, m2, v[e], c0 + e, -INFINITY);
+        for (int e = 0; e < CPL; ++e)
+          if (c0 + e < a.V) merge_top2(m, idx, m2, v[e], c0 + e, -INFINITY);
+      } else {
+        // every column valid: the max, its first index, and the largest value
+        // at any other index (a tie gives the max itself)
+        m = v[0];
 #pragma unroll
-      for (int off = 1; off < LPS; off <<= 1) {
-        const float om = __shfl_xor(m, off, 64);
-        const int oi = __shfl_xor(idx, off, 64);
-        const float om2 = __shfl_xor(m2, off, 64);
+        for (int e = 1; e < CPL; ++e) m = fmaxf(m, v[e]);
+        int first = CPL - 1;
+#pragma unroll
+        for (int e = CPL - 2; e >= 0; --e) first = (v[e] == m) ? e : first;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) m2 = fmaxf(m2, e == first ? -INFINITY : v[e]);
+        idx = c0 + first;
+      }
+      {  // the slice's 8 lanes
+        int oi;
+        float om, om2;
+        om = dpp_q1(m); oi = dpp_q1(idx); om2 = dpp_q1(m2);
+        merge_top2(m, idx, m2, om, oi, om2);
+        om = dpp_q2(m); oi = dpp_q2(idx); om2 = dpp_q2(m2);
+        merge_top2(m, idx, m2, om, oi, om2);
+        om = dpp_hm(m); oi = dpp_hm(idx); om2 = dpp_hm(m2);
         merge_top2(m, idx, m2, om, oi, om2);
       }
       res = make_float2(m, __int_as_float(idx));
@@ -292,15 +310,13 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
       float m = v[0];
 #pragma unroll
       for (int e = 1; e < CPL; ++e) m = fmaxf(m, v[e]);
-#pragma unroll
-      for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      m = lanes8_max(m);
       const bool empty = m == -INFINITY;
       const float mc = empty ? 0.f : m * a.c2;
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) s += fast_exp2(fmaf(v[e], a.c2, -mc));
-#pragma unroll
-      for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
+      s = lanes8_sum(s);
       res = make_float2(empty ? -INFINITY : mc, s);
     }
     const int slice = wbase / kRowSlice + lane / LPS;
@@ -310,6 +326,13 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
     if constexpr (GREEDY) {
       if (a.ppart2) buffer_store4_untracked(o2rs, runner_up, voff / 2u, 0u);  // offsets past the resource drop
     }
+  };
+  auto reduce = [&](int item, const u32x4 (&w)[LOADS]) {
+    const int row = item / a.nchunks;
+    const int chunk = item - row * a.nchunks;
+    const int wbase = chunk * kRowChunk + wave * kWaveColsR;
+    if (wbase + kWaveColsR > a.V) reduce_as(std::true_type{}, row, wbase, w);  // wave-uniform branch
+    else reduce_as(std::false_type{}, row, wbase, w);
   };
 
   int item = blockIdx.x;
