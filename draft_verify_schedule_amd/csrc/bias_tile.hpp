@@ -486,9 +486,12 @@ __device__ __forceinline__ float bias_chunk64(const uint16_t* __restrict__ w1row
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int k = k0 + 8 * i;
-    const bool ok = k < r;
-    av[i] = ok ? *reinterpret_cast<const u32x4*>(w1row + k) : u32x4{0u, 0u, 0u, 0u};
-    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2col + k) : u32x4{0u, 0u, 0u, 0u};
+    const bool ok = k < r;  // uniform; the load is unconditional (address clamped) so that
+    const int kk = ok ? k : 0;  // every load of the chunk stays in one basic block
+    const u32x4 x = *reinterpret_cast<const u32x4*>(w1row + kk);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(w2col + kk);
+    av[i] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    bv[i] = ok ? y : u32x4{0u, 0u, 0u, 0u};
   }
   float s = 0.f;
 #pragma unroll
@@ -516,10 +519,12 @@ __device__ __forceinline__ float bias_chunk64_swz(const uint16_t* __restrict__ w
   for (int i = 0; i < 8; ++i) {
     const int k = k0 + 8 * i;
     const bool ok = k < r;
-    const int f = b * kc_count + (k >> 5);
-    av[i] = ok ? *reinterpret_cast<const u32x4*>(w1row + k) : u32x4{0u, 0u, 0u, 0u};
-    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2blk + (size_t)f * 1024 + (16 * ((k >> 3) & 3) + a) * 16)
-               : u32x4{0u, 0u, 0u, 0u};
+    const int kk = ok ? k : 0;
+    const int f = b * kc_count + (kk >> 5);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(w1row + kk);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(w2blk + (size_t)f * 1024 + (16 * ((kk >> 3) & 3) + a) * 16);
+    av[i] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    bv[i] = ok ? y : u32x4{0u, 0u, 0u, 0u};
   }
   float s = 0.f;
 #pragma unroll
@@ -544,9 +549,13 @@ __device__ __forceinline__ float bias_chunk64_rows(const float* __restrict__ oro
   for (int i = 0; i < 8; ++i) {
     const int k = k0 + 8 * i;
     const bool ok = k < r;
-    av[2 * i] = ok ? *reinterpret_cast<const f32x4*>(orow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
-    av[2 * i + 1] = ok ? *reinterpret_cast<const f32x4*>(orow + k + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    bv[i] = ok ? *reinterpret_cast<const u32x4*>(w2col + k) : u32x4{0u, 0u, 0u, 0u};
+    const int kk = ok ? k : 0;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow + kk);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow + kk + 4);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(w2col + kk);
+    av[2 * i] = ok ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
+    av[2 * i + 1] = ok ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
+    bv[i] = ok ? y : u32x4{0u, 0u, 0u, 0u};
   }
   float s = 0.f;
 #pragma unroll
@@ -596,6 +605,68 @@ __device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w
   part[wave * 64 + lane] = v;
   __syncthreads();
   return ((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane];
+}
+
+// Bias of one column per lane, all of r <= 256 (r % 8 == 0), for the draft's
+// one-wave re-scan.  The bias input row is the same for the whole wave and has
+// been staged in LDS by the caller, zero-filled to 256 values (row: 32 entries
+// of 8 bf16 W1 weights, or with ROWS 64 entries of 4 fp32 values of the RNN
+// head's output part).  Each lane streams its column of W2 through the buffer
+// resource w2 (column-major: the column's r weights at byte offset off0; swz:
+// the lane's entries of the slice's fragment-ordered block at off0); every
+// load is issued before the first product, and a load past r (or with !ok)
+// gets an offset past the resource and reads zeros.  Chunks of 64 in k
+// order, the chunk sums added left to right; within a chunk the W1 bias takes
+// packed bf16 dot products of the pairs (k, k + 1) in index order
+// (v_dot2c_f32_bf16, fp32 accumulation), the RNN head's fp32 row fp32 FMAs in
+// index order.  Zero terms past r leave the sums unchanged.  !ok gives 0.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+template <bool ROWS>
+__device__ __forceinline__ float lane_bias_staged(const u32x4* row, rsrc_t w2, uint32_t w2_bytes, uint32_t off0,
+                                                  bool swz, int r, bool ok, int lane) {
+  u32x4 bv[32];
+  const int a = 4 * (lane >> 4) + (lane & 3);  // swz: MFMA A-row of the lane's column ...
+  const int b = (lane >> 2) & 3;               // ... in block b
+  const int kc_count = (r + 31) / 32;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int k = 8 * i;
+    const uint32_t off = swz ? off0 + (uint32_t)(b * kc_count + (k >> 5)) * 1024u + (uint32_t)(16 * ((k >> 3) & 3) + a) * 16u
+                             : off0 + (uint32_t)k * 2u;
+    bv[i] = buffer_load16(w2, (ok && k < r) ? off : w2_bytes, 0u);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load requested before the first product
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 8 * j; i < 8 * j + 8; ++i) {
+      if constexpr (ROWS) {
+        const u32x4 p0 = row[2 * i];
+        const u32x4 p1 = row[2 * i + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const u32x4& pa = e < 2 ? p0 : p1;
+          s = fmaf(__uint_as_float(pa[2 * (e % 2)]), __uint_as_float(bv[i][e] << 16), s);
+          s = fmaf(__uint_as_float(pa[2 * (e % 2) + 1]), __uint_as_float(bv[i][e] & 0xFFFF0000u), s);
+        }
+      } else {
+        // bf16 pairs straight into the packed dot product (k, k + 1 per dword)
+        const u32x4 av = row[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // the dwords go through scalars: a bit cast of a vector element
+          // expression is not reliable here
+          const uint32_t x = av[e], y = bv[i][e];
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, y), s, false);
+        }
+      }
+    }
+    c[j] = s;
+  }
+  return ok ? ((c[0] + c[1]) + c[2]) + c[3] : 0.f;
 }
 
 }  // namespace dspark

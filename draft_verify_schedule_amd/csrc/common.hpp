@@ -83,6 +83,12 @@ __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voffset, uint3
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, (int)soffset, 0));
 }
 
+__device__ __forceinline__ float2 buffer_load8(rsrc_t r, uint32_t voffset, uint32_t soffset) {
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+  const u32x2 d = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voffset, (int)soffset, 0));
+  return make_float2(__uint_as_float(d[0]), __uint_as_float(d[1]));
+}
+
 // Raw-buffer range checking covers voffset + soffset: a load whose offset is
 // at or past the resource size returns zeros without touching memory, and
 // such a store is dropped.  Kernels use this as a branch-free mask: an offset
@@ -212,6 +218,53 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
     const double o = __shfl_up(v, off, kWave);
     if (lane >= off) v += o;
   }
+  return v;
+}
+
+// The same scans on the DPP path (no LDS): Hillis-Steele steps of 1, 2, 4, 8
+// lanes inside each 16-lane row (row_shr, lanes without a source add 0), then
+// the row totals carried across rows (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3).  Exact sums are those of the LDS versions;
+// rounding can differ in the last place (another association).
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t v, int n) {
+  switch (n) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+    case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+  }
+}
+__device__ __forceinline__ uint32_t dpp_bcast15(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_bcast31(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+}
+__device__ __forceinline__ float wave_inclusive_scan_dpp(float v) {
+#pragma unroll
+  for (int n = 1; n <= 8; n <<= 1) v += __uint_as_float(dpp_shr(__float_as_uint(v), n));
+  v += __uint_as_float(dpp_bcast15(__float_as_uint(v)));
+  v += __uint_as_float(dpp_bcast31(__float_as_uint(v)));
+  return v;
+}
+__device__ __forceinline__ double dpp_f64(double v, int step) {  // step 0..3: row_shr 1,2,4,8; 4: bcast15; 5: bcast31
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  if (step < 4) {
+    lo = dpp_shr(lo, 1 << step);
+    hi = dpp_shr(hi, 1 << step);
+  } else if (step == 4) {
+    lo = dpp_bcast15(lo);
+    hi = dpp_bcast15(hi);
+  } else {
+    lo = dpp_bcast31(lo);
+    hi = dpp_bcast31(hi);
+  }
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_inclusive_scan_dpp(double v) {
+#pragma unroll
+  for (int step = 0; step < 6; ++step) v += dpp_f64(v, step);
   return v;
 }
 

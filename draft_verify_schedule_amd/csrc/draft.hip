@@ -428,59 +428,80 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
   }
 }
 
-// One workgroup (256 threads) per request.  Thread t owns a contiguous run
-// of at most kLocPer slices, read once into registers; block reductions give
-// the global max M and the normaliser S = sum_s s_s 2^(m_s - M); a block scan
-// of the per-thread sums finds the thread whose run holds the crossing of
-// u * S, that thread walks its run (in registers), and wave 0 re-evaluates
-// the chosen slice's 64 logits (one column per lane).  Rows with more than
-// 256 * kLocPer slices take the same steps with reloads.
-constexpr int kLocPer = 16;
+// One wave per request.  Lane l owns the contiguous run of slices
+// [l * per, (l + 1) * per), per = ceil(nslices / 64), read once into
+// registers (rows of more than 64 * kLocRun slices re-read their runs).  Wave
+// reductions give M = max of the slices' scaled maxima and each run's mass in
+// fp64; an fp64 wave scan of the run masses finds the lane whose run holds
+// the crossing of u * S; every lane walks its own run and the owner's
+// crossing is broadcast; then each lane re-evaluates one of the chosen
+// slice's 64 logits and a wave scan of their masses picks the token.  No
+// barrier and two dependent memory round trips (the partials, then the
+// slice's base logits and W2 block).
+constexpr int kLocRun = 40;
+constexpr int kMaxRankRow = 64;  // 16-byte entries of the staged bias row: r <= 256 fp32 values
 
 template <typename UT, bool GREEDY>
-__global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
-  __shared__ float red_f[4];
-  __shared__ int red_i[4];
-  __shared__ double wave_tot[4];
-  __shared__ int sh_slice;
-  __shared__ double sh_before;
-  __shared__ double sh_w[kLocPer];
-  __shared__ double sh_acc0;
-  __shared__ int sh_s0;
-  __shared__ float bias_part[256];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_index();
+__global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
+  const int lane = threadIdx.x;
   const int b = blockIdx.x;
   const size_t out = (size_t)b * a.K + (a.k - 1);
   const int prev = a.prev[(size_t)b * a.prev_stride];
   const float2* part = a.part + (size_t)b * a.nslices;
   const int ns = a.nslices;
-  const int per = (ns + 255) / 256;
-  const int s0 = min(ns, tid * per);
+  const int per = (ns + 63) / 64;
+  const int s0 = min(ns, lane * per);
   const int s1 = min(ns, s0 + per);
-  const bool in_regs = per <= kLocPer;
-  float2 p[kLocPer];
+  const bool in_regs = per <= kLocRun;
+  // the bias input row of the re-scan (W1[prev], or the RNN head's output
+  // part), the same for the whole wave, is staged in LDS while the partials
+  // are in flight
+  __shared__ u32x4 sh_row[kMaxRankRow];
+  const bool prev_ok = prev >= 0 && prev < a.V;
+  float2 p[kLocRun];
+  if (in_regs) {
+    // every load is issued (no branch): slots past the lane's run read zeros
+    // from past the end of the row's resource, a slice with no mass
+    const rsrc_t prow = make_rsrc(part, (uint32_t)ns * (uint32_t)sizeof(float2));
+#pragma unroll
+    for (int i = 0; i < kLocRun; ++i)
+      p[i] = buffer_load8(prow, (s0 + i < s1) ? (uint32_t)(s0 + i) * 8u : (uint32_t)ns * 8u, 0u);
+  }
+  // the bias input row, requested after the partials (its address waits for
+  // prev; no branch: a lane past r, or a request without a bias row, reads
+  // zeros) and written to LDS once needed
+  u32x4 row_in = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (!GREEDY) {
+    const bool has_row = a.r > 0 && prev_ok;
+    const int n = a.O ? a.r / 4 : a.r / 8;
+    const rsrc_t rr = a.O ? make_rsrc(a.O + out * a.r, (uint32_t)a.r * 4u)
+                          : make_rsrc(a.W1 + (size_t)(prev_ok ? prev : 0) * a.r, (uint32_t)a.r * 2u);
+    row_in = buffer_load16(rr, (has_row && lane < n) ? (uint32_t)lane * 16u : 0xFFFFFFF0u, 0u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < kLocPer; ++i) p[i] = (s0 + i < s1) ? part[s0 + i] : make_float2(-INFINITY, 0.f);
+    for (int i = 0; i < kLocRun; ++i)
+      if (s0 + i >= s1) p[i].x = -INFINITY;  // past the run (read as zeros): no maximum
   }
-  if (prev < 0 || prev >= a.V) {
-    if (tid == 0) {
+  if (!prev_ok) {
+    if (lane == 0) {
       a.x_out[out] = -1;
       a.q_out[out] = NAN;
       a.lse_out[out] = NAN;
     }
     return;
   }
+  // the decision uniform, computed while the loads are in flight
+  const float u = GREEDY ? 0.f : decision_uniform(a.seed, a.step, (uint32_t)b, (uint32_t)a.k, kPurposeDraft);
 
   if constexpr (GREEDY) {
     float m = -INFINITY;
     int idx = -1;
     if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < kLocPer; ++i)
-        if (s0 + i < s1) merge_argmax(m, idx, p[i].x, __float_as_int(p[i].y));
+      for (int i = 0; i < kLocRun; ++i)
+        if (s0 + i < s1) merge_argmax(m, idx, p[i].x, __float_as_int(p[i].y));  // (no load in the branch)
     } else {
       for (int s = s0; s < s1; ++s) merge_argmax(m, idx, part[s].x, __float_as_int(part[s].y));
     }
@@ -491,12 +512,6 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
       merge_argmax(m, idx, m2, i2);
     }
     if (lane == 0) {
-      red_f[wave] = m;
-      red_i[wave] = idx;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < 4; ++w) merge_argmax(m, idx, red_f[w], red_i[w]);
       a.x_out[out] = idx;
       a.q_out[out] = 1.0f;
       a.lse_out[out] = m;
@@ -504,128 +519,133 @@ __global__ __launch_bounds__(256) void draft_locate_kernel(DraftArgs a) {
     return;
   }
 
-  // global max
   float M = -INFINITY;
   if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < kLocPer; ++i) M = fmaxf(M, p[i].x);
+    for (int i = 0; i < kLocRun; ++i) M = fmaxf(M, p[i].x);
   } else {
     for (int s = s0; s < s1; ++s) M = fmaxf(M, part[s].x);
   }
   M = wave_max(M);
-  if (lane == 0) red_f[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
   // slice masses in fp32, their CDF in fp64
   auto weight = [&](float2 q) { return (q.x == -INFINITY) ? 0.0 : (double)(q.y * fast_exp2(q.x - M)); };
-  // per-thread mass and its block-wide inclusive scan (thread order = slice order)
   double local = 0.0;
   if (in_regs) {
+    double l4[4] = {0.0, 0.0, 0.0, 0.0};  // four chains in flight
 #pragma unroll
-    for (int i = 0; i < kLocPer; ++i) local += weight(p[i]);
+    for (int i = 0; i < kLocRun; ++i) l4[i & 3] += weight(p[i]);
+    local = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   } else {
     for (int s = s0; s < s1; ++s) local += weight(part[s]);
   }
-  double incl = wave_inclusive_scan(local);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  double before_wave = 0.0;
-  for (int w = 0; w < wave; ++w) before_wave += wave_tot[w];
-  incl += before_wave;
-  const double S = ((wave_tot[0] + wave_tot[1]) + wave_tot[2]) + wave_tot[3];
-  const float u = decision_uniform(a.seed, a.step, (uint32_t)b, (uint32_t)a.k, kPurposeDraft);
+  const double incl = wave_inclusive_scan_dpp(local);
+  const double S = __shfl(incl, 63, 64);
   const double target = (double)u * S;
-  // owner: first thread whose inclusive sum passes the target, else the last with mass
-  {
-    const int f = wave_first_lane(incl > target);
+  // owner: first lane whose inclusive sum passes the target, else the last with mass
+  int owner = wave_first_lane(incl > target);
+  if (owner < 0) {
     const unsigned long long mm = __ballot(local > 0.0);
-    if (lane == 0) {
-      red_i[wave] = f < 0 ? 0x7FFFFFFF : wave * 64 + f;
-      red_f[wave] = mm ? (float)(wave * 64 + 63 - __clzll((long long)mm)) : -1.f;
-    }
+    owner = mm ? 63 - __clzll((long long)mm) : 0;
   }
-  __syncthreads();
-  int owner = min(min(red_i[0], red_i[1]), min(red_i[2], red_i[3]));
-  if (owner == 0x7FFFFFFF) {
-    const float last = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    owner = last < 0.f ? 0 : (int)last;
-  }
-  // The owner's slices hold the crossing.  Registers path: the owner puts
-  // their masses in LDS and every wave finds the crossing with a wave scan.
-  // Otherwise the owner walks its run and shares the result.
-  if (tid == owner) {
-    const double acc0 = incl - local;
-    if (in_regs) {
-#pragma unroll
-      for (int i = 0; i < kLocPer; ++i) sh_w[i] = (s0 + i < s1) ? weight(p[i]) : 0.0;
-      sh_acc0 = acc0;
-      sh_s0 = s0;
-    } else {
-      double acc = acc0;
-      int hit = -1, last = -1;
-      double hit_before = 0.0, last_before = acc;
-      for (int s = s0; s < s1; ++s) {
-        const double w = weight(part[s]);
-        if (w > 0.0) {
-          if (hit < 0 && acc + w > target) {
-            hit = s;
-            hit_before = acc;
-          }
-          last = s;
-          last_before = acc;
-        }
-        acc += w;
-      }
-      if (hit < 0) {
-        hit = last;
-        hit_before = last_before;
-      }
-      sh_slice = hit < 0 ? 0 : hit;  // no mass at all (non-finite logits): stay in range
-      sh_before = hit_before;
-    }
-  }
-  __syncthreads();
+  // the owner's run: its first slice with mass whose cumulative sum passes
+  // the target, else its last slice with mass
   int s_star;
   double before;
+  float m_s;
   if (in_regs) {
-    const double w = lane < kLocPer ? sh_w[lane] : 0.0;
-    const double acc0 = sh_acc0;
-    const double cum = acc0 + wave_inclusive_scan(w);
+    // the owner lane puts its run in LDS (in-order LDS access within the
+    // wave: no barrier), lane i takes its slice i and an fp64 wave scan of
+    // the masses finds the crossing
+    __shared__ float2 sh_run[kLocRun];
+    sh_row[lane] = row_in;  // the bias row, zero-filled past r
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i < kLocRun; ++i) sh_run[i] = p[i];
+    }
+    const double acc0 = __shfl(incl - local, owner, 64);
+    const int os0 = __shfl(s0, owner, 64);
+    const float2 q = lane < kLocRun ? sh_run[lane] : make_float2(-INFINITY, 0.f);
+    const double w = weight(q);
+    const double cum = acc0 + wave_inclusive_scan_dpp(w);
     int pick = wave_first_lane(cum > target && w > 0.0);
     if (pick < 0) {  // rounding: the last slice with mass
       const unsigned long long mm = __ballot(w > 0.0);
       pick = mm ? 63 - __clzll((long long)mm) : -1;
     }
-    const double cb = __shfl(cum - w, pick < 0 ? 0 : pick, 64);
-    s_star = pick < 0 ? 0 : sh_s0 + pick;  // no mass at all (non-finite logits): stay in range
-    before = pick < 0 ? acc0 : cb;
+    if (pick < 0) {  // no mass at all (non-finite logits): stay in range
+      s_star = 0;
+      before = acc0;
+      m_s = __shfl(p[0].x, 0, 64);
+    } else {
+      s_star = os0 + pick;
+      before = __shfl(cum - w, pick, 64);
+      m_s = __shfl(q.x, pick, 64);
+    }
   } else {
-    s_star = sh_slice;
-    before = sh_before;
+    sh_row[lane] = row_in;
+    double acc = incl - local;
+    int hit = -1, last = -1;
+    double hit_before = 0.0, last_before = acc;
+    float hit_m = 0.f, last_m = 0.f;
+    for (int s = s0; s < s1; ++s) {
+      const float2 q = part[s];
+      const double w = weight(q);
+      if (w > 0.0) {
+        if (hit < 0 && acc + w > target) {
+          hit = s;
+          hit_before = acc;
+          hit_m = q.x;
+        }
+        last = s;
+        last_before = acc;
+        last_m = q.x;
+      }
+      acc += w;
+    }
+    if (hit < 0) {
+      hit = last;
+      hit_before = last_before;
+      hit_m = last_m;
+    }
+    if (hit < 0) {  // no mass at all (non-finite logits): stay in range
+      hit = 0;
+      hit_before = incl - local;
+      hit_m = part[0].x;
+    }
+    s_star = __shfl(hit, owner, 64);
+    before = __shfl(hit_before, owner, 64);
+    m_s = __shfl(hit_m, owner, 64);
   }
-  // re-evaluate the 64 logits of slice s_star, one column per lane; the four
-  // waves share the bias dot products (a quarter of r each); wave 0's base
-  // logit and slice maximum are requested first
+
+  // re-evaluate the 64 logits of slice s_star, one column per lane
   const int col = s_star * kWaveCols + lane;
   const bool col_ok = col < a.V;
   const UT* urow = reinterpret_cast<const UT*>(a.U) + ((size_t)b * a.K + (a.k - 1)) * a.V;
-  float base = 0.f;
-  float m_s = 0.f;
-  if (wave == 0) {
-    base = col_ok ? load_logit(urow, col) : 0.f;
-    m_s = part[s_star].x;
-  }
+  // the base logit and the W2 weights are requested together (buffer loads:
+  // a column past V reads zero, no branch)
+  const rsrc_t ur = make_rsrc(urow, (uint32_t)a.V * (uint32_t)sizeof(UT));
+  const uint32_t uoff = col_ok ? (uint32_t)col * (uint32_t)sizeof(UT) : 0xFFFFFFF0u;
+  float base;
+  if constexpr (sizeof(UT) == 2)
+    base = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ur, (int)uoff, 0, 0) << 16);
+  else
+    base = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ur, (int)uoff, 0, 0));
   float bias = 0.f;
-  if (a.r > 0)
-    bias = valu_bias_4waves(a.W1 + (size_t)prev * a.r, a.O ? a.O + out * a.r : nullptr,
-                            a.W2t + (size_t)(col_ok ? col : 0) * a.r, a.r, col_ok, wave, lane, bias_part,
-                            a.W2s ? reinterpret_cast<const char*>(a.W2s) + (size_t)s_star * 4 * ((a.r + 31) / 32) * 1024
-                                  : nullptr);
-  if (wave != 0) return;
+  if (a.r > 0) {
+    const int kc_count = (a.r + 31) / 32;
+    const bool swz = a.W2s != nullptr && a.O == nullptr;
+    const uint32_t w2_bytes = swz ? (uint32_t)((size_t)((a.V + kWaveCols - 1) / kWaveCols) * 4 * kc_count * 1024)
+                                  : (uint32_t)((size_t)a.V * a.r * 2);
+    const rsrc_t w2 = make_rsrc(swz ? static_cast<const void*>(a.W2s) : static_cast<const void*>(a.W2t), w2_bytes);
+    const uint32_t off0 = swz ? (uint32_t)s_star * 4u * (uint32_t)kc_count * 1024u
+                              : (uint32_t)(col_ok ? col : 0) * (uint32_t)a.r * 2u;
+    bias = a.O ? lane_bias_staged<true>(sh_row, w2, w2_bytes, off0, false, a.r, col_ok, lane)
+               : lane_bias_staged<false>(sh_row, w2, w2_bytes, off0, swz, a.r, col_ok, lane);
+  }
   const float t_in = (float)((target - before) / (double)fast_exp2(m_s - M));
   const float z = col_ok ? base + bias : -INFINITY;
-  const float e = (col < a.V) ? fast_exp2(fmaf(z, a.c2, -m_s)) : 0.f;
-  const float cum = wave_inclusive_scan(e);
+  const float e = col_ok ? fast_exp2(fmaf(z, a.c2, -m_s)) : 0.f;
+  const float cum = wave_inclusive_scan_dpp(e);
   int pick = wave_first_lane(cum > t_in && e > 0.f);
   if (pick < 0) {
     const unsigned long long mm = __ballot(e > 0.f);
@@ -764,7 +784,7 @@ static int run_draft_typed(DraftArgs a, bool vec, bool make_w2s, const RnnParams
     }
     int rc = vec ? dispatch_kc<UT, true, GREEDY>(a, stream) : dispatch_kc<UT, false, GREEDY>(a, stream);
     if (rc) return rc;
-    rc = launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3(a.B), dim3(256), stream, a);
+    rc = launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3(a.B), dim3(64), stream, a);
     if (rc) return rc;
   }
   return 0;
