@@ -9,22 +9,26 @@
 //     so that ascending keys = a descending, then j ascending, then r
 //     ascending (a is positive, so its bit pattern orders like its value);
 //     keys are distinct, so the sorted position of a key is the number of
-//     keys below it: 32 partial counts per key (1024 threads), summed, and the
-//     key is written to that position of the workspace;
-//   schedule (one workgroup of 1024 threads):
-//     1. survival products again (a_out, the domain check, the candidate
-//        count n_c), then thread t loads sorted keys t*E .. t*E+E-1
-//        (E = candidates / 1024 rounded up to a power of two);
-//     2. tau increments floor(a * 2^32) (exact int64 fixed point), block
+//     keys below it (each wave ranks two keys, its lanes counting in
+//     parallel); the key is written to that position of the workspace and
+//     the position to the candidate's rank slot (no position for a = 0).
+//     Workgroup 0 also
+//     writes a_out, the domain check and the number of candidates n_c;
+//   schedule (one workgroup of 1024 threads): every input it needs (n_c, the
+//     domain flag, thread t's sorted keys t*E .. t*E+E-1 with
+//     E = candidates / 1024 rounded up to a power of two, their SPS entries,
+//     the ranks of thread t's requests' candidates) requested in one round
+//     trip, then
+//     1. tau increments floor(a * 2^32) (exact int64 fixed point), block
 //        prefix scan, Theta_n = double(tau_n) * 2^-32 * SPS[R + n] for every
 //        admission count n; the cut n* is the first drop minus one
 //        (EARLY_STOP), the earliest maximum (GLOBAL) or min(capacity, |E|)
 //        (TOPK).  The fixed-point sum is exact, so this parallel evaluation
 //        equals the sequential walk bit for bit;
-//     3. l_r = number of r's candidates whose key lies below the n*-th sorted
-//        key (a prefix of positions by construction), and cu_seqlens by a
-//        block scan.
+//     2. l_r = number of r's candidates ranked below n* (a prefix of
+//        positions by construction), and cu_seqlens by a block scan.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -65,94 +69,122 @@ __device__ __forceinline__ uint64_t key_increment(uint64_t key) {
   return (uint64_t)((double)a * 4294967296.0);  // a in (0, 1]: exact, truncation = floor
 }
 
-// Block-wide exclusive scan of one uint64 per thread (1024 threads = 16 waves).
+// uint64 lane exchanges on the DPP path: both halves moved with the same
+// control; lanes without a source (or outside row_mask) receive `fill`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v, uint64_t fill) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)fill, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(fill >> 32), (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive uint64 prefix sum across the wave: row_shr 1, 2, 4, 8 inside each
+// 16-lane row, then row totals carried by row_bcast:15 and row_bcast:31.
+// Integer sums: exact whatever the association.
+__device__ __forceinline__ uint64_t wave_inclusive_scan_u64(uint64_t v) {
+  v += dpp64<0x111>(v, 0);
+  v += dpp64<0x112>(v, 0);
+  v += dpp64<0x114>(v, 0);
+  v += dpp64<0x118>(v, 0);
+  v += dpp64<0x142, 0xA>(v, 0);
+  v += dpp64<0x143, 0xC>(v, 0);
+  return v;
+}
+
+// Block-wide exclusive scan of one uint64 per thread (1024 threads = 16
+// waves): wave scans on DPP, the wave totals through LDS (one barrier before
+// they are read, one after so the array can be reused).
 __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* wave_sums,
                                                          uint64_t& total) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  uint64_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const uint64_t incl = wave_inclusive_scan_u64(v);
   if (lane == 63) wave_sums[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    uint64_t w = lane < kSchedThreads / 64 ? wave_sums[lane] : 0;
+  uint64_t before = 0, all = 0;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const uint64_t o = __shfl_up(w, off, 64);
-      if (lane >= off) w += o;
-    }
-    if (lane < kSchedThreads / 64) wave_sums[lane] = w;  // inclusive wave totals
+  for (int w = 0; w < kSchedThreads / 64; ++w) {
+    const uint64_t t = wave_sums[w];
+    before += w < wave ? t : 0;
+    all += t;
   }
-  __syncthreads();
-  const uint64_t before = wave ? wave_sums[wave - 1] : 0;
-  total = wave_sums[kSchedThreads / 64 - 1];
+  total = all;
   __syncthreads();
   return before + incl - v;
 }
 
-constexpr int kRankKeysPerWG = 32;
-constexpr int kRankParts = kSchedThreads / kRankKeysPerWG;
+// Wave reductions on the DPP path: quad xor 1 and 2, row half mirror and row
+// mirror give every lane its row's result, row_bcast:15 / :31 fold the rows
+// into lane 63, which is read back for the whole wave.  Lanes without a
+// source take the identity.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dppi(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_min_i32(int x) {
+  x = min(x, dppi<0xB1>(x, 0x7FFFFFFF));
+  x = min(x, dppi<0x4E>(x, 0x7FFFFFFF));
+  x = min(x, dppi<0x141>(x, 0x7FFFFFFF));
+  x = min(x, dppi<0x140>(x, 0x7FFFFFFF));
+  x = min(x, dppi<0x142, 0xA>(x, 0x7FFFFFFF));
+  x = min(x, dppi<0x143, 0xC>(x, 0x7FFFFFFF));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+// (Theta, n): the larger Theta, on equal Theta the smaller n
+__device__ __forceinline__ void best_merge(double& b, int& n, double b2, int n2) {
+  if (b2 > b || (b2 == b && n2 < n)) {
+    b = b2;
+    n = n2;
+  }
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void best_step(double& b, int& n) {
+  const double b2 = __longlong_as_double(
+      (long long)dpp64<CTRL, ROWS>((uint64_t)__double_as_longlong(b), (uint64_t)__double_as_longlong(-INFINITY)));
+  const int n2 = dppi<CTRL, ROWS>(n, 0x7FFFFFFF);
+  best_merge(b, n, b2, n2);
+}
+__device__ __forceinline__ void wave_best(double& b, int& n) {
+  best_step<0xB1>(b, n);
+  best_step<0x4E>(b, n);
+  best_step<0x141>(b, n);
+  best_step<0x140>(b, n);
+  best_step<0x142, 0xA>(b, n);
+  best_step<0x143, 0xC>(b, n);
+  const uint64_t bits = (uint64_t)__double_as_longlong(b);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 63);
+  b = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  n = __builtin_amdgcn_readlane(n, 63);
+}
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_rank_kernel(ScheduleArgs a, uint64_t* __restrict__ sorted) {
+constexpr int kRankKeysPerWG = 2 * (kSchedThreads / 64);  // two keys per wave
+constexpr int32_t kNoRank = 0x7FFFFFFF;  // a candidate with a = 0 is never admitted
+
+// Workspace: the sorted keys, every candidate's rank, then (n_c, domain flag).
+struct ScheduleWork {
+  uint64_t* sorted;
+  int32_t* rank;
+  int32_t* meta;
+};
+__host__ __device__ inline size_t sched_align(size_t b) { return (b + 255) & ~(size_t)255; }
+inline ScheduleWork schedule_work(void* ws, int n) {
+  char* p = reinterpret_cast<char*>(ws);
+  return ScheduleWork{reinterpret_cast<uint64_t*>(p), reinterpret_cast<int32_t*>(p + sched_align((size_t)n * 8)),
+                      reinterpret_cast<int32_t*>(p + sched_align((size_t)n * 8) + sched_align((size_t)n * 4))};
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_rank_kernel(ScheduleArgs a, ScheduleWork w) {
   __shared__ uint64_t keys[kSchedMaxKeys];
-  __shared__ uint32_t part_cnt[kRankParts][kRankKeysPerWG];
+  __shared__ int red_i[kSchedThreads / 64];
+  __shared__ int bad;
   const int tid = threadIdx.x;
   const int R = a.R, K = a.K;
   const int n = R * K;
-  for (int r = tid; r < R; r += kSchedThreads) {
-    float cv[kSchedMaxK];
-    load_confidences(a, r, cv);
-    float acc = 1.0f;
-#pragma unroll
-    for (int j = 0; j < kSchedMaxK; ++j) {
-      if (j < K) {
-        acc = __fmul_rn(acc, cv[j]);
-        keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
-      }
-    }
-  }
+  const bool first = blockIdx.x == 0;  // workgroup 0 also writes a_out, n_c and the domain flag
+  if (first && tid == 0) bad = 0;
   __syncthreads();
-  // thread (part p, key slot q): keys of part p below key kk
-  const int q = tid % kRankKeysPerWG;
-  const int p = tid / kRankKeysPerWG;
-  const int kk = blockIdx.x * kRankKeysPerWG + q;
-  const uint64_t x = kk < n ? keys[kk] : ~0ull;
-  const int y0 = (int)((int64_t)p * n / kRankParts);
-  const int y1 = (int)((int64_t)(p + 1) * n / kRankParts);
-  uint32_t cnt = 0;
-  for (int y = y0; y < y1; ++y) cnt += keys[y] < x ? 1u : 0u;
-  part_cnt[p][q] = cnt;
-  __syncthreads();
-  if (tid < kRankKeysPerWG && kk < n && x != ~0ull) {
-    uint32_t rank = 0;
-#pragma unroll
-    for (int i = 0; i < kRankParts; ++i) rank += part_cnt[i][tid];
-    sorted[rank] = x;  // rank < number of candidates with a > 0
-  }
-}
-
-template <int E>
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
-                                                                const uint64_t* __restrict__ sorted) {
-  __shared__ uint64_t wave_sums[kSchedThreads / 64];
-  __shared__ int bad;
-  __shared__ int red_i[kSchedThreads / 64];
-  __shared__ double red_d[kSchedThreads / 64];
-  __shared__ uint64_t threshold_s;
-  constexpr int P = kSchedThreads * E;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_index();
-  const int R = a.R, K = a.K;
-
-  if (tid == 0) bad = 0;
-  __syncthreads();
-
-  // 1. survival products, the domain check and the number of candidates
   int cnt = 0;
   for (int r = tid; r < R; r += kSchedThreads) {
     float cv[kSchedMaxK];
@@ -164,19 +196,89 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
       if (j < K) {
         ok = ok && (cv[j] >= 0.0f && cv[j] <= 1.0f);  // NaN fails both tests
         acc = __fmul_rn(acc, cv[j]);
-        a.a_out[(size_t)r * K + j] = acc;
+        keys[r * K + j] = (acc > 0.0f) ? make_key(acc, j, r) : ~0ull;
+        if (first) a.a_out[(size_t)r * K + j] = acc;
         cnt += acc > 0.0f;
       }
     }
-    if (!ok) bad = 1;
+    if (first && !ok) bad = 1;
   }
+  __syncthreads();
+  if (first) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-  if (lane == 0) red_i[wave] = cnt;
-  __syncthreads();
-  int n_c = 0;
-  for (int w = 0; w < kSchedThreads / 64; ++w) n_c += red_i[w];
-  __syncthreads();
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if ((tid & 63) == 0) red_i[wave_index()] = cnt;
+  }
+  // wave w ranks keys kk0 = 32 g + 2 w and kk0 + 1: lane l counts the keys
+  // y = l, l + 64, ... below each (coalesced, conflict-free LDS reads), the
+  // two counts are packed in one uint64 and summed across the wave
+  const int lane = tid & 63;
+  const int kk0 = blockIdx.x * kRankKeysPerWG + 2 * wave_index();
+  const uint64_t x0 = kk0 < n ? keys[kk0] : ~0ull;
+  const uint64_t x1 = kk0 + 1 < n ? keys[kk0 + 1] : ~0ull;
+  uint32_t c0 = 0, c1 = 0;
+  for (int y = lane; y < n; y += 64) {
+    const uint64_t k = keys[y];
+    c0 += k < x0 ? 1u : 0u;
+    c1 += k < x1 ? 1u : 0u;
+  }
+  const uint64_t both = wave_inclusive_scan_u64((uint64_t)c0 | ((uint64_t)c1 << 32));  // lane 63: the totals
+  if (lane == 63) {
+    const uint32_t r0 = (uint32_t)both, r1 = (uint32_t)(both >> 32);
+    if (kk0 < n) {
+      if (x0 != ~0ull) w.sorted[r0] = x0;  // rank < number of candidates with a > 0
+      w.rank[kk0] = x0 != ~0ull ? (int32_t)r0 : kNoRank;
+    }
+    if (kk0 + 1 < n) {
+      if (x1 != ~0ull) w.sorted[r1] = x1;
+      w.rank[kk0 + 1] = x1 != ~0ull ? (int32_t)r1 : kNoRank;
+    }
+  }
+  __syncthreads();  // workgroup 0: every wave's count is in red_i
+  if (first && tid == 0) {
+    int n_c = 0;
+    for (int i = 0; i < kSchedThreads / 64; ++i) n_c += red_i[i];
+    w.meta[0] = n_c;
+    w.meta[1] = bad;
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a, ScheduleWork w) {
+  __shared__ uint64_t wave_sums[kSchedThreads / 64];
+  __shared__ int red_i[kSchedThreads / 64];
+  __shared__ double red_d[kSchedThreads / 64];
+  constexpr int P = kSchedThreads * E;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_index();
+  const int R = a.R, K = a.K;
+  const int n = R * K;
+  const int i0 = tid * E;
+  const int i1 = i0 + E;
+  const int rper = (R + kSchedThreads - 1) / kSchedThreads;
+  const int r0 = min(R, tid * rper);
+  const int r1 = min(R, r0 + rper);
+
+  // every input in one round trip: n_c and the domain flag, this thread's
+  // sorted keys (those past n_c are masked below), their SPS entries
+  // (sps_len > R + n), the TOPK capacity, and with one request per thread
+  // its candidates' ranks
+  const int n_c = w.meta[0];
+  const int bad = w.meta[1];
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = (i0 + e < n) ? w.sorted[i0 + e] : ~0ull;
+  double spsv[E + 1];
+#pragma unroll
+  for (int e = 0; e <= E; ++e) spsv[e] = (i0 + e <= n) ? a.sps[R + i0 + e] : 0.0;
+  const int cap = (a.mode == 2 && a.capacity_dev) ? *a.capacity_dev : a.capacity;
+  const double sps_R = a.sps[R];
+  int32_t rk[kSchedMaxK];
+  if (rper == 1) {
+#pragma unroll
+    for (int j = 0; j < kSchedMaxK; ++j) rk[j] = (j < K && r0 < r1) ? w.rank[(size_t)r0 * K + j] : kNoRank;
+  }
 
   if (bad) {  // documented data error: a valid layout with no drafts
     for (int r = tid; r < R; r += kSchedThreads) {
@@ -190,18 +292,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
     }
     return;
   }
-
-  // thread tid holds sorted keys tid*E .. tid*E+E-1 (padding ~0)
-  uint64_t v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    v[e] = (i < n_c) ? sorted[i] : ~0ull;
-  }
+  for (int e = 0; e < E; ++e)
+    if (i0 + e >= n_c) v[e] = ~0ull;
 
-  // 2. fixed-point tau over this thread's chunk, Theta per admission count
-  const int i0 = tid * E;
-  const int i1 = i0 + E;
+  // 1. fixed-point tau over this thread's chunk, Theta per admission count
   uint64_t local = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e)
@@ -209,7 +304,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
   uint64_t total;
   const uint64_t prefix = block_exclusive_scan(local, wave_sums, total);
   const uint64_t tau0 = (uint64_t)R << 32;
-  const double theta0 = (double)tau0 * 0x1p-32 * a.sps[R];
+  const double theta0 = (double)tau0 * 0x1p-32 * sps_R;
 
   // candidate answer of this thread: EARLY_STOP -> first n with a drop;
   // GLOBAL -> best (Theta, smallest n)
@@ -217,38 +312,26 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
   double best = (tid == 0) ? theta0 : -INFINITY;
   int best_n = (tid == 0) ? 0 : 0x7FFFFFFF;
   if (a.mode != 2 && i0 < n_c) {
-    // SPS[R + i0 .. R + i1] of this thread's admission counts, requested together
-    double spsv[E + 1];
-#pragma unroll
-    for (int e = 0; e <= E; ++e) spsv[e] = (i0 + e <= n_c) ? a.sps[R + i0 + e] : 0.0;
     uint64_t tau = tau0 + prefix;
     double prev_theta = (i0 == 0) ? theta0 : (double)tau * 0x1p-32 * spsv[0];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (i0 + e < n_c) {
         tau += key_increment(v[e]);
-        const int n = i0 + e + 1;
+        const int nn = i0 + e + 1;
         const double theta = (double)tau * 0x1p-32 * spsv[e + 1];
-        if (theta <= prev_theta && n < first_drop) first_drop = n;
+        if (theta <= prev_theta && nn < first_drop) first_drop = nn;
         if (theta > best) {
           best = theta;
-          best_n = n;
+          best_n = nn;
         }
         prev_theta = theta;
       }
     }
   }
   // block reductions: min first_drop; max (best, -best_n)
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    first_drop = min(first_drop, __shfl_xor(first_drop, off, 64));
-    const double b2 = __shfl_xor(best, off, 64);
-    const int n2 = __shfl_xor(best_n, off, 64);
-    if (b2 > best || (b2 == best && n2 < best_n)) {
-      best = b2;
-      best_n = n2;
-    }
-  }
+  first_drop = wave_min_i32(first_drop);
+  wave_best(best, best_n);
   __shared__ int red_drop[kSchedThreads / 64];
   if (lane == 0) {
     red_drop[wave] = first_drop;
@@ -256,28 +339,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
     red_d[wave] = best;
   }
   __syncthreads();
-  __shared__ int n_star_s;
-  if (tid == 0) {
+  // every thread combines the sixteen wave results (no second barrier)
+  int n_star;
+  {
     int fd = 0x7FFFFFFF, bn = 0x7FFFFFFF;
     double bv = -INFINITY;
-    for (int w = 0; w < kSchedThreads / 64; ++w) {
-      fd = min(fd, red_drop[w]);
-      if (red_d[w] > bv || (red_d[w] == bv && red_i[w] < bn)) {
-        bv = red_d[w];
-        bn = red_i[w];
-      }
+#pragma unroll
+    for (int i = 0; i < kSchedThreads / 64; ++i) {
+      fd = min(fd, red_drop[i]);
+      best_merge(bv, bn, red_d[i], red_i[i]);
     }
-    int n_star;
     if (a.mode == 0) n_star = (fd == 0x7FFFFFFF) ? n_c : fd - 1;
     else if (a.mode == 1) n_star = bn;
-    else n_star = min(max(a.capacity_dev ? *a.capacity_dev : a.capacity, 0), n_c);
-    n_star_s = n_star;
-    if (n_star >= P) threshold_s = ~0ull;
+    else n_star = min(max(cap, 0), n_c);
   }
-  __syncthreads();
-  const int n_star = n_star_s;
-  // Theta of the chosen admission count and the threshold key (sorted index
-  // n*), from the threads owning those indices
+  // Theta of the chosen admission count, from the thread owning index n* - 1
   if (n_star == 0) {
     if (tid == 0) *a.theta_out = theta0;
   } else if (n_star - 1 >= i0 && n_star - 1 < i1) {
@@ -285,48 +361,45 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleArgs a,
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (i0 + e < n_star) tau += key_increment(v[e]);
-    *a.theta_out = (double)tau * 0x1p-32 * a.sps[R + n_star];
-  }
-  if (n_star >= i0 && n_star < i1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (i0 + e == n_star) threshold_s = v[e];
+    *a.theta_out = (double)tau * 0x1p-32 * spsv[n_star - i0];
   }
   if (tid == 0) *a.n_out = n_star;
-  __syncthreads();
-  const uint64_t threshold = threshold_s;
 
-  // 3. lengths and the flattened layout
-  const int rper = (R + kSchedThreads - 1) / kSchedThreads;
-  const int r0 = min(R, tid * rper);
-  const int r1 = min(R, r0 + rper);
+  // 2. lengths (candidates ranked below n*) and the flattened layout
   uint64_t mine = 0;
-  for (int r = r0; r < r1; ++r) {
-    float cv[kSchedMaxK];
-    load_confidences(a, r, cv);
-    int ell = 0;
-    float acc = 1.0f;
+  if (rper == 1) {
+    if (r0 < r1) {
+      int ell = 0;
 #pragma unroll
-    for (int j = 0; j < kSchedMaxK; ++j) {
-      if (j < K) {
-        acc = __fmul_rn(acc, cv[j]);
-        if (acc > 0.0f && make_key(acc, j, r) < threshold) ++ell;
-      }
+      for (int j = 0; j < kSchedMaxK; ++j) ell += rk[j] < n_star ? 1 : 0;
+      a.ell_out[r0] = ell;
+      mine = 1 + ell;
+      rk[0] = ell;
     }
-    a.ell_out[r] = ell;
-    mine += 1 + ell;
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      int ell = 0;
+      for (int j = 0; j < K; ++j) ell += w.rank[(size_t)r * K + j] < n_star ? 1 : 0;
+      a.ell_out[r] = ell;
+      mine += 1 + ell;
+    }
   }
   uint64_t all;
   uint64_t run = block_exclusive_scan(mine, wave_sums, all);
   if (tid == 0) a.cu_out[0] = 0;
-  for (int r = r0; r < r1; ++r) {
-    run += 1 + a.ell_out[r];
-    a.cu_out[r + 1] = (int32_t)run;
+  if (rper == 1) {
+    if (r0 < r1) a.cu_out[r0 + 1] = (int32_t)(run + 1 + rk[0]);
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      run += 1 + a.ell_out[r];
+      a.cu_out[r + 1] = (int32_t)run;
+    }
   }
 }
 
 size_t schedule_workspace_bytes(int R, int K) {
-  return (((size_t)R * K * sizeof(uint64_t)) + 255) & ~(size_t)255;
+  const size_t n = (size_t)R * K;
+  return sched_align(n * 8) + sched_align(n * 4) + 256;
 }
 
 // An empty batch (R = 0): no candidates, B = tau = 0, so the layout is
@@ -346,27 +419,28 @@ int run_schedule(int R, int K, const float* c, const double* sps, int mode, int 
   if (R == 0)
     return launch_kernel("schedule", schedule_empty_kernel, dim3(1), dim3(64), stream, sps, cu_out, n_out, theta_out);
   ScheduleArgs a{R, K, c, sps, mode, capacity, a_out, ell_out, cu_out, n_out, theta_out, capacity_dev};
-  uint64_t* sorted = reinterpret_cast<uint64_t*>(workspace);
   const int n = R * K;
+  const ScheduleWork w = schedule_work(workspace, n);
   int rc = launch_kernel("schedule_rank", schedule_rank_kernel, dim3((n + kRankKeysPerWG - 1) / kRankKeysPerWG),
-                         dim3(kSchedThreads), stream, a, sorted);
+                         dim3(kSchedThreads), stream, a, w);
   if (rc) return rc;
-  const uint64_t* cs = sorted;
-  if (n <= kSchedThreads) return launch_kernel("schedule", schedule_kernel<1>, dim3(1), dim3(kSchedThreads), stream, a, cs);
-  if (n <= 2 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<2>, dim3(1), dim3(kSchedThreads), stream, a, cs);
-  if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a, cs);
-  if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a, cs);
-  return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a, cs);
+  if (n <= kSchedThreads) return launch_kernel("schedule", schedule_kernel<1>, dim3(1), dim3(kSchedThreads), stream, a, w);
+  if (n <= 2 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<2>, dim3(1), dim3(kSchedThreads), stream, a, w);
+  if (n <= 4 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<4>, dim3(1), dim3(kSchedThreads), stream, a, w);
+  if (n <= 8 * kSchedThreads) return launch_kernel("schedule", schedule_kernel<8>, dim3(1), dim3(kSchedThreads), stream, a, w);
+  return launch_kernel("schedule", schedule_kernel<16>, dim3(1), dim3(kSchedThreads), stream, a, w);
 }
 
 // ---- the schedule without a caller workspace --------------------------------
-// The sorted candidate keys live in this library-owned device array instead
-// of a workspace: every GPU the library runs on holds its own copy (128 KB)
-// until the process ends, and every call on that GPU shares it.  In host
-// code the name is a host-side stand-in, not a device address: kernels get
-// the address hipGetSymbolAddress returns for the current device.
+// The schedule's workspace (sorted candidate keys, candidate ranks, two
+// counters) lives in this library-owned device array instead: every GPU the
+// library runs on holds its own copy (about 193 KB) until the process ends,
+// and every call on that GPU shares it.  In host code the name is a host-side
+// stand-in, not a device address: kernels get the address hipGetSymbolAddress
+// returns for the current device.
 constexpr int kScratchKeys = kSchedMaxKeys;
-static __device__ __align__(256) uint64_t scratch[kScratchKeys];
+constexpr size_t kScratchWords = (kScratchKeys * 8 + kScratchKeys * 4 + 256) / 8;  // schedule_workspace_bytes at the cap
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
 
 constexpr int kScratchMaxDevices = 64;
 static std::mutex g_scratch_lock;
@@ -388,13 +462,14 @@ static void* scratch_address() {
 
 int schedule_scratch_keys() { return kScratchKeys; }
 
-// dspark_schedule's launches with the sorted keys in the scratch array (no
-// allocation, no workspace).  Returns -1 when R * K exceeds the array or its
-// address cannot be had.  Nothing in the array needs to start at zero: the
-// rank kernel writes every key the admission kernel reads.
+// dspark_schedule's launches with their workspace in the scratch array (no
+// allocation, no workspace argument).  Returns -1 when R * K exceeds the
+// array or its address cannot be had.  Nothing in the array needs to start at
+// zero: the rank kernel writes every key, rank and counter the admission
+// kernel reads.
 int run_schedule_noalloc(int R, int K, const float* c, const double* sps, int mode, int capacity, float* a_out,
                          int32_t* ell_out, int32_t* cu_out, int32_t* n_out, double* theta_out, hipStream_t stream) {
-  if ((int64_t)R * K > kScratchKeys) return -1;
+  if ((int64_t)R * K > kScratchKeys || schedule_workspace_bytes(R, K) > sizeof(scratch)) return -1;
   if (R == 0) return run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_out, n_out, theta_out,
                                   nullptr, stream);
   void* ptr = scratch_address();

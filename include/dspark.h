@@ -168,7 +168,8 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature,
  * Data errors: any c outside [0, 1] or NaN gives ell = 0, cu_seqlens[r] = r,
  * n_admitted = -1, theta = NaN (a valid no-draft layout).
  * Workspace: dspark_schedule_workspace_bytes(R, K) bytes (the sorted
- * candidate keys), caller-owned, contents need not be initialised.
+ * candidate keys, each candidate's rank and two counters), caller-owned,
+ * contents need not be initialised.
  * Two launches: candidate ranks across many workgroups, then one workgroup
  * for the admission scan and the layout.
  * ------------------------------------------------------------------------ */
@@ -186,14 +187,15 @@ int dspark_schedule(int R, int K, const float* c,
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, outputs, limits, data
  * errors and results as dspark_schedule, minus the workspace: the sorted
- * candidate keys go to a library-owned device array of
- * DSPARK_NOALLOC_MAX_CANDIDATES 64-bit keys (128 KB on each GPU the library
- * runs on, held until the process ends).  The call allocates nothing and
+ * candidate keys, the candidates' ranks and two counters go to a
+ * library-owned device array sized for DSPARK_NOALLOC_MAX_CANDIDATES
+ * candidates (192.25 KB on each GPU the library runs on, held until the
+ * process ends).  The call allocates nothing and
  * calls no allocating routine; R * K above DSPARK_NOALLOC_MAX_CANDIDATES
  * returns DSPARK_E_SHAPE.  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (other streams, other host threads) race on
  * it and must be ordered by the caller.  Nothing in the array needs to start
- * at zero (each call writes every key it reads).
+ * at zero (each call writes every key, rank and counter it reads).
  * ------------------------------------------------------------------------ */
 #define DSPARK_NOALLOC_MAX_CANDIDATES 16384
 int dspark_schedule_noalloc(int R, int K, const float* c,
