@@ -229,7 +229,7 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)dspark::w2_f16_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)B * K * d * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
-  if ((uint64_t)3 * r * (2 * r + d) * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if ((uint64_t)3 * r * ((uint64_t)2 * r + (uint64_t)d) * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !H || !W || !W1 || !W2 || !x0 || !x_out || !q_tok_out || !lse_out || !o_out) return DSPARK_E_NULL;
@@ -274,7 +274,7 @@ int dspark_schedule(int R, int K, const float* c, const double* sps, int sps_len
   if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
   if (!sps || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
   if (R > 0 && (!c || !a_out || !ell_out)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
+  if (R > 0 && (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K))) return DSPARK_E_WORKSPACE;
   return hip_status(dspark::run_schedule(R, K, c, sps, mode, capacity, nullptr, a_out, ell_out, cu_seqlens_out,
                                          n_admitted_out, theta_out, workspace,
                                          reinterpret_cast<hipStream_t>(stream)));
@@ -302,7 +302,7 @@ int dspark_schedule_async(int R, int K, const float* c, const double* sps, int s
   if ((int64_t)sps_len <= (int64_t)R * (K + 1)) return DSPARK_E_RANGE;
   if (!sps || !cu_seqlens_out || !n_admitted_out || !theta_out) return DSPARK_E_NULL;
   if (R > 0 && (!c || !capacity || !a_out || !ell_out)) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K)) return DSPARK_E_WORKSPACE;
+  if (R > 0 && (!workspace || workspace_bytes < dspark::schedule_workspace_bytes(R, K))) return DSPARK_E_WORKSPACE;
   return hip_status(dspark::run_schedule(R, K, c, sps, DSPARK_SCHED_TOPK, 0, capacity, a_out, ell_out,
                                          cu_seqlens_out, n_admitted_out, theta_out, workspace,
                                          reinterpret_cast<hipStream_t>(stream)));

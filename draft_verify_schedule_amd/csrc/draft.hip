@@ -745,13 +745,13 @@ __global__ __launch_bounds__(256) void w2_swizzle_kernel(const uint16_t* __restr
 size_t w2_swizzle_bytes(int V, int r) {
   if (r <= 0) return 0;
   const size_t kc = (size_t)(r + 31) / 32;
-  return (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 1024;
+  return (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols) * 4 * kc * 1024;
 }
 
 // W2 (column-major) into fragment order for kc chunks of 32 (zeros past r)
 // at out, ceil(V / 64) * 4 * kc KB; f16: as fp16 values.
 int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream) {
-  const size_t n = (size_t)((V + kWaveCols - 1) / kWaveCols) * 4 * kc * 64;
+  const size_t n = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols) * 4 * kc * 64;
   const dim3 grid((unsigned)std::max<size_t>(std::min<size_t>((n + 255) / 256, 8192), 1));
   u32x4* o = reinterpret_cast<u32x4*>(out);
   return f16 ? launch_kernel("w2_to_f16", w2_swizzle_kernel<true>, grid, dim3(256), stream, W2, o, V, r, kc, n)
@@ -856,7 +856,7 @@ int run_markov_lse(int R, int K, int V, int r, float temperature, const void* D,
 
 size_t draft_workspace_bytes(int B, int K, int V) {
   (void)K;
-  const size_t ns = (size_t)(V + kWaveCols - 1) / kWaveCols;
+  const size_t ns = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols);
   return ((size_t)B * ns * sizeof(float2) + 255) / 256 * 256;
 }
 

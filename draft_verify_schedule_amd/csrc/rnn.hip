@@ -235,7 +235,7 @@ int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16
 constexpr int kRnnChunks = 8;
 size_t w2_f16_bytes(int V, int r) {
   (void)r;
-  return (size_t)((V + 63) / 64) * 4 * kRnnChunks * 1024;
+  return (size_t)(((int64_t)V + 63) / 64) * 4 * kRnnChunks * 1024;
 }
 
 size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h) {

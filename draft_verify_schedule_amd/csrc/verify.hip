@@ -1189,8 +1189,8 @@ int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16
 // margins: the per-row decision margins and the greedy runner-ups.
 static VerifyLayout verify_layout(int R, int K, int V, int N, int r, bool lse_pass, bool make_w2s, bool margins) {
   VerifyLayout l{};
-  const size_t nsP = (V + kRowSlice - 1) / kRowSlice;
-  const size_t ns64 = (V + kWaveCols - 1) / kWaveCols;
+  const size_t nsP = (size_t)(((int64_t)V + kRowSlice - 1) / kRowSlice);
+  const size_t ns64 = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols);
   size_t off = 0;
   auto take = [&](size_t& at, size_t bytes) {
     at = off;
@@ -1482,7 +1482,7 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
 // r > 0 (Markov head): plus W2 in fragment order for the residual pass
 size_t label_workspace_bytes(int B, int K, int V, int r) {
   const size_t N = (size_t)B * K;
-  const size_t nsP = (V + kRowSlice - 1) / kRowSlice, ns64 = (V + kWaveCols - 1) / kWaveCols;
+  const size_t nsP = (size_t)(((int64_t)V + kRowSlice - 1) / kRowSlice), ns64 = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols);
   return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(N * ns64 * sizeof(float)) +
          w2_swizzle_bytes(V, r);
 }
