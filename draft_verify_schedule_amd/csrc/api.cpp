@@ -60,13 +60,13 @@ struct KernelTotal {
   int64_t launches = 0;
   double ms = 0.0;
 };
-// The timer may be driven from several host threads: the open bracket is
-// per thread, the totals and the pending events are under one lock.
+// The timer may be driven from several host threads: the kernel's index is
+// looked up, and the finished event pairs are queued, under one lock.
 std::atomic<bool> g_prof{false};
 std::mutex g_lock;
 std::deque<KernelTotal> g_totals;  // a deque keeps each name's storage in place as it grows
 std::vector<Pending> g_pending;
-thread_local Pending g_open{-1, nullptr, nullptr};
+thread_local int g_open_kernel = -1;
 
 int kernel_index(const char* name) {
   for (size_t i = 0; i < g_totals.size(); ++i)
@@ -91,26 +91,33 @@ void drain_pending() {
 
 bool profiler_on() { return g_prof.load(std::memory_order_relaxed); }
 
-void profiler_begin(const char* name, hipStream_t stream) {
+bool profiler_begin(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   {
     std::lock_guard<std::mutex> hold(g_lock);
-    g_open.kernel = kernel_index(name);
+    g_open_kernel = kernel_index(name);
   }
-  if (hipEventCreate(&g_open.start) != hipSuccess || hipEventCreate(&g_open.stop) != hipSuccess) {
-    g_open.kernel = -1;
-    return;
+  *start = *stop = nullptr;
+  if (hipEventCreate(start) != hipSuccess) {
+    *start = nullptr;
+    g_open_kernel = -1;
+    return false;
   }
-  (void)hipEventRecord(g_open.start, stream);
+  if (hipEventCreate(stop) != hipSuccess) {
+    (void)hipEventDestroy(*start);
+    *start = *stop = nullptr;
+    g_open_kernel = -1;
+    return false;
+  }
+  return true;
 }
 
-void profiler_end(hipStream_t stream) {
-  if (g_open.kernel < 0) return;
-  (void)hipEventRecord(g_open.stop, stream);
+void profiler_end(hipEvent_t start, hipEvent_t stop) {
+  if (g_open_kernel < 0) return;
   {
     std::lock_guard<std::mutex> hold(g_lock);
-    g_pending.push_back(g_open);
+    g_pending.push_back(Pending{g_open_kernel, start, stop});
   }
-  g_open.kernel = -1;
+  g_open_kernel = -1;
 }
 }  // namespace dspark
 

@@ -21,7 +21,6 @@ extern "C" hipError_t hipEventCreate(hipEvent_t* e) {
   return hipSuccess;
 }
 extern "C" hipError_t hipEventDestroy(hipEvent_t) { return hipSuccess; }
-extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 extern "C" hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 extern "C" hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
   *ms = 0.25f;
@@ -30,13 +29,14 @@ extern "C" hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
 
 namespace dspark {
 bool profiler_on();
-void profiler_begin(const char* name, hipStream_t stream);
-void profiler_end(hipStream_t stream);
+bool profiler_begin(const char* name, hipEvent_t* start, hipEvent_t* stop);
+void profiler_end(hipEvent_t start, hipEvent_t stop);
 
-static int launch(const char* name, hipStream_t s) {
-  if (profiler_on()) profiler_begin(name, s);
+static int launch(const char* name, hipStream_t) {
+  hipEvent_t a = nullptr, b = nullptr;
+  const bool prof = profiler_on() && profiler_begin(name, &a, &b);
   g_launches.fetch_add(1);
-  if (profiler_on()) profiler_end(s);
+  if (prof) profiler_end(a, b);
   return 0;
 }
 static size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
