@@ -35,7 +35,7 @@ size_t label_workspace_bytes(int B, int K, int V, int r);
 int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h_bf16, const float* w_h,
                         const float* w_e, float bias, const void* W1, const int32_t* x0, const int32_t* x,
                         const float* T, float* c_out, float* logit_out, hipStream_t stream);
-size_t sts_workspace_bytes(int G);
+size_t sts_workspace_bytes(int N, int G);
 int run_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int G, const float* grid, int nbins,
                 float* T_out, float* ece_out, void* workspace, hipStream_t stream);
 int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16, const void* D, bool d_bf16,
@@ -465,18 +465,18 @@ int dspark_confidence_head(int B, int K, int V, int d, int r, const void* H, int
 }
 
 size_t dspark_sts_fit_workspace_bytes(int N, int K, int n_grid) {
-  if (N <= 0 || K <= 0 || n_grid <= 0) return 0;
-  return dspark::sts_workspace_bytes(n_grid);
+  if (N <= 0 || K <= 0 || n_grid <= 0 || n_grid > DSPARK_STS_MAX_GRID) return 0;
+  return dspark::sts_workspace_bytes(N, n_grid);
 }
 
 int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int n_grid, const float* grid,
                    int n_bins, float* T_out, float* ece_out, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (N <= 0 || K <= 0 || K > DSPARK_MAX_K || n_grid <= 0) return DSPARK_E_SHAPE;
+  if (N <= 0 || K <= 0 || K > DSPARK_MAX_K || n_grid <= 0 || n_grid > DSPARK_STS_MAX_GRID) return DSPARK_E_SHAPE;
   if ((uint64_t)N * K * sizeof(float) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (n_bins < 1 || n_bins > DSPARK_STS_MAX_BINS) return DSPARK_E_RANGE;
   if (!logits || !survived || !grid || !T_out) return DSPARK_E_NULL;
-  if (!workspace || workspace_bytes < dspark::sts_workspace_bytes(n_grid)) return DSPARK_E_WORKSPACE;
+  if (!workspace || workspace_bytes < dspark::sts_workspace_bytes(N, n_grid)) return DSPARK_E_WORKSPACE;
   return hip_status(dspark::run_sts_fit(N, K, logits, survived, n_grid, grid, n_bins, T_out, ece_out, workspace,
                                         reinterpret_cast<hipStream_t>(stream)));
 }

@@ -8,14 +8,17 @@
 // lanes take strided elements of both dot products (fp32), the wave sum is a
 // fixed xor tree.
 //
-// sts_ece: one workgroup per grid temperature T_g, at position k (the
-// temperatures of positions < k already fixed in T_out): for every held-out
-// sample n, pred = prod_{i<k} sigmoid(l_{n,i} / T_i) * sigmoid(l_{n,k} / T_g)
-// (fp64, left to right), bin = floor(pred * n_bins) (last bin closed); each
-// thread keeps its own bin counts, label counts and prediction sums in LDS
-// (bin-major, no atomics), reduced in thread order, so the ECE
-// sum_b |labels_b - sum pred_b| / N is deterministic.
-// sts_pick: the first grid value with the smallest ECE becomes T_k.
+// sts_advance / sts_ece / sts_pick, for each position k in order (the
+// temperatures of positions < k already fixed in T_out): sts_advance writes
+// one 16-byte record per held-out sample (prefix = prod_{i<k} sigmoid(l_{n,i}
+// / T_i) in fp64, left to right, advanced by one factor per position; this
+// position's logit and label); sts_ece, one workgroup per (chunk of samples,
+// 4 grid temperatures): pred = prefix * sigmoid(l_{n,k} / T_g), bin =
+// floor(pred * n_bins) (last bin closed), per-thread bin slots in LDS (no
+// atomics) added by a fixed pairwise tree into one partial per (T_g, chunk,
+// bin); sts_pick merges the partials in chunk order, ECE_g = sum_b |labels_b
+// - sum pred_b| / N, and the first grid value with the smallest ECE becomes
+// T_k.  Every sum runs in a fixed order, so the result is deterministic.
 #include <math.h>
 
 #include "common.hpp"
@@ -107,80 +110,226 @@ int run_confidence_head(int B, int K, int d, int r, int V, const void* H, bool h
 // ------------------------------------------------------------------- STS --
 constexpr int kStsThreads = 256;
 constexpr int kStsMaxBins = 32;
+constexpr int kStsPerThread = 16;                          // samples per thread of an ECE workgroup
+constexpr int kStsChunk = kStsPerThread * kStsThreads;     // samples per ECE workgroup
+constexpr int kStsTemps = 4;                               // grid temperatures per ECE workgroup
+
+// One held-out sample at the current position: the cumulative product of
+// the earlier positions' calibrated sigmoids, this position's logit and label.
+struct alignas(16) StsRec {
+  double prefix;
+  float logit;
+  int32_t label;
+};
 
 struct StsArgs {
-  int N, K, G, nbins, k;
+  int N, K, G, nbins, k, nchunks;
   const float* logits;     // [N, K]
   const uint8_t* survived; // [N, K]
   const float* grid;       // [G]
   float* T_out;            // [K]
   float* ece_out;          // [K] or null
-  double* ece_grid;        // [G] workspace
+  StsRec* rec;             // [N]
+  double* psum;            // [G, nchunks, kStsMaxBins]: prediction sums per chunk and bin
+  int32_t* pcnt;           // [G, nchunks, kStsMaxBins]: samples | labels << 16 per chunk and bin
 };
 
-__device__ __forceinline__ double sigmoid_d(double z) { return 1.0 / (1.0 + exp(-z)); }
+// sigmoid in fp64 without forming exp of a large positive argument:
+// e = exp(-|z|); 1 / (1 + e) for z >= 0, e / (1 + e) below (branch-free, so
+// a wave with logits of both signs evaluates one exp and one division)
+__device__ __forceinline__ double sigmoid_d(double z) {
+  const double e = exp(-fabs(z));
+  return (z >= 0.0 ? 1.0 : e) / (1.0 + e);
+}
 
+// The records of position k: at k = 0 the product is 1; after T_{k-1} is
+// fixed, prefix <- prefix * sigmoid(l_{n,k-1} / T_{k-1}) (left to right, as
+// the cumulative product is defined), then this position's logit and label.
+__global__ __launch_bounds__(kStsThreads) void sts_advance_kernel(StsArgs a) {
+  const int n = blockIdx.x * kStsThreads + threadIdx.x;
+  if (n >= a.N) return;
+  double pre = 1.0;
+  if (a.k > 0) {
+    const StsRec r = a.rec[n];
+    pre = r.prefix * sigmoid_d((double)r.logit / (double)a.T_out[a.k - 1]);
+  }
+  StsRec out;
+  out.prefix = pre;
+  out.logit = a.logits[(size_t)n * a.K + a.k];
+  out.label = a.survived[(size_t)n * a.K + a.k] ? 1 : 0;
+  a.rec[n] = out;
+}
+
+// One workgroup per (chunk of kStsChunk samples, kStsTemps grid temperatures)
+// at position k.  Each thread loads its kStsPerThread records once; for each
+// temperature T_g: pred = prefix * sigmoid(l / T_g), bin = floor(pred *
+// n_bins) clamped to the last bin, accumulated in the thread's own LDS slots
+// (prediction sums in fp64, sample and label counts packed in one int: at
+// most 16 samples per thread), so no atomics; a fixed pairwise tree over the
+// threads then gives the chunk's partial per bin.  A sample with no
+// prediction (NaN) is in no bin.
+template <int NB>
 __global__ __launch_bounds__(kStsThreads) void sts_ece_kernel(StsArgs a) {
-  __shared__ double sp[kStsMaxBins * kStsThreads];
-  __shared__ int cnt[kStsMaxBins * kStsThreads];
-  __shared__ int lab[kStsMaxBins * kStsThreads];
+  __shared__ double sp[NB * kStsThreads];
+  __shared__ int32_t sc[NB * kStsThreads];
   const int t = threadIdx.x;
-  const int g = blockIdx.x;
-  for (int b = 0; b < a.nbins; ++b) {
-    sp[b * kStsThreads + t] = 0.0;
-    cnt[b * kStsThreads + t] = 0;
-    lab[b * kStsThreads + t] = 0;
-  }
-  const double tg = (double)a.grid[g];
-  for (int n = t; n < a.N; n += kStsThreads) {
-    const float* l = a.logits + (size_t)n * a.K;
-    double pred = 1.0;
-    for (int i = 0; i < a.k; ++i) pred *= sigmoid_d((double)l[i] / (double)a.T_out[i]);
-    pred *= sigmoid_d((double)l[a.k] / tg);
-    int b = (int)(pred * a.nbins);
-    b = b < 0 ? 0 : (b >= a.nbins ? a.nbins - 1 : b);
-    sp[b * kStsThreads + t] += pred;
-    cnt[b * kStsThreads + t] += 1;
-    lab[b * kStsThreads + t] += a.survived[(size_t)n * a.K + a.k] ? 1 : 0;
-  }
-  __syncthreads();
-  if (t < a.nbins) {  // thread b reduces bin b in thread order
-    double s = 0.0;
-    long long c = 0, y = 0;
-    for (int u = 0; u < kStsThreads; ++u) {
-      s += sp[t * kStsThreads + u];
-      c += cnt[t * kStsThreads + u];
-      y += lab[t * kStsThreads + u];
+  const int c = blockIdx.x;
+  const int n0 = c * kStsChunk + t;
+  StsRec r[kStsPerThread];
+#pragma unroll
+  for (int i = 0; i < kStsPerThread; ++i) {
+    const int n = n0 + i * kStsThreads;
+    if (n < a.N) {
+      r[i] = a.rec[n];
+    } else {
+      r[i].prefix = NAN;  // past the end: no prediction
+      r[i].logit = 0.f;
+      r[i].label = 0;
     }
-    sp[t * kStsThreads] = c ? fabs((double)y - s) : 0.0;
+  }
+  for (int tg = 0; tg < kStsTemps; ++tg) {
+    const int g = blockIdx.y * kStsTemps + tg;
+    if (g >= a.G) break;  // uniform over the workgroup
+    if (tg > 0) __syncthreads();  // the previous temperature's partials are read
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      sp[b * kStsThreads + t] = 0.0;
+      sc[b * kStsThreads + t] = 0;
+    }
+    const double T = (double)a.grid[g];
+#pragma unroll
+    for (int i = 0; i < kStsPerThread; ++i) {
+      const double pred = r[i].prefix * sigmoid_d((double)r[i].logit / T);
+      const bool has = !isnan(pred);  // branch-free: a NaN adds zero to bin 0
+      int b = has ? (int)(pred * a.nbins) : 0;
+      b = b < 0 ? 0 : (b >= a.nbins ? a.nbins - 1 : b);
+      sp[b * kStsThreads + t] += has ? pred : 0.0;
+      sc[b * kStsThreads + t] += has ? 1 + (r[i].label << 16) : 0;
+    }
+    // at most kStsChunk samples per chunk: the packed halves never carry
+    for (int h = kStsThreads / 2; h > 0; h >>= 1) {
+      __syncthreads();
+      if (t < h) {
+        for (int b = 0; b < a.nbins; ++b) {
+          sp[b * kStsThreads + t] += sp[b * kStsThreads + t + h];
+          sc[b * kStsThreads + t] += sc[b * kStsThreads + t + h];
+        }
+      }
+    }
+    __syncthreads();
+    if (t < a.nbins) {
+      const size_t o = ((size_t)g * a.nchunks + c) * kStsMaxBins + t;
+      a.psum[o] = sp[t * kStsThreads];
+      a.pcnt[o] = sc[t * kStsThreads];
+    }
+  }
+}
+
+// One workgroup, in blocks of grid values: thread p of a block merges pair
+// (T_g, bin b)'s chunk partials in chunk order into |labels - sum pred| (0 for
+// an empty bin), then thread g adds its bins in order: ECE_g = sum / N.  The
+// first grid value with the smallest ECE becomes T_k.
+constexpr int kStsPickThreads = 1024;
+constexpr int kStsPickTerms = 4096;
+
+// (e2, i2) before (e1, i1) in the argmin order: a missing entry (index < 0)
+// never wins, NaN comes first (as an argmin over values with NaN returns the
+// first NaN), then the smaller value, then the lower index
+__device__ __forceinline__ bool sts_before(double e2, int i2, double e1, int i1) {
+  if (i2 < 0) return false;
+  if (i1 < 0) return true;
+  const bool n1 = isnan(e1), n2 = isnan(e2);
+  if (n1 || n2) return n2 && (!n1 || i2 < i1);
+  return e2 < e1 || (e2 == e1 && i2 < i1);
+}
+
+__global__ __launch_bounds__(kStsPickThreads) void sts_pick_kernel(StsArgs a) {
+  __shared__ double term[kStsPickTerms];
+  __shared__ double se[kStsPickThreads];
+  __shared__ int si[kStsPickThreads];
+  const int t = threadIdx.x;
+  const int nb = a.nbins;
+  const int per_block = kStsPickTerms / nb;  // grid values per block
+  double best = INFINITY;
+  int bi = -1;
+  for (int g0 = 0; g0 < a.G; g0 += per_block) {
+    const int ng = min(per_block, a.G - g0);
+    for (int p = t; p < ng * nb; p += kStsPickThreads) {
+      const int g = g0 + p / nb, b = p - (p / nb) * nb;
+      const size_t o = (size_t)g * a.nchunks * kStsMaxBins + b;
+      double s = 0.0;
+      int64_t cnt = 0, lab = 0;
+#pragma unroll 8
+      for (int c = 0; c < a.nchunks; ++c) {
+        s += a.psum[o + (size_t)c * kStsMaxBins];
+        const int32_t cl = a.pcnt[o + (size_t)c * kStsMaxBins];
+        cnt += cl & 0xFFFF;
+        lab += (uint32_t)cl >> 16;
+      }
+      term[p] = cnt ? fabs((double)lab - s) : 0.0;
+    }
+    __syncthreads();
+    if (t < ng) {
+      double e = 0.0;
+      for (int b = 0; b < nb; ++b) e += term[t * nb + b];
+      e /= (double)a.N;
+      if (sts_before(e, g0 + t, best, bi)) {
+        best = e;
+        bi = g0 + t;
+      }
+    }
+    __syncthreads();
+  }
+  // argmin by a pairwise tree: the smaller ECE, the lower grid index on ties
+  se[t] = best;
+  si[t] = bi;
+  for (int h = kStsPickThreads / 2; h > 0; h >>= 1) {
+    __syncthreads();
+    if (t < h) {
+      const double e2 = se[t + h];
+      const int i2 = si[t + h];
+      if (sts_before(e2, i2, se[t], si[t])) {
+        se[t] = e2;
+        si[t] = i2;
+      }
+    }
   }
   __syncthreads();
   if (t == 0) {
-    double e = 0.0;
-    for (int b = 0; b < a.nbins; ++b) e += sp[b * kStsThreads];
-    a.ece_grid[g] = e / (double)a.N;
+    a.T_out[a.k] = a.grid[si[0]];
+    if (a.ece_out) a.ece_out[a.k] = (float)se[0];
   }
 }
 
-__global__ __launch_bounds__(64) void sts_pick_kernel(StsArgs a) {
-  if (threadIdx.x != 0) return;
-  int best = 0;
-  for (int g = 1; g < a.G; ++g)
-    if (a.ece_grid[g] < a.ece_grid[best]) best = g;  // the first minimum
-  a.T_out[a.k] = a.grid[best];
-  if (a.ece_out) a.ece_out[a.k] = (float)a.ece_grid[best];
-}
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+static int sts_chunks(int N) { return (N + kStsChunk - 1) / kStsChunk; }
 
-size_t sts_workspace_bytes(int G) { return ((size_t)G * sizeof(double) + 255) / 256 * 256; }
+size_t sts_workspace_bytes(int N, int G) {
+  const size_t parts = (size_t)G * sts_chunks(N) * kStsMaxBins;
+  return align256((size_t)N * sizeof(StsRec)) + align256(parts * sizeof(double)) +
+         align256(parts * sizeof(int32_t));
+}
 
 int run_sts_fit(int N, int K, const float* logits, const uint8_t* survived, int G, const float* grid, int nbins,
                 float* T_out, float* ece_out, void* workspace, hipStream_t stream) {
-  StsArgs a{N, K, G, nbins, 0, logits, survived, grid, T_out, ece_out, reinterpret_cast<double*>(workspace)};
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int nchunks = sts_chunks(N);
+  const size_t parts = (size_t)G * nchunks * kStsMaxBins;
+  const size_t rec_bytes = align256((size_t)N * sizeof(StsRec));
+  StsRec* rec = reinterpret_cast<StsRec*>(ws);
+  double* psum = reinterpret_cast<double*>(ws + rec_bytes);
+  int32_t* pcnt = reinterpret_cast<int32_t*>(ws + rec_bytes + align256(parts * sizeof(double)));
+  StsArgs a{N, K, G, nbins, 0, nchunks, logits, survived, grid, T_out, ece_out, rec, psum, pcnt};
+  const dim3 egrid(nchunks, (G + kStsTemps - 1) / kStsTemps);
   for (int k = 0; k < K; ++k) {
     a.k = k;
-    int rc = launch_kernel("sts_ece", sts_ece_kernel, dim3(G), dim3(kStsThreads), stream, a);
+    int rc = launch_kernel("sts_advance", sts_advance_kernel, dim3((N + kStsThreads - 1) / kStsThreads),
+                           dim3(kStsThreads), stream, a);
     if (rc) return rc;
-    rc = launch_kernel("sts_pick", sts_pick_kernel, dim3(1), dim3(64), stream, a);
+    rc = nbins <= 16 ? launch_kernel("sts_ece", sts_ece_kernel<16>, egrid, dim3(kStsThreads), stream, a)
+                     : launch_kernel("sts_ece", sts_ece_kernel<kStsMaxBins>, egrid, dim3(kStsThreads), stream, a);
+    if (rc) return rc;
+    rc = launch_kernel("sts_pick", sts_pick_kernel, dim3(1), dim3(kStsPickThreads), stream, a);
     if (rc) return rc;
   }
   return 0;

@@ -83,6 +83,7 @@ enum dspark_sched_mode {
 #define DSPARK_MAX_RANK 256          /* Markov rank r */
 #define DSPARK_MAX_CANDIDATES 16384  /* R * K for dspark_schedule */
 #define DSPARK_STS_MAX_BINS 32        /* ECE bins for dspark_sts_fit */
+#define DSPARK_STS_MAX_GRID 65535     /* grid temperatures for dspark_sts_fit */
 
 /* Human-readable text for a status code (static storage). */
 const char* dspark_status_string(int status);
@@ -447,14 +448,19 @@ int dspark_confidence_head(int B, int K, int V, int d, int r,
  * (1 where positions 1..k were all accepted), T_1..T_{k-1} already fixed.
  * ECE: n_bins equal-width bins on [0, 1] (last one closed), sum over bins of
  * |labels - predictions| / N; products and sums in fp64, reduced in a fixed
- * order (deterministic).
+ * order (deterministic).  A sample whose logit is NaN (dspark_confidence_head
+ * reports NaN for an invalid token) has no prediction from that position on:
+ * it falls in no bin but still counts in N.
  * Inputs (device): logits [N, K] f32 (logit_out of dspark_confidence_head on
  * held-out requests), survived [N, K] uint8, grid [n_grid] f32 (> 0).
  * Outputs (device): T_out [K] f32; ece_out [K] f32 (the ECE at the chosen
  * temperature) or NULL.
- * Limits: N >= 1, 1 <= K <= DSPARK_MAX_K, n_grid >= 1,
+ * Limits: N >= 1, 1 <= K <= DSPARK_MAX_K, 1 <= n_grid <= DSPARK_STS_MAX_GRID,
  * 1 <= n_bins <= DSPARK_STS_MAX_BINS.  Workspace:
- * dspark_sts_fit_workspace_bytes(N, K, n_grid) bytes.
+ * dspark_sts_fit_workspace_bytes(N, K, n_grid) bytes (a 16-byte record per
+ * sample holding its fp64 cumulative product, and per-bin partials of each
+ * grid temperature over chunks of 4096 samples; about
+ * 16 N + 12 * 32 * n_grid * ceil(N / 4096)).
  * ------------------------------------------------------------------------ */
 size_t dspark_sts_fit_workspace_bytes(int N, int K, int n_grid);
 int dspark_sts_fit(int N, int K, const float* logits, const uint8_t* survived,

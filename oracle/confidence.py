@@ -60,10 +60,14 @@ def confidence_head_ref(H, w_h, w_e, bias, W1, x0, x, temperatures=None):
 
 
 def ece_ref(pred, label, n_bins):
-    """Expected calibration error of predictions in [0, 1] against 0/1 labels."""
+    """Expected calibration error of predictions in [0, 1] against 0/1 labels.
+    A sample without a prediction (NaN, from a NaN logit) falls in no bin but
+    still counts in the sample total."""
     pred = np.asarray(pred, dtype=np.float64)
     label = np.asarray(label, dtype=np.float64)
-    b = np.minimum((pred * n_bins).astype(np.int64), n_bins - 1)
+    b = np.full(pred.shape, -1, dtype=np.int64)
+    ok = ~np.isnan(pred)
+    b[ok] = np.minimum((pred[ok] * n_bins).astype(np.int64), n_bins - 1)
     total = 0.0
     for i in range(n_bins):
         m = b == i

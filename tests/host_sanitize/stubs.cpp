@@ -65,7 +65,9 @@ size_t verify_workspace_bytes(int R, int K, int V, int r, int N) {
 size_t label_workspace_bytes(int B, int K, int V, int r) {
   return al((size_t)B * K * (size_t)(((int64_t)V + 255) / 256) * 16) + w2_swizzle_bytes(V, r);
 }
-size_t sts_workspace_bytes(int G) { return al((size_t)G * 64); }
+size_t sts_workspace_bytes(int N, int G) {
+  return al((size_t)N * 16) + 2 * al((size_t)G * (size_t)((N + 4095) / 4096) * 32 * 8);
+}
 size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h) {
   return al((size_t)B * K * 3 * r * 4) + 2 * al((size_t)B * r * 4) + (with_w2h ? w2_f16_bytes(V, r) : 0);
 }

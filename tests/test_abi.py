@@ -139,11 +139,14 @@ def test_confidence_and_sts_argument_errors(lib):
         return lib.dspark_sts_fit(N, K, lg, sv, G, grid, nb, T, NULL, ws, wsb, NULL)
     assert sts(N=0) == -2
     assert sts(G=0) == -2
+    assert sts(G=65536) == -2        # more grid temperatures than one launch dimension holds
+    assert lib.dspark_sts_fit_workspace_bytes(100, 7, 65536) == 0
     assert sts(nb=0) == -4
     assert sts(nb=33) == -4
     assert sts(lg=NULL) == -1
     assert sts(ws=NULL) == -5
-    assert lib.dspark_sts_fit_workspace_bytes(100, 7, 9) >= 9 * 8
+    # the samples' fp64 cumulative products and per-bin partials of every grid value
+    assert lib.dspark_sts_fit_workspace_bytes(100, 7, 9) >= 100 * 16 + 9 * 32 * 12
 
 
 def test_draft_argument_errors(lib):

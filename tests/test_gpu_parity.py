@@ -681,6 +681,28 @@ def test_sts_fit_matches_oracle(n_bins):
     np.testing.assert_allclose(ece.cpu().numpy(), er, rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("N,K,G,n_bins,nan", [(300, 4, 33, 7, False), (1, 2, 5, 3, False),
+                                               (9000, 7, 121, 15, False), (5000, 5, 61, 10, True)])
+def test_sts_fit_small_ragged_and_repeatable(N, K, G, n_bins, nan):
+    """Fewer samples than one chunk, a single sample, chunks with a ragged
+    last one, and held-out logits with NaN (invalid tokens: no prediction from
+    that position on): temperatures equal the oracle's, and a second call
+    gives the same bits (every sum runs in a fixed order)."""
+    logits, surv = _sts_data(5 + N, N, K, np.linspace(0.7, 2.0, K))
+    if nan:
+        rng = np.random.default_rng(N)
+        logits[rng.integers(0, N, 200), rng.integers(0, K, 200)] = np.nan
+    grid = np.exp(np.linspace(np.log(0.3), np.log(3.0), G)).astype(np.float32)
+    args = (torch.from_numpy(logits).to(DEV), torch.from_numpy(surv).to(DEV), torch.from_numpy(grid).to(DEV), n_bins)
+    T1, e1 = ds().dspark_sts_fit(*args)
+    T2, e2 = ds().dspark_sts_fit(*args)
+    torch.cuda.synchronize()
+    Tr, er = oracle.sts_fit_ref(logits, surv, grid.astype(np.float64), n_bins)
+    np.testing.assert_array_equal(T1.cpu().numpy(), Tr.astype(np.float32))
+    np.testing.assert_allclose(e1.cpu().numpy(), er, rtol=1e-5, atol=1e-7)
+    assert torch.equal(T1, T2) and torch.equal(e1.view(torch.int32), e2.view(torch.int32))
+
+
 
 # ------------------------------------------------------------- RNN head
 def _rnn_inputs(B, K, V, r, d, dtype, seed, scale=3.0, wscale=0.3):

@@ -61,6 +61,11 @@ def test_ece_hand_worked():
     assert ece_ref([1.0, 1.0, 0.0], [1, 1, 0], 4) == 0.0
     # a single bin: |mean label - mean prediction|
     assert ece_ref(pred, lab, 1) == pytest.approx(abs(lab.mean() - pred.mean()), abs=1e-15)
+    # a sample with no prediction (NaN) is in no bin but counts in the total:
+    # the hand-worked sums over 6 samples instead of 5
+    pn = np.append(pred, np.nan)
+    ln = np.append(lab, 1)
+    assert ece_ref(pn, ln, 2) == pytest.approx(expect * 5 / 6, abs=1e-15)
 
 
 def test_sts_recovers_generating_temperatures():
