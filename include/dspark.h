@@ -478,8 +478,10 @@ int dspark_uniforms(uint64_t seed, uint64_t step, int n, int position, int purpo
 
 /* ------------------------------------------------------------------------ *
  * Kernel timing (instrumentation, not part of the method).  While enabled,
- * every kernel the calls above launch is bracketed by a pair of HIP events
- * recorded on the caller's stream.  dspark_profiler_read waits for the
+ * every kernel the calls above launch carries a start and a stop HIP event
+ * that the dispatch itself records around the kernel's execution
+ * (hipExtLaunchKernel), so no extra packets enter the caller's stream and
+ * the times match a kernel trace.  dspark_profiler_read waits for the
  * recorded events and reports, per kernel name, the number of launches and the
  * summed event time.  Host-side state shared by every thread of the process
  * (calls from several threads are safe); a name returned by
