@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 namespace dspark {
@@ -165,11 +166,20 @@ __device__ __forceinline__ void row_pair32(int v, int& a, int& b) {
   a = (int)p[0];
   b = (int)p[1];
 }
+// max of two values that come from arithmetic or exchanges of such values
+// (never a signalling NaN), as one v_max_f32: fmaxf would first quiet each
+// exchanged operand with an extra instruction.  A quiet NaN operand yields the
+// other operand, as fmaxf does.
+__device__ __forceinline__ float max_arith(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float rows_max(float v) {
   float a, b;
   row_pair16(v, a, b);
-  row_pair32(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
+  row_pair32(max_arith(a, b), a, b);
+  return max_arith(a, b);
 }
 __device__ __forceinline__ float rows_sum(float v) {
   float a, b;

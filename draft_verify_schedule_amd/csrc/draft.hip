@@ -80,14 +80,16 @@ __device__ __forceinline__ float2 slice_values(const float (&z)[16], int cbase, 
 #pragma unroll
     for (int e = 1; e < 16; ++e) m = fmaxf(m, z[e]);
     m = rows_max(m);
-    // branch-free: a slice with no finite logit gets exp2(-inf) = 0 terms
-    const bool empty = m == -INFINITY;
-    const float mc = empty ? 0.f : m * c2;
+    const float mc = m * c2;
+    // branch-free: a slice with no finite logit (mc = -inf) subtracts
+    // -FLT_MAX instead, so its terms are exp2(-inf) = 0 and it reports
+    // (-inf, 0); any other slice subtracts its own scaled maximum
+    const float base = max_arith(mc, -FLT_MAX);
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -mc));
+    for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(z[e], c2, -base));
     s = rows_sum(s);
-    return make_float2(empty ? -INFINITY : mc, s);
+    return make_float2(mc, s);
   }
 }
 
