@@ -72,6 +72,10 @@ struct VerifyArgs {
   float* margin;            // [N]  decision margin of each flat row (else null)
   float* rmin;              // [R]  smallest accept margin of each request (T > 0)
   float* min_margin_out;    // [R]  or null
+  // acceptance label, streamed residual pass: per (job, item) fp64 sums of the
+  // residual masses a job (one wave of one workgroup) swept for that item
+  double* lpart;            // [njobs, N]
+  int njobs;
 };
 
 // Whether row q of a pass over the draft rows is judged by the layout
@@ -838,6 +842,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   GroupLogitsBuf<DT> db0, db1;
   const bool xpf = PF && ngroups % 2 == 0;
   bool first = true;
+  double lacc0 = 0.0, lacc1 = 0.0;  // LABEL: this wave's sums for rows lane, 64 + lane
   for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
     const int nxt = blk + 4;
     const bool has_next = nxt < blk_end;
@@ -890,9 +895,15 @@ void verify_residual_stream_kernel(VerifyArgs a) {
           s += fmaxf(p - q, 0.f);
         }
       s = rows_sum(s);
-      if (lv && lane < 16) {
-        const int item = row0 + 16 * g + lane;
-        a.rpart[(size_t)(LABEL ? item : a.rej_list[item]) * a.ns64 + blk] = s;
+      if constexpr (LABEL) {
+        // the label needs each item's total only: group g's row sums are kept
+        // by the lanes of quarter g % 4 (lane l ends with rows l and 64 + l of
+        // the stage), added in block order in fp64
+        const double ds = (lane >> 4) == (g & 3) ? (double)s : 0.0;
+        if (g < 4) lacc0 += ds;
+        else lacc1 += ds;
+      } else if (lv && lane < 16) {
+        a.rpart[(size_t)a.rej_list[row0 + 16 * g + lane] * a.ns64 + blk] = s;
       }
     };
     if constexpr (CX) {
@@ -928,6 +939,13 @@ void verify_residual_stream_kernel(VerifyArgs a) {
       }
     }
     first = false;
+  }
+  if constexpr (LABEL) {
+    // one partial per (job, item), jobs = (split, wave); written even when the
+    // wave had no block (zeros), so every partial the reduction reads is set
+    const size_t job = (size_t)split * 4 + wave;
+    if (lane < nrows) a.lpart[job * count + row0 + lane] = lacc0;
+    if (64 + lane < nrows) a.lpart[job * count + row0 + 64 + lane] = lacc1;
   }
 }
 
@@ -1295,6 +1313,21 @@ __global__ __launch_bounds__(256) void label_reduce_kernel(VerifyArgs a, float* 
   if (lane == 0) c_out[i] = ok ? (float)fmin(1.0, fmax(0.0, 1.0 - z)) : NAN;
 }
 
+// The label from the streamed residual pass: c = 1 - (sum over jobs, in job
+// order, of the item's fp64 partial sums), one thread per item.
+__global__ __launch_bounds__(256) void label_reduce_jobs_kernel(VerifyArgs a, float* __restrict__ c_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.N) return;
+  const int k = i % a.K;
+  const int prev = k == 0 ? a.x0[i / a.K] : a.x[i - 1];
+  const int xi = a.x[i];
+  const bool ok = prev >= 0 && prev < a.V && xi >= 0 && xi < a.V;
+  double z = 0.0;
+#pragma unroll 8
+  for (int j = 0; j < a.njobs; ++j) z += a.lpart[(size_t)j * a.N + i];
+  c_out[i] = ok ? (float)fmin(1.0, fmax(0.0, 1.0 - z)) : NAN;
+}
+
 template <typename PT, typename DT, bool VEC_P, bool VEC_D, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual(const VerifyArgs& a, hipStream_t stream) {
   return launch_kernel(LABEL ? "label_residual" : "verify_residual",
@@ -1320,11 +1353,21 @@ static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
   }
 }
 
+// Grid of the streamed residual pass over `rows` items: about two workgroups
+// per CU, and enough 8-slot rows for every stage.
+static int residual_stream_slots(int rows) { return std::max(64, (rows + kStageRows - 1) / kStageRows); }
+
+// Jobs (workgroup split x wave) of one stage in that grid, each writing one
+// partial per item of the acceptance label: the kernel's own split arithmetic.
+static int label_jobs(int N) {
+  const int active = (N + kStageRows - 1) / kStageRows;
+  return residual_stream_slots(N) / active * 8 * 4;
+}
+
 template <typename PT, typename DT, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
-  // about two workgroups per CU, and enough 8-slot rows for every stage
   const int rows = LABEL ? a.R * a.K : a.R;
-  const int slots = std::max(64, (rows + kStageRows - 1) / kStageRows);
+  const int slots = residual_stream_slots(rows);
   return launch_kernel(LABEL ? "label_residual" : "verify_residual",
                        verify_residual_stream_kernel<PT, DT, KC, LABEL, ROWS>, dim3(8 * slots), dim3(256), stream, a);
 }
@@ -1483,8 +1526,10 @@ int run_verify(int R, int K, int V, float temperature, const void* P, bool p_bf1
 size_t label_workspace_bytes(int B, int K, int V, int r) {
   const size_t N = (size_t)B * K;
   const size_t nsP = (size_t)(((int64_t)V + kRowSlice - 1) / kRowSlice), ns64 = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols);
-  return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(N * ns64 * sizeof(float)) +
-         w2_swizzle_bytes(V, r);
+  // the residual region holds per-slice masses (unaligned rows) or the
+  // streamed pass's per-(job, item) sums
+  const size_t resid = std::max(N * ns64 * sizeof(float), (size_t)label_jobs((int)N) * N * sizeof(double));
+  return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(resid) + w2_swizzle_bytes(V, r);
 }
 
 template <typename PT, typename DT>
@@ -1508,8 +1553,15 @@ static int run_label_typed(VerifyArgs& a, float* c_out, bool greedy, bool vec_p,
   if (rc) return rc;
   rc = launch_kernel("label_merge", label_merge_kernel<false>, per_row, b256, stream, a);
   if (rc) return rc;
-  if (vec_p && vec_d) rc = dispatch_residual_stream<PT, DT, true>(a, stream);
-  else if (vec_p) rc = dispatch_residual<PT, DT, true, false, true>(a, stream);
+  if (vec_p && vec_d) {
+    // per-(job, item) sums instead of per-slice masses, in the same region
+    a.lpart = reinterpret_cast<double*>(a.rpart);
+    a.njobs = label_jobs(a.N);
+    rc = dispatch_residual_stream<PT, DT, true>(a, stream);
+    if (rc) return rc;
+    return launch_kernel("label_reduce", label_reduce_jobs_kernel, dim3((a.N + 255) / 256), b256, stream, a, c_out);
+  }
+  if (vec_p) rc = dispatch_residual<PT, DT, true, false, true>(a, stream);
   else if (vec_d) rc = dispatch_residual<PT, DT, false, true, true>(a, stream);
   else rc = dispatch_residual<PT, DT, false, false, true>(a, stream);
   if (rc) return rc;
@@ -1550,7 +1602,7 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   a.rowms = reinterpret_cast<float2*>(ws + off);
   off += align256((size_t)N * sizeof(float2));
   a.rpart = reinterpret_cast<float*>(ws + off);
-  off += align256((size_t)N * a.ns64 * sizeof(float));
+  off += align256(std::max((size_t)N * a.ns64 * sizeof(float), (size_t)label_jobs(N) * N * sizeof(double)));
   const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
   const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
