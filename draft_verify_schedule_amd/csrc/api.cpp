@@ -219,10 +219,9 @@ int dspark_rnn_prepare_w2(int V, int r, const void* W2, void* W2h, size_t W2h_by
 }
 
 size_t dspark_rnn_draft_workspace_bytes(int B, int K, int V, int r, int d) {
-  (void)d;
-  if (B <= 0 || K <= 0 || V <= 0 || r <= 0) return 0;
+  if (B <= 0 || K <= 0 || V <= 0 || r <= 0 || d < 64) return 0;
   const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
-  return base + dspark::rnn_workspace_bytes(B, K, V, r);
+  return base + dspark::rnn_workspace_bytes(B, K, V, r, d);
 }
 
 int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const void* U, int u_dtype,
@@ -241,7 +240,7 @@ int dspark_rnn_draft(int B, int K, int V, int r, int d, float temperature, const
   if (B == 0) return DSPARK_OK;  // empty batch
   if (!U || !H || !W || !W1 || !W2 || !x0 || !x_out || !q_tok_out || !lse_out || !o_out) return DSPARK_E_NULL;
   const size_t base = (dspark::draft_workspace_bytes(B, K, V) + 255) / 256 * 256;
-  const size_t need = base + dspark::rnn_workspace_bytes(B, K, V, r, W2h == nullptr);
+  const size_t need = base + dspark::rnn_workspace_bytes(B, K, V, r, d, W2h == nullptr);
   if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (!aligned16(W1) || !aligned16(W2) || !aligned16(H) || !aligned16(W) || !aligned16(o_out) || !aligned16(W2h))

@@ -29,16 +29,23 @@ namespace dspark {
 
 // ---------------------------------------------------------------- hproj --
 // 128 x 128 output tile per workgroup (n: projection rows, m: (request,
-// position) rows).  4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA blocks with
-// A = W rows (n) and B = h rows (m): lane l ends with 4 consecutive n of one
-// m, stored as one 16-byte vector.  The contraction runs in stages of 64
-// columns through double-buffered LDS; rows past M or N read as zero through
-// the buffer resources' range check.
+// position) rows) and one slice of the contraction (blockIdx.y of hp_split:
+// the 32-column stages are dealt in contiguous ranges), so that the
+// full-size GEMM (168 tiles) gives every CU about three workgroups (40 KB of
+// LDS each): the kernel is bound by the latency of each stage's loads, which
+// the other workgroups of the CU hide.
+// 4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA blocks with A = W rows (n) and
+// B = h rows (m): lane l ends with 4 consecutive n of one m, stored as one
+// 16-byte vector into the slice's partial.  The stages run through
+// double-buffered LDS; rows past M or N read as zero through the buffer
+// resources' range check.
 constexpr int kHpTile = 128;
-constexpr int kHpK = 64;
-constexpr int kHpPitch = kHpK + 8;  // bf16 per LDS row: 144 bytes
+constexpr int kHpK = 32;
+constexpr int kHpPitch = kHpK + 8;  // bf16 per LDS row: 80 bytes
+constexpr int kHpChunks = kHpTile * kHpK / 8 / 256;  // 16-byte chunks per thread and operand
 
-__global__ __launch_bounds__(256) void rnn_hproj_kernel(RnnParams p, int mtiles, int ntiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void rnn_hproj_kernel(RnnParams p, int mtiles,
+                                                                                            int ntiles) {
   int mt, nt;
   if (!xcd_tile(blockIdx.x, mtiles, ntiles, mt, nt)) return;
   __shared__ uint16_t hs[2][kHpTile][kHpPitch];
@@ -48,35 +55,39 @@ __global__ __launch_bounds__(256) void rnn_hproj_kernel(RnnParams p, int mtiles,
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int wn = wave >> 1, wm = wave & 1;
   const int m0 = mt * kHpTile, n0 = nt * kHpTile;
+  const int nk_all = p.d / kHpK;
+  const int kt0 = (int)((int64_t)blockIdx.y * nk_all / p.hp_split);
+  const int kt1 = (int)((int64_t)(blockIdx.y + 1) * nk_all / p.hp_split);
+  float* const out = p.Hp + (size_t)blockIdx.y * M * N;
   const uint32_t hbytes = (uint32_t)((uint64_t)M * d * 2);
   const uint32_t wbytes = (uint32_t)((uint64_t)N * ldw * 2);
   const rsrc_t hr = make_rsrc(p.H, hbytes);
   const rsrc_t wr = make_rsrc(p.W, wbytes);
-  // global -> LDS: four 16-byte chunks per thread and operand; chunk id / 8 is
-  // the tile row, id % 8 the 8-column group
-  uint32_t hoff[4], woff[4];
-  int lrow[4], lcol[4];
+  // global -> LDS: kHpChunks 16-byte chunks per thread and operand; chunk
+  // id / (kHpK / 8) is the tile row, id % (kHpK / 8) the 8-column group
+  uint32_t hoff[kHpChunks], woff[kHpChunks];
+  int lrow[kHpChunks], lcol[kHpChunks];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kHpChunks; ++q) {
     const int id = tid + 256 * q;
-    lrow[q] = id >> 3;
-    lcol[q] = (id & 7) * 8;
+    lrow[q] = id / (kHpK / 8);
+    lcol[q] = (id % (kHpK / 8)) * 8;
     const int m = m0 + lrow[q], n = n0 + lrow[q];
     hoff[q] = m < M ? (uint32_t)(((uint64_t)m * d + lcol[q]) * 2) : hbytes;
     woff[q] = n < N ? (uint32_t)(((uint64_t)n * ldw + 2 * p.r + lcol[q]) * 2) : wbytes;
   }
-  u32x4 hv[4], wv[4];
+  u32x4 hv[kHpChunks], wv[kHpChunks];
   auto gload = [&](int kt) {
     const uint32_t so = (uint32_t)kt * (kHpK * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kHpChunks; ++q) {
       hv[q] = buffer_load16(hr, hoff[q], so);
       wv[q] = buffer_load16(wr, woff[q], so);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kHpChunks; ++q) {
       *reinterpret_cast<u32x4*>(&hs[buf][lrow[q]][lcol[q]]) = hv[q];
       *reinterpret_cast<u32x4*>(&ws[buf][lrow[q]][lcol[q]]) = wv[q];
     }
@@ -86,14 +97,14 @@ __global__ __launch_bounds__(256) void rnn_hproj_kernel(RnnParams p, int mtiles,
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nk = d / kHpK;
-  gload(0);
+  const int nk = kt1 - kt0;  // at least one stage: hp_split <= d / 64
+  gload(kt0);
   lstore(0);
   __syncthreads();
   const int fr = lane & 15, fk = 8 * (lane >> 4);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + 1 < nk) gload(kt0 + kt + 1);
 #pragma unroll
     for (int kc = 0; kc < kHpK / 32; ++kc) {
       bf16x8 af[4], bf[4];
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(256) void rnn_hproj_kernel(RnnParams p, int mtiles,
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = m0 + 64 * wm + 16 * mb + fr;
-      if (m < M && n < N) *reinterpret_cast<f32x4*>(p.Hp + (size_t)m * N + n) = acc[nb][mb];
+      if (m < M && n < N) *reinterpret_cast<f32x4*>(out + (size_t)m * N + n) = acc[nb][mb];
     }
   }
 }
@@ -203,10 +214,15 @@ __global__ __launch_bounds__(256) void rnn_step_kernel(RnnParams p, int k, const
     pre[comp] = ((red[0][comp][lane] + red[1][comp][lane]) + red[2][comp][lane]) + red[3][comp][lane];
   const int jj = j0 + 4 * (lane >> 4);
   const size_t row = (size_t)b * p.K + (k - 1);
-  const float* hp = p.Hp + row * (size_t)(3 * r);
-  const f32x4 hg = *reinterpret_cast<const f32x4*>(hp + jj);
-  const f32x4 hc = *reinterpret_cast<const f32x4*>(hp + r + jj);
-  const f32x4 ho = *reinterpret_cast<const f32x4*>(hp + 2 * r + jj);
+  // the hidden-state part: the projection's slice partials added in order
+  f32x4 hg = f32x4{0.f, 0.f, 0.f, 0.f}, hc = hg, ho = hg;
+  const size_t slice = (size_t)p.B * p.K * 3 * r;
+  for (int q = 0; q < p.hp_split; ++q) {
+    const float* hp = p.Hp + q * slice + row * (size_t)(3 * r);
+    hg += *reinterpret_cast<const f32x4*>(hp + jj);
+    hc += *reinterpret_cast<const f32x4*>(hp + r + jj);
+    ho += *reinterpret_cast<const f32x4*>(hp + 2 * r + jj);
+  }
   f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
   if (s_prev) sp = *reinterpret_cast<const f32x4*>(s_prev + (size_t)b * r + jj);
   f32x4 sn, o;
@@ -238,15 +254,23 @@ size_t w2_f16_bytes(int V, int r) {
   return (size_t)(((int64_t)V + 63) / 64) * 4 * kRnnChunks * 1024;
 }
 
-size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h) {
-  return align256_rnn((size_t)B * K * 3 * r * sizeof(float)) + 2 * align256_rnn((size_t)B * r * sizeof(float)) +
-         (with_w2h ? w2_f16_bytes(V, r) : 0);
+// Contraction slices of the projection GEMM: enough (tile, slice) workgroups
+// for about three per CU, at most 4, never more than the d / 32 stages.
+static int rnn_hp_split(int B, int K, int r, int d) {
+  const int tiles = ((B * K + kHpTile - 1) / kHpTile) * ((3 * r + kHpTile - 1) / kHpTile);
+  return std::max(1, std::min({4, 768 / tiles, d / kHpK}));
+}
+
+size_t rnn_workspace_bytes(int B, int K, int V, int r, int d, bool with_w2h) {
+  return align256_rnn((size_t)rnn_hp_split(B, K, r, d) * B * K * 3 * r * sizeof(float)) +
+         2 * align256_rnn((size_t)B * r * sizeof(float)) + (with_w2h ? w2_f16_bytes(V, r) : 0);
 }
 
 void rnn_bind_workspace(RnnParams& p, void* workspace) {
   char* ws = reinterpret_cast<char*>(workspace);
+  p.hp_split = rnn_hp_split(p.B, p.K, p.r, p.d);
   p.Hp = reinterpret_cast<float*>(ws);
-  ws += align256_rnn((size_t)p.B * p.K * 3 * p.r * sizeof(float));
+  ws += align256_rnn((size_t)p.hp_split * p.B * p.K * 3 * p.r * sizeof(float));
   p.s[0] = reinterpret_cast<float*>(ws);
   ws += align256_rnn((size_t)p.B * p.r * sizeof(float));
   p.s[1] = reinterpret_cast<float*>(ws);
@@ -261,8 +285,8 @@ int run_w2_to_f16(const uint16_t* W2, uint16_t* out, int V, int r, hipStream_t s
 int run_rnn_hproj(const RnnParams& p, hipStream_t stream) {
   const int mtiles = (p.B * p.K + kHpTile - 1) / kHpTile;
   const int ntiles = (3 * p.r + kHpTile - 1) / kHpTile;
-  return launch_kernel("rnn_hproj", rnn_hproj_kernel, dim3(xcd_grid(mtiles, ntiles)), dim3(256), stream, p, mtiles,
-                       ntiles);
+  return launch_kernel("rnn_hproj", rnn_hproj_kernel, dim3(xcd_grid(mtiles, ntiles), p.hp_split), dim3(256), stream,
+                       p, mtiles, ntiles);
 }
 
 int run_rnn_step(const RnnParams& p, int k, hipStream_t stream) {

@@ -68,8 +68,9 @@ size_t label_workspace_bytes(int B, int K, int V, int r) {
 size_t sts_workspace_bytes(int N, int G) {
   return al((size_t)N * 16) + 2 * al((size_t)G * (size_t)((N + 4095) / 4096) * 32 * 8);
 }
-size_t rnn_workspace_bytes(int B, int K, int V, int r, bool with_w2h) {
-  return al((size_t)B * K * 3 * r * 4) + 2 * al((size_t)B * r * 4) + (with_w2h ? w2_f16_bytes(V, r) : 0);
+size_t rnn_workspace_bytes(int B, int K, int V, int r, int d, bool with_w2h) {
+  return 4 * al((size_t)B * K * 3 * r * 4) + 2 * al((size_t)B * r * 4) + (with_w2h ? w2_f16_bytes(V, r) : 0) +
+         (size_t)d * 0;
 }
 void rnn_bind_workspace(RnnParams& p, void* ws) {
   char* c = reinterpret_cast<char*>(ws);
