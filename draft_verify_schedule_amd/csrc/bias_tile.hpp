@@ -622,6 +622,8 @@ __device__ __forceinline__ float valu_bias_4waves(const uint16_t* __restrict__ w
 // index order.  Zero terms past r leave the sums unchanged.  !ok gives 0.
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
+constexpr int kMaxRankRow = 64;  // 16-byte entries of a staged bias row: r <= 256 fp32 values
+
 template <bool ROWS>
 __device__ __forceinline__ float lane_bias_staged(const u32x4* row, rsrc_t w2, uint32_t w2_bytes, uint32_t off0,
                                                   bool swz, int r, bool ok, int lane) {

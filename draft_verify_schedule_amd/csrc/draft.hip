@@ -441,7 +441,6 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
 // barrier and two dependent memory round trips (the partials, then the
 // slice's base logits and W2 block).
 constexpr int kLocRun = 40;
-constexpr int kMaxRankRow = 64;  // 16-byte entries of the staged bias row: r <= 256 fp32 values
 
 template <typename UT, bool GREEDY>
 __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {

@@ -958,44 +958,6 @@ struct SliceHit {
   double before;
 };
 
-// find_slice over weights held in registers: lane l's run is w[0..cnt) for
-// slices s_begin.. (fp32 values, summed in fp64 in slice order).  Every lane
-// walks its own run without branches; the owner's result is broadcast.
-template <int N>
-__device__ __forceinline__ SliceHit find_slice_regs(int ns, double target, double incl, double local, int s_begin,
-                                                    int cnt, const float (&w)[N]) {
-  int owner = wave_first_lane(incl > target);
-  if (owner < 0) {
-    const unsigned long long m = __ballot(local > 0.0);
-    owner = m ? 63 - __clzll((long long)m) : 0;
-  }
-  double acc = incl - local;
-  int s_star = -1, last = -1;
-  double before = 0.0, last_before = acc;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const double wi = i < cnt ? (double)w[i] : 0.0;
-    if (wi > 0.0 && s_star < 0) {
-      last = s_begin + i;
-      last_before = acc;
-      if (acc + wi > target) {
-        s_star = s_begin + i;
-        before = acc;
-      }
-    }
-    acc += wi;
-  }
-  if (s_star < 0) {
-    s_star = last;
-    before = last_before;
-  }
-  SliceHit h;
-  h.slice = __shfl(s_star, owner, 64);
-  h.before = __shfl(before, owner, 64);
-  if (h.slice < 0 || h.slice >= ns) h.slice = 0;
-  return h;
-}
-
 constexpr int kSamPer = 40;  // slices per lane held in registers by the sample kernel
 
 template <typename WeightFn>
@@ -1038,12 +1000,88 @@ __device__ __forceinline__ SliceHit find_slice(int ns, double target, double inc
   return h;
 }
 
+// The crossing of `target` over slice weights held in registers (lane l's
+// contiguous run w[0..N) of slices s0.., fp32 values whose running sum is
+// kept in fp64): the owner lane (the first whose inclusive sum passes the
+// target, else the last with mass) puts its run in this wave's LDS slots
+// `run`, lane i takes entry i, and an fp64 wave scan finds the first entry
+// with mass whose running sum passes the target, else the last with mass.
+// Returns the slice (0 when nothing has mass) and the mass before it; `pick`
+// is the entry's index in the owner's run (-1 when nothing has mass).  LDS
+// accesses of one wave complete in order: no barrier.
+template <int N, typename T>
+__device__ __forceinline__ SliceHit cross_in_run(double target, double incl, double local, int s0, int ns,
+                                                 const T (&run_regs)[N], T* run, float (*weight)(T, float),
+                                                 float M, int lane, int& pick) {
+  int owner = wave_first_lane(incl > target);
+  if (owner < 0) {
+    const unsigned long long m = __ballot(local > 0.0);
+    owner = m ? 63 - __clzll((long long)m) : 0;
+  }
+  if (lane == owner) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) run[i] = run_regs[i];
+  }
+  const double acc0 = __shfl(incl - local, owner, 64);
+  const int os0 = __shfl(s0, owner, 64);
+  const double w = lane < N ? (double)weight(run[lane < N ? lane : 0], M) : 0.0;
+  const double cum = acc0 + wave_inclusive_scan_dpp(w);
+  pick = wave_first_lane(cum > target && w > 0.0);
+  if (pick < 0) {  // rounding: the last entry with mass
+    const unsigned long long m = __ballot(w > 0.0);
+    pick = m ? 63 - __clzll((long long)m) : -1;
+  }
+  SliceHit h;
+  if (pick < 0) {
+    h.slice = 0;
+    h.before = acc0;
+  } else {
+    h.slice = os0 + pick;
+    h.before = __shfl(cum - w, pick, 64);
+  }
+  if (h.slice >= ns) h.slice = 0;
+  return h;
+}
+
+__device__ __forceinline__ float mass_of(float w, float) { return w; }
+__device__ __forceinline__ float mass_of_part(float2 q, float M) {
+  return q.x == -INFINITY ? 0.f : q.y * fast_exp2(q.x - M);
+}
+
+// One wave per request.  Correction: the residual slice masses of the
+// request are requested together with its decision (branch-free buffer
+// loads, all in flight), the bias input row (W1[x_{j-1}] or the RNN output
+// part) while they are reduced, and the crossing slice's 64 columns are
+// re-evaluated (draft base logit + bias from the staged row and the slice's
+// W2 block, target logit) with every load requested together.  Bonus (or a
+// correction with no residual mass): the target row's 256-column partials,
+// then the crossing slice's 256 logits.
 template <typename PT, typename DT>
 __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave_index();
+  const int wv = wave_index();
+  const int r = blockIdx.x * 4 + wv;
   if (r >= a.R) return;
+  __shared__ u32x4 sh_row[4][kMaxRankRow];
+  __shared__ float sh_run[4][kSamPer];
+  __shared__ float2 sh_prun[4][kSamPer];
+
+  // correction weights: requested before the decision is known (a request
+  // that takes the bonus leaves them unused)
+  const int ns64 = a.ns64;
+  const int per64 = (ns64 + 63) / 64;
+  const int c0 = min(ns64, lane * per64), c1 = min(ns64, c0 + per64);
+  const bool cregs = per64 <= kSamPer;
+  float cw[kSamPer];
+  if (cregs) {
+    const rsrc_t rr = make_rsrc(a.rpart + (size_t)r * ns64, (uint32_t)ns64 * 4u);
+#pragma unroll
+    for (int i = 0; i < kSamPer; ++i)
+      cw[i] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rr, (int)((c0 + i < c1) ? (uint32_t)(c0 + i) * 4u : (uint32_t)ns64 * 4u), 0, 0));
+  }
   const int4 in = a.info[r];
+  __builtin_amdgcn_sched_barrier(0);
   if (in.x < 0) return;  // decide already wrote -1
   const float u = decision_uniform(a.seed, a.step, (uint32_t)r, (uint32_t)in.z, kPurposeResample);
   const PT* prow = reinterpret_cast<const PT*>(a.P) + (size_t)in.y * a.V;
@@ -1052,43 +1090,78 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   bool use_p = in.x == 0;
 
   if (!use_p) {
-    // correction: residual mass per 64-column slice
-    const float* rp = a.rpart + (size_t)r * a.ns64;
-    const int ns = a.ns64;
-    const int per = (ns + 63) / 64;
-    const int s_begin = min(ns, lane * per), s_end = min(ns, s_begin + per);
-    const bool regs = per <= kSamPer;
-    float wv[kSamPer];
-    double local = 0.0;
-    if (regs) {
-#pragma unroll
-      for (int i = 0; i < kSamPer; ++i) wv[i] = (s_begin + i < s_end) ? rp[s_begin + i] : 0.f;
-#pragma unroll
-      for (int i = 0; i < kSamPer; ++i) local += (double)wv[i];
-    } else {
-      for (int s = s_begin; s < s_end; ++s) local += (double)rp[s];
+    // the bias input row (its address waits for the previous token), staged
+    // in LDS once the crossing is known; lanes past r read zeros
+    const size_t drow = (size_t)r * a.K + in.w;
+    const int prev = in.w == 0 ? a.x0[r] : a.x[drow - 1];
+    const bool prev_ok = prev >= 0 && prev < a.V;
+    u32x4 row_in = u32x4{0u, 0u, 0u, 0u};
+    if (a.r > 0) {
+      const int n = a.O ? a.r / 4 : a.r / 8;
+      const rsrc_t rr = a.O ? make_rsrc(a.O + drow * a.r, (uint32_t)a.r * 4u)
+                            : make_rsrc(a.W1 + (size_t)(prev_ok ? prev : 0) * a.r, (uint32_t)a.r * 2u);
+      row_in = buffer_load16(rr, ((a.O || prev_ok) && lane < n) ? (uint32_t)lane * 16u : 0xFFFFFFF0u, 0u);
     }
-    const double incl = wave_inclusive_scan(local);
+    double local = 0.0;
+    if (cregs) {
+      double l4[4] = {0.0, 0.0, 0.0, 0.0};  // four chains in flight
+#pragma unroll
+      for (int i = 0; i < kSamPer; ++i) l4[i & 3] += (double)cw[i];  // past the run: read as zero
+      local = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    } else {
+      const float* rp = a.rpart + (size_t)r * ns64;
+      for (int s = c0; s < c1; ++s) local += (double)rp[s];
+    }
+    const double incl = wave_inclusive_scan_dpp(local);
     const double Z = __shfl(incl, 63, 64);
     if (Z > 0.0 && Z <= 2.0) {
       const double target = (double)u * Z;
-      const SliceHit h = regs ? find_slice_regs(ns, target, incl, local, s_begin, s_end - s_begin, wv)
-                              : find_slice(ns, target, incl, local, s_begin, s_end, [&](int s) { return (double)rp[s]; });
+      SliceHit h;
+      if (cregs) {
+        int pk;
+        h = cross_in_run<kSamPer, float>(target, incl, local, c0, ns64, cw, sh_run[wv], mass_of, 0.f, lane, pk);
+      } else {
+        const float* rp = a.rpart + (size_t)r * ns64;
+        h = find_slice(ns64, target, incl, local, c0, c1, [&](int s) { return (double)rp[s]; });
+      }
+      sh_row[wv][lane] = row_in;
+      // the slice's 64 columns, one per lane: draft and target logits and the
+      // W2 block requested together (a column past V reads zero, no branch)
       const int col = h.slice * kWaveCols + lane;
+      const bool col_ok = col < a.V;
+      const rsrc_t dr = make_rsrc(reinterpret_cast<const DT*>(a.D) + drow * a.V, (uint32_t)a.V * (uint32_t)sizeof(DT));
+      const rsrc_t pr = make_rsrc(prow, (uint32_t)a.V * (uint32_t)sizeof(PT));
+      const uint32_t doff = col_ok ? (uint32_t)col * (uint32_t)sizeof(DT) : 0xFFFFFFF0u;
+      const uint32_t poff = col_ok ? (uint32_t)col * (uint32_t)sizeof(PT) : 0xFFFFFFF0u;
+      float zq, zp;
+      if constexpr (sizeof(DT) == 2)
+        zq = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(dr, (int)doff, 0, 0) << 16);
+      else
+        zq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dr, (int)doff, 0, 0));
+      if constexpr (sizeof(PT) == 2)
+        zp = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pr, (int)poff, 0, 0) << 16);
+      else
+        zp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, (int)poff, 0, 0));
+      if (a.r > 0 && (a.O || prev_ok)) {
+        const int kc_count = (a.r + 31) / 32;
+        const bool swz = a.W2s != nullptr && a.O == nullptr;
+        const uint32_t w2_bytes = swz ? (uint32_t)((size_t)((a.V + kWaveCols - 1) / kWaveCols) * 4 * kc_count * 1024)
+                                      : (uint32_t)((size_t)a.V * a.r * 2);
+        const rsrc_t w2 = make_rsrc(swz ? static_cast<const void*>(a.W2s) : static_cast<const void*>(a.W2t), w2_bytes);
+        const uint32_t off0 = swz ? (uint32_t)h.slice * 4u * (uint32_t)kc_count * 1024u
+                                  : (uint32_t)(col_ok ? col : 0) * (uint32_t)a.r * 2u;
+        zq += a.O ? lane_bias_staged<true>(sh_row[wv], w2, w2_bytes, off0, false, a.r, col_ok, lane)
+                  : lane_bias_staged<false>(sh_row[wv], w2, w2_bytes, off0, swz, a.r, col_ok, lane);
+      }
+      const float lq = a.lse_d[drow] * kLog2e;
       float rho = 0.f;
-      if (col < a.V) {
-        const int prev = in.w == 0 ? a.x0[r] : a.x[(size_t)r * a.K + in.w - 1];
-        const DT* drow = reinterpret_cast<const DT*>(a.D) + ((size_t)r * a.K + in.w) * a.V;
-        float zq = load_logit(drow, col);
-        if (a.O) zq += valu_bias_rows(a.O + ((size_t)r * a.K + in.w) * a.r, a.W2t + (size_t)col * a.r, a.r);
-        else if (a.r > 0) zq += valu_bias(a.W1 + (size_t)prev * a.r, a.W2t + (size_t)col * a.r, a.r);
-        const float lq = a.lse_d[(size_t)r * a.K + in.w] * kLog2e;
-        const float p = fast_exp2(fmaf(load_logit(prow, col), a.c2, -lp));
+      if (col_ok) {
+        const float p = fast_exp2(fmaf(zp, a.c2, -lp));
         const float q = fast_exp2(fmaf(zq, a.c2, -lq));
         rho = fmaxf(p - q, 0.f);
       }
       const float t_in = (float)(target - h.before);
-      const float cum = wave_inclusive_scan(rho);
+      const float cum = wave_inclusive_scan_dpp(rho);
       int pick = wave_first_lane(cum > t_in && rho > 0.f);
       // the draw's margin: distance of the target from the nearer CDF edge of
       // the drawn column, over the total mass (0 when rounding picked it)
@@ -1119,8 +1192,14 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   float2 pv[kSamPer];
   float M = -INFINITY;
   if (regs) {
+    const rsrc_t prr = make_rsrc(pp, (uint32_t)ns * 8u);
 #pragma unroll
-    for (int i = 0; i < kSamPer; ++i) pv[i] = (s_begin + i < s_end) ? pp[s_begin + i] : make_float2(-INFINITY, 0.f);
+    for (int i = 0; i < kSamPer; ++i)
+      pv[i] = buffer_load8(prr, (s_begin + i < s_end) ? (uint32_t)(s_begin + i) * 8u : (uint32_t)ns * 8u, 0u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kSamPer; ++i)
+      if (s_begin + i >= s_end) pv[i].x = -INFINITY;  // past the run (read as zeros): no mass
 #pragma unroll
     for (int i = 0; i < kSamPer; ++i) M = fmaxf(M, pv[i].x);
   } else {
@@ -1132,33 +1211,59 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     return (p.x == -INFINITY) ? 0.0 : (double)(p.y * fast_exp2(p.x - M));
   };
   double local = 0.0;
-  float wv[kSamPer];
   if (regs) {
+    double l4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int i = 0; i < kSamPer; ++i) {
-      wv[i] = (pv[i].x == -INFINITY) ? 0.f : pv[i].y * fast_exp2(pv[i].x - M);
-      local += (double)wv[i];
-    }
+    for (int i = 0; i < kSamPer; ++i) l4[i & 3] += (double)mass_of_part(pv[i], M);
+    local = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   } else {
     for (int s = s_begin; s < s_end; ++s) local += weight(s);
   }
-  const double incl = wave_inclusive_scan(local);
+  const double incl = wave_inclusive_scan_dpp(local);
   const double S = __shfl(incl, 63, 64);
   const double target = (double)u * S;
-  const SliceHit h = regs ? find_slice_regs(ns, target, incl, local, s_begin, s_end - s_begin, wv)
-                          : find_slice(ns, target, incl, local, s_begin, s_end, weight);
-  const float m_s = pp[h.slice].x;
+  SliceHit h;
+  float m_s;
+  if (regs) {
+    int pk;
+    h = cross_in_run<kSamPer, float2>(target, incl, local, s_begin, ns, pv, sh_prun[wv], mass_of_part, M, lane, pk);
+    m_s = pk >= 0 ? sh_prun[wv][pk].x : pp[h.slice].x;
+  } else {
+    h = find_slice(ns, target, incl, local, s_begin, s_end, weight);
+    m_s = pp[h.slice].x;
+  }
   const float t_in = (float)((target - h.before) / (double)fast_exp2(m_s - M));
-  // 256 columns, 4 consecutive per lane
+  // 256 columns, 4 consecutive per lane, one load per lane
   float e[4];
   float lsum = 0.f;
+  {
+    const int col0 = h.slice * kRowSlice + 4 * lane;
+    const rsrc_t pr = make_rsrc(prow, (uint32_t)a.V * (uint32_t)sizeof(PT));
+    float v[4];
+    if (col0 + 3 < a.V && (a.V % 4) == 0) {
+      if constexpr (sizeof(PT) == 2) {
+        const float2 d = buffer_load8(pr, (uint32_t)col0 * 2u, 0u);
+        const uint32_t w0 = __float_as_uint(d.x), w1 = __float_as_uint(d.y);
+        v[0] = __uint_as_float(w0 << 16);
+        v[1] = __uint_as_float(w0 & 0xFFFF0000u);
+        v[2] = __uint_as_float(w1 << 16);
+        v[3] = __uint_as_float(w1 & 0xFFFF0000u);
+      } else {
+        const u32x4 d = buffer_load16(pr, (uint32_t)col0 * 4u, 0u);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int col = h.slice * kRowSlice + 4 * lane + k;
-    e[k] = (col < a.V) ? fast_exp2(load_logit(prow, col) * a.c2 - m_s) : 0.f;
-    lsum += e[k];
+        for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(d[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = (col0 + k < a.V) ? load_logit(prow, col0 + k) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      e[k] = (col0 + k < a.V) ? fast_exp2(v[k] * a.c2 - m_s) : 0.f;
+      lsum += e[k];
+    }
   }
-  const float incl2 = wave_inclusive_scan(lsum);
+  const float incl2 = wave_inclusive_scan_dpp(lsum);
   int owner = wave_first_lane(incl2 > t_in && lsum > 0.f);
   if (owner < 0) {
     const unsigned long long m = __ballot(lsum > 0.f);
