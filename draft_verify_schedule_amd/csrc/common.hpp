@@ -207,6 +207,23 @@ __device__ __forceinline__ float lanes8_sum(float v) {
   v += dpp_q2(v);
   return v + dpp_hm(v);
 }
+// Lane i <-> 15 - i inside each 16-lane row: after an 8-lane reduction it
+// joins the row's two halves.
+__device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
+__device__ __forceinline__ float dpp_mirror(float v) { return __int_as_float(dpp_mirror(__float_as_int(v))); }
+// Whole-wave maximum and sum without LDS: 8 lanes on DPP, the row's halves by
+// the row mirror, then the four rows by the row swaps.  Every lane ends with
+// the result; the order of the additions is fixed.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = lanes8_max(v);
+  v = fmaxf(v, dpp_mirror(v));
+  return rows_max(v);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = lanes8_sum(v);
+  v += dpp_mirror(v);
+  return rows_sum(v);
+}
 
 // Inclusive prefix sum across the 64 lanes in lane order.
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
@@ -324,6 +341,30 @@ __device__ __forceinline__ void merge_top2(float& m, int& idx, float& m2, float 
   } else {
     m2 = fmaxf(m2, om);
   }
+}
+
+// merge_top2 over the whole wave, every lane ending with the result: 8 lanes
+// on DPP, the row mirror, then the row swaps (merge_top2 is symmetric in its
+// two operands, so both lanes of each exchange agree).
+__device__ __forceinline__ void wave_merge_top2(float& m, int& idx, float& m2) {
+  float om, om2;
+  int oi;
+  om = dpp_q1(m); oi = dpp_q1(idx); om2 = dpp_q1(m2);
+  merge_top2(m, idx, m2, om, oi, om2);
+  om = dpp_q2(m); oi = dpp_q2(idx); om2 = dpp_q2(m2);
+  merge_top2(m, idx, m2, om, oi, om2);
+  om = dpp_hm(m); oi = dpp_hm(idx); om2 = dpp_hm(m2);
+  merge_top2(m, idx, m2, om, oi, om2);
+  om = dpp_mirror(m); oi = dpp_mirror(idx); om2 = dpp_mirror(m2);
+  merge_top2(m, idx, m2, om, oi, om2);
+  float a, b, a2, b2;
+  int ia, ib;
+  row_pair16(m, a, b); row_pair16(idx, ia, ib); row_pair16(m2, a2, b2);
+  m = a; idx = ia; m2 = a2;
+  merge_top2(m, idx, m2, b, ib, b2);
+  row_pair32(m, a, b); row_pair32(idx, ia, ib); row_pair32(m2, a2, b2);
+  m = a; idx = ia; m2 = a2;
+  merge_top2(m, idx, m2, b, ib, b2);
 }
 
 // Loads of 16 consecutive logits (bf16 or f32) starting at column n of a row,

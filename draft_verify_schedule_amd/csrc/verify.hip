@@ -5,7 +5,7 @@
 //
 // Request r owns flat target rows cu[r] .. cu[r+1]-1 (its l_r drafts, then the
 // bonus row).  Launches:
-//   verify_rowstats   one HBM pass over every flat target row: per 256-column
+//   verify_rowstats   one HBM pass over every flat target row: per 2048-column
 //                     slice the softmax partial (max, sum exp2) of t * log2(e)/T,
 //                     or (max, first argmax) when greedy;
 //   verify_accept     one wave per flat row: merges its partials into the
@@ -19,7 +19,7 @@
 //                     the mass of max(0, p - q);
 //   verify_sample     (T > 0) one wave per request: inverse-CDF draw of the
 //                     correction (residual partials, 64-column re-scan) or the
-//                     bonus (target partials, 256-column re-scan).
+//                     bonus (target partials, 2048-column re-scan).
 // Drafts of the RNN head (DSpark paper, section 3.1, RNN head) pass their
 // output parts O [R, K, r] fp32: the draft row of position j then carries the
 // bias O[r, j-1] W2, staged as split hi/lo bf16 rows for the MFMA.
@@ -32,7 +32,10 @@
 namespace dspark {
 
 constexpr int kRowChunk = 8192;   // columns per rowstats workgroup (2048 per wave)
-constexpr int kRowSlice = 256;    // columns per target-row partial
+// columns per target-row partial: one per wave of the row-statistics pass
+// (fewer, coarser partials: the pass's writes cost far more than their bytes
+// inside its read stream)
+constexpr int kRowSlice = 2048;
 constexpr int kRowstatsWGs = 1024;  // persistent rowstats grid: 4 workgroups per CU (measured faster than 8)
 constexpr int kMaxPositions = 16;   // draft positions per request (the ABI's limit on K)
 
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
     constexpr int EPL = 16 / sizeof(PT);          // elements per 16-byte load
     constexpr int COLS = 64 * EPL;                // columns per load instruction
     constexpr int ITERS = (kRowChunk / 4) / COLS; // loads per wave
-    constexpr int LPS = kRowSlice / EPL;          // lanes per slice
+    static_assert(kRowSlice == kRowChunk / 4, "one slice per wave");
     float v[ITERS][EPL];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -127,113 +130,101 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
         for (int e = 0; e < EPL; ++e) v[it][e] = -INFINITY;
       }
     }
+    // one slice per wave: the lane's ITERS x EPL values in column order
+    const int slice = wbase / kRowSlice;
+    if constexpr (GREEDY) {
+      float m = -INFINITY, m2 = -INFINITY;
+      int idx = -1;
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int c = wbase + it * COLS + lane * EPL;
-      const int slice = (wbase + it * COLS) / kRowSlice + lane / LPS;
-      if constexpr (GREEDY) {
-        float m = -INFINITY, m2 = -INFINITY;
-        int idx = -1;
+      for (int it = 0; it < ITERS; ++it) {
+        const int c = wbase + it * COLS + lane * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
           if (c + e < a.V) merge_top2(m, idx, m2, v[it][e], c + e, -INFINITY);
+      }
+      wave_merge_top2(m, idx, m2);
+      if (lane == 0 && slice < a.nsP && idx >= 0) {
+        out[slice] = make_float2(m, __int_as_float(idx));
+        if (out2) out2[slice] = m2;
+      }
+    } else {
+      float m = -INFINITY;
 #pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) {
-          const float om = __shfl_xor(m, off, 64);
-          const int oi = __shfl_xor(idx, off, 64);
-          const float om2 = __shfl_xor(m2, off, 64);
-          merge_top2(m, idx, m2, om, oi, om2);
-        }
-        if ((lane % LPS) == 0 && slice < a.nsP && idx >= 0) {
-          out[slice] = make_float2(m, __int_as_float(idx));
-          if (out2) out2[slice] = m2;
-        }
-      } else {
-        float m = -INFINITY;
+      for (int it = 0; it < ITERS; ++it)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          v[it][e] *= a.c2;
+          v[it][e] *= a.c2;  // past V: -inf
           m = fmaxf(m, v[it][e]);
         }
+      m = wave_max_dpp(m);
+      float s = 0.f;
+      if (m != -INFINITY) {
 #pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        float s = 0.f;
-        if (m != -INFINITY) {
+        for (int it = 0; it < ITERS; ++it)
 #pragma unroll
           for (int e = 0; e < EPL; ++e) s += exp2f(v[it][e] - m);
-        }
-#pragma unroll
-        for (int off = 1; off < LPS; off <<= 1) s += __shfl_xor(s, off, 64);
-        if ((lane % LPS) == 0 && slice < a.nsP && c < a.V) out[slice] = make_float2(m, s);
       }
+      s = wave_sum_dpp(s);
+      if (lane == 0 && slice < a.nsP) out[slice] = make_float2(m, s);
     }
   } else {
-    // any alignment: lane-strided scalar loads, one 256-column slice per 4 steps
-    for (int sl = 0; sl < (kRowChunk / 4) / kRowSlice; ++sl) {
-      const int sbase = wbase + sl * kRowSlice;
-      if (sbase >= a.V) break;
-      float v[4];
+    // any alignment: lane-strided scalar loads, the wave's 2048 columns (one
+    // slice) held as 32 values per lane, lane l taking columns l, l + 64, ...
+    constexpr int T = kRowSlice / 64;
+    float v[T];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = sbase + 64 * t + lane;
-        v[t] = (c < a.V) ? load_logit(prow, c) : -INFINITY;
+    for (int t = 0; t < T; ++t) {
+      const int c = wbase + 64 * t + lane;
+      v[t] = (c < a.V) ? load_logit(prow, c) : -INFINITY;
+    }
+    const int slice = wbase / kRowSlice;
+    if constexpr (GREEDY) {
+      float m = -INFINITY, m2 = -INFINITY;
+      int idx = -1;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int c = wbase + 64 * t + lane;
+        if (c < a.V) merge_top2(m, idx, m2, v[t], c, -INFINITY);
       }
-      const int slice = sbase / kRowSlice;
-      if constexpr (GREEDY) {
-        float m = -INFINITY, m2 = -INFINITY;
-        int idx = -1;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int c = sbase + 64 * t + lane;
-          if (c < a.V) merge_top2(m, idx, m2, v[t], c, -INFINITY);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const float om = __shfl_xor(m, off, 64);
-          const int oi = __shfl_xor(idx, off, 64);
-          const float om2 = __shfl_xor(m2, off, 64);
-          merge_top2(m, idx, m2, om, oi, om2);
-        }
-        if (lane == 0) {
-          out[slice] = make_float2(m, __int_as_float(idx));
-          if (out2) out2[slice] = m2;
-        }
-      } else {
-        float m = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v[t] *= a.c2;
-          m = fmaxf(m, v[t]);
-        }
-        m = wave_max(m);
-        float s = 0.f;
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) s += exp2f(v[t] - m);
-        }
-        s = wave_sum(s);
-        if (lane == 0) out[slice] = make_float2(m, s);
+      wave_merge_top2(m, idx, m2);
+      if (lane == 0 && idx >= 0) {
+        out[slice] = make_float2(m, __int_as_float(idx));
+        if (out2) out2[slice] = m2;
       }
+    } else {
+      float m = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        v[t] *= a.c2;
+        m = fmaxf(m, v[t]);
+      }
+      m = wave_max_dpp(m);
+      float s = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) s += exp2f(v[t] - m);
+      }
+      s = wave_sum_dpp(s);
+      if (lane == 0) out[slice] = make_float2(m, s);
     }
   }
 }
 
 // Aligned-row variant: persistent grid-stride over (row, 8192-column chunk)
-// items.  Wave w covers columns [2048 w, 2048 w + 2048) of the chunk and lane
-// l the 32 contiguous columns from 32 l, so lanes 8s .. 8s+7 hold 256-column
-// slice s of the wave: each lane reduces its 32 values, then three lane swaps
-// finish the slice.  The next item's loads (buffer resource, per-lane VGPR
+// items.  Wave w covers columns [2048 w, 2048 w + 2048) of the chunk, one
+// slice, and lane l the 32 contiguous columns from 32 l: each lane reduces
+// its 32 values, then DPP steps and the row swaps finish the slice, and lane 0
+// writes its partial.  The next item's loads (buffer resource, per-lane VGPR
 // offset, scalar row offset) are issued before the current item is reduced;
-// the loop body has no branches: loads past the last item and stores of lanes
-// that do not lead a slice get offsets past their buffer resource.
+// the loop body has no branches: loads past the last item and stores of the
+// other lanes get offsets past their buffer resource.
 template <typename PT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs a) {
   constexpr int kWaveColsR = kRowChunk / 4;     // 2048
   constexpr int CPL = kWaveColsR / 64;          // columns per lane per item
   constexpr int EPL = 16 / sizeof(PT);          // elements per 16-byte load
   constexpr int LOADS = CPL / EPL;
-  constexpr int LPS = kRowSlice / CPL;          // lanes per slice
-  static_assert(LPS == 8, "three lane swaps per slice");
+  static_assert(kRowSlice == kWaveColsR, "one slice per wave");
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const int items = a.N * a.nchunks;
@@ -242,7 +233,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
   const uint32_t lane_off = (uint32_t)(lane * CPL * sizeof(PT));
   const uint32_t obytes = (uint32_t)((uint64_t)a.N * a.nsP * sizeof(float2));
   const int4v ors = raw_rsrc_words(a.ppart, obytes);
-  const bool leader = (lane % LPS) == 0;
+  const bool leader = lane == 0;
 
   const uint32_t o2bytes = a.ppart2 ? obytes / 2u : 0u;
   const int4v o2rs = raw_rsrc_words(a.ppart2, o2bytes);
@@ -298,32 +289,23 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
         for (int e = 0; e < CPL; ++e) m2 = fmaxf(m2, e == first ? -INFINITY : v[e]);
         idx = c0 + first;
       }
-      {  // the slice's 8 lanes
-        int oi;
-        float om, om2;
-        om = dpp_q1(m); oi = dpp_q1(idx); om2 = dpp_q1(m2);
-        merge_top2(m, idx, m2, om, oi, om2);
-        om = dpp_q2(m); oi = dpp_q2(idx); om2 = dpp_q2(m2);
-        merge_top2(m, idx, m2, om, oi, om2);
-        om = dpp_hm(m); oi = dpp_hm(idx); om2 = dpp_hm(m2);
-        merge_top2(m, idx, m2, om, oi, om2);
-      }
+      wave_merge_top2(m, idx, m2);  // the slice is the whole wave
       res = make_float2(m, __int_as_float(idx));
       runner_up = m2;
     } else {
       float m = v[0];
 #pragma unroll
       for (int e = 1; e < CPL; ++e) m = fmaxf(m, v[e]);
-      m = lanes8_max(m);
+      m = wave_max_dpp(m);
       const bool empty = m == -INFINITY;
       const float mc = empty ? 0.f : m * a.c2;
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) s += fast_exp2(fmaf(v[e], a.c2, -mc));
-      s = lanes8_sum(s);
+      s = wave_sum_dpp(s);
       res = make_float2(empty ? -INFINITY : mc, s);
     }
-    const int slice = wbase / kRowSlice + lane / LPS;
+    const int slice = wbase / kRowSlice;
     const uint32_t voff = (leader && slice < a.nsP) ? (uint32_t)(((uint64_t)row * a.nsP + slice) * sizeof(float2))
                                                     : obytes;
     buffer_store8_untracked(ors, res, voff, 0u);
@@ -1054,8 +1036,8 @@ __device__ __forceinline__ float mass_of_part(float2 q, float M) {
 // part) while they are reduced, and the crossing slice's 64 columns are
 // re-evaluated (draft base logit + bias from the staged row and the slice's
 // W2 block, target logit) with every load requested together.  Bonus (or a
-// correction with no residual mass): the target row's 256-column partials,
-// then the crossing slice's 256 logits.
+// correction with no residual mass): the target row's 2048-column partials,
+// then the crossing slice's 2048 logits.
 template <typename PT, typename DT>
 __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & 63;
@@ -1065,6 +1047,7 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
   __shared__ u32x4 sh_row[4][kMaxRankRow];
   __shared__ float sh_run[4][kSamPer];
   __shared__ float2 sh_prun[4][kSamPer];
+  __shared__ float sh_bonus[4][kRowSlice / 64];
 
   // correction weights: requested before the decision is known (a request
   // that takes the bonus leaves them unused)
@@ -1183,7 +1166,7 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     use_p = true;  // zero residual mass (rounding only): draw from p
   }
 
-  // bonus (or fallback): target partials per 256-column slice
+  // bonus (or fallback): target partials per 2048-column slice
   const float2* pp = a.ppart + (size_t)in.y * a.nsP;
   const int ns = a.nsP;
   const int per = (ns + 63) / 64;
@@ -1232,64 +1215,76 @@ __global__ __launch_bounds__(256) void verify_sample_kernel(VerifyArgs a) {
     h = find_slice(ns, target, incl, local, s_begin, s_end, weight);
     m_s = pp[h.slice].x;
   }
-  const float t_in = (float)((target - h.before) / (double)fast_exp2(m_s - M));
-  // 256 columns, 4 consecutive per lane, one load per lane
-  float e[4];
-  float lsum = 0.f;
+  // the target inside the slice, in the slice's own scale (fp64: 2048 terms)
+  const double t_in = (target - h.before) / (double)fast_exp2(m_s - M);
+  // the slice's columns, kBonusPer consecutive per lane (16-byte loads when
+  // whole vectors lie inside the row, past V reading zero)
+  constexpr int kBonusPer = kRowSlice / 64;
+  float e[kBonusPer];
+  double lsum = 0.0;
   {
-    const int col0 = h.slice * kRowSlice + 4 * lane;
+    const int col0 = h.slice * kRowSlice + kBonusPer * lane;
     const rsrc_t pr = make_rsrc(prow, (uint32_t)a.V * (uint32_t)sizeof(PT));
-    float v[4];
-    if (col0 + 3 < a.V && (a.V % 4) == 0) {
-      if constexpr (sizeof(PT) == 2) {
-        const float2 d = buffer_load8(pr, (uint32_t)col0 * 2u, 0u);
-        const uint32_t w0 = __float_as_uint(d.x), w1 = __float_as_uint(d.y);
-        v[0] = __uint_as_float(w0 << 16);
-        v[1] = __uint_as_float(w0 & 0xFFFF0000u);
-        v[2] = __uint_as_float(w1 << 16);
-        v[3] = __uint_as_float(w1 & 0xFFFF0000u);
-      } else {
-        const u32x4 d = buffer_load16(pr, (uint32_t)col0 * 4u, 0u);
+    constexpr int EPL = 16 / sizeof(PT);
+    float v[kBonusPer];
+    if (a.V % EPL == 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(d[k]);
+      for (int q = 0; q < kBonusPer / EPL; ++q) {
+        const int c = col0 + EPL * q;
+        const u32x4 d = buffer_load16(pr, c < a.V ? (uint32_t)c * (uint32_t)sizeof(PT) : 0xFFFFFFF0u, 0u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (sizeof(PT) == 2) {
+            v[EPL * q + 2 * k] = __uint_as_float(d[k] << 16);
+            v[EPL * q + 2 * k + 1] = __uint_as_float(d[k] & 0xFFFF0000u);
+          } else {
+            v[EPL * q + k] = __uint_as_float(d[k]);
+          }
+        }
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = (col0 + k < a.V) ? load_logit(prow, col0 + k) : 0.f;
+      for (int k = 0; k < kBonusPer; ++k) v[k] = (col0 + k < a.V) ? load_logit(prow, col0 + k) : 0.f;
     }
+    double l4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBonusPer; ++k) {
       e[k] = (col0 + k < a.V) ? fast_exp2(v[k] * a.c2 - m_s) : 0.f;
-      lsum += e[k];
+      l4[k & 3] += (double)e[k];
     }
+    lsum = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   }
-  const float incl2 = wave_inclusive_scan_dpp(lsum);
-  int owner = wave_first_lane(incl2 > t_in && lsum > 0.f);
+  const double incl2 = wave_inclusive_scan_dpp(lsum);
+  int owner = wave_first_lane(incl2 > t_in && lsum > 0.0);
   if (owner < 0) {
-    const unsigned long long m = __ballot(lsum > 0.f);
+    const unsigned long long m = __ballot(lsum > 0.0);
     owner = m ? 63 - __clzll((long long)m) : 0;
   }
-  int pick = -1;
+  // the owner's kBonusPer values through LDS (in-order LDS access within the
+  // wave: no barrier), lane i takes value i, and an fp64 wave scan finds the
+  // first column with mass whose running sum passes the target, else the
+  // last column with mass
   if (lane == owner) {
-    float acc = incl2 - lsum;
-    int last = 0;
-    float edge = 0.f;  // distance of the target from the drawn column's CDF edges (0: picked by rounding)
-    for (int k = 0; k < 4; ++k) {
-      if (e[k] > 0.f) {
-        last = k;
-        if (acc + e[k] > t_in) {
-          pick = k;
-          edge = fminf(acc + e[k] - t_in, t_in - acc);
-          break;
-        }
-      }
-      acc += e[k];
-    }
-    if (pick < 0) pick = last;
-    a.tok_out[r] = h.slice * kRowSlice + 4 * lane + pick;
+#pragma unroll
+    for (int k = 0; k < kBonusPer; ++k) sh_bonus[wv][k] = e[k];
+  }
+  const double acc0 = __shfl(incl2 - lsum, owner, 64);
+  const double w = lane < kBonusPer ? (double)sh_bonus[wv][lane < kBonusPer ? lane : 0] : 0.0;
+  const double cum = acc0 + wave_inclusive_scan_dpp(w);
+  int pick = wave_first_lane(cum > t_in && w > 0.0);
+  double edge = 0.0;  // distance of the target from the drawn column's CDF edges (0: picked by rounding)
+  if (pick >= 0) {
+    const double hi = __shfl(cum, pick, 64), wp = __shfl(w, pick, 64);
+    edge = fmin(hi - t_in, t_in - (hi - wp));
+  } else {
+    const unsigned long long m = __ballot(w > 0.0);
+    pick = m ? 63 - __clzll((long long)m) : 0;
+  }
+  if (lane == 0) {
+    a.tok_out[r] = h.slice * kRowSlice + kBonusPer * owner + pick;
     if (a.min_margin_out) {
       // the slice's values are scaled by 2^(M - m_s) against the masses summing to S
-      const float mg = S > 0.0 ? (float)((double)edge * (double)fast_exp2(m_s - M) / S) : 0.f;
+      const float mg = S > 0.0 ? (float)(edge * (double)fast_exp2(m_s - M) / S) : 0.f;
       a.min_margin_out[r] = fminf(a.rmin[r], mg);
     }
   }
@@ -1345,7 +1340,7 @@ size_t verify_workspace_need(int R, int K, int V, int r, int N, bool lse_given, 
   return verify_layout(R, K, V, N, r, lse_pass, !w2f_given, margins).total;
 }
 
-// Log-normaliser of each row from its 256-column rowstats partials (one wave
+// Log-normaliser of each row from its 2048-column rowstats partials (one wave
 // per row): lse = (M + log2 S) ln 2, the draft's convention.
 __global__ __launch_bounds__(256) void row_lse_kernel(const float2* __restrict__ part, int nrows, int ns,
                                                       float* __restrict__ lse) {

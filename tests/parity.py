@@ -22,7 +22,7 @@ MARGIN = 1e-5
 MAX_NEAR_TIE_FRACTION = 1e-4
 
 # session totals over every parity test that called check_near_ties
-POOL = {"tests": 0, "decisions": 0, "near_ties": 0, "excluded": 0}
+POOL = {"tests": 0, "decisions": 0, "near_ties": 0, "excluded": 0, "with_ties": []}
 
 
 class Report:
@@ -49,6 +49,8 @@ class Report:
         POOL["decisions"] += self.decisions
         POOL["near_ties"] += self.near_ties
         POOL["excluded"] += self.excluded
+        if self.near_ties:
+            POOL["with_ties"].append(str(self))
         if self.decisions * MAX_NEAR_TIE_FRACTION >= 1:
             assert self.near_ties < MAX_NEAR_TIE_FRACTION * self.decisions, str(self)
 

@@ -17,4 +17,6 @@ def test_pooled_near_tie_rate():
     rate = POOL["near_ties"] / max(POOL["decisions"], 1)
     print("pooled over %d parity tests: %d decisions, %d counted near-ties (rate %.2e), %d excluded"
           % (POOL["tests"], POOL["decisions"], POOL["near_ties"], rate, POOL["excluded"]), flush=True)
-    assert rate < MAX_NEAR_TIE_FRACTION
+    for line in POOL["with_ties"]:
+        print("  near-ties in: " + line, flush=True)
+    assert rate < MAX_NEAR_TIE_FRACTION, "; ".join(POOL["with_ties"])
