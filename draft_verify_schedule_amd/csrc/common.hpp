@@ -343,6 +343,24 @@ __device__ __forceinline__ void merge_top2(float& m, int& idx, float& m2, float 
   }
 }
 
+// merge_argmax over the whole wave (the greedy statistics without the
+// runner-up), every lane ending with the result: the same exchanges as
+// wave_merge_top2.
+__device__ __forceinline__ void wave_merge_argmax(float& m, int& idx) {
+  merge_argmax(m, idx, dpp_q1(m), dpp_q1(idx));
+  merge_argmax(m, idx, dpp_q2(m), dpp_q2(idx));
+  merge_argmax(m, idx, dpp_hm(m), dpp_hm(idx));
+  merge_argmax(m, idx, dpp_mirror(m), dpp_mirror(idx));
+  float a, b;
+  int ia, ib;
+  row_pair16(m, a, b); row_pair16(idx, ia, ib);
+  m = a; idx = ia;
+  merge_argmax(m, idx, b, ib);
+  row_pair32(m, a, b); row_pair32(idx, ia, ib);
+  m = a; idx = ia;
+  merge_argmax(m, idx, b, ib);
+}
+
 // merge_top2 over the whole wave, every lane ending with the result: 8 lanes
 // on DPP, the row mirror, then the row swaps (merge_top2 is symmetric in its
 // two operands, so both lanes of each exchange agree).

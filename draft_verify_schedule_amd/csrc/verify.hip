@@ -285,11 +285,15 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
         int first = CPL - 1;
 #pragma unroll
         for (int e = CPL - 2; e >= 0; --e) first = (v[e] == m) ? e : first;
+        if (a.ppart2) {  // runner-up only when decision margins are asked for (wave-uniform)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) m2 = fmaxf(m2, e == first ? -INFINITY : v[e]);
+          for (int e = 0; e < CPL; ++e) m2 = fmaxf(m2, e == first ? -INFINITY : v[e]);
+        }
         idx = c0 + first;
       }
-      wave_merge_top2(m, idx, m2);  // the slice is the whole wave
+      // the slice is the whole wave
+      if (a.ppart2) wave_merge_top2(m, idx, m2);
+      else wave_merge_argmax(m, idx);
       res = make_float2(m, __int_as_float(idx));
       runner_up = m2;
     } else {
