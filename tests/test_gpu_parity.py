@@ -105,6 +105,8 @@ def test_draft_tiny_workload(T):
     (384, 2, 4096, 256, torch.bfloat16, 1.0),  # a 256-row stage pair and a leftover full 128-row stage
     (300, 2, 2048, 64, torch.bfloat16, 0.8),   # a 256-row stage pair and a partial stage
     (272, 3, 2048, 128, torch.bfloat16, 0.0),  # greedy over a 256-row stage pair
+    (260, 2, 2056, 64, torch.bfloat16, 1.0),   # a 256-row stage pair with a column tail of 8
+    (256, 2, 1000, 32, torch.bfloat16, 0.0),   # greedy, a 256-row stage pair with a column tail of 40
 ])
 def test_draft_shapes(B, K, V, r, dtype, T):
     _say("draft shape B=%d K=%d V=%d r=%d %s T=%g" % (B, K, V, r, dtype, T))
