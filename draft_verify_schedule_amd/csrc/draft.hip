@@ -167,8 +167,10 @@ struct UCoal {
   __device__ __forceinline__ void load_if(GroupLogitsBuf<uint16_t>& b, int row, int blk, bool valid) const {
     const uint32_t off = (uint32_t)((uint64_t)row * row_bytes + (uint64_t)blk * kWaveCols * 2u);
     const uint32_t off8 = (uint32_t)((uint64_t)(row + 8) * row_bytes + (uint64_t)blk * kWaveCols * 2u);
-    b.w[0] = buffer_load16(rsrc, lane_off, valid ? off : bytes);
-    b.w[1] = buffer_load16(rsrc, lane_off, valid ? off8 : bytes);
+    // each base logit is read once per call: non-temporal, so that the
+    // stream does not displace W2, which the next position reads again
+    b.w[0] = buffer_load16_nt(rsrc, lane_off, valid ? off : bytes);
+    b.w[1] = buffer_load16_nt(rsrc, lane_off, valid ? off8 : bytes);
   }
 };
 

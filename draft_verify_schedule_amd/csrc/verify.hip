@@ -802,10 +802,12 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     if constexpr (CX) {
       const ResidualRow r0 = rows[16 * g + (lane >> 3)], r1 = rows[16 * g + 8 + (lane >> 3)];
       const uint32_t c = (uint32_t)blk * kWaveCols * 2u + 16u * (uint32_t)(lane & 7);
-      pb.w[0] = buffer_load16(prs, r0.p_off + c, 0u);
-      pb.w[1] = buffer_load16(prs, r1.p_off + c, 0u);
-      db.w[0] = buffer_load16(drs, r0.d_off + c, 0u);
-      db.w[1] = buffer_load16(drs, r1.d_off + c, 0u);
+      // target and draft rows are read once here: non-temporal, so that
+      // they do not displace W2, which every block of the pass reads again
+      pb.w[0] = buffer_load16_nt(prs, r0.p_off + c, 0u);
+      pb.w[1] = buffer_load16_nt(prs, r1.p_off + c, 0u);
+      db.w[0] = buffer_load16_nt(drs, r0.d_off + c, 0u);
+      db.w[1] = buffer_load16_nt(drs, r1.d_off + c, 0u);
     }
   };
   auto xpose = [&](auto& b) {
