@@ -212,8 +212,12 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(VerifyArgs a) {
 
 // Aligned-row variant: persistent grid-stride over (row, 8192-column chunk)
 // items.  Wave w covers columns [2048 w, 2048 w + 2048) of the chunk, one
-// slice, and lane l the 32 contiguous columns from 32 l: each lane reduces
-// its 32 values, then DPP steps and the row swaps finish the slice, and lane 0
+// slice.  Load l of lane l' reads the 16 bytes at 1024 l + 16 l' of the
+// wave's columns, so each load instruction covers whole 128-byte lines (a
+// lane holding 32 contiguous columns would read each line in four
+// instructions of two lanes each, four times the cache accesses), and the
+// loads are non-temporal (each row is read once); each lane reduces its 32
+// values, then DPP steps and the row swaps finish the slice, and lane 0
 // writes its partial.  The next item's loads (buffer resource, per-lane VGPR
 // offset, scalar row offset) are issued before the current item is reduced;
 // the loop body has no branches: loads past the last item and stores of the
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
   const int items = a.N * a.nchunks;
   const uint32_t pbytes = (uint32_t)((uint64_t)a.N * a.V * sizeof(PT));
   const rsrc_t rs = make_rsrc(a.P, pbytes);
-  const uint32_t lane_off = (uint32_t)(lane * CPL * sizeof(PT));
+  const uint32_t lane_off = (uint32_t)lane * 16u;
   const uint32_t obytes = (uint32_t)((uint64_t)a.N * a.nsP * sizeof(float2));
   const int4v ors = raw_rsrc_words(a.ppart, obytes);
   const bool leader = lane == 0;
@@ -244,18 +248,20 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
     const int wbase = chunk * kRowChunk + wave * kWaveColsR;
     const uint32_t soff = live ? (uint32_t)(((uint64_t)row * a.V + wbase) * sizeof(PT)) : pbytes;
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) w[l] = buffer_load16(rs, lane_off + (uint32_t)(16 * l), soff);
+    for (int l = 0; l < LOADS; ++l) w[l] = buffer_load16_nt(rs, lane_off + (uint32_t)(1024 * l), soff);
   };
   // one item's statistics; MASK: the wave's 2048 columns pass the end of the
   // row (only then are values masked: V is a multiple of EPL, so whole
   // vectors are in or out)
   auto reduce_as = [&](auto mask_tag, int row, int wbase, const u32x4 (&w)[LOADS]) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int c0 = wbase + lane * CPL;
+    // value e = l * EPL + j of the lane is column col(e): increasing in e
+    const int c0 = wbase + lane * EPL;
+    auto col = [&](int e) { return c0 + (e / EPL) * (64 * EPL) + e % EPL; };
     float v[CPL];
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      const bool ok = !MASK || c0 + l * EPL < a.V;
+      const bool ok = !MASK || col(l * EPL) < a.V;
       if constexpr (sizeof(PT) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
       if constexpr (MASK) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e)
-          if (c0 + e < a.V) merge_top2(m, idx, m2, v[e], c0 + e, -INFINITY);
+          if (col(e) < a.V) merge_top2(m, idx, m2, v[e], col(e), -INFINITY);
       } else {
         // every column valid: the max, its first index, and the largest value
         // at any other index (a tie gives the max itself)
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(256) void verify_rowstats_stream_kernel(VerifyArgs 
 #pragma unroll
           for (int e = 0; e < CPL; ++e) m2 = fmaxf(m2, e == first ? -INFINITY : v[e]);
         }
-        idx = c0 + first;
+        idx = col(first);
       }
       // the slice is the whole wave
       if (a.ppart2) wave_merge_top2(m, idx, m2);
