@@ -307,14 +307,15 @@ def test_verify_all_positions(name, T):
     _say(str(rep) + " mean n_acc %.3f" % n_acc.mean())
 
 
-@pytest.mark.parametrize("name", ["ds_stepped", "sched_stress"])
-def test_verify_scheduled_prefixes(name):
+@pytest.mark.parametrize("name,T", [("ds_stepped", 1.0), ("sched_stress", 1.0),
+                                    ("sched_stress", 0.0)])  # fp32 rows, greedy over full 2048-column waves
+def test_verify_scheduled_prefixes(name, T):
     w = wl().make(name)
-    _say("verify scheduled %s" % name)
+    _say("verify scheduled %s T=%g" % (name, T))
     s = oracle.schedule_ref(w.c.numpy(), w.sps.numpy(), 0)
-    d = oracle.draft_ref(f64(w.U), None, None, w.x0.numpy(), 1.0, w.rng_seed, 0)
-    n_acc, tok, ref = _verify_case(w, 1.0, s["cu_seqlens"], d["x"], d["q_tok"], d["lse"])
-    rep = Report("verify %s" % name)
+    d = oracle.draft_ref(f64(w.U), None, None, w.x0.numpy(), T, w.rng_seed, 0)
+    n_acc, tok, ref = _verify_case(w, T, s["cu_seqlens"], d["x"], d["q_tok"], d["lse"])
+    rep = Report("verify %s T=%g" % (name, T))
     compare_verify(rep, n_acc, tok, ref)
     rep.check_near_ties()
     _say(str(rep) + " N=%d" % s["cu_seqlens"][-1])
