@@ -18,8 +18,9 @@ time), the dominant kernel's roofline (algorithmic bytes per launch / mean
 launch time from HIP events on the library's stream), the other workloads'
 rows (tiny step latency, the verify-only Qwen3-vocabulary workload, the
 DeepSeek-vocabulary and scheduler-stress workloads), a measured device copy
-bandwidth, a cold-cache step time, and the CPU oracle timed on the same
-workload with a process pool over requests.
+bandwidth, a cold-cache step time, the median and 10th / 90th percentiles
+of 50 back-to-back steps timed one by one, and the CPU oracle timed on the
+same workload with a process pool over requests.
 """
 import argparse
 import hashlib
@@ -62,8 +63,12 @@ def cpu_model():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: the GPU reaches its steady clock only after a few tens of
+    # milliseconds of this load (measured: 0.66 ms per step with 5 warm-up
+    # steps, 0.60-0.61 ms after 50 or more), so the warm-up covers that ramp;
+    # 100 timed steps take about 60 ms
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="full_step")
     ap.add_argument("--mode", type=int, default=0, help="0 early stop, 1 global, 2 top-K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,6 +183,18 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         warm.append(e0.elapsed_time(e1))
+    # the per-step distribution in the steady state: 50 steps back to back,
+    # an event pair around each (median, 10th and 90th percentiles)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(4000 + i)
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    step_dist = {"steps": len(per_step), "median_ms": round(per_step[len(per_step) // 2], 4),
+                 "p10_ms": round(per_step[len(per_step) // 10], 4),
+                 "p90_ms": round(per_step[(9 * len(per_step)) // 10], 4)}
     del flush
     copy_gbs = copy_bandwidth(torch, dev, calibrate=args.calibrate_copy)
 
@@ -220,6 +237,7 @@ def main():
            "roofline": roof, "kernels_us": {k: round(v["mean_us"], 2) for k, v in kernels.items()},
            "cold_cache_step_ms": round(sorted(cold)[len(cold) // 2], 4),
            "warm_single_step_ms": round(sorted(warm)[len(warm) // 2], 4),
+           "step_ms_distribution": step_dist,
            "library_build_id": ds.dspark_build_id()}
     if next_rows:
         out["next_rows"] = next_rows
