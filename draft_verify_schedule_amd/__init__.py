@@ -10,7 +10,8 @@ there is no fallback path.
 """
 
 _BINDING_NAMES = {
-    "dspark_markov_draft", "dspark_schedule", "dspark_schedule_async", "dspark_schedule_noalloc", "dspark_verify",
+    "dspark_markov_draft", "dspark_markov_draft_with_confidence",
+    "dspark_schedule", "dspark_schedule_async", "dspark_schedule_noalloc", "dspark_verify",
     "dspark_markov_draft_workspace_bytes", "dspark_schedule_workspace_bytes", "dspark_verify_workspace_bytes",
     "dspark_acceptance_label", "dspark_acceptance_label_workspace_bytes",
     "dspark_confidence_head", "dspark_sts_fit", "dspark_sts_fit_workspace_bytes",

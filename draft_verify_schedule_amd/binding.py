@@ -51,6 +51,10 @@ def load_library():
     lib.dspark_markov_draft.restype = c_int
     lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp, vp,
                                         c_u64, c_u64, vp, vp, vp, vp, c_size, vp]
+    lib.dspark_markov_draft_with_confidence.restype = c_int
+    lib.dspark_markov_draft_with_confidence.argtypes = [c_int, c_int, c_int, c_int, c_float, vp, c_int, vp, vp, vp,
+                                                        vp, c_u64, c_u64, vp, vp, vp, c_int, vp, c_int, vp, vp,
+                                                        c_float, vp, vp, vp, vp, c_size, vp]
     lib.dspark_markov_w2_frag_bytes.restype = c_size
     lib.dspark_markov_w2_frag_bytes.argtypes = [c_int, c_int]
     lib.dspark_markov_prepare_w2.restype = c_int
@@ -237,6 +241,51 @@ def dspark_markov_draft(U, W1, W2, x0, temperature, seed, step, out=None, worksp
     if st != 0:
         raise DSparkError("dspark_markov_draft", st)
     return x, q, lse
+
+
+def dspark_markov_draft_with_confidence(U, W1, W2, x0, temperature, seed, step, H, w_h, w_e, bias,
+                                        sts_temperature=None, out=None, workspace=None, w2f=None, logits_out=False):
+    """dspark_markov_draft plus the confidence head of every position,
+    evaluated inside the draft.  Arguments as for dspark_markov_draft, then
+    H [B, K, d] f32/bf16, w_h [d] f32, w_e [r] f32 (or None when W1 is None),
+    bias, sts_temperature [K] f32 or None.
+    Returns (x, q_tok, lse, c) [B, K], and the head's logits when logits_out.
+    """
+    lib = load_library()
+    B, K, V = U.shape
+    _check(U, "U")
+    r = 0
+    if W1 is not None or W2 is not None:
+        r = W1.shape[1]
+        _check(W1, "W1", torch.bfloat16, (V, r))
+        _check(W2, "W2", torch.bfloat16, (V, r))
+        _check(w_e, "w_e", torch.float32, (r,))
+    _check(x0, "x0", torch.int32, (B,))
+    _check(H, "H")
+    d = H.shape[2]
+    _check(H, "H", None, (B, K, d))
+    _check(w_h, "w_h", torch.float32, (d,))
+    if sts_temperature is not None:
+        _check(sts_temperature, "sts_temperature", torch.float32, (K,))
+    dev = U.device
+    if out is None:
+        out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev))
+    x, q, lse, c = out
+    z = torch.empty((B, K), dtype=torch.float32, device=dev) if logits_out else None
+    need = lib.dspark_markov_draft_workspace_bytes(B, K, V, r)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    st = lib.dspark_markov_draft_with_confidence(
+        B, K, V, r, float(temperature), _ptr(U), _dtype_code(U), _ptr(W1), _ptr(W2), _ptr(w2f), _ptr(x0),
+        int(seed), int(step), _ptr(x), _ptr(q), _ptr(lse), d, _ptr(H), _dtype_code(H), _ptr(w_h),
+        _ptr(w_e if r > 0 else None), float(bias), _ptr(sts_temperature), _ptr(c), _ptr(z), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise DSparkError("dspark_markov_draft_with_confidence", st)
+    return (x, q, lse, c, z) if logits_out else (x, q, lse, c)
 
 
 def dspark_schedule_workspace_bytes(R, K):

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "draft_head.hpp"
 #include "rnn.hpp"
 
 namespace dspark {
@@ -19,7 +20,8 @@ size_t draft_workspace_bytes(int B, int K, int V);
 size_t w2_swizzle_bytes(int V, int r);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
               const void* W2, const void* W2f, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out,
-              float* q_out, float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
+              float* q_out, float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream,
+              const DraftHead* head = nullptr);
 int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
 size_t schedule_workspace_bytes(int R, int K);
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
@@ -180,26 +182,67 @@ size_t dspark_markov_draft_workspace_bytes(int B, int K, int V, int r) {
   return dspark::draft_workspace_bytes(B, K, V) + dspark::w2_swizzle_bytes(V, r);
 }
 
-int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
-                        const void* W1, const void* W2, const void* W2f, const int32_t* x0, uint64_t seed,
-                        uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+// Checks of dspark_markov_draft's arguments, before any work: DSPARK_OK, or
+// the status to return (B == 0 returns DSPARK_OK through *empty).
+static int check_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
+                              const void* W1, const void* W2, const void* W2f, const int32_t* x0, int32_t* x_out,
+                              float* q_tok_out, float* lse_out, void* workspace, size_t workspace_bytes,
+                              bool* empty) {
+  *empty = false;
   if (B < 0 || K <= 0 || K > DSPARK_MAX_K || V <= 0 || !rank_ok(r)) return DSPARK_E_SHAPE;
   if (!is_dtype(u_dtype)) return DSPARK_E_DTYPE;
   if ((uint64_t)B * K * V * dtype_bytes(u_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)V * r * 2 >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if ((uint64_t)dspark::w2_swizzle_bytes(V, r) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
   if (!(temperature >= 0.f) || std::isinf(temperature)) return DSPARK_E_RANGE;
-  if (B == 0) return DSPARK_OK;  // empty batch
+  if (B == 0) {  // empty batch
+    *empty = true;
+    return DSPARK_OK;
+  }
   if (!U || !x0 || !x_out || !q_tok_out || !lse_out) return DSPARK_E_NULL;
   if (r > 0 && (!W1 || !W2)) return DSPARK_E_NULL;
   const size_t need = dspark::draft_workspace_bytes(B, K, V) + (W2f ? 0 : dspark::w2_swizzle_bytes(V, r));
   if (!workspace || workspace_bytes < need) return DSPARK_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return DSPARK_E_WORKSPACE;
   if (r > 0 && (!aligned16(W1) || !aligned16(W2) || !aligned16(W2f))) return DSPARK_E_RANGE;
+  return DSPARK_OK;
+}
+
+int dspark_markov_draft(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
+                        const void* W1, const void* W2, const void* W2f, const int32_t* x0, uint64_t seed,
+                        uint64_t step, int32_t* x_out, float* q_tok_out, float* lse_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  bool empty;
+  const int st = check_markov_draft(B, K, V, r, temperature, U, u_dtype, W1, W2, W2f, x0, x_out, q_tok_out, lse_out,
+                                    workspace, workspace_bytes, &empty);
+  if (st != DSPARK_OK || empty) return st;
   return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr,
                                       x0, seed, step, x_out, q_tok_out, lse_out, workspace, nullptr,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dspark_markov_draft_with_confidence(int B, int K, int V, int r, float temperature, const void* U, int u_dtype,
+                                        const void* W1, const void* W2, const void* W2f, const int32_t* x0,
+                                        uint64_t seed, uint64_t step, int32_t* x_out, float* q_tok_out,
+                                        float* lse_out, int d, const void* H, int h_dtype, const float* w_h,
+                                        const float* w_e, float bias, const float* sts_temperature, float* c_out,
+                                        float* logit_out, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty;
+  const int st = check_markov_draft(B, K, V, r, temperature, U, u_dtype, W1, W2, W2f, x0, x_out, q_tok_out, lse_out,
+                                    workspace, workspace_bytes, &empty);
+  if (st != DSPARK_OK) return st;
+  // the confidence head's checks (those of dspark_confidence_head)
+  if (d <= 0) return DSPARK_E_SHAPE;
+  if (!is_dtype(h_dtype)) return DSPARK_E_DTYPE;
+  if ((uint64_t)B * K * d * dtype_bytes(h_dtype) >= kMaxBufferBytes) return DSPARK_E_SHAPE;
+  if (!std::isfinite(bias)) return DSPARK_E_RANGE;
+  if (empty) return DSPARK_OK;
+  if (!H || !w_h || !c_out) return DSPARK_E_NULL;
+  if (r > 0 && !w_e) return DSPARK_E_NULL;
+  const dspark::DraftHead head{H, h_dtype == DSPARK_BF16, d, w_h, w_e, bias, sts_temperature, c_out, logit_out};
+  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr,
+                                      x0, seed, step, x_out, q_tok_out, lse_out, workspace, nullptr,
+                                      reinterpret_cast<hipStream_t>(stream), &head));
 }
 
 size_t dspark_rnn_w2_f16_bytes(int V, int r) {

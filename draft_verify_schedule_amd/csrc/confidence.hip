@@ -22,6 +22,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "head.hpp"
 #include "launch.hpp"
 
 namespace dspark {
@@ -48,46 +49,18 @@ __global__ __launch_bounds__(256) void confidence_head_kernel(HeadArgs a) {
   const int r = i / a.K, k = i - r * a.K;
   const int prev = k == 0 ? a.x0[r] : a.x[i - 1];
   const HT* h = reinterpret_cast<const HT*>(a.H) + (size_t)i * a.d;
-  float s = 0.f;
-  if constexpr (VEC) {
-    // 16-byte loads: lane takes 4 (f32) or 8 (bf16) consecutive elements per step
-    constexpr int E = 16 / sizeof(HT);
-    for (int j = lane * E; j < a.d; j += 64 * E) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(h + j);
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(a.w_h + j);
-      if constexpr (sizeof(HT) == 2) {
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(a.w_h + j + 4);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          s = fmaf(w0[2 * e], __uint_as_float(v[e] << 16), s);
-          s = fmaf(w0[2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), s);
-          s = fmaf(w1[2 * e], __uint_as_float(v[e + 2] << 16), s);
-          s = fmaf(w1[2 * e + 1], __uint_as_float(v[e + 2] & 0xFFFF0000u), s);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = fmaf(w0[e], __uint_as_float(v[e]), s);
-      }
-    }
-  } else {
-    for (int j = lane; j < a.d; j += 64) {
-      float hv;
-      if constexpr (sizeof(HT) == 2) hv = bf16_bits_to_f32(h[j]);
-      else hv = h[j];
-      s = fmaf(a.w_h[j], hv, s);
-    }
-  }
+  float s = head_hidden_part<HT, VEC>(h, a.w_h, a.d, lane);
   const bool ok = prev >= 0 && prev < a.V;
   if (a.r > 0 && ok) {
     const uint16_t* e = a.W1 + (size_t)prev * a.r;
-    for (int j = lane; j < a.r; j += 64) s = fmaf(a.w_e[j], bf16_bits_to_f32(e[j]), s);
+    const float* w_e = a.w_e;
+    s = head_markov_part(s, a.r, lane, [&](int t) { return w_e[lane + 64 * t]; }, [&](int j) { return e[j]; });
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  s = head_wave_sum(s);
   if (lane == 0) {
     const float z = s + a.bias;
     const float t = a.T ? a.T[k] : 1.f;
-    a.c_out[i] = ok ? 1.f / (1.f + expf(-z / t)) : NAN;
+    a.c_out[i] = ok ? head_sigmoid(z, t) : NAN;
     if (a.logit_out) a.logit_out[i] = ok ? z : NAN;
   }
 }

@@ -88,6 +88,24 @@ static void draft_cases() {
   EXPECT(dspark_markov_draft(B, K, V, r, 1.f, U.p, DSPARK_F32, W1.p, W2.p, W2f.p, x0.as<int32_t>(), 1, 2,
                              x.as<int32_t>(), q.as<float>(), l.as<float>(), ws.p, small, nullptr),
          DSPARK_OK);
+  // with the confidence head evaluated inside the draft
+  const int d = 96;
+  Buf H((size_t)B * K * d * 2), wh(d * 4), we(r * 4), c(B * K * 4), z(B * K * 4), T(K * 4);
+  auto head = [&](int b, int dd, int ht, float bias, const void* h, const float* w_e, float* c_out) {
+    return dspark_markov_draft_with_confidence(b, K, V, r, 1.f, U.p, DSPARK_F32, W1.p, W2.p, W2f.p, x0.as<int32_t>(),
+                                               1, 2, x.as<int32_t>(), q.as<float>(), l.as<float>(), dd, h, ht,
+                                               wh.as<float>(), w_e, bias, T.as<float>(), c_out, z.as<float>(), ws.p,
+                                               small, nullptr);
+  };
+  EXPECT(head(B, d, DSPARK_BF16, 0.5f, H.p, we.as<float>(), c.as<float>()), DSPARK_OK);
+  EXPECT(head(0, d, DSPARK_BF16, 0.5f, nullptr, nullptr, nullptr), DSPARK_OK);  // empty batch
+  EXPECT(head(B, 0, DSPARK_BF16, 0.5f, H.p, we.as<float>(), c.as<float>()), DSPARK_E_SHAPE);
+  EXPECT(head(B, INT_MAX, DSPARK_F32, 0.5f, H.p, we.as<float>(), c.as<float>()), DSPARK_E_SHAPE);
+  EXPECT(head(B, d, 7, 0.5f, H.p, we.as<float>(), c.as<float>()), DSPARK_E_DTYPE);
+  EXPECT(head(B, d, DSPARK_BF16, INFINITY, H.p, we.as<float>(), c.as<float>()), DSPARK_E_RANGE);
+  EXPECT(head(B, d, DSPARK_BF16, 0.5f, nullptr, we.as<float>(), c.as<float>()), DSPARK_E_NULL);
+  EXPECT(head(B, d, DSPARK_BF16, 0.5f, H.p, nullptr, c.as<float>()), DSPARK_E_NULL);
+  EXPECT(head(B, d, DSPARK_BF16, 0.5f, H.p, we.as<float>(), nullptr), DSPARK_E_NULL);
 }
 
 static void schedule_cases() {

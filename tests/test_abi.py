@@ -177,6 +177,34 @@ def test_draft_argument_errors(lib):
     assert call(wsb=ctypes.c_size_t(part)) == -5                                    # without it: too small
 
 
+def test_draft_with_confidence_argument_errors(lib):
+    """The draft's checks first, then the head's (those of dspark_confidence_head)."""
+    f = ctypes.c_float
+    ws = ctypes.c_size_t(1 << 30)
+
+    def call(B=4, K=7, V=1024, r=16, T=1.0, U=FAKE, W1=FAKE, x0=FAKE, d=64, H=FAKE, ht=1, wh=FAKE, we=FAKE, b=0.0,
+             c=FAKE, wsp=FAKE, wsb=ws):
+        return lib.dspark_markov_draft_with_confidence(B, K, V, r, f(T), U, 1, W1, FAKE, NULL, x0, ctypes.c_uint64(1),
+                                                       ctypes.c_uint64(0), FAKE, FAKE, FAKE, d, H, ht, wh, we, f(b),
+                                                       NULL, c, NULL, wsp, wsb, NULL)
+    assert call(K=17) == -2
+    assert call(r=12) == -2
+    assert call(T=-1.0) == -4
+    assert call(U=NULL) == -1
+    assert call(W1=NULL) == -1
+    assert call(wsb=ctypes.c_size_t(16)) == -5
+    assert call(d=0) == -2
+    assert call(ht=5) == -3
+    assert call(b=float("nan")) == -4
+    assert call(H=NULL) == -1
+    assert call(wh=NULL) == -1
+    assert call(c=NULL) == -1
+    assert call(we=NULL) == -1           # the Markov part needs w_e when r > 0
+    # empty batch: a no-op that still checks shapes and scalars
+    assert call(B=0, U=NULL, W1=NULL, x0=NULL, H=NULL, wh=NULL, we=NULL, c=NULL, wsp=NULL) == 0
+    assert call(B=0, d=0, U=NULL, H=NULL) == -2
+
+
 def test_prepare_w2_argument_errors(lib):
     V, r = 1000, 64
     need = lib.dspark_markov_w2_frag_bytes(V, r)

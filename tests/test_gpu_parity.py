@@ -658,6 +658,51 @@ def test_confidence_head_bad_previous_token():
     assert np.isnan(c[1, 2]) and np.all(np.isfinite(np.delete(c.ravel(), 5)))
 
 
+@pytest.mark.parametrize("name,T,h_dtype,d", [
+    ("tiny", 1.0, torch.bfloat16, 160), ("tiny", 0.0, torch.bfloat16, 160), ("tiny", 1.0, torch.float32, 160),
+    ("tiny", 1.0, torch.bfloat16, 157), ("tiny", 1.0, torch.bfloat16, 4104), ("tiny", 0.0, torch.float32, 157),
+    ("full_step", 1.0, torch.bfloat16, 4096), ("full_step", 0.0, torch.bfloat16, 4096)])
+def test_draft_with_confidence(name, T, h_dtype, d):
+    """The draft with the confidence head evaluated inside it: x, q_tok and
+    lse bit-equal to dspark_markov_draft's; c and the head's logits bit-equal
+    to dspark_confidence_head's on the drafted tokens, and within the head's
+    tolerance of the oracle.  Two requests have an invalid anchor (their
+    confidences are NaN).  Hidden widths: vector steps (160, 4096), wider
+    than the locate pass's prefetch (4104), and the element-wise path (157)."""
+    _say("draft with confidence %s T=%g %s d=%d" % (name, T, h_dtype, d))
+    w = wl().make(name, device=DEV)
+    B, K, V, r = w.B, w.K, w.V, w.r
+    g = torch.Generator().manual_seed(777 + d)
+    H = torch.randn((B, K, d), generator=g).to(h_dtype).to(DEV)
+    w_h = (torch.randn(d, generator=g) * 0.05).to(DEV)
+    w_e = (torch.randn(r, generator=g) * 2.0).to(DEV)
+    T_sts = torch.linspace(0.6, 1.8, K).to(DEV)
+    x0 = w.x0.clone()
+    x0[1] = -3
+    x0[B - 1] = V
+    x, q, lse, c, z = ds().dspark_markov_draft_with_confidence(
+        w.U, w.W1, w.W2, x0, T, 11, 2, H, w_h, w_e, 0.25, sts_temperature=T_sts, logits_out=True)
+    xs, qs, ls = ds().dspark_markov_draft(w.U, w.W1, w.W2, x0, T, 11, 2)
+    cs, zs = ds().dspark_confidence_head(H, w_h, w_e, 0.25, w.W1, x0, xs, V, sts_temperature=T_sts,
+                                         logits_out=True)
+    torch.cuda.synchronize()
+    bits = lambda t: t.cpu().view(torch.int32).numpy()
+    np.testing.assert_array_equal(x.cpu().numpy(), xs.cpu().numpy())
+    np.testing.assert_array_equal(bits(q), bits(qs))
+    np.testing.assert_array_equal(bits(lse), bits(ls))
+    np.testing.assert_array_equal(bits(c), bits(cs))
+    np.testing.assert_array_equal(bits(z), bits(zs))
+    c, z, xs = c.cpu().numpy(), z.cpu().numpy(), xs.cpu().numpy()
+    assert np.all(np.isnan(c[[1, B - 1]])) and np.all(np.isnan(z[[1, B - 1]]))
+    ok = np.setdiff1d(np.arange(B), [1, B - 1])
+    zr = oracle.confidence_logits_ref(f64(H)[ok], f64(w_h), f64(w_e), 0.25, f64(w.W1), x0.cpu().numpy()[ok], xs[ok])
+    cr = oracle.confidence_head_ref(f64(H)[ok], f64(w_h), f64(w_e), 0.25, f64(w.W1), x0.cpu().numpy()[ok], xs[ok],
+                                    f64(T_sts))
+    _say("  max |dz| %.2e, max |dc| %.2e" % (np.abs(z[ok] - zr).max(), np.abs(c[ok] - cr).max()))
+    np.testing.assert_allclose(z[ok], zr, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(c[ok], cr, rtol=0, atol=2e-6)
+
+
 def _sts_data(seed, N, K, T_true):
     rng = np.random.default_rng(seed)
     logits = rng.normal(1.5, 2.0, size=(N, K)).astype(np.float32)
