@@ -249,7 +249,8 @@ def dspark_markov_draft_with_confidence(U, W1, W2, x0, temperature, seed, step, 
     evaluated inside the draft.  Arguments as for dspark_markov_draft, then
     H [B, K, d] f32/bf16, w_h [d] f32, w_e [r] f32 (or None when W1 is None),
     bias, sts_temperature [K] f32 or None.
-    Returns (x, q_tok, lse, c) [B, K], and the head's logits when logits_out.
+    Returns (x, q_tok, lse, c) [B, K], and the head's logits when logits_out
+    (True, or a [B, K] f32 tensor to write them into).
     """
     lib = load_library()
     B, K, V = U.shape
@@ -274,7 +275,11 @@ def dspark_markov_draft_with_confidence(U, W1, W2, x0, temperature, seed, step, 
                torch.empty((B, K), dtype=torch.float32, device=dev),
                torch.empty((B, K), dtype=torch.float32, device=dev))
     x, q, lse, c = out
-    z = torch.empty((B, K), dtype=torch.float32, device=dev) if logits_out else None
+    if isinstance(logits_out, torch.Tensor):
+        _check(logits_out, "logits_out", torch.float32, (B, K))
+        z = logits_out
+    else:
+        z = torch.empty((B, K), dtype=torch.float32, device=dev) if logits_out else None
     need = lib.dspark_markov_draft_workspace_bytes(B, K, V, r)
     if workspace is None:
         workspace = _workspace(need, dev)
@@ -285,7 +290,7 @@ def dspark_markov_draft_with_confidence(U, W1, W2, x0, temperature, seed, step, 
         workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise DSparkError("dspark_markov_draft_with_confidence", st)
-    return (x, q, lse, c, z) if logits_out else (x, q, lse, c)
+    return (x, q, lse, c, z) if z is not None else (x, q, lse, c)
 
 
 def dspark_schedule_workspace_bytes(R, K):

@@ -12,7 +12,6 @@
 #include <string>
 #include <vector>
 
-#include "draft_head.hpp"
 #include "rnn.hpp"
 
 namespace dspark {
@@ -20,8 +19,7 @@ size_t draft_workspace_bytes(int B, int K, int V);
 size_t w2_swizzle_bytes(int V, int r);
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16, const void* W1,
               const void* W2, const void* W2f, const int32_t* x0, uint64_t seed, uint64_t step, int32_t* x_out,
-              float* q_out, float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream,
-              const DraftHead* head = nullptr);
+              float* q_out, float* lse_out, void* workspace, const RnnParams* rnn, hipStream_t stream);
 int run_w2_swizzle(const uint16_t* W2, void* out, int V, int r, int kc, bool f16, hipStream_t stream);
 size_t schedule_workspace_bytes(int R, int K);
 int run_schedule(int R, int K, const float* c, const double* sps, int mode, int capacity,
@@ -239,10 +237,16 @@ int dspark_markov_draft_with_confidence(int B, int K, int V, int r, float temper
   if (empty) return DSPARK_OK;
   if (!H || !w_h || !c_out) return DSPARK_E_NULL;
   if (r > 0 && !w_e) return DSPARK_E_NULL;
-  const dspark::DraftHead head{H, h_dtype == DSPARK_BF16, d, w_h, w_e, bias, sts_temperature, c_out, logit_out};
-  return hip_status(dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr,
-                                      x0, seed, step, x_out, q_tok_out, lse_out, workspace, nullptr,
-                                      reinterpret_cast<hipStream_t>(stream), &head));
+  // the head runs as its own launch right after the draft, on the drafted
+  // tokens: evaluated inside the draft's locate pass it cost more (its
+  // hidden-state row and w_h more than double that latency-bound pass's
+  // memory traffic)
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int rc = dspark::run_draft(B, K, V, r, temperature, U, u_dtype == DSPARK_BF16, W1, W2, r > 0 ? W2f : nullptr,
+                                   x0, seed, step, x_out, q_tok_out, lse_out, workspace, nullptr, s);
+  if (rc) return hip_status(rc);
+  return hip_status(dspark::run_confidence_head(B, K, d, r, V, H, h_dtype == DSPARK_BF16, w_h, r > 0 ? w_e : nullptr,
+                                                bias, W1, x0, x_out, sts_temperature, c_out, logit_out, s));
 }
 
 size_t dspark_rnn_w2_f16_bytes(int V, int r) {

@@ -22,7 +22,6 @@
 #include <math.h>
 
 #include "common.hpp"
-#include "head.hpp"
 #include "launch.hpp"
 
 namespace dspark {
@@ -49,18 +48,88 @@ __global__ __launch_bounds__(256) void confidence_head_kernel(HeadArgs a) {
   const int r = i / a.K, k = i - r * a.K;
   const int prev = k == 0 ? a.x0[r] : a.x[i - 1];
   const HT* h = reinterpret_cast<const HT*>(a.H) + (size_t)i * a.d;
-  float s = head_hidden_part<HT, VEC>(h, a.w_h, a.d, lane);
   const bool ok = prev >= 0 && prev < a.V;
-  if (a.r > 0 && ok) {
-    const uint16_t* e = a.W1 + (size_t)prev * a.r;
-    const float* w_e = a.w_e;
-    s = head_markov_part(s, a.r, lane, [&](int t) { return w_e[lane + 64 * t]; }, [&](int j) { return e[j]; });
+  float s = 0.f;
+  if constexpr (VEC) {
+    // 16-byte loads: lane takes 4 (f32) or 8 (bf16) consecutive elements per
+    // step.  The first kPre steps, and the Markov part's elements (r <= 256:
+    // at most 4 per lane), are all requested before the first product (one
+    // memory round trip for rows up to 64 * kPre * E wide); wider rows loop
+    // over the rest.  The products are taken in the same order either way.
+    constexpr int E = 16 / sizeof(HT);
+    constexpr int NW = sizeof(HT) == 2 ? 2 : 1;  // f32x4 of w_h per step
+    constexpr int kPre = 8;
+    u32x4 hv[kPre];
+    f32x4 hw[kPre][NW];
+#pragma unroll
+    for (int t = 0; t < kPre; ++t) {
+      const int j = lane * E + 64 * E * t;
+      if (j < a.d) {
+        hv[t] = *reinterpret_cast<const u32x4*>(h + j);
+#pragma unroll
+        for (int q = 0; q < NW; ++q) hw[t][q] = *reinterpret_cast<const f32x4*>(a.w_h + j + 4 * q);
+      }
+    }
+    float we[4];
+    uint32_t ev[4];
+    const bool markov = a.r > 0 && ok;
+    if (markov) {
+      const uint16_t* e = a.W1 + (size_t)prev * a.r;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = lane + 64 * t;
+        if (j < a.r) {
+          we[t] = a.w_e[j];
+          ev[t] = e[j];
+        }
+      }
+    }
+    auto step = [&](u32x4 v, const f32x4 (&w)[NW]) {
+      if constexpr (sizeof(HT) == 2) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          s = fmaf(w[0][2 * e], __uint_as_float(v[e] << 16), s);
+          s = fmaf(w[0][2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), s);
+          s = fmaf(w[NW - 1][2 * e], __uint_as_float(v[e + 2] << 16), s);
+          s = fmaf(w[NW - 1][2 * e + 1], __uint_as_float(v[e + 2] & 0xFFFF0000u), s);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(w[0][e], __uint_as_float(v[e]), s);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < kPre; ++t)
+      if (lane * E + 64 * E * t < a.d) step(hv[t], hw[t]);
+    for (int j = lane * E + 64 * E * kPre; j < a.d; j += 64 * E) {
+      f32x4 w[NW];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) w[q] = *reinterpret_cast<const f32x4*>(a.w_h + j + 4 * q);
+      step(*reinterpret_cast<const u32x4*>(h + j), w);
+    }
+    if (markov) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (lane + 64 * t < a.r) s = fmaf(we[t], bf16_bits_to_f32(ev[t]), s);
+    }
+  } else {
+    for (int j = lane; j < a.d; j += 64) {
+      float hv;
+      if constexpr (sizeof(HT) == 2) hv = bf16_bits_to_f32(h[j]);
+      else hv = h[j];
+      s = fmaf(a.w_h[j], hv, s);
+    }
+    if (a.r > 0 && ok) {
+      const uint16_t* e = a.W1 + (size_t)prev * a.r;
+      for (int j = lane; j < a.r; j += 64) s = fmaf(a.w_e[j], bf16_bits_to_f32(e[j]), s);
+    }
   }
-  s = head_wave_sum(s);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
   if (lane == 0) {
     const float z = s + a.bias;
     const float t = a.T ? a.T[k] : 1.f;
-    a.c_out[i] = ok ? head_sigmoid(z, t) : NAN;
+    a.c_out[i] = ok ? 1.f / (1.f + expf(-z / t)) : NAN;
     if (a.logit_out) a.logit_out[i] = ok ? z : NAN;
   }
 }

@@ -20,8 +20,6 @@
 #include <type_traits>
 
 #include "bias_tile.hpp"
-#include "draft_head.hpp"
-#include "head.hpp"
 #include "launch.hpp"
 #include "rnn.hpp"
 
@@ -48,18 +46,7 @@ struct DraftArgs {
   const float* O;          // RNN head: output parts [B, K, r] fp32, row b * K + k - 1 (else null)
   const uint16_t* W2h;     // RNN head: fp16 copy of W2t
   const uint16_t* W2s;     // Markov head: W2t rearranged into MFMA fragment order (w2_swizzle_kernel)
-  // confidence head evaluated by draft_locate (Markov head only; c_out null: off)
-  const void* hH;          // hidden states [B, K, hd]
-  const float* hw_h;       // [hd]
-  const float* hw_e;       // [r]
-  const float* hT;         // calibration temperatures [K], or null (T = 1)
-  float* c_out;            // [B, K]
-  float* c_logit_out;      // [B, K] or null
-  float hbias;
-  int hd;
-  int hmode;               // kHeadBf16Vec, kHeadBf16, kHeadF32Vec or kHeadF32
 };
-constexpr int kHeadBf16Vec = 0, kHeadBf16 = 1, kHeadF32Vec = 2, kHeadF32 = 3;
 
 // Epilogue of one group: z = base logits + bias for 16 consecutive columns of
 // one row per lane; the four lanes sharing a row (l, l^16, l^32, l^48) cover the
@@ -454,12 +441,10 @@ void draft_partials_kernel(DraftArgs a, int stage0, int nstages) {
 // crossing is broadcast; then each lane re-evaluates one of the chosen
 // slice's 64 logits and a wave scan of their masses picks the token.  No
 // barrier and two dependent memory round trips (the partials, then the
-// slice's base logits and W2 block).  HEAD: the pass also evaluates the
-// confidence head of its position (its inputs requested ahead of the
-// partials; the same arithmetic as the standalone head).
+// slice's base logits and W2 block).
 constexpr int kLocRun = 40;
 
-template <typename UT, bool GREEDY, bool HEAD = false>
+template <typename UT, bool GREEDY>
 __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
@@ -476,34 +461,6 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
   // are in flight
   __shared__ u32x4 sh_row[kMaxRankRow];
   const bool prev_ok = prev >= 0 && prev < a.V;
-  // The confidence head of this position, when requested (Markov head): its
-  // hidden-state row, w_h and w_e are requested before the slice partials,
-  // so that the hidden-state products are summed while the partials are in
-  // flight; the Markov part uses the previous token's W1 row, which this
-  // pass stages in LDS for its re-scan anyway.
-  constexpr bool head = HEAD;
-  constexpr int kHeadPre = 8;  // vector steps requested up front (bf16 rows up to 4096 wide)
-  u32x4 hv[kHeadPre];
-  f32x4 hw[kHeadPre][2];
-  float hwe[kHeadMarkovSteps];
-  if (head) {
-    if (a.hmode == kHeadBf16Vec) {
-      // steps past the row read zeros and are not summed
-      const rsrc_t hr = make_rsrc(static_cast<const uint16_t*>(a.hH) + out * a.hd, (uint32_t)a.hd * 2u);
-      const rsrc_t wr = make_rsrc(a.hw_h, (uint32_t)a.hd * 4u);
-#pragma unroll
-      for (int t = 0; t < kHeadPre; ++t) {
-        const uint32_t j = (uint32_t)(lane * 8 + 512 * t);
-        hv[t] = buffer_load16(hr, 2u * j, 0u);
-        hw[t][0] = __builtin_bit_cast(f32x4, buffer_load16(wr, 4u * j, 0u));
-        hw[t][1] = __builtin_bit_cast(f32x4, buffer_load16(wr, 4u * j + 16u, 0u));
-      }
-    }
-    const rsrc_t er = make_rsrc(a.hw_e, (uint32_t)(a.hw_e ? a.r : 0) * 4u);
-#pragma unroll
-    for (int t = 0; t < kHeadMarkovSteps; ++t)
-      hwe[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(er, (int)(4 * (lane + 64 * t)), 0, 0));
-  }
   float2 p[kLocRun];
   if (in_regs) {
     // every load is issued (no branch): slots past the lane's run read zeros
@@ -517,7 +474,7 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
   // prev; no branch: a lane past r, or a request without a bias row, reads
   // zeros) and written to LDS once needed
   u32x4 row_in = u32x4{0u, 0u, 0u, 0u};
-  if (!GREEDY || head) {
+  if constexpr (!GREEDY) {
     const bool has_row = a.r > 0 && prev_ok;
     const int n = a.O ? a.r / 4 : a.r / 8;
     const rsrc_t rr = a.O ? make_rsrc(a.O + out * a.r, (uint32_t)a.r * 4u)
@@ -525,43 +482,6 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
     row_in = buffer_load16(rr, (has_row && lane < n) ? (uint32_t)lane * 16u : 0xFFFFFFF0u, 0u);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // the head's hidden-state part: waits for its own loads only, which were
-  // requested before the partials
-  float hs = 0.f;
-  if (head) {
-    const size_t hrow = out * (size_t)a.hd;
-    if (a.hmode == kHeadBf16Vec) {
-#pragma unroll
-      for (int t = 0; t < kHeadPre; ++t)
-        if (lane * 8 + 512 * t < a.hd) hs = head_step_bf16(hs, hv[t], hw[t][0], hw[t][1]);
-      const uint16_t* h = static_cast<const uint16_t*>(a.hH) + hrow;
-      for (int j = lane * 8 + 512 * kHeadPre; j < a.hd; j += 512)  // rows wider than the prefetch
-        hs = head_step_bf16(hs, *reinterpret_cast<const u32x4*>(h + j), *reinterpret_cast<const f32x4*>(a.hw_h + j),
-                            *reinterpret_cast<const f32x4*>(a.hw_h + j + 4));
-    } else if (a.hmode == kHeadBf16) {
-      hs = head_hidden_part<uint16_t, false>(static_cast<const uint16_t*>(a.hH) + hrow, a.hw_h, a.hd, lane);
-    } else if (a.hmode == kHeadF32Vec) {
-      hs = head_hidden_part<float, true>(static_cast<const float*>(a.hH) + hrow, a.hw_h, a.hd, lane);
-    } else {
-      hs = head_hidden_part<float, false>(static_cast<const float*>(a.hH) + hrow, a.hw_h, a.hd, lane);
-    }
-  }
-  // the head's Markov part (from the W1 row staged in sh_row), the wave sum
-  // and the confidence; NaN without a valid previous token
-  auto head_finish = [&](bool ok) {
-    float s = hs;
-    if (ok && a.r > 0) {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(sh_row);
-      s = head_markov_part(s, a.r, lane, [&](int t) { return hwe[t]; }, [&](int j) { return e[j]; });
-    }
-    s = head_wave_sum(s);
-    if (lane == 0) {
-      const float z = s + a.hbias;
-      const float t = a.hT ? a.hT[a.k - 1] : 1.f;
-      a.c_out[out] = ok ? head_sigmoid(z, t) : NAN;
-      if (a.c_logit_out) a.c_logit_out[out] = ok ? z : NAN;
-    }
-  };
   if (in_regs) {
 #pragma unroll
     for (int i = 0; i < kLocRun; ++i)
@@ -573,7 +493,6 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
       a.q_out[out] = NAN;
       a.lse_out[out] = NAN;
     }
-    if (head) head_finish(false);
     return;
   }
   // the decision uniform, computed while the loads are in flight
@@ -599,10 +518,6 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
       a.x_out[out] = idx;
       a.q_out[out] = 1.0f;
       a.lse_out[out] = m;
-    }
-    if (head) {
-      sh_row[lane] = row_in;  // the W1 row (in-order LDS access within the wave: no barrier)
-      head_finish(true);
     }
     return;
   }
@@ -745,7 +660,6 @@ __global__ __launch_bounds__(64) void draft_locate_kernel(DraftArgs a) {
     a.q_out[out] = fast_exp2(fmaf(zx, a.c2, -M)) / (float)S;
     a.lse_out[out] = (M + fast_log2((float)S)) * kLn2;
   }
-  if (head) head_finish(true);  // sh_row holds the W1 row
 }
 
 // Full 128-row stages and the trailing partial stage (B not a multiple of
@@ -873,8 +787,7 @@ static int run_draft_typed(DraftArgs a, bool vec, bool make_w2s, const RnnParams
     }
     int rc = vec ? dispatch_kc<UT, true, GREEDY>(a, stream) : dispatch_kc<UT, false, GREEDY>(a, stream);
     if (rc) return rc;
-    rc = a.c_out ? launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY, true>, dim3(a.B), dim3(64), stream, a)
-                 : launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3(a.B), dim3(64), stream, a);
+    rc = launch_kernel("draft_locate", draft_locate_kernel<UT, GREEDY>, dim3(a.B), dim3(64), stream, a);
     if (rc) return rc;
   }
   return 0;
@@ -953,22 +866,8 @@ size_t draft_workspace_bytes(int B, int K, int V) {
 int run_draft(int B, int K, int V, int r, float temperature, const void* U, bool u_bf16,
               const void* W1, const void* W2, const void* W2f, const int32_t* x0, uint64_t seed, uint64_t step,
               int32_t* x_out, float* q_out, float* lse_out, void* workspace, const RnnParams* rnn,
-              hipStream_t stream, const DraftHead* head) {
+              hipStream_t stream) {
   DraftArgs a{};
-  if (head) {  // the confidence head, evaluated by draft_locate at each position
-    a.hH = head->H;
-    a.hd = head->d;
-    a.hw_h = head->w_h;
-    a.hw_e = r > 0 ? head->w_e : nullptr;
-    a.hbias = head->bias;
-    a.hT = head->T;
-    a.c_out = head->c_out;
-    a.c_logit_out = head->logit_out;
-    // vector steps: rows and w_h 16-byte aligned (the standalone head's rule)
-    const bool hvec = head->d % (head->h_bf16 ? 8 : 4) == 0 && reinterpret_cast<uintptr_t>(head->H) % 16 == 0 &&
-                      reinterpret_cast<uintptr_t>(head->w_h) % 16 == 0;
-    a.hmode = head->h_bf16 ? (hvec ? kHeadBf16Vec : kHeadBf16) : (hvec ? kHeadF32Vec : kHeadF32);
-  }
   a.U = U;
   a.W1 = reinterpret_cast<const uint16_t*>(W1);
   a.W2t = reinterpret_cast<const uint16_t*>(W2);

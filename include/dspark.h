@@ -148,19 +148,18 @@ int dspark_markov_draft(int B, int K, int V, int r, float temperature,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
- * Markov draft with the confidence head of every position.  DSpark paper
- * sections 3.1 (Markov head) and 3.2.1 (Confidence Head: the head reads the
- * Markov feature of the previously sampled token, so c_k is known as soon as
- * x_{k-1} is drawn); "Speculative decoding, from zero to DSpark", section 8.
+ * Markov draft with the confidence head of every position, in one call.
+ * DSpark paper sections 3.1 (Markov head) and 3.2.1 (Confidence Head: the
+ * head reads the Markov feature of the previously sampled token);
+ * "Speculative decoding, from zero to DSpark", section 8.
  *
  * The outputs of dspark_markov_draft (same arguments, same meaning, bit for
  * bit the same values) and those of dspark_confidence_head on the drafted
  * tokens (x0, x_out), bit for bit the same values as that call:
  *   z[b, k] = w_h . H[b, k] + w_e . W1[x_{b,k-1}] + bias,  x_{b,0} = x0[b]
  *   c_out[b, k] = sigmoid(z[b, k] / T_k)
- * computed at each position by the pass that draws x_{b,k-1}, while its
- * softmax partials are in flight, instead of in a launch of its own after
- * the draft.  Head inputs: d the hidden width; H [B, K, d] (h_dtype);
+ * The head runs as one launch after the draft's last position, on the same
+ * stream.  Head inputs: d the hidden width; H [B, K, d] (h_dtype);
  * w_h [d] f32; w_e [r] f32 (unused when r == 0); sts_temperature [K] f32 or
  * NULL (T_k = 1).  Head outputs: c_out [B, K] f32; logit_out [B, K] f32 (z)
  * or NULL.  Limits and data errors: those of both calls (a previous token

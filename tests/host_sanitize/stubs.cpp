@@ -11,7 +11,6 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../draft_verify_schedule_amd/csrc/draft_head.hpp"
 #include "../../draft_verify_schedule_amd/csrc/rnn.hpp"
 
 std::atomic<int> g_launches{0};
@@ -82,8 +81,7 @@ void rnn_bind_workspace(RnnParams& p, void* ws) {
 }
 
 int run_draft(int, int, int, int, float, const void*, bool, const void*, const void*, const void*, const int32_t*,
-              uint64_t, uint64_t, int32_t*, float*, float*, void*, const RnnParams*, hipStream_t s,
-              const DraftHead*) {
+              uint64_t, uint64_t, int32_t*, float*, float*, void*, const RnnParams*, hipStream_t s) {
   return launch("draft_partials", s) | launch("draft_locate", s);
 }
 int run_w2_swizzle(const uint16_t*, void*, int, int, int, bool, hipStream_t s) { return launch("w2_swizzle", s); }

@@ -4,9 +4,9 @@ on which row stage of the sweep it falls in.
 
 * Canaries: every output and workspace lives in the middle of a buffer whose
   4 KB margins hold 0xA5; after the call the margins must be untouched
-  (draft, schedule with and without a workspace, verify from logits with
-  margins, acceptance label, RNN draft and verify, prepared weights,
-  uniforms).
+  (draft, draft with the confidence head, schedule with and without a
+  workspace, verify from logits with margins, acceptance label, RNN draft
+  and verify, prepared weights, uniforms).
 * Determinism: the draft -> schedule -> verify -> label chain run twice on
   the same inputs gives the same bits.
 * Batch split: the draft of B = 384 bf16 requests sweeps requests 0..255 as
@@ -99,6 +99,19 @@ def _chain(w, step, lib, guarded=None):
         w.U, w.W1, w.W2, w.x0, w.temperature, w.rng_seed, step,
         out=(g((B, K), torch.int32, "x"), g((B, K), torch.float32, "q"), g((B, K), torch.float32, "lse")),
         workspace=gw(lib.dspark_markov_draft_workspace_bytes(B, K, V, 0), "draft workspace"), w2f=w2f)
+    # the same draft with the confidence head inside it (hidden width 264:
+    # vector steps, the last one partial for some lanes)
+    gen = torch.Generator().manual_seed(606)
+    d = 264
+    H = (torch.randn((B, K, d), generator=gen)).to(torch.bfloat16).to(DEV)
+    w_h = (torch.randn(d, generator=gen) * 0.05).to(DEV)
+    w_e = (torch.randn(r, generator=gen) * 0.5).to(DEV)
+    xh, qh, lh, c, z = ds().dspark_markov_draft_with_confidence(
+        w.U, w.W1, w.W2, w.x0, w.temperature, w.rng_seed, step, H, w_h, w_e, 0.1,
+        out=(g((B, K), torch.int32, "x (with head)"), g((B, K), torch.float32, "q (with head)"),
+             g((B, K), torch.float32, "lse (with head)"), g((B, K), torch.float32, "c")),
+        workspace=gw(lib.dspark_markov_draft_workspace_bytes(B, K, V, 0), "draft workspace (with head)"), w2f=w2f,
+        logits_out=g((B, K), torch.float32, "head logits"))
     sched_out = {"a": g((B, K), torch.float32, "a"), "ell": g((B,), torch.int32, "ell"),
                  "cu_seqlens": g((B + 1,), torch.int32, "cu"), "n_admitted": g((1,), torch.int32, "n"),
                  "theta": g((1,), torch.float64, "theta")}
@@ -127,7 +140,8 @@ def _chain(w, step, lib, guarded=None):
     torch.cuda.synchronize()
     return {"x": x, "q": q, "lse": lse, "a": s["a"], "ell": s["ell"], "cu": cu, "n": s["n_admitted"],
             "theta": s["theta"], "ell_global": s2["ell"], "n_acc": n_acc, "tok": tok, "mm": mm, "n_acc2": n_acc2,
-            "tok2": tok2, "mm2": mm2, "label": c_lab, "u": u}
+            "tok2": tok2, "mm2": mm2, "label": c_lab, "u": u, "x_head": xh, "q_head": qh, "lse_head": lh, "c": c,
+            "z": z}
 
 
 def test_canaries_markov_chain():
