@@ -703,6 +703,25 @@ def test_draft_with_confidence(name, T, h_dtype, d):
     np.testing.assert_allclose(c[ok], cr, rtol=0, atol=2e-6)
 
 
+def test_draft_with_confidence_without_markov_head():
+    """r = 0 (no W1, W2 or w_e): the head is w_h . h + bias alone; outputs
+    bit-equal to the two separate calls, and the oracle's."""
+    g = torch.Generator().manual_seed(909)
+    B, K, V, d = 6, 4, 700, 96
+    U = (torch.randn((B, K, V), generator=g) * 2).to(DEV)
+    x0 = torch.randint(0, V, (B,), generator=g, dtype=torch.int32).to(DEV)
+    H = torch.randn((B, K, d), generator=g).to(torch.bfloat16).to(DEV)
+    w_h = (torch.randn(d, generator=g) * 0.1).to(DEV)
+    x, q, lse, c = ds().dspark_markov_draft_with_confidence(U, None, None, x0, 1.0, 3, 0, H, w_h, None, -0.2)
+    xs, qs, ls = ds().dspark_markov_draft(U, None, None, x0, 1.0, 3, 0)
+    cs = ds().dspark_confidence_head(H, w_h, None, -0.2, None, x0, xs, V)
+    torch.cuda.synchronize()
+    for a, b in ((x, xs), (q, qs), (lse, ls), (c, cs)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    cr = oracle.confidence_head_ref(f64(H), f64(w_h), None, -0.2, None, x0.cpu().numpy(), xs.cpu().numpy())
+    np.testing.assert_allclose(c.cpu().numpy(), cr, rtol=0, atol=2e-6)
+
+
 def _sts_data(seed, N, K, T_true):
     rng = np.random.default_rng(seed)
     logits = rng.normal(1.5, 2.0, size=(N, K)).astype(np.float32)
