@@ -244,8 +244,8 @@ struct EStageLoad {
   }
 };
 
-template <int KC, typename PrevFn>
-__device__ __forceinline__ void stage_e(EStage<KC>& st, const uint16_t* __restrict__ W1, int r,
+template <int KC, typename PrevFn, int NR>
+__device__ __forceinline__ void stage_e(EStage<KC, false, NR>& st, const uint16_t* __restrict__ W1, int r,
                                         int V, int row0, int nrows, PrevFn prev_of) {
   EStageLoad<KC> ld;
   ld.load(W1, r, V, row0, nrows, prev_of);

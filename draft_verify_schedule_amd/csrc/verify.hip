@@ -710,7 +710,10 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
 // Aligned-row variant: only the compacted correcting requests stream.
 // Persistent workgroups (about two per CU) pick a 128-request stage of the
 // list and a range of 64-column blocks at run time, from the list length the
-// decide kernel left on the device.  Per request, the row offsets and the
+// decide kernel left on the device.  G = 16 (bf16 Markov verification with
+// more than 128 requests): 256-request stages swept by one 8-wave workgroup
+// per CU, so each W2 block a wave loads serves twice the rows and a typical
+// list of a few hundred corrections is one stage.  Per request, the row offsets and the
 // two log-normalisers sit in LDS; target and draft rows go through buffer
 // resources; each draft row seeds the MFMA accumulators, so the MFMAs leave
 // z = D + bias directly.
@@ -719,14 +722,19 @@ struct ResidualRow {
   float lp, lq;           // log2-normalisers of p and q
 };
 
-template <typename PT, typename DT, int KC, bool LABEL = false, bool ROWS = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename PT, typename DT, int KC, bool LABEL = false, bool ROWS = false, int G = kGroupsPerWG>
+__global__ __launch_bounds__(G * 32) __attribute__((amdgpu_waves_per_eu(2)))
 void verify_residual_stream_kernel(VerifyArgs a) {
+  constexpr int kRows = 16 * G;  // requests per stage
+  constexpr int kWaves = G / 2;  // waves per workgroup
+  static_assert(G == kGroupsPerWG || (G == 2 * kGroupsPerWG && !LABEL && !ROWS && KC > 0 &&
+                                      std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>),
+                "256-request stages: bf16 Markov verification only");
   // LABEL: one item per (request, position) pair, item i = r * K + k, with
   // target row i and draft row i; otherwise the compacted correcting requests
   const int count = LABEL ? a.R * a.K : *a.rej_count;
   if (count <= 0) return;
-  const int active = (count + kStageRows - 1) / kStageRows;
+  const int active = (count + kRows - 1) / kRows;
   const int slots = gridDim.x / 8;
   const int per_stage = slots / active;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -735,16 +743,16 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   const int nsplit = per_stage * 8, split = sp * 8 + xcd;
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const int row0 = stage * kStageRows;
-  const int nrows = min(kStageRows, count - row0);
+  const int row0 = stage * kRows;
+  const int nrows = min(kRows, count - row0);
   const int ngroups = (nrows + 15) / 16;
   const int nblocks = (a.V + kWaveCols - 1) / kWaveCols;
   const int blk_begin = (int)((int64_t)split * nblocks / nsplit);
   const int blk_end = (int)((int64_t)(split + 1) * nblocks / nsplit);
 
-  __shared__ ResidualRow rows[kStageRows];
-  __shared__ EStage<(KC > 0 ? KC : 1), ROWS> st;
-  if (threadIdx.x < kStageRows) {
+  __shared__ ResidualRow rows[kRows];
+  __shared__ EStage<(KC > 0 ? KC : 1), ROWS, kRows> st;
+  if (threadIdx.x < kRows) {
     ResidualRow rr{0u, 0u, 0.f, 0.f};
     if ((int)threadIdx.x < nrows) {
       const int item = row0 + threadIdx.x;
@@ -803,7 +811,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   // The lanes end up with the bytes the MFMA-layout loads would have read.
   // One tile serves both rows: LDS operations of a wave complete in order.
   constexpr bool CX = std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>;
-  __shared__ u32x4 xtile[CX ? 4 : 1][16 * 9];
+  __shared__ u32x4 xtile[CX ? kWaves : 1][16 * 9];
   auto cload = [&](GroupLogitsBuf<PT>& pb, GroupLogitsBuf<DT>& db, int g, int blk) {
     if constexpr (CX) {
       const ResidualRow r0 = rows[16 * g + (lane >> 3)], r1 = rows[16 * g + 8 + (lane >> 3)];
@@ -837,8 +845,8 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   const bool xpf = PF && ngroups % 2 == 0;
   bool first = true;
   double lacc0 = 0.0, lacc1 = 0.0;  // LABEL: this wave's sums for rows lane, 64 + lane
-  for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
-    const int nxt = blk + 4;
+  for (int blk = blk_begin + wave; blk < blk_end; blk += kWaves) {
+    const int nxt = blk + kWaves;
     const bool has_next = nxt < blk_end;
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
@@ -937,7 +945,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   if constexpr (LABEL) {
     // one partial per (job, item), jobs = (split, wave); written even when the
     // wave had no block (zeros), so every partial the reduction reads is set
-    const size_t job = (size_t)split * 4 + wave;
+    const size_t job = (size_t)split * kWaves + wave;
     if (lane < nrows) a.lpart[job * count + row0 + lane] = lacc0;
     if (64 + lane < nrows) a.lpart[job * count + row0 + 64 + lane] = lacc1;
   }
@@ -1466,8 +1474,10 @@ static int dispatch_residual(const VerifyArgs& a, hipStream_t stream) {
 }
 
 // Grid of the streamed residual pass over `rows` items: about two workgroups
-// per CU, and enough 8-slot rows for every stage.
-static int residual_stream_slots(int rows) { return std::max(64, (rows + kStageRows - 1) / kStageRows); }
+// per CU (one for 256-row stages), and enough 8-slot rows for every stage.
+static int residual_stream_slots(int rows, int stage_rows = kStageRows) {
+  return std::max(stage_rows == kStageRows ? 64 : 32, (rows + stage_rows - 1) / stage_rows);
+}
 
 // Jobs (workgroup split x wave) of one stage in that grid, each writing one
 // partial per item of the acceptance label: the kernel's own split arithmetic.
@@ -1479,6 +1489,13 @@ static int label_jobs(int N) {
 template <typename PT, typename DT, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   const int rows = LABEL ? a.R * a.K : a.R;
+  if constexpr (!LABEL && !ROWS && KC > 0 && std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>) {
+    if (rows > kStageRows) {  // more possible corrections than one 128-request stage
+      constexpr int G = 2 * kGroupsPerWG;
+      return launch_kernel("verify_residual", verify_residual_stream_kernel<PT, DT, KC, false, false, G>,
+                           dim3(8 * residual_stream_slots(rows, 16 * G)), dim3(32 * G), stream, a);
+    }
+  }
   const int slots = residual_stream_slots(rows);
   return launch_kernel(LABEL ? "label_residual" : "verify_residual",
                        verify_residual_stream_kernel<PT, DT, KC, LABEL, ROWS>, dim3(8 * slots), dim3(256), stream, a);
