@@ -727,9 +727,9 @@ __global__ __launch_bounds__(G * 32) __attribute__((amdgpu_waves_per_eu(2)))
 void verify_residual_stream_kernel(VerifyArgs a) {
   constexpr int kRows = 16 * G;  // requests per stage
   constexpr int kWaves = G / 2;  // waves per workgroup
-  static_assert(G == kGroupsPerWG || (G == 2 * kGroupsPerWG && !LABEL && !ROWS && KC > 0 &&
-                                      std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>),
-                "256-request stages: bf16 Markov verification only");
+  static_assert(G == kGroupsPerWG || (G == 2 * kGroupsPerWG && !ROWS && KC > 0 && std::is_same_v<PT, uint16_t> &&
+                                      std::is_same_v<DT, uint16_t>),
+                "256-request stages: bf16 rows of the Markov head only");
   // LABEL: one item per (request, position) pair, item i = r * K + k, with
   // target row i and draft row i; otherwise the compacted correcting requests
   const int count = LABEL ? a.R * a.K : *a.rej_count;
@@ -844,7 +844,9 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   GroupLogitsBuf<DT> db0, db1;
   const bool xpf = PF && ngroups % 2 == 0;
   bool first = true;
-  double lacc0 = 0.0, lacc1 = 0.0;  // LABEL: this wave's sums for rows lane, 64 + lane
+  // LABEL: this wave's sums for rows lane, 64 + lane, ... of the stage (named
+  // registers: an array indexed by the group stayed in scratch memory)
+  double lacc0 = 0.0, lacc1 = 0.0, lacc2 = 0.0, lacc3 = 0.0;
   for (int blk = blk_begin + wave; blk < blk_end; blk += kWaves) {
     const int nxt = blk + kWaves;
     const bool has_next = nxt < blk_end;
@@ -899,11 +901,18 @@ void verify_residual_stream_kernel(VerifyArgs a) {
       s = rows_sum(s);
       if constexpr (LABEL) {
         // the label needs each item's total only: group g's row sums are kept
-        // by the lanes of quarter g % 4 (lane l ends with rows l and 64 + l of
-        // the stage), added in block order in fp64
+        // by the lanes of quarter g % 4 (lane l ends with rows l, 64 + l, ...
+        // of the stage), added in block order in fp64
         const double ds = (lane >> 4) == (g & 3) ? (double)s : 0.0;
-        if (g < 4) lacc0 += ds;
-        else lacc1 += ds;
+        // rows 64 q + lane come from groups 4 q .. 4 q + 3 (the sums are >= 0,
+        // so adding 0.0 to the other accumulators leaves them unchanged)
+        const int q = g >> 2;
+        lacc0 += q == 0 ? ds : 0.0;
+        lacc1 += q == 1 ? ds : 0.0;
+        if constexpr (G > 8) {
+          lacc2 += q == 2 ? ds : 0.0;
+          lacc3 += q == 3 ? ds : 0.0;
+        }
       } else if (lv && lane < 16) {
         a.rpart[(size_t)a.rej_list[row0 + 16 * g + lane] * a.ns64 + blk] = s;
       }
@@ -946,8 +955,10 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     // one partial per (job, item), jobs = (split, wave); written even when the
     // wave had no block (zeros), so every partial the reduction reads is set
     const size_t job = (size_t)split * kWaves + wave;
-    if (lane < nrows) a.lpart[job * count + row0 + lane] = lacc0;
-    if (64 + lane < nrows) a.lpart[job * count + row0 + 64 + lane] = lacc1;
+    const double sums[4] = {lacc0, lacc1, lacc2, lacc3};
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q)
+      if (64 * q + lane < nrows) a.lpart[job * count + row0 + 64 * q + lane] = sums[q];
   }
 }
 
@@ -1479,20 +1490,30 @@ static int residual_stream_slots(int rows, int stage_rows = kStageRows) {
   return std::max(stage_rows == kStageRows ? 64 : 32, (rows + stage_rows - 1) / stage_rows);
 }
 
+// Rows per stage of the streamed residual pass over `rows` items: 256 for
+// bf16 rows of the Markov head (big) when there are more than 128, else 128.
+static int residual_stage_rows(int rows, bool big) { return big && rows > kStageRows ? 2 * kStageRows : kStageRows; }
+
 // Jobs (workgroup split x wave) of one stage in that grid, each writing one
-// partial per item of the acceptance label: the kernel's own split arithmetic.
-static int label_jobs(int N) {
-  const int active = (N + kStageRows - 1) / kStageRows;
-  return residual_stream_slots(N) / active * 8 * 4;
+// partial per item of the acceptance label: the kernel's own split arithmetic
+// (stage_rows / 32 waves per workgroup).
+static int label_jobs(int N, int stage_rows) {
+  const int active = (N + stage_rows - 1) / stage_rows;
+  return residual_stream_slots(N, stage_rows) / active * 8 * (stage_rows / 32);
+}
+// room for either stage size (the workspace query does not see the dtypes)
+static int label_jobs_max(int N) {
+  return std::max(label_jobs(N, kStageRows), label_jobs(N, residual_stage_rows(N, true)));
 }
 
 template <typename PT, typename DT, int KC, bool LABEL, bool ROWS = false>
 static int launch_residual_stream(const VerifyArgs& a, hipStream_t stream) {
   const int rows = LABEL ? a.R * a.K : a.R;
-  if constexpr (!LABEL && !ROWS && KC > 0 && std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>) {
-    if (rows > kStageRows) {  // more possible corrections than one 128-request stage
+  if constexpr (!ROWS && KC > 0 && std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>) {
+    if (residual_stage_rows(rows, true) != kStageRows) {  // more items than one 128-row stage
       constexpr int G = 2 * kGroupsPerWG;
-      return launch_kernel("verify_residual", verify_residual_stream_kernel<PT, DT, KC, false, false, G>,
+      return launch_kernel(LABEL ? "label_residual" : "verify_residual",
+                           verify_residual_stream_kernel<PT, DT, KC, LABEL, false, G>,
                            dim3(8 * residual_stream_slots(rows, 16 * G)), dim3(32 * G), stream, a);
     }
   }
@@ -1657,7 +1678,7 @@ size_t label_workspace_bytes(int B, int K, int V, int r) {
   const size_t nsP = (size_t)(((int64_t)V + kRowSlice - 1) / kRowSlice), ns64 = (size_t)(((int64_t)V + kWaveCols - 1) / kWaveCols);
   // the residual region holds per-slice masses (unaligned rows) or the
   // streamed pass's per-(job, item) sums
-  const size_t resid = std::max(N * ns64 * sizeof(float), (size_t)label_jobs((int)N) * N * sizeof(double));
+  const size_t resid = std::max(N * ns64 * sizeof(float), (size_t)label_jobs_max((int)N) * N * sizeof(double));
   return align256(N * nsP * sizeof(float2)) + align256(N * sizeof(float2)) + align256(resid) + w2_swizzle_bytes(V, r);
 }
 
@@ -1685,7 +1706,8 @@ static int run_label_typed(VerifyArgs& a, float* c_out, bool greedy, bool vec_p,
   if (vec_p && vec_d) {
     // per-(job, item) sums instead of per-slice masses, in the same region
     a.lpart = reinterpret_cast<double*>(a.rpart);
-    a.njobs = label_jobs(a.N);
+    constexpr bool big = std::is_same_v<PT, uint16_t> && std::is_same_v<DT, uint16_t>;
+    a.njobs = label_jobs(a.N, residual_stage_rows(a.N, big && a.r > 0 && !a.O));
     rc = dispatch_residual_stream<PT, DT, true>(a, stream);
     if (rc) return rc;
     return launch_kernel("label_reduce", label_reduce_jobs_kernel, dim3((a.N + 255) / 256), b256, stream, a, c_out);
@@ -1731,7 +1753,7 @@ int run_label(int B, int K, int V, float temperature, const void* P, bool p_bf16
   a.rowms = reinterpret_cast<float2*>(ws + off);
   off += align256((size_t)N * sizeof(float2));
   a.rpart = reinterpret_cast<float*>(ws + off);
-  off += align256(std::max((size_t)N * a.ns64 * sizeof(float), (size_t)label_jobs(N) * N * sizeof(double)));
+  off += align256(std::max((size_t)N * a.ns64 * sizeof(float), (size_t)label_jobs_max(N) * N * sizeof(double)));
   const uintptr_t pb = reinterpret_cast<uintptr_t>(P), db = reinterpret_cast<uintptr_t>(D);
   const bool vec_p = (pb % 16 == 0) && (V % (p_bf16 ? 8 : 4) == 0);
   const bool vec_d = (db % 16 == 0) && (V % (d_bf16 ? 8 : 4) == 0);
