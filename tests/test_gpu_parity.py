@@ -321,6 +321,31 @@ def test_verify_scheduled_prefixes(name, T):
     _say(str(rep) + " N=%d" % s["cu_seqlens"][-1])
 
 
+def test_verify_many_corrections_two_stages():
+    """More than 256 correcting requests with bf16 rows and a Markov head: the
+    residual pass's 256-request stages run twice, the second one partial.
+    Target rows independent of the draft make most requests reject early."""
+    w = wl().make("full_step", B=320, V=4096)
+    B, K, V = w.B, w.K, w.V
+    d = oracle.draft_ref(f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), 1.0, w.rng_seed, 0)
+    cu = np.arange(0, B * (K + 1) + 1, K + 1)
+    g = torch.Generator().manual_seed(4321)
+    P = (torch.randn((B * (K + 1), V), generator=g) * 3).to(torch.bfloat16)
+    n_acc, tok = ds().dspark_verify(P.to(DEV), torch.as_tensor(cu, dtype=torch.int32).to(DEV), w.U.to(DEV),
+                                    w.W1.to(DEV), w.W2.to(DEV), w.x0.to(DEV),
+                                    torch.as_tensor(d["x"], dtype=torch.int32).to(DEV),
+                                    torch.as_tensor(d["q_tok"], dtype=torch.float32).to(DEV),
+                                    torch.as_tensor(d["lse"], dtype=torch.float32).to(DEV), 1.0, w.rng_seed, 0)
+    torch.cuda.synchronize()
+    n_acc, tok = n_acc.cpu().numpy(), tok.cpu().numpy()
+    ref = oracle.verify_ref(f64(P), cu, f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), d["x"], 1.0, w.rng_seed, 0)
+    rep = Report("verify, %d corrections" % int((ref["n_acc"] < K).sum()))
+    compare_verify(rep, n_acc, tok, ref)
+    rep.check_near_ties()
+    _say(str(rep))
+    assert int((ref["n_acc"] < K).sum()) > 256  # the case this test is for
+
+
 def test_verify_edge_layouts():
     w = wl().make("tiny")
     d = oracle.draft_ref(f64(w.U), f64(w.W1), f64(w.W2).T, w.x0.numpy(), 1.0, w.rng_seed, 0)
