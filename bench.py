@@ -156,11 +156,14 @@ def main():
     prof_steps = min(args.steps, 10)
     ds.dspark_profiler_reset()
     ds.dspark_profiler_enable(True)
+    corr = []  # correcting requests of each profiled step (the residual pass's rows)
     for s in range(prof_steps):
         step(1000 + s)
+        corr.append((n_acc < sch["ell"]).sum())
     torch.cuda.synchronize()
     ds.dspark_profiler_enable(False)
     kt = ds.dspark_profiler_read()
+    n_corr = float(torch.stack(corr).float().mean().item())
     kernels = {k: {"launches": n, "mean_us": 1000.0 * ms / n} for k, (n, ms) in kt.items() if n}
 
     # cold caches: a 512 MB write between steps evicts U, W2 and the partials
@@ -222,6 +225,13 @@ def main():
         roof["verify_rowstats"] = {"bytes": vb, "mean_us": round(vus, 2),
                                    "GB/s": round(vb / (vus * 1e-6) / 1e9, 1),
                                    "frac": round(vb / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if "verify_residual" in kernels:
+        # the target and draft rows of the correcting requests, and W2 once
+        rb = n_corr * V * (P.element_size() + U.element_size()) + (V * r * 2 if r else 0)
+        rus = kernels["verify_residual"]["mean_us"]
+        roof["verify_residual"] = {"bytes": int(rb), "correcting_requests": round(n_corr, 1),
+                                   "mean_us": round(rus, 2), "GB/s": round(rb / (rus * 1e-6) / 1e9, 1),
+                                   "frac": round(rb / (rus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     next_rows = {} if args.no_next_rows else measure_next_rows(ds, w, x, lse, sch, ws_s, P, args, w2f)
 

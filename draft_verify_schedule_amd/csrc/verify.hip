@@ -712,8 +712,8 @@ __global__ __launch_bounds__(256) void verify_residual_kernel(VerifyArgs a) {
 // list and a range of 64-column blocks at run time, from the list length the
 // decide kernel left on the device.  G = 16 (bf16 Markov verification with
 // more than 128 requests): 256-request stages swept by one 8-wave workgroup
-// per CU, so each W2 block a wave loads serves twice the rows and a typical
-// list of a few hundred corrections is one stage.  Per request, the row offsets and the
+// per CU, so each W2 block a wave loads serves up to twice the rows and the
+// stage's W1 rows are gathered by half as many workgroups.  Per request, the row offsets and the
 // two log-normalisers sit in LDS; target and draft rows go through buffer
 // resources; each draft row seeds the MFMA accumulators, so the MFMAs leave
 // z = D + bias directly.
