@@ -774,6 +774,11 @@ void verify_residual_stream_kernel(VerifyArgs a) {
   constexpr bool SWZ = LABEL || ROWS;
   std::conditional_t<SWZ, W2SwzFrags, W2AnyFrags> wf;
   if constexpr (KC > 0) {
+    // the wave's first W2 block is requested before the stage's gather (it
+    // does not depend on it), so the two latencies overlap
+    if constexpr (SWZ) wf.setup(ROWS ? a.W2h : a.W2s, KC, a.V, lane);
+    else wf.setup(a.W2t, a.W2s, a.r, a.V, lane);
+    if (blk_begin + wave < blk_end) wf.template load<KC>((blk_begin + wave) * kWaveCols, w2);
     const int32_t* list = a.rej_list;
     const int4* info = a.info;
     const int32_t* x0 = a.x0;
@@ -793,8 +798,6 @@ void verify_residual_stream_kernel(VerifyArgs a) {
         return in.w == 0 ? x0[r] : x[(size_t)r * K + in.w - 1];
       });
     }
-    if constexpr (SWZ) wf.setup(ROWS ? a.W2h : a.W2s, KC, a.V, lane);
-    else wf.setup(a.W2t, a.W2s, a.r, a.V, lane);
   }
   __syncthreads();
 
@@ -853,7 +856,7 @@ void verify_residual_stream_kernel(VerifyArgs a) {
     const int cbase = blk * kWaveCols + (int)lane_col;
     const uint32_t pcol = (uint32_t)cbase * sizeof(PT), dcol = (uint32_t)cbase * sizeof(DT);
     if constexpr (KC > 0) {
-      if (!PF || first) wf.template load<KC>(blk * kWaveCols, w2);
+      if (!PF && !first) wf.template load<KC>(blk * kWaveCols, w2);  // the first block's was requested above
     }
     const int e_off = launder(e_lane_offset<(KC > 0 ? KC : 1), ROWS>(lane));
     // one group in the MFMA layout: the draft rows seed the accumulators, the
